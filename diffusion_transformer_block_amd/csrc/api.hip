@@ -1,0 +1,703 @@
+// C ABI of the block-stage library: argument validation, packed-weight and
+// workspace layouts, the block driver and the graph-captured denoise loop.
+// The meaning of every entry point is documented in include/blk.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/blk.h"
+#include "common.h"
+#include "internal.h"
+
+using namespace blk;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(BLK_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// ---------------------------------------------------------------- validation
+int check_config(const blk_config* c) {
+  if (!c) return fail(BLK_EINVAL, "cfg is NULL");
+  if (c->hidden <= 0 || c->ffn <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
+      c->head_dim <= 0 || c->max_pos <= 0)
+    return fail(BLK_EINVAL, "cfg has a non-positive size");
+  if (!std::isfinite(c->rope_base) || c->rope_base <= 0.f)
+    return fail(BLK_EINVAL, "rope_base must be finite and > 0");
+  if (!std::isfinite(c->rms_eps) || c->rms_eps < 0.f)
+    return fail(BLK_EINVAL, "rms_eps must be finite and >= 0");
+  const int d = c->head_dim;
+  if (d != 64 && d != 128 && d != 256)
+    return fail(BLK_EUNSUPPORTED, "head_dim %d not in {64, 128, 256}", d);
+  if (c->hidden % 128 != 0 || c->hidden > 16384)
+    return fail(BLK_EUNSUPPORTED, "hidden %d must be a multiple of 128 and <= 16384", c->hidden);
+  if (c->ffn % 64 != 0 || c->ffn > 65536)
+    return fail(BLK_EUNSUPPORTED, "ffn %d must be a multiple of 64 and <= 65536", c->ffn);
+  if (c->n_q_heads % c->n_kv_heads != 0)
+    return fail(BLK_EUNSUPPORTED, "n_q_heads %d is not a multiple of n_kv_heads %d",
+                c->n_q_heads, c->n_kv_heads);
+  if ((c->n_q_heads * d) % 128 != 0 || ((c->n_q_heads + 2 * c->n_kv_heads) * d) % 128 != 0)
+    return fail(BLK_EUNSUPPORTED, "Hq*d and (Hq+2Hkv)*d must be multiples of 128");
+  if (c->max_pos > (1 << 20)) return fail(BLK_EUNSUPPORTED, "max_pos > 2^20");
+  return BLK_OK;
+}
+
+// ---------------------------------------------------------------- packed layout
+struct Layout {
+  size_t rope_cos = 0, rope_sin = 0;
+  size_t layer0 = 0, layer_bytes = 0;
+  size_t wqkv = 0, wo = 0, wgu = 0, wd = 0;  // offsets inside a layer
+  bool has_head = false;
+  size_t h_wfused = 0, h_table = 0, h_dt = 0, h_w3 = 0, h_b3 = 0, h_ws = 0, h_bs = 0,
+         h_wout = 0, h_bout = 0;
+  size_t total = 0;
+  int n_layers = 0, n_steps = 0, n_actions = 0, action_dim = 0;
+};
+
+Layout make_layout(const blk_config& c, int n_layers, bool head, int n_steps, int N, int A) {
+  Layout L;
+  const size_t D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  size_t off = 0;
+  L.rope_cos = off;
+  off += align_up((size_t)c.max_pos * (d / 2) * 4);
+  L.rope_sin = off;
+  off += align_up((size_t)c.max_pos * (d / 2) * 4);
+  L.layer0 = off;
+  size_t lo = 0;
+  L.wqkv = lo;
+  lo += align_up(D * (Hq + 2 * Hkv) * d * 2);
+  L.wo = lo;
+  lo += align_up(Hq * d * D * 2);
+  L.wgu = lo;
+  lo += align_up(D * 2 * F * 2);
+  L.wd = lo;
+  lo += align_up(F * D * 2);
+  L.layer_bytes = lo;
+  off += (size_t)n_layers * lo;
+  L.n_layers = n_layers;
+  if (head) {
+    L.has_head = true;
+    L.n_steps = n_steps;
+    L.n_actions = N;
+    L.action_dim = A;
+    L.h_wfused = off;
+    off += align_up((size_t)A * D * 4);
+    L.h_table = off;
+    off += align_up((size_t)n_steps * D * 4);
+    L.h_dt = off;
+    off += align_up((size_t)n_steps * 4);
+    L.h_w3 = off;
+    off += align_up(D * D * 2);
+    L.h_b3 = off;
+    off += align_up(D * 4);
+    L.h_ws = off;
+    off += align_up((size_t)A * D * 4);
+    L.h_bs = off;
+    off += align_up(D * 4);
+    L.h_wout = off;
+    off += align_up(D * (size_t)A * 4);
+    L.h_bout = off;
+    off += align_up((size_t)A * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+struct PackRecord {
+  blk_config cfg;
+  Layout lay;
+};
+
+std::mutex g_mu;
+std::map<const void*, PackRecord> g_packs;
+
+bool same_cfg(const blk_config& a, const blk_config& b) {
+  return a.hidden == b.hidden && a.ffn == b.ffn && a.n_q_heads == b.n_q_heads &&
+         a.n_kv_heads == b.n_kv_heads && a.head_dim == b.head_dim && a.max_pos == b.max_pos &&
+         a.rope_base == b.rope_base && a.rms_eps == b.rms_eps;
+}
+
+int lookup(const void* packed, const blk_config& cfg, PackRecord* out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_packs.find(packed);
+  if (it == g_packs.end())
+    return fail(BLK_ESTATE, "packed buffer %p was not prepared by blk_prepare_weights", packed);
+  if (!same_cfg(it->second.cfg, cfg))
+    return fail(BLK_ESTATE, "cfg differs from the one the packed buffer was prepared with");
+  *out = it->second;
+  return BLK_OK;
+}
+
+// ---------------------------------------------------------------- workspace layout
+struct BlockWs {
+  size_t q, o, h, a, r1, r2, part, ss, att_o, att_ml;
+  size_t ctr_qkv, ctr_o, ctr_gu, ctr_d, ctr_att;
+  size_t total;
+};
+
+BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
+                        size_t extra_part = 0) {
+  BlockWs w;
+  const size_t M = (size_t)B * T;
+  const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const int gq = (Hq + 2 * Hkv) * d / 32, go = D / 32, ggu = F / 16, gd = D / 32;
+  size_t off = base;
+  w.q = off;
+  off += align_up(M * Hq * d * 2);
+  w.o = off;
+  off += align_up(M * Hq * d * 2);
+  w.h = off;
+  off += align_up(M * D * 2);
+  w.a = off;
+  off += align_up(M * F * 2);
+  w.r1 = off;
+  off += align_up(M * 4);
+  w.r2 = off;
+  off += align_up(M * 4);
+  size_t part = 0, ss = 0;
+  if ((int)M <= kSkinnyMaxM && M > 0) {
+    const int m = (int)M;
+    part = std::max(std::max(skinny_part_floats(m, D, gq), skinny_part_floats(m, Hq * d, go)),
+                    std::max(skinny_part_floats(m, D, ggu), skinny_part_floats(m, F, gd)));
+    ss = std::max(std::max(skinny_ss_floats(m, D, gq), skinny_ss_floats(m, Hq * d, go)),
+                  std::max(skinny_ss_floats(m, D, ggu), skinny_ss_floats(m, F, gd)));
+  }
+  part = std::max(part, extra_part);
+  w.part = off;
+  off += align_up(part * 4);
+  w.ss = off;
+  off += align_up(ss * 4);
+  w.att_o = off;
+  off += align_up(attn_part_o_floats(B, T, P, Hq, Hkv, d) * 4);
+  w.att_ml = off;
+  off += align_up(attn_part_ml_floats(B, T, P, Hq, Hkv, d) * 4);
+  w.ctr_qkv = off;
+  off += align_up((size_t)gq * 4);
+  w.ctr_o = off;
+  off += align_up((size_t)go * 4);
+  w.ctr_gu = off;
+  off += align_up((size_t)ggu * 4);
+  w.ctr_d = off;
+  off += align_up((size_t)gd * 4);
+  w.ctr_att = off;
+  off += align_up(attn_counters(B, T, P, Hq, Hkv, d) * 4);
+  w.total = off;
+  return w;
+}
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
+}
+template <class T>
+const T* at(const void* base, size_t off) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
+}
+
+// ---------------------------------------------------------------- block driver
+struct BlockIO {
+  const bf16_t* x;
+  const bf16_t* kp;
+  const bf16_t* vp;
+  int64_t prefix_stride;
+  bf16_t* y;
+  bf16_t* kn;
+  bf16_t* vn;
+  int64_t new_stride;
+};
+
+void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, int layer, int B,
+                   int T, int P, const BlockIO& io, void* ws, const BlockWs& w, hipStream_t st) {
+  const int M = B * T;
+  const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const uint8_t* lw = at<uint8_t>(packed, lay.layer0 + (size_t)layer * lay.layer_bytes);
+  const bool skinny = M <= kSkinnyMaxM;
+  bf16_t* q = at<bf16_t>(ws, w.q);
+  bf16_t* o = at<bf16_t>(ws, w.o);
+  bf16_t* h = at<bf16_t>(ws, w.h);
+  bf16_t* a = at<bf16_t>(ws, w.a);
+  float* r1 = at<float>(ws, w.r1);
+  float* r2 = at<float>(ws, w.r2);
+
+  GemmArgs base{};
+  base.M = M;
+  base.eps = c.rms_eps;
+  base.part = at<float>(ws, w.part);
+  base.ss_part = at<float>(ws, w.ss);
+
+  // 1. RMS(x) -> fused QKV GEMM with row scale and RoPE epilogue
+  {
+    GemmArgs ga = base;
+    ga.A = io.x;
+    ga.lda = D;
+    ga.K = D;
+    ga.Bp = lw + lay.wqkv;
+    ga.n_groups = (Hq + 2 * Hkv) * d / 32;
+    ga.counters = at<unsigned>(ws, w.ctr_qkv);
+    if (skinny) {
+      ga.rms_fused = 1;
+    } else {
+      launch_rms_rows(io.x, M, D, c.rms_eps, r1, st);
+      ga.r = r1;
+    }
+    EpiQKV e{q, io.kn, io.vn, io.new_stride, at<float>(packed, lay.rope_cos),
+             at<float>(packed, lay.rope_sin), T, P, Hq, Hkv, d};
+    launch_gemm_qkv(ga, e, st);
+  }
+  // 2. attention over [prefix ; own]
+  {
+    AttnArgs aa{};
+    aa.q = q;
+    aa.kp = io.kp;
+    aa.vp = io.vp;
+    aa.prefix_stride = io.prefix_stride;
+    aa.kn = io.kn;
+    aa.vn = io.vn;
+    aa.new_stride = io.new_stride;
+    aa.o = o;
+    aa.B = B;
+    aa.T = T;
+    aa.P = P;
+    aa.Hq = Hq;
+    aa.Hkv = Hkv;
+    aa.d = d;
+    attn_plan(B, T, P, Hq, Hkv, d, &aa.splits, &aa.keys_per_split);
+    aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    aa.part_o = at<float>(ws, w.att_o);
+    aa.part_ml = at<float>(ws, w.att_ml);
+    aa.counters = at<unsigned>(ws, w.ctr_att);
+    launch_attention(aa, st);
+  }
+  // 3. h = x + O W_o
+  {
+    GemmArgs ga = base;
+    ga.A = o;
+    ga.lda = Hq * d;
+    ga.K = Hq * d;
+    ga.Bp = lw + lay.wo;
+    ga.n_groups = D / 32;
+    ga.counters = at<unsigned>(ws, w.ctr_o);
+    launch_gemm_residual(ga, EpiResidual{io.x, h, D}, st);
+  }
+  // 4. RMS(h) -> gate/up GEMM with SiLU(gate) * up epilogue
+  {
+    GemmArgs ga = base;
+    ga.A = h;
+    ga.lda = D;
+    ga.K = D;
+    ga.Bp = lw + lay.wgu;
+    ga.n_groups = F / 16;
+    ga.counters = at<unsigned>(ws, w.ctr_gu);
+    if (skinny) {
+      ga.rms_fused = 1;
+    } else {
+      launch_rms_rows(h, M, D, c.rms_eps, r2, st);
+      ga.r = r2;
+    }
+    launch_gemm_gateup(ga, EpiGateUp{a, F}, st);
+  }
+  // 5. y = h + a W_d
+  {
+    GemmArgs ga = base;
+    ga.A = a;
+    ga.lda = F;
+    ga.K = F;
+    ga.Bp = lw + lay.wd;
+    ga.n_groups = D / 32;
+    ga.counters = at<unsigned>(ws, w.ctr_d);
+    launch_gemm_residual(ga, EpiResidual{h, io.y, D}, st);
+  }
+}
+
+// ---------------------------------------------------------------- flow workspace + driver
+struct FlowWs {
+  BlockWs blk;
+  size_t x0, x1, z, kn, vn, total;
+};
+
+FlowWs flow_ws_layout(const blk_config& c, int N, int P) {
+  FlowWs f;
+  const int T = N + 1;
+  const size_t D = c.hidden;
+  size_t off = 0;
+  f.x0 = off;
+  off += align_up((size_t)T * D * 2);
+  f.x1 = off;
+  off += align_up((size_t)T * D * 2);
+  f.z = off;
+  off += align_up((size_t)N * D * 2);
+  f.kn = off;
+  off += align_up((size_t)T * c.n_kv_heads * c.head_dim * 2);
+  f.vn = off;
+  off += align_up((size_t)T * c.n_kv_heads * c.head_dim * 2);
+  // the embedding's W3 GEMM (N rows, K = D, D/32 groups) shares the split-K scratch
+  f.blk = block_ws_layout(c, 1, T, P, off, skinny_part_floats(N, (int)D, (int)D / 32));
+  f.total = f.blk.total;
+  return f;
+}
+
+void enqueue_flow(const blk_config& c, const Layout& lay, const void* packed, int n_layers,
+                  int n_steps, int P, const uint16_t* const* kp, const uint16_t* const* vp,
+                  const float* noise, const float* state, float* actions, void* ws,
+                  const FlowWs& fw, hipStream_t st) {
+  const int N = lay.n_actions, A = lay.action_dim, D = c.hidden, T = N + 1;
+  bf16_t* X[2] = {at<bf16_t>(ws, fw.x0), at<bf16_t>(ws, fw.x1)};
+  bf16_t* z = at<bf16_t>(ws, fw.z);
+  for (int s = 0; s < n_steps; ++s) {
+    const float* a_in = s == 0 ? noise : actions;
+    FlowEmbedArgs ea{a_in,
+                     state,
+                     at<float>(packed, lay.h_wfused),
+                     at<float>(packed, lay.h_table) + (size_t)s * D,
+                     at<float>(packed, lay.h_ws),
+                     at<float>(packed, lay.h_bs),
+                     z,
+                     X[0],
+                     N,
+                     A,
+                     D};
+    launch_flow_embed(ea, st);
+    GemmArgs ga{};
+    ga.A = z;
+    ga.lda = D;
+    ga.M = N;
+    ga.K = D;
+    ga.Bp = at<uint8_t>(packed, lay.h_w3);
+    ga.n_groups = D / 32;
+    ga.part = at<float>(ws, fw.blk.part);
+    ga.ss_part = at<float>(ws, fw.blk.ss);
+    ga.counters = at<unsigned>(ws, fw.blk.ctr_o);  // W3 is D x D like W_o's group count
+    launch_gemm_bias(ga, EpiBias{at<float>(packed, lay.h_b3), X[0], D, 1}, st);
+    int cur = 0;
+    for (int l = 0; l < n_layers; ++l) {
+      BlockIO io{X[cur],  kp[l],  vp[l], 0, X[cur ^ 1], at<bf16_t>(ws, fw.kn),
+                 at<bf16_t>(ws, fw.vn), 0};
+      enqueue_block(c, lay, packed, l, 1, T, P, io, ws, fw.blk, st);
+      cur ^= 1;
+    }
+    FlowVelArgs va{X[cur],
+                   at<float>(packed, lay.h_wout),
+                   at<float>(packed, lay.h_bout),
+                   a_in,
+                   actions,
+                   at<float>(packed, lay.h_dt) + s,
+                   N,
+                   A,
+                   D,
+                   c.rms_eps};
+    launch_flow_velocity(va, st);
+  }
+}
+
+// ---------------------------------------------------------------- graph cache
+struct GraphKey {
+  int device;
+  const void* packed;
+  int n_layers, n_steps, P;
+  std::vector<const void*> ptrs;
+  blk_config cfg;
+  bool operator<(const GraphKey& o) const {
+    if (device != o.device) return device < o.device;
+    if (packed != o.packed) return packed < o.packed;
+    if (n_layers != o.n_layers) return n_layers < o.n_layers;
+    if (n_steps != o.n_steps) return n_steps < o.n_steps;
+    if (P != o.P) return P < o.P;
+    if (ptrs != o.ptrs) return ptrs < o.ptrs;
+    return std::memcmp(&cfg, &o.cfg, sizeof cfg) < 0;
+  }
+};
+
+struct GraphEntry {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+std::mutex g_graph_mu;
+std::map<GraphKey, GraphEntry> g_graphs;
+constexpr size_t kMaxGraphs = 16;
+
+void destroy_entry(GraphEntry& e) {
+  if (e.exec) (void)hipGraphExecDestroy(e.exec);
+  if (e.graph) (void)hipGraphDestroy(e.graph);
+  e.exec = nullptr;
+  e.graph = nullptr;
+}
+
+}  // namespace
+
+// ============================================================================ exports
+extern "C" {
+
+const char* blk_last_error(void) { return g_err.c_str(); }
+
+int blk_version(void) { return 1; }
+
+void blk_release(void) {
+  {
+    std::lock_guard<std::mutex> lk(g_graph_mu);
+    for (auto& kv : g_graphs) destroy_entry(kv.second);
+    g_graphs.clear();
+  }
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_packs.clear();
+}
+
+int blk_prepare_weights(const blk_config* cfg, const blk_layer_src* layers, int n_layers,
+                        const blk_flow_head_src* head, const double* t_schedule, int n_steps,
+                        void* dst, size_t* bytes, void* stream) {
+  g_err.clear();
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!bytes) return fail(BLK_EINVAL, "bytes is NULL");
+  if (n_layers < 0) return fail(BLK_EINVAL, "n_layers < 0");
+  if (n_layers > 0 && !layers) return fail(BLK_EINVAL, "layers is NULL");
+  int N = 0, A = 0;
+  if (head) {
+    N = head->n_actions;
+    A = head->action_dim;
+    if (N <= 0 || N + 1 > kSkinnyMaxM)
+      return fail(BLK_EUNSUPPORTED, "n_actions %d must be in [1, %d]", N, kSkinnyMaxM - 1);
+    if (A <= 0 || A > 64) return fail(BLK_EUNSUPPORTED, "action_dim %d must be in [1, 64]", A);
+    if (cfg->hidden > 8192) return fail(BLK_EUNSUPPORTED, "flow head needs hidden <= 8192");
+    if (n_steps <= 0 || n_steps > kMaxSteps)
+      return fail(BLK_EUNSUPPORTED, "n_steps %d must be in [1, %d]", n_steps, kMaxSteps);
+    if (!t_schedule) return fail(BLK_EINVAL, "t_schedule is NULL");
+    for (int s = 0; s < n_steps; ++s)
+      if (!std::isfinite(t_schedule[s])) return fail(BLK_EINVAL, "t_schedule[%d] is not finite", s);
+    const void* hp[] = {head->w1, head->b1, head->w2, head->b2, head->w3, head->b3, head->ws,
+                        head->bs, head->g_f, head->w_out, head->b_out};
+    for (const void* p : hp)
+      if (!p) return fail(BLK_EINVAL, "a flow head pointer is NULL");
+  }
+  const Layout lay = make_layout(*cfg, n_layers, head != nullptr, n_steps, N, A);
+  if (!dst) {
+    *bytes = lay.total;
+    return BLK_OK;
+  }
+  if (*bytes < lay.total)
+    return fail(BLK_ESIZE, "dst has %zu bytes, %zu needed", *bytes, lay.total);
+  for (int l = 0; l < n_layers; ++l) {
+    const blk_layer_src& s = layers[l];
+    const void* lp[] = {s.g_attn, s.w_q, s.w_k, s.w_v, s.w_o, s.g_ffn, s.w_gate, s.w_up, s.w_down};
+    for (const void* p : lp)
+      if (!p) return fail(BLK_EINVAL, "layer %d has a NULL pointer", l);
+  }
+
+  hipStream_t st = (hipStream_t)stream;
+  const blk_config& c = *cfg;
+  const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  uint8_t* base = reinterpret_cast<uint8_t*>(dst);
+  (void)hipGetLastError();
+  launch_rope_table(c.max_pos, d / 2, (double)c.rope_base, at<float>(dst, lay.rope_cos),
+                    at<float>(dst, lay.rope_sin), st);
+  for (int l = 0; l < n_layers; ++l) {
+    const blk_layer_src& s = layers[l];
+    uint8_t* lw = base + lay.layer0 + (size_t)l * lay.layer_bytes;
+    {
+      PackSrc ps{{(const bf16_t*)s.w_q, (const bf16_t*)s.w_k, (const bf16_t*)s.w_v},
+                 {Hq * d, Hkv * d, Hkv * d},
+                 3,
+                 s.g_attn};
+      ColMapArgs cm{kColRopePairs, d, (Hq + Hkv) * d, 0};
+      launch_pack_frag(ps, cm, D, (Hq + 2 * Hkv) * d / 32, lw + lay.wqkv, st);
+    }
+    {
+      PackSrc ps{{(const bf16_t*)s.w_o, nullptr, nullptr}, {D, 0, 0}, 1, nullptr};
+      ColMapArgs cm{kColPlain, d, 0, 0};
+      launch_pack_frag(ps, cm, Hq * d, D / 32, lw + lay.wo, st);
+    }
+    {
+      PackSrc ps{{(const bf16_t*)s.w_gate, (const bf16_t*)s.w_up, nullptr}, {F, F, 0}, 2, s.g_ffn};
+      ColMapArgs cm{kColGateUp, d, 0, F};
+      launch_pack_frag(ps, cm, D, F / 16, lw + lay.wgu, st);
+    }
+    {
+      PackSrc ps{{(const bf16_t*)s.w_down, nullptr, nullptr}, {D, 0, 0}, 1, nullptr};
+      ColMapArgs cm{kColPlain, d, 0, 0};
+      launch_pack_frag(ps, cm, F, D / 32, lw + lay.wd, st);
+    }
+  }
+  if (head) {
+    launch_fold_action((const bf16_t*)head->w1, (const bf16_t*)head->w2, A, D,
+                       at<float>(dst, lay.h_wfused), st);
+    Schedule sched{};
+    sched.n = n_steps;
+    for (int s = 0; s < n_steps; ++s) sched.t[s] = t_schedule[s];
+    launch_fold_time(head->b1, (const bf16_t*)head->w2, head->b2, D, sched,
+                     at<float>(dst, lay.h_table), at<float>(dst, lay.h_dt), st);
+    PackSrc ps{{(const bf16_t*)head->w3, nullptr, nullptr}, {D, 0, 0}, 1, nullptr};
+    ColMapArgs cm{kColPlain, d, 0, 0};
+    launch_pack_frag(ps, cm, D, D / 32, base + lay.h_w3, st);
+    launch_copy_f32(head->b3, D, at<float>(dst, lay.h_b3), st);
+    launch_widen((const bf16_t*)head->ws, nullptr, D, (size_t)A * D, at<float>(dst, lay.h_ws), st);
+    launch_copy_f32(head->bs, D, at<float>(dst, lay.h_bs), st);
+    launch_widen((const bf16_t*)head->w_out, head->g_f, A, (size_t)D * A,
+                 at<float>(dst, lay.h_wout), st);
+    launch_copy_f32(head->b_out, A, at<float>(dst, lay.h_bout), st);
+  }
+  HIP_TRY(hipGetLastError());
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_packs[dst] = PackRecord{c, lay};
+  return BLK_OK;
+}
+
+int blk_forward(const blk_config* cfg, const void* packed, int layer, int batch, int tokens,
+                int prefix, const uint16_t* x, const uint16_t* k_prefix,
+                const uint16_t* v_prefix, int64_t prefix_stride, uint16_t* y, uint16_t* k_new,
+                uint16_t* v_new, int64_t new_stride, void* ws, size_t* ws_bytes, void* stream) {
+  g_err.clear();
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!ws_bytes) return fail(BLK_EINVAL, "ws_bytes is NULL");
+  if (batch < 0 || tokens < 0 || prefix < 0) return fail(BLK_EINVAL, "negative batch/tokens/prefix");
+  if ((long)prefix + tokens > cfg->max_pos)
+    return fail(BLK_EUNSUPPORTED, "prefix + tokens = %ld exceeds max_pos %d",
+                (long)prefix + tokens, cfg->max_pos);
+  if ((long)batch * tokens > (1L << 24)) return fail(BLK_EUNSUPPORTED, "batch * tokens too large");
+  const BlockWs w = block_ws_layout(*cfg, batch, tokens, prefix, 0);
+  if (!ws) {
+    *ws_bytes = w.total;
+    return BLK_OK;
+  }
+  if (*ws_bytes < w.total) return fail(BLK_ESIZE, "ws has %zu bytes, %zu needed", *ws_bytes, w.total);
+  if (!packed) return fail(BLK_EINVAL, "packed is NULL");
+  PackRecord rec;
+  rc = lookup(packed, *cfg, &rec);
+  if (rc) return rc;
+  if (layer < 0 || layer >= rec.lay.n_layers)
+    return fail(BLK_EINVAL, "layer %d out of range [0, %d)", layer, rec.lay.n_layers);
+  if (batch == 0 || tokens == 0) return BLK_OK;
+  if (!x || !y || !k_new || !v_new) return fail(BLK_EINVAL, "x, y, k_new and v_new must be non-NULL");
+  if (prefix > 0 && (!k_prefix || !v_prefix)) return fail(BLK_EINVAL, "prefix K/V is NULL with prefix > 0");
+  const int64_t kvrow = (int64_t)cfg->n_kv_heads * cfg->head_dim;
+  if (batch > 1) {
+    if (prefix > 0 && prefix_stride < (int64_t)prefix * kvrow)
+      return fail(BLK_EINVAL, "prefix_stride smaller than one stream's prefix");
+    if (new_stride < (int64_t)tokens * kvrow)
+      return fail(BLK_EINVAL, "new_stride smaller than one stream's tokens");
+  }
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  BlockIO io{x, k_prefix, v_prefix, prefix_stride, y, k_new, v_new, new_stride};
+  enqueue_block(*cfg, rec.lay, packed, layer, batch, tokens, prefix, io, ws, w, st);
+  HIP_TRY(hipGetLastError());
+  return BLK_OK;
+}
+
+int flow_denoise(const blk_config* cfg, const void* packed, int n_layers, int n_steps, int prefix,
+                 const uint16_t* const* k_prefix, const uint16_t* const* v_prefix,
+                 const float* noise, const float* state, float* actions, void* ws,
+                 size_t* ws_bytes, void* stream) {
+  g_err.clear();
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!ws_bytes) return fail(BLK_EINVAL, "ws_bytes is NULL");
+  if (!packed) return fail(BLK_EINVAL, "packed is NULL");
+  if (prefix < 0 || n_layers <= 0 || n_steps <= 0)
+    return fail(BLK_EINVAL, "prefix must be >= 0, n_layers and n_steps > 0");
+  PackRecord rec;
+  rc = lookup(packed, *cfg, &rec);
+  if (rc) return rc;
+  const Layout& lay = rec.lay;
+  if (!lay.has_head) return fail(BLK_ESTATE, "packed buffer has no flow head");
+  if (n_steps != lay.n_steps)
+    return fail(BLK_ESTATE, "n_steps %d differs from the prepared schedule's %d", n_steps, lay.n_steps);
+  if (n_layers > lay.n_layers)
+    return fail(BLK_EINVAL, "n_layers %d exceeds the %d prepared layers", n_layers, lay.n_layers);
+  const int T = lay.n_actions + 1;
+  if ((long)prefix + T > cfg->max_pos)
+    return fail(BLK_EUNSUPPORTED, "prefix + %d tokens exceeds max_pos %d", T, cfg->max_pos);
+  const FlowWs fw = flow_ws_layout(*cfg, lay.n_actions, prefix);
+  if (!ws) {
+    *ws_bytes = fw.total;
+    return BLK_OK;
+  }
+  if (*ws_bytes < fw.total) return fail(BLK_ESIZE, "ws has %zu bytes, %zu needed", *ws_bytes, fw.total);
+  if (!noise || !state || !actions) return fail(BLK_EINVAL, "noise, state and actions must be non-NULL");
+  if (prefix > 0) {
+    if (!k_prefix || !v_prefix) return fail(BLK_EINVAL, "k_prefix / v_prefix arrays are NULL");
+    for (int l = 0; l < n_layers; ++l)
+      if (!k_prefix[l] || !v_prefix[l]) return fail(BLK_EINVAL, "prefix pointer of layer %d is NULL", l);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  GraphKey key;
+  key.device = dev;
+  key.packed = packed;
+  key.n_layers = n_layers;
+  key.n_steps = n_steps;
+  key.P = prefix;
+  key.cfg = *cfg;
+  for (int l = 0; l < n_layers; ++l) {
+    key.ptrs.push_back(prefix > 0 ? k_prefix[l] : nullptr);
+    key.ptrs.push_back(prefix > 0 ? v_prefix[l] : nullptr);
+  }
+  key.ptrs.push_back(noise);
+  key.ptrs.push_back(state);
+  key.ptrs.push_back(actions);
+  key.ptrs.push_back(ws);
+
+  std::lock_guard<std::mutex> lk(g_graph_mu);
+  auto it = g_graphs.find(key);
+  if (it == g_graphs.end()) {
+    if (g_graphs.size() >= kMaxGraphs) {
+      destroy_entry(g_graphs.begin()->second);
+      g_graphs.erase(g_graphs.begin());
+    }
+    std::vector<const uint16_t*> kp(n_layers, nullptr), vp(n_layers, nullptr);
+    for (int l = 0; l < n_layers && prefix > 0; ++l) {
+      kp[l] = k_prefix[l];
+      vp[l] = v_prefix[l];
+    }
+    hipStream_t cs = nullptr;
+    HIP_TRY(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+    GraphEntry e;
+    (void)hipGetLastError();
+    hipError_t err = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (err == hipSuccess) {
+      enqueue_flow(*cfg, lay, packed, n_layers, n_steps, prefix, kp.data(), vp.data(), noise,
+                   state, actions, ws, fw, cs);
+      hipError_t launch_err = hipGetLastError();
+      err = hipStreamEndCapture(cs, &e.graph);
+      if (err == hipSuccess) err = launch_err;
+    }
+    if (err == hipSuccess) err = hipGraphInstantiate(&e.exec, e.graph, nullptr, nullptr, 0);
+    (void)hipStreamDestroy(cs);
+    if (err != hipSuccess) {
+      destroy_entry(e);
+      return fail(BLK_EHIP, "graph capture of the denoise loop failed: %s", hipGetErrorString(err));
+    }
+    it = g_graphs.emplace(key, e).first;
+  }
+  HIP_TRY(hipGraphLaunch(it->second.exec, st));
+  return BLK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Shared device-side definitions for the block-stage kernels (gfx950 / CDNA4).
+//
+// Storage types: bf16 is carried as its 16-bit pattern (uint16_t); fp32 for
+// gains, statistics, tables and accumulators.  MFMA operands are 8 x bf16 per
+// lane (16 bytes), the operand width of v_mfma_f32_16x16x32_bf16.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace blk {
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// float -> bf16, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 16-byte streaming load (read once: weights).
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// ---------------------------------------------------------------- packed weight fragments
+//
+// A weight matrix W [K x N] ([in, out], row-major) is stored as MFMA B-operand
+// fragments.  Columns are taken in groups of 32 (two 16-column tiles); which
+// logical columns form a group depends on the matrix (see col_of_group below).
+// Fragment (group g, k-tile kt, tile i) holds W[32 kt + 8 (l/16) + e][col(g,i) + l%16]
+// for lane l < 64, element e < 8, as 16 contiguous bytes at lane offset 16 l.
+// Fragments are ordered [g][kt][i], 1 KiB each, so one wave reads one
+// fragment with a single fully-coalesced 16-byte-per-lane load and the two
+// tiles of a group over consecutive k-tiles are contiguous.
+constexpr int kFragBytes = 1024;
+
+__host__ __device__ inline size_t frag_offset(int g, int kt, int i, int KT) {
+  return ((size_t)(g * KT + kt) * 2 + i) * kFragBytes;
+}
+
+// Column maps from a group index to the logical column of each of its tiles.
+enum ColMap : int {
+  kColPlain = 0,    // group g = columns [32g, 32g + 32)
+  kColRopePairs = 1,// fused QKV: rotated heads pair column j with j + d/2 in one group
+  kColGateUp = 2,   // fused gate/up: tile 0 = gate columns, tile 1 = up columns
+};
+
+struct ColMapArgs {
+  int mode;
+  int head_dim;   // kColRopePairs
+  int n_rot;      // kColRopePairs: number of rotated columns ((Hq + Hkv) d)
+  int half_n;     // kColGateUp: F (gate columns precede up columns)
+};
+
+// Logical column (in the concatenated source matrix) of tile i's first column.
+__host__ __device__ inline int col_of_group(const ColMapArgs& m, int g, int i) {
+  if (m.mode == kColRopePairs) {
+    int gpr = m.head_dim / 32;            // groups per rotated head
+    int n_rot_groups = m.n_rot / 32;
+    if (g < n_rot_groups) {
+      int head = g / gpr, t = g % gpr;
+      return head * m.head_dim + 16 * t + i * (m.head_dim / 2);
+    }
+    return m.n_rot + 32 * (g - n_rot_groups) + 16 * i;
+  }
+  if (m.mode == kColGateUp) return i == 0 ? 16 * g : m.half_n + 16 * g;
+  return 32 * g + 16 * i;
+}
+
+}  // namespace blk

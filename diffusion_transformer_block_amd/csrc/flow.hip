@@ -1,0 +1,88 @@
+// Flow-matching head of the action expert: suffix embedding ahead of the
+// layer stack and velocity + Euler update behind it.
+//
+// [RT] reading note on "Running VLAs at Real-time Speed" (Ma et al.,
+// arXiv:2510.26742v1): §2 -- 63 action tokens plus the state token, actions
+// padded to 32 dims, 10 flow-matching steps; §4.2 -- the action projection
+// and the linear after the [action, time] concatenation are pre-multiplied
+// (W_fused = W1 W2a) and the time branch at the fixed timesteps is a table
+// folded into the bias ahead of SiLU.  The linear after SiLU (W3) runs as a
+// skinny MFMA GEMM with a bias epilogue; these two kernels are the small
+// float32 pieces around it.
+#include "common.h"
+#include "internal.h"
+
+namespace blk {
+
+// Block (row, column tile): rows 0..N-1 -> z[row] = SiLU(a[row] W_fused + bias);
+// row N -> X row 0 = state Ws + bs (the state token, constant over steps but
+// recomputed here so the loop needs no other kernel).
+__global__ __launch_bounds__(256) void flow_embed_kernel(FlowEmbedArgs a) {
+  __shared__ float vin[64];
+  const int row = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const bool state_row = row == a.N;
+  if (threadIdx.x < a.A)
+    vin[threadIdx.x] = state_row ? a.state[threadIdx.x] : a.act[(size_t)row * a.A + threadIdx.x];
+  __syncthreads();
+  if (n >= a.D) return;
+  if (state_row) {
+    float acc = a.bs[n];
+    for (int k = 0; k < a.A; ++k) acc = fmaf(vin[k], a.ws[(size_t)k * a.D + n], acc);
+    a.x0[n] = f2bf(acc);
+  } else {
+    float acc = a.bias_row[n];
+    for (int k = 0; k < a.A; ++k) acc = fmaf(vin[k], a.w_fused[(size_t)k * a.D + n], acc);
+    a.z[(size_t)row * a.D + n] = f2bf(silu(acc));
+  }
+}
+
+void launch_flow_embed(const FlowEmbedArgs& a, hipStream_t st) {
+  flow_embed_kernel<<<dim3((a.D + 255) / 256, a.N + 1), 256, 0, st>>>(a);
+}
+
+// One block per action row i: r = RMS(X[i + 1]); v[a] = r sum_k X[i+1][k] W_out'[k][a]
+// + b_out[a]; a_out[i][a] = a_in[i][a] + dt v[a].  256 threads = (A columns)
+// x (256 / A) slices of k, reduced through LDS in a fixed order.
+__global__ __launch_bounds__(256) void flow_velocity_kernel(FlowVelArgs a) {
+  __shared__ float xs[8192];
+  __shared__ float red[256];
+  __shared__ float wsum[4];
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const bf16_t* xr = a.X + (size_t)(i + 1) * a.D;
+  float ss = 0.f;
+  for (int k = tid; k < a.D; k += 256) {
+    const float v = bf2f(xr[k]);
+    xs[k] = v;
+    ss = fmaf(v, v, ss);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  __syncthreads();
+  const float r = rsqrtf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) / (float)a.D + a.eps);
+  const int nsl = 256 / a.A;          // k slices
+  const int col = tid % a.A, sl = tid / a.A;
+  float acc = 0.f;
+  if (sl < nsl) {
+    const int kper = (a.D + nsl - 1) / nsl;
+    const int k0 = sl * kper, k1 = min(a.D, k0 + kper);
+    for (int k = k0; k < k1; ++k) acc = fmaf(xs[k], a.w_out[(size_t)k * a.A + col], acc);
+  }
+  red[tid] = acc;
+  __syncthreads();
+  if (tid < a.A) {
+    float v = 0.f;
+    for (int q = 0; q < nsl; ++q) v += red[q * a.A + tid];
+    v = v * r + a.b_out[tid];
+    const float dt = *a.dt;
+    a.a_out[(size_t)i * a.A + tid] = a.a_in[(size_t)i * a.A + tid] + dt * v;
+  }
+}
+
+void launch_flow_velocity(const FlowVelArgs& a, hipStream_t st) {
+  flow_velocity_kernel<<<a.N, 256, 0, st>>>(a);
+}
+
+}  // namespace blk

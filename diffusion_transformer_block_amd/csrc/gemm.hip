@@ -1,0 +1,388 @@
+// MFMA GEMMs of the block with fused epilogues.
+//
+// [RT] = reading note on "Running VLAs at Real-time Speed" (Ma et al.,
+// arXiv:2510.26742v1).  §5: bias / residual / activation are merged into the
+// GEMM tail; the gated FFN's two up-projections share one load of their input
+// and the activation, elementwise gate and write-back are fused; the per-row
+// RMS statistic is computed first and consumed fused (with the gain already
+// folded into the weights it is just a row scale of the product); a partial
+// split-K balances skinny shapes over the compute units.  §6.2: at few tokens
+// a GEMM is bound by reading its bf16 weights.
+//
+// Two kernels:
+//  * skinny_gemm (M <= 64 rows): each workgroup streams a contiguous run of
+//    weight fragments for one 32-column group and one K split, with 16-byte
+//    coalesced loads issued UK k-tiles ahead; the four waves split the run and
+//    reduce through LDS; K splits reduce through a float32 scratch buffer and
+//    the last-arriving workgroup of a group (device-scope arrival counter,
+//    reset by that workgroup) sums the splits in a fixed order and runs the
+//    epilogue.  With RMS fused, every workgroup also sums x^2 over its K
+//    slice of the rows it already loaded, so the statistic costs no extra pass.
+//  * tiled_gemm (large M): 128 x 128 output tile per workgroup, K step 64,
+//    A (activations) staged through double-buffered LDS, B (packed weight
+//    fragments) loaded straight into registers one step ahead; 2 x 2 waves of
+//    64 x 64 each.
+#include "common.h"
+#include "internal.h"
+
+namespace blk {
+
+__device__ __forceinline__ float sumsq8(uint4 v) {
+  float s = 0.f;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(w[i] << 16);
+    const float hi = __uint_as_float(w[i] & 0xffff0000u);
+    s = fmaf(lo, lo, s);
+    s = fmaf(hi, hi, s);
+  }
+  return s;
+}
+
+// ============================================================================ skinny
+template <int MT, int UK, bool RMS, class Epi>
+__global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs ga, Epi epi) {
+  __shared__ __attribute__((aligned(16))) float red[4][MT * 512];
+  __shared__ float ssr[4][16 * MT];
+  __shared__ float rrow[16 * MT];
+  __shared__ int last_flag;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int g = blockIdx.x, s = blockIdx.y;
+  const int KT = ga.K >> 5;
+  const int KTS = KT / ga.splits;
+  const int KW = KTS >> 2;
+  const int kt0 = s * KTS + w * KW;
+
+  const bf16_t* arow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = min(16 * mt + lr, ga.M - 1);
+    arow[mt] = ga.A + (size_t)row * ga.lda + (size_t)kt0 * 32 + 8 * lg;
+  }
+  const uint4* bp = reinterpret_cast<const uint4*>(ga.Bp + frag_offset(g, kt0, 0, KT)) + l;
+
+  f32x4 acc[MT][2];
+  float ss[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    acc[mt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ss[mt] = 0.f;
+  }
+
+  for (int u = 0; u < KW; u += UK) {
+    uint4 bv[UK][2];
+    uint4 av[UK][MT];
+#pragma unroll
+    for (int q = 0; q < UK; ++q) {
+      bv[q][0] = ld_stream(bp + (u + q) * 128);
+      bv[q][1] = ld_stream(bp + (u + q) * 128 + 64);
+    }
+#pragma unroll
+    for (int q = 0; q < UK; ++q)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        av[q][mt] = *reinterpret_cast<const uint4*>(arow[mt] + (u + q) * 32);
+#pragma unroll
+    for (int q = 0; q < UK; ++q)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (RMS) ss[mt] += sumsq8(av[q][mt]);
+        acc[mt][0] = mfma16(as_bf16x8(av[q][mt]), as_bf16x8(bv[q][0]), acc[mt][0]);
+        acc[mt][1] = mfma16(as_bf16x8(av[q][mt]), as_bf16x8(bv[q][1]), acc[mt][1]);
+      }
+  }
+
+  // ---- reduce the four waves' K ranges through LDS
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<f32x4*>(&red[w][((mt * 2 + i) * 64 + l) * 4]) = acc[mt][i];
+  if (RMS) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float v = ss[mt];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (lg == 0) ssr[w][16 * mt + lr] = v;
+    }
+  }
+  __syncthreads();
+
+  float v0[MT], v1[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int i0 = ((mt * 2 + 0) * 64 + (tid >> 2)) * 4 + (tid & 3);
+    const int i1 = ((mt * 2 + 1) * 64 + (tid >> 2)) * 4 + (tid & 3);
+    v0[mt] = ((red[0][i0] + red[1][i0]) + red[2][i0]) + red[3][i0];
+    v1[mt] = ((red[0][i1] + red[1][i1]) + red[2][i1]) + red[3][i1];
+  }
+  float ssum = 0.f;
+  if (RMS && tid < 16 * MT) ssum = ((ssr[0][tid] + ssr[1][tid]) + ssr[2][tid]) + ssr[3][tid];
+
+  // ---- K splits: publish, count arrivals, the last workgroup sums in order
+  if (ga.splits > 1) {
+    const size_t stride = (size_t)ga.n_groups * MT * 256;
+    float2* pbase = reinterpret_cast<float2*>(ga.part) + (size_t)g * MT * 256 + tid;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) pbase[s * stride + mt * 256] = make_float2(v0[mt], v1[mt]);
+    if (RMS && tid < 16 * MT) ga.ss_part[((size_t)s * ga.n_groups + g) * 64 + tid] = ssum;
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned old = atomicAdd(&ga.counters[g], 1u);
+      last_flag = (old == (unsigned)(ga.splits - 1));
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    __threadfence();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      v0[mt] = 0.f;
+      v1[mt] = 0.f;
+    }
+    ssum = 0.f;
+    for (int s2 = 0; s2 < ga.splits; ++s2) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const float2 p = pbase[s2 * stride + mt * 256];
+        v0[mt] += p.x;
+        v1[mt] += p.y;
+      }
+      if (RMS && tid < 16 * MT)
+        ssum += ga.ss_part[((size_t)s2 * ga.n_groups + g) * 64 + tid];
+    }
+    if (tid == 0) atomicExch(&ga.counters[g], 0u);
+  }
+
+  if (RMS) {
+    if (tid < 16 * MT) rrow[tid] = rsqrtf(ssum / (float)ga.K + ga.eps);
+    __syncthreads();
+  }
+  const int c = (tid >> 2) & 15;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = 16 * mt + 4 * (tid >> 6) + (tid & 3);
+    if (m < ga.M) {
+      const float r = RMS ? rrow[m] : (ga.r ? ga.r[m] : 1.f);
+      epi.store(m, g, c, v0[mt], v1[mt], r);
+    }
+  }
+}
+
+int skinny_splits(int M, int K, int n_groups) {
+  (void)M;
+  const int KT = K / 32;
+  int best = 1;
+  for (int s = 1; s <= 64; s *= 2) {
+    if (KT % (4 * s) != 0) break;
+    if (n_groups * s > 512) break;
+    best = s;
+  }
+  return best;
+}
+
+size_t skinny_part_floats(int M, int K, int n_groups) {
+  const int s = skinny_splits(M, K, n_groups);
+  if (s == 1) return 0;
+  const int MT = (M + 15) / 16;
+  return (size_t)s * n_groups * MT * 256 * 2;
+}
+
+size_t skinny_ss_floats(int M, int K, int n_groups) {
+  const int s = skinny_splits(M, K, n_groups);
+  if (s == 1) return 0;
+  return (size_t)s * n_groups * 64;
+}
+
+template <int MT, int UK, bool RMS, class Epi>
+static void skinny_go(const GemmArgs& ga, const Epi& e, hipStream_t st) {
+  skinny_gemm_kernel<MT, UK, RMS, Epi><<<dim3(ga.n_groups, ga.splits), 256, 0, st>>>(ga, e);
+}
+
+template <int MT, bool RMS, class Epi>
+static void skinny_uk(const GemmArgs& ga, const Epi& e, int UK, hipStream_t st) {
+  if (UK == 4) skinny_go<MT, 4, RMS>(ga, e, st);
+  else if (UK == 2) skinny_go<MT, 2, RMS>(ga, e, st);
+  else skinny_go<MT, 1, RMS>(ga, e, st);
+}
+
+template <bool RMS, class Epi>
+static void launch_skinny(GemmArgs ga, const Epi& e, hipStream_t st) {
+  ga.splits = skinny_splits(ga.M, ga.K, ga.n_groups);
+  const int KW = (ga.K / 32) / ga.splits / 4;
+  // the unroll must divide the per-wave k-tile count exactly
+  const int UK = (KW % 4 == 0) ? 4 : (KW % 2 == 0) ? 2 : 1;
+  const int MT = (ga.M + 15) / 16;
+  switch (MT) {
+    case 1: skinny_uk<1, RMS>(ga, e, UK, st); break;
+    case 2: skinny_uk<2, RMS>(ga, e, UK, st); break;
+    case 3: skinny_uk<3, RMS>(ga, e, UK, st); break;
+    default: skinny_uk<4, RMS>(ga, e, UK, st); break;
+  }
+}
+
+// ============================================================================ tiled
+template <class Epi>
+__global__ __launch_bounds__(256) void tiled_gemm_kernel(GemmArgs ga, Epi epi) {
+  constexpr int BM = 128, BK = 64, LDS_ROW = BK + 8;
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDS_ROW];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int wm = w >> 1, wn = w & 1;
+  const int nb = blockIdx.x, mb = blockIdx.y;
+  const int KT = ga.K >> 5;
+  const int nsteps = ga.K / BK;
+
+  const bf16_t* ag[4];
+  int lds_off[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int cidx = tid + 256 * q;
+    const int row = cidx >> 3, col = (cidx & 7) * 8;
+    const int grow = min(mb * BM + row, ga.M - 1);
+    ag[q] = ga.A + (size_t)grow * ga.lda + col;
+    lds_off[q] = row * LDS_ROW + col;
+  }
+  const uint4* bg[2];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int gq = min(4 * nb + 2 * wn + gi, ga.n_groups - 1);
+    bg[gi] = reinterpret_cast<const uint4*>(ga.Bp + frag_offset(gq, 0, 0, KT)) + l;
+  }
+
+  uint4 areg[4], breg[2][2][2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) areg[q] = *reinterpret_cast<const uint4*>(ag[q]);
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) breg[gi][kk][i] = bg[gi][(kk * 2 + i) * 64];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(&As[0][lds_off[q]]) = areg[q];
+  __syncthreads();
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int step = 0; step < nsteps; ++step) {
+    const int cur = step & 1;
+    const bool more = step + 1 < nsteps;
+    uint4 bnext[2][2][2];
+    if (more) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        areg[q] = *reinterpret_cast<const uint4*>(ag[q] + (size_t)(step + 1) * BK);
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            bnext[gi][kk][i] = bg[gi][(((step + 1) * 2 + kk) * 2 + i) * 64];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint4 af = *reinterpret_cast<const uint4*>(
+            &As[cur][(64 * wm + 16 * mt + lr) * LDS_ROW + 32 * kk + 8 * lg]);
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            acc[mt][2 * gi + i] =
+                mfma16(as_bf16x8(af), as_bf16x8(breg[gi][kk][i]), acc[mt][2 * gi + i]);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(&As[cur ^ 1][lds_off[q]]) = areg[q];
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int i = 0; i < 2; ++i) breg[gi][kk][i] = bnext[gi][kk][i];
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int g = 4 * nb + 2 * wn + gi;
+      if (g >= ga.n_groups) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = mb * BM + 64 * wm + 16 * mt + 4 * lg + j;
+        if (row < ga.M) {
+          const float r = ga.r ? ga.r[row] : 1.f;
+          epi.store(row, g, lr, acc[mt][2 * gi][j], acc[mt][2 * gi + 1][j], r);
+        }
+      }
+    }
+}
+
+template <class Epi>
+static void launch_tiled(const GemmArgs& ga, const Epi& e, hipStream_t st) {
+  dim3 grid((ga.n_groups + 3) / 4, (ga.M + 127) / 128);
+  tiled_gemm_kernel<Epi><<<grid, 256, 0, st>>>(ga, e);
+}
+
+// ============================================================================ dispatch
+void launch_gemm_qkv(const GemmArgs& ga, const EpiQKV& e, hipStream_t st) {
+  if (ga.M <= kSkinnyMaxM) {
+    if (ga.rms_fused) launch_skinny<true>(ga, e, st);
+    else launch_skinny<false>(ga, e, st);
+  } else {
+    launch_tiled(ga, e, st);
+  }
+}
+void launch_gemm_residual(const GemmArgs& ga, const EpiResidual& e, hipStream_t st) {
+  if (ga.M <= kSkinnyMaxM) launch_skinny<false>(ga, e, st);
+  else launch_tiled(ga, e, st);
+}
+void launch_gemm_gateup(const GemmArgs& ga, const EpiGateUp& e, hipStream_t st) {
+  if (ga.M <= kSkinnyMaxM) {
+    if (ga.rms_fused) launch_skinny<true>(ga, e, st);
+    else launch_skinny<false>(ga, e, st);
+  } else {
+    launch_tiled(ga, e, st);
+  }
+}
+void launch_gemm_bias(const GemmArgs& ga, const EpiBias& e, hipStream_t st) {
+  if (ga.M <= kSkinnyMaxM) launch_skinny<false>(ga, e, st);
+  else launch_tiled(ga, e, st);
+}
+
+// ============================================================================ RMS rows
+__global__ __launch_bounds__(256) void rms_rows_kernel(const bf16_t* __restrict__ x, int M, int K,
+                                                       float eps, float* __restrict__ r) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (row >= M) return;
+  const bf16_t* p = x + (size_t)row * K;
+  float s = 0.f;
+  for (int k = 8 * l; k < K; k += 512) s += sumsq8(*reinterpret_cast<const uint4*>(p + k));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  if (l == 0) r[row] = rsqrtf(s / (float)K + eps);
+}
+
+void launch_rms_rows(const bf16_t* x, int M, int K, float eps, float* r, hipStream_t st) {
+  rms_rows_kernel<<<(M + 3) / 4, 256, 0, st>>>(x, M, K, eps, r);
+}
+
+}  // namespace blk

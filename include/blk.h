@@ -1,0 +1,199 @@
+/*
+ * blk.h -- C ABI of the MI355X (gfx950) block-stage library `libblk.so`.
+ *
+ * One transformer-block stage runs on a small chunk of query tokens that
+ * reads a cached prefix / history K/V.  The same stage, repeated over a layer
+ * stack and a flow-matching Euler loop, is an action expert's denoise step.
+ *
+ * Sources for what is computed:
+ *   [PS] AREX Feed article on PhysisServe: a pipeline stage is one Transformer
+ *        block at one denoise step; a chunk reads the cached (noisy) KV of
+ *        earlier chunks; the KV cache stays on its GPU; only hidden states
+ *        move between stages (section on splitting the pipeline per block
+ *        and step).
+ *   [RT] reading note on "Running VLAs at Real-time Speed" (Ma et al.,
+ *        arXiv:2510.26742v1): RMSNorm gain folded into the next linear layer
+ *        (§4.1); action and time-embedding linears pre-multiplied, the time
+ *        branch tabulated for fixed timesteps and folded into the bias ahead
+ *        of SiLU (§4.2); Q/K/V merged into one matrix with RoPE fused into
+ *        the product (§4.3); gated FFN, bias/residual/activation epilogues
+ *        and precomputed RMS statistics (§5); graph capture of a fixed
+ *        sequence of GPU work with stable shapes and addresses (§3).
+ *
+ * Conventions for every call:
+ *   - Matrices are row-major [in, out] (row-vector convention y = x W).
+ *   - bf16 tensors are passed as their 16-bit patterns (uint16_t).  Gains,
+ *     biases, tables, noise, state and actions are float32.
+ *   - Every pointer named "device" is device memory owned by the caller; the
+ *     library never frees or retains caller memory beyond the call, except
+ *     that flow_denoise's captured graph keeps the pointers of its key
+ *     (see flow_denoise).  The library allocates no device memory.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and is asynchronous; no call synchronizes the device except
+ *     flow_denoise while it captures a new graph.
+ *   - Return value 0 = success, negative = one of the BLK_E* codes below.
+ *     All arguments are validated before anything is enqueued; on error
+ *     nothing is enqueued and blk_last_error() returns a message (per
+ *     calling thread).  No call aborts or throws.
+ *   - Size-query protocol: a call whose output buffer pointer is NULL only
+ *     writes the required byte count to *bytes / *ws_bytes and returns 0.
+ *   - Calls sharing a workspace must not overlap in time (same stream is
+ *     fine).  A workspace must be zero-filled before its first use; every
+ *     call leaves its synchronization counters at zero again.
+ */
+#ifndef BLK_H_
+#define BLK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BLK_OK 0
+#define BLK_EINVAL (-1)       /* NULL pointer, negative size, out-of-range index      */
+#define BLK_EUNSUPPORTED (-2) /* shape outside the supported set                     */
+#define BLK_ESIZE (-3)        /* a buffer is smaller than its size query              */
+#define BLK_ESTATE (-4)       /* packed buffer unknown, or config/steps do not match */
+#define BLK_EHIP (-5)         /* a HIP runtime call failed (message has the reason)  */
+
+/* Shape of one block.  Supported: head_dim in {64, 128, 256}; hidden % 128 == 0;
+ * ffn % 64 == 0; n_q_heads % n_kv_heads == 0; 1 <= max_pos <= 1<<20. */
+typedef struct blk_config {
+  int32_t hidden;      /* D: model width                                         */
+  int32_t ffn;         /* F: gated-FFN width                                      */
+  int32_t n_q_heads;   /* Hq                                                      */
+  int32_t n_kv_heads;  /* Hkv (Hq == Hkv: MHA; Hkv == 1: MQA); head h reads kv-head
+                          floor(h * Hkv / Hq)                                     */
+  int32_t head_dim;    /* d                                                       */
+  int32_t max_pos;     /* RoPE table length: every position P + t must be < max_pos */
+  float rope_base;     /* theta_j = rope_base^(-2j/d), pairs (j, j + d/2)         */
+  float rms_eps;       /* RMSNorm: x * (mean x^2 + eps)^-1/2 * g                  */
+} blk_config;
+
+/* One layer's raw (unfolded) weights, all device pointers. */
+typedef struct blk_layer_src {
+  const float* g_attn;     /* [D]          RMSNorm gain ahead of attention          */
+  const uint16_t* w_q;     /* bf16 [D][Hq*d]                                        */
+  const uint16_t* w_k;     /* bf16 [D][Hkv*d]                                       */
+  const uint16_t* w_v;     /* bf16 [D][Hkv*d]                                       */
+  const uint16_t* w_o;     /* bf16 [Hq*d][D]                                        */
+  const float* g_ffn;      /* [D]          RMSNorm gain ahead of the FFN            */
+  const uint16_t* w_gate;  /* bf16 [D][F]                                           */
+  const uint16_t* w_up;    /* bf16 [D][F]                                           */
+  const uint16_t* w_down;  /* bf16 [F][D]                                           */
+} blk_layer_src;
+
+/* Flow-matching head of an action expert ([RT] §2, §4.2), device pointers. */
+typedef struct blk_flow_head_src {
+  int32_t n_actions;       /* N action tokens (the chunk is N + 1 tokens: state first) */
+  int32_t action_dim;      /* A (<= 64)                                              */
+  const uint16_t* w1;      /* bf16 [A][D]   action projection                        */
+  const float* b1;         /* [D]                                                    */
+  const uint16_t* w2;      /* bf16 [2D][D]  rows 0..D-1: action branch, D..2D-1: time */
+  const float* b2;         /* [D]                                                    */
+  const uint16_t* w3;      /* bf16 [D][D]   linear after SiLU                        */
+  const float* b3;         /* [D]                                                    */
+  const uint16_t* ws;      /* bf16 [A][D]   state projection                         */
+  const float* bs;         /* [D]                                                    */
+  const float* g_f;        /* [D]           final RMSNorm gain                       */
+  const uint16_t* w_out;   /* bf16 [D][A]   velocity projection                      */
+  const float* b_out;      /* [A]                                                    */
+} blk_flow_head_src;
+
+/*
+ * blk_prepare_weights -- the weight-prep pass ([RT] §4.1-4.3), once per model.
+ *
+ * Packs n_layers layers (host array `layers` of device pointers) and, if
+ * `head` is non-NULL, a flow head for the n_steps evaluation times
+ * t_schedule[0..n_steps-1] (host float64 array) into one opaque device buffer
+ * `dst`:
+ *   - RMSNorm gains folded into the following projection: diag(g) W, product
+ *     formed exactly and rounded once to bf16;
+ *   - W_q | W_k | W_v concatenated into one matrix, columns regrouped so the
+ *     RoPE pair (j, j + d/2) of every rotated head is produced together;
+ *     W_gate and W_up interleaved per 16-column tile; all matrices stored as
+ *     MFMA operand fragments;
+ *   - RoPE cos/sin table [max_pos][d/2] (float64 math, float32 storage);
+ *   - flow head: W1 W2a (float32), bias table b1 W2a + tau(t_s) W2t + b2 per
+ *     step (float32; tau is the sinusoidal embedding of t_s), Euler steps
+ *     t_{s+1} - t_s (t_{n_steps} = 0), final gain folded into W_out.
+ * The table depends on the schedule: a different schedule needs a new prepare.
+ * dst == NULL: only *bytes is set.  Otherwise *bytes must be >= the query.
+ * The source buffers must stay valid until the enqueued work has run; dst is
+ * registered in a host-side table (keyed by address) that blk_forward and
+ * flow_denoise consult.  Errors: BLK_EINVAL, BLK_EUNSUPPORTED, BLK_ESIZE,
+ * BLK_EHIP.
+ */
+int blk_prepare_weights(const blk_config* cfg, const blk_layer_src* layers, int n_layers,
+                        const blk_flow_head_src* head, const double* t_schedule, int n_steps,
+                        void* dst, size_t* bytes, void* stream);
+
+/*
+ * blk_forward -- one block stage over cached K/V ([PS]; [RT] §4-§5).
+ *
+ * For each of `batch` streams b (all on the same layer weights, [PS] batching
+ * of one block's tasks across chunks), with T = tokens, P = prefix:
+ *   x       device bf16 [batch][T][D]           chunk hidden states (input)
+ *   k_prefix, v_prefix  device bf16, stream b at element offset
+ *           b * prefix_stride, each [P][Hkv][d]  cached keys (already rotated)
+ *           and values; read only; may be NULL when P == 0
+ *   y       device bf16 [batch][T][D]           block output
+ *   k_new, v_new  device bf16, stream b at b * new_stride, each [T][Hkv][d]:
+ *           the chunk's own keys (after RoPE) and values.  They may alias
+ *           rows P..P+T-1 of the caller's cache (k_new = k_prefix + P*Hkv*d,
+ *           new_stride = prefix_stride) to append the chunk to the cache.
+ *   ws      device workspace of *ws_bytes bytes (query with ws == NULL);
+ *           zero-filled before its first use.
+ * Computes y = h + FFN(RMSNorm(h) g2), h = x + Attn(RoPE(Q), [K_p; RoPE(K)],
+ * [V_p; V]) W_o with Q, K, V = RMSNorm(x) g1 [W_q|W_k|W_v]; chunk token t is at
+ * position P + t; no attention mask (every query sees all P + T keys).
+ * `packed` must come from blk_prepare_weights with an identical cfg; `layer`
+ * selects the layer.  Errors: BLK_EINVAL, BLK_EUNSUPPORTED (P + T > max_pos),
+ * BLK_ESIZE (ws too small), BLK_ESTATE (packed unknown / cfg differs), BLK_EHIP.
+ */
+int blk_forward(const blk_config* cfg, const void* packed, int layer, int batch, int tokens,
+                int prefix, const uint16_t* x, const uint16_t* k_prefix,
+                const uint16_t* v_prefix, int64_t prefix_stride, uint16_t* y, uint16_t* k_new,
+                uint16_t* v_new, int64_t new_stride, void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * flow_denoise -- the action expert's Euler flow-matching loop ([RT] §2-§4).
+ *
+ * For s = 0..n_steps-1: X = [state Ws + bs ; SiLU(a W1W2a + table[s]) W3 + b3]
+ * ([N + 1][D]); X = block_l(X) for l = 0..n_layers-1 (layer l reads its own
+ * prefix k_prefix[l], v_prefix[l], each device bf16 [P][Hkv][d]; chunk token t
+ * at position P + t); v = RMSNorm(X[1:]) g_F W_out + b_out; a += dt_s v.
+ *   k_prefix, v_prefix  host arrays of n_layers device pointers
+ *   noise    device float32 [N][A]  a_0 (read only)
+ *   state    device float32 [A]
+ *   actions  device float32 [N][A]  a_{n_steps} (also the loop's running state)
+ *   ws       device workspace (query with ws == NULL), zero-filled before first use
+ * `packed` must hold a flow head prepared for exactly n_steps steps and at
+ * least n_layers layers.  The whole loop is captured once into a hipGraph
+ * keyed on (packed, n_layers, n_steps, P, every pointer argument); later calls
+ * with the same key replay it with one launch, a changed key captures anew
+ * (capture synchronizes the device once).  The key's buffers must stay valid
+ * while the graph is cached (until blk_release or re-capture).
+ * Errors: BLK_EINVAL, BLK_EUNSUPPORTED, BLK_ESIZE, BLK_ESTATE, BLK_EHIP.
+ */
+int flow_denoise(const blk_config* cfg, const void* packed, int n_layers, int n_steps,
+                 int prefix, const uint16_t* const* k_prefix, const uint16_t* const* v_prefix,
+                 const float* noise, const float* state, float* actions, void* ws,
+                 size_t* ws_bytes, void* stream);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* blk_last_error(void);
+
+/* Destroys every cached graph and forgets every registered packed buffer.
+ * Call with no library work in flight. */
+void blk_release(void);
+
+/* Library ABI version (bumped when a signature or a layout changes). */
+int blk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BLK_H_ */

@@ -237,3 +237,27 @@ def flow_case(flow: FlowShape, n_layers: int | None = None) -> dict:
         "layers": [flow_layer(flow, l) for l in range(L)],
         "schedule": flow_schedule(flow),
     }
+
+
+# --------------------------------------------------------------------------
+# device copies (torch is imported lazily; used by GPU tests, bench and smoke)
+# --------------------------------------------------------------------------
+def to_device(value, device="cuda"):
+    """Bf16 -> torch.bfloat16 tensor with the same bits; float arrays -> float32."""
+    import torch
+    if isinstance(value, Bf16):
+        t = torch.from_numpy(np.ascontiguousarray(value.bits).view(np.int16)).view(torch.bfloat16)
+        return t.to(device)
+    if isinstance(value, np.ndarray):
+        return torch.from_numpy(np.ascontiguousarray(value, dtype=np.float32)).to(device)
+    return value
+
+
+def tree_to_device(d: dict, device="cuda") -> dict:
+    return {k: to_device(v, device) for k, v in d.items()}
+
+
+def bf16_tensor_to_f32(t) -> np.ndarray:
+    """Exact float32 values of a torch.bfloat16 tensor (any device)."""
+    import torch
+    return t.detach().float().cpu().numpy()
