@@ -1,0 +1,332 @@
+"""Benchmark of the block stage over cached K/V on one MI355X.
+
+Default run (one JSON line on stdout):
+  * headline: the 64-token action-expert block (hidden 1024, FFN 4096, 8 query
+    heads x 256 sharing one KV head, 520 cached prefix tokens), block-stage
+    microseconds with the weights cold: 16 packed-weight and prefix-KV copies
+    (570 MB, over twice the 256 MB last-level cache) are used in rotation.
+    One step = one block stage (the five kernels of blk_forward); the steps are
+    replayed from a captured graph so host launch overhead is not timed.
+  * roofline: achieved HBM GB/s of the block stage (compulsory bytes: packed
+    weights, prefix K/V, x, y, K_new, V_new) against the 8 TB/s HBM3E peak.
+  * loop: the full 18-layer x 10-step flow-matching loop (flow_denoise, one
+    graph launch), 768 prefix tokens per layer; cold by construction (625 MB
+    of weights per step).
+  * large_chunk: the 1560-token video block and the 8 x 880-token batched
+    block, MFMA utilisation against the 2.5 PFLOP/s bf16 dense peak.
+  * cpu_baseline: the NumPy oracle on the host cores, a bounded sample of the
+    headline workload.
+
+--gpus N with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "block-stage µs + achieved HBM GB/s (64-tok) / MFMA util (large chunk)"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=320, help="timed block stages (multiple of 16)")
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--only", choices=["all", "block", "loop", "large", "video", "batched"],
+                    default="all", help="restrict the run (for profiling)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--rotate", type=int, default=16, help="weight copies in rotation")
+    return ap.parse_args()
+
+
+def block_bytes(shape, P):
+    """Compulsory HBM bytes of one block stage."""
+    D, F, d, Hq, Hkv = shape.hidden, shape.ffn, shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    B, T = shape.batch, shape.tokens
+    weights = 2 * (D * (Hq + 2 * Hkv) * d + Hq * d * D + 2 * D * F + F * D)
+    kv_prefix = 2 * 2 * B * P * Hkv * d
+    io = 2 * B * T * D * 2 + 2 * 2 * B * T * Hkv * d
+    return weights, kv_prefix + io
+
+
+def block_flops(shape, P):
+    D, F, d, Hq, Hkv = shape.hidden, shape.ffn, shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    M = shape.batch * shape.tokens
+    gemm = 2 * M * (D * (Hq + 2 * Hkv) * d + Hq * d * D + 2 * D * F + F * D)
+    att = 2 * 2 * shape.batch * Hq * shape.tokens * (P + shape.tokens) * d
+    return gemm, att
+
+
+def config_of(blk, shape, max_pos=None):
+    return blk.make_config(shape.hidden, shape.ffn, shape.n_q_heads, shape.n_kv_heads,
+                           shape.head_dim, max_pos or (shape.prefix + shape.tokens),
+                           shape.rope_base, shape.rms_eps)
+
+
+def time_block(shape, steps, warmup, rotate):
+    """Block-stage time with `rotate` weight / KV copies, replayed from a graph."""
+    import torch
+    import diffusion_transformer_block_amd as blk
+    import synth
+    case = synth.block_case(shape)
+    cfg = config_of(blk, shape)
+    w_dev = synth.tree_to_device(case["weights"])
+    x = torch.stack([synth.to_device(s["x"]) for s in case["streams"]])
+    kp0 = torch.stack([synth.to_device(s["k_prefix"]) for s in case["streams"]])
+    vp0 = torch.stack([synth.to_device(s["v_prefix"]) for s in case["streams"]])
+    packs = [blk.blk_prepare_weights(cfg, [w_dev]) for _ in range(rotate)]
+    kps = [kp0.clone() for _ in range(rotate)]
+    vps = [vp0.clone() for _ in range(rotate)]
+    del w_dev
+    B, T = shape.batch, shape.tokens
+    y = torch.empty_like(x)
+    kn = torch.empty(B, T, shape.n_kv_heads, shape.head_dim, dtype=torch.bfloat16, device="cuda")
+    vn = torch.empty_like(kn)
+    ws = torch.zeros(blk.forward_workspace_bytes(cfg, B, T, shape.prefix), dtype=torch.uint8,
+                     device="cuda")
+
+    def run(i):
+        blk.blk_forward(cfg, packs[i], 0, x, kps[i], vps[i], y=y, k_new=kn, v_new=vn, ws=ws)
+
+    # eager reference output, then the graph of one rotation
+    run(0)
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(rotate):
+            run(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(rotate):
+            run(i)
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_eager), "graph replay differs from the eager block"
+
+    n_rep = max(1, steps // rotate)
+    for _ in range(max(1, warmup // rotate)):
+        g.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(n_rep):
+        g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    us_graph = e0.elapsed_time(e1) * 1e3 / (n_rep * rotate)
+
+    # eager (one C call per block, five launches each)
+    for i in range(rotate):
+        run(i)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for r in range(n_rep):
+        for i in range(rotate):
+            run(i)
+    e1.record(st)
+    torch.cuda.synchronize()
+    us_eager = e0.elapsed_time(e1) * 1e3 / (n_rep * rotate)
+    del g, packs, kps, vps
+    torch.cuda.empty_cache()
+    return {"us": us_graph, "us_eager": us_eager, "timed_steps": n_rep * rotate}
+
+
+def time_loop(warmup, reps=20):
+    import torch
+    import diffusion_transformer_block_amd as blk
+    import synth
+    flow = synth.FLOW
+    case = synth.flow_case(flow)
+    fb = flow.block
+    cfg = config_of(blk, fb, fb.prefix + flow.n_actions + 1)
+    layers = [synth.tree_to_device(l) for l in case["layers"]]
+    head = synth.tree_to_device(case["head"])
+    head["n_actions"] = flow.n_actions
+    packed = blk.blk_prepare_weights(cfg, layers, head, list(case["schedule"]))
+    kp = [l["k_prefix"] for l in layers]
+    vp = [l["v_prefix"] for l in layers]
+    for l in layers:
+        for k in list(l):
+            if k not in ("k_prefix", "v_prefix"):
+                del l[k]
+    ws = torch.zeros(blk.flow_workspace_bytes(cfg, packed, flow.n_layers, flow.n_steps,
+                                              fb.prefix), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(head["noise"])
+    call = lambda: blk.flow_denoise(cfg, packed, flow.n_steps, kp, vp, head["noise"],
+                                    head["state"], actions=out, ws=ws)
+    for _ in range(max(2, warmup // 8)):
+        call()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        call()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    w_bytes, _ = block_bytes(fb, fb.prefix)
+    D, A = fb.hidden, flow.action_dim
+    head_bytes = 2 * D * D + 4 * (A * D * 3 + 3 * D)     # W3 bf16, W_fused/Ws/W_out f32, biases
+    kv_bytes = 2 * 2 * fb.prefix * fb.n_kv_heads * fb.head_dim
+    step_bytes = flow.n_layers * (w_bytes + kv_bytes) + head_bytes
+    gbs = flow.n_steps * step_bytes / (ms * 1e-3) / 1e9
+    del packed, ws
+    torch.cuda.empty_cache()
+    return {"workload": flow.name, "layers": flow.n_layers, "steps": flow.n_steps,
+            "prefix": fb.prefix, "ms_per_loop": round(ms, 4),
+            "us_per_layer_step": round(ms * 1e3 / (flow.n_layers * flow.n_steps), 3),
+            "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "timed_loops": reps}
+
+
+def time_large(shape, reps):
+    import torch
+    import diffusion_transformer_block_amd as blk
+    import synth
+    case = synth.block_case(shape)
+    cfg = config_of(blk, shape)
+    packed = blk.blk_prepare_weights(cfg, [synth.tree_to_device(case["weights"])])
+    x = torch.stack([synth.to_device(s["x"]) for s in case["streams"]])
+    kp = torch.stack([synth.to_device(s["k_prefix"]) for s in case["streams"]])
+    vp = torch.stack([synth.to_device(s["v_prefix"]) for s in case["streams"]])
+    B, T = shape.batch, shape.tokens
+    y = torch.empty_like(x)
+    kn = torch.empty(B, T, shape.n_kv_heads, shape.head_dim, dtype=torch.bfloat16, device="cuda")
+    vn = torch.empty_like(kn)
+    ws = torch.zeros(blk.forward_workspace_bytes(cfg, B, T, shape.prefix), dtype=torch.uint8,
+                     device="cuda")
+    run = lambda: blk.blk_forward(cfg, packed, 0, x, kp, vp, y=y, k_new=kn, v_new=vn, ws=ws)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        run()
+    e1.record(st)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    gemm, att = block_flops(shape, shape.prefix)
+    tflops = (gemm + att) / (us * 1e-6) / 1e12
+    del packed, x, kp, vp, ws
+    torch.cuda.empty_cache()
+    return {"workload": shape.name, "us_per_block": round(us, 2),
+            "gemm_gflop": round(gemm / 1e9, 2), "attn_gflop": round(att / 1e9, 2),
+            "achieved_TFLOPs": round(tflops, 1), "mfma_util": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "timed_blocks": reps}
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle, as it stands, timed on the host on the headline workload."""
+    import numpy as np
+    import oracle
+    import synth
+    shape = synth.AE_BLOCK
+    case = synth.block_case(shape)
+    w = {k: (v.f32 if isinstance(v, synth.Bf16) else v) for k, v in case["weights"].items()}
+    st = case["streams"][0]
+    kw = dict(n_q_heads=shape.n_q_heads, n_kv_heads=shape.n_kv_heads, head_dim=shape.head_dim,
+              rope_base=shape.rope_base, eps=shape.rms_eps)
+    x, kp, vp = st["x"].f32, st["k_prefix"].f32, st["v_prefix"].f32
+    oracle.block_forward(x, w, kp, vp, **kw)    # warm
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        oracle.block_forward(x, w, kp, vp, **kw)
+        n += 1
+    dt = time.perf_counter() - t0
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    return {"value": round(dt / n * 1e6, 1), "unit": "us", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} block stages of the 64-token AE block (NumPy float32, {dt:.1f} s)"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {max(args.gpus, world)} is not "
+              "supported (the stage shards by pipeline stage and stream, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    rotate = max(1, args.rotate)
+    steps = max(rotate, (args.steps // rotate) * rotate)
+    shape = synth.AE_BLOCK
+    line = {"metric": METRIC}
+    if args.only in ("all", "block"):
+        log(f"block {shape.name}: {steps} timed stages, {rotate} weight copies")
+        r = time_block(shape, steps, args.warmup, rotate)
+        wb, ob = block_bytes(shape, shape.prefix)
+        gbs = (wb + ob) / (r["us"] * 1e-6) / 1e9
+        line.update({
+            "value": round(r["us"], 3), "unit": "us", "n_gpus": 1, "steps": r["timed_steps"],
+            "warmup": args.warmup, "ms_per_step": round(r["us"] / 1e3, 6),
+            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) activations / K/V, N(0,0.02^2) weights)",
+            "config": {"workload": shape.name, "hidden": shape.hidden, "ffn": shape.ffn,
+                       "q_heads": shape.n_q_heads, "kv_heads": shape.n_kv_heads,
+                       "head_dim": shape.head_dim, "tokens": shape.tokens,
+                       "prefix": shape.prefix, "weight_copies": rotate,
+                       "parallelism": "single GPU"},
+            "eager_us": round(r["us_eager"], 3),
+            "roofline": {"bound": "hbm", "kernel": "block_stage (qkv_rope, attention, o_proj, "
+                         "gate_up, down: one graph-replayed sequence)",
+                         "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": wb + ob,
+                         "traffic": None},
+        })
+        log(f"  {r['us']:.2f} us/stage graph, {r['us_eager']:.2f} us eager, {gbs:.0f} GB/s")
+    if args.only in ("all", "loop"):
+        log("loop flow_18x10")
+        line["loop"] = time_loop(args.warmup)
+        log(f"  {line['loop']}")
+    if args.only in ("all", "large", "video", "batched"):
+        large = []
+        if args.only in ("all", "large", "video"):
+            log("large chunk video_dit_1560tok")
+            large.append(time_large(synth.VIDEO_DIT, 20))
+            log(f"  {large[-1]}")
+        if args.only in ("all", "large", "batched"):
+            log("large chunk batched_8x880tok")
+            large.append(time_large(synth.BATCHED, 5))
+            log(f"  {large[-1]}")
+        line["large_chunk"] = large
+    if args.only in ("all", "block") and not args.no_cpu:
+        log("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline()
+    torch.cuda.synchronize()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -190,22 +190,16 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(AttnArgs a) {
   {
     float* po = a.part_o + ((size_t)split * n_rbt + rb_id) * 64 * HD + (size_t)(16 * w + lr) * HD + 4 * lg;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt) = o[dt];
+    for (int dt = 0; dt < NDT; ++dt) {
+      st_dev2(po + 16 * dt, o[dt][0], o[dt][1]);
+      st_dev2(po + 16 * dt + 2, o[dt][2], o[dt][3]);
+    }
     if (lg == 0) {
       float* pm = a.part_ml + (((size_t)split * n_rbt + rb_id) * 64 + 16 * w + lr) * 2;
-      pm[0] = m_run;
-      pm[1] = l_tot;
+      st_dev2(pm, m_run, l_tot);
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned old = atomicAdd(&a.counters[rb_id], 1u);
-    last_flag = (old == (unsigned)(a.splits - 1));
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
+  if (!arrive_last(&a.counters[rb_id], (unsigned)a.splits, &last_flag)) return;
 
   // 4 threads per row, each HD/4 columns
   const int row = tid >> 2;
@@ -213,24 +207,22 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(AttnArgs a) {
   if (qrow2 < rows) {
     float mx = -INFINITY;
     for (int sp = 0; sp < a.splits; ++sp)
-      mx = fmaxf(mx, a.part_ml[(((size_t)sp * n_rbt + rb_id) * 64 + row) * 2]);
+      mx = fmaxf(mx, ld_dev2(a.part_ml + (((size_t)sp * n_rbt + rb_id) * 64 + row) * 2).x);
     float den = 0.f;
     constexpr int QC = HD / 4;
     float num[QC];
 #pragma unroll
     for (int c = 0; c < QC; ++c) num[c] = 0.f;
     for (int sp = 0; sp < a.splits; ++sp) {
-      const float* pm = a.part_ml + (((size_t)sp * n_rbt + rb_id) * 64 + row) * 2;
-      const float wgt = exp2f(pm[0] - mx);
-      den += wgt * pm[1];
+      const float2 ml = ld_dev2(a.part_ml + (((size_t)sp * n_rbt + rb_id) * 64 + row) * 2);
+      const float wgt = exp2f(ml.x - mx);
+      den += wgt * ml.y;
       const float* po = a.part_o + ((size_t)sp * n_rbt + rb_id) * 64 * HD + (size_t)row * HD + (tid & 3) * QC;
 #pragma unroll
-      for (int c = 0; c < QC; c += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(po + c);
-        num[c] += wgt * v[0];
-        num[c + 1] += wgt * v[1];
-        num[c + 2] += wgt * v[2];
-        num[c + 3] += wgt * v[3];
+      for (int c = 0; c < QC; c += 2) {
+        const float2 v = ld_dev2(po + c);
+        num[c] += wgt * v.x;
+        num[c + 1] += wgt * v.y;
       }
     }
     const float inv = 1.f / den;
@@ -240,7 +232,6 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(AttnArgs a) {
     for (int c = 0; c < QC; c += 2)
       *reinterpret_cast<uint32_t*>(op + c) = pack2(num[c] * inv, num[c + 1] * inv);
   }
-  if (tid == 0) atomicExch(&a.counters[rb_id], 0u);
 }
 
 void attn_plan(int B, int T, int P, int Hq, int Hkv, int d, int* splits, int* keys_per_split) {

@@ -39,6 +39,47 @@ __device__ __forceinline__ uint4 ld_stream(const uint4* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// ---------------------------------------------------------------- cross-workgroup hand-off
+// Partial results that another workgroup of the same kernel reads back go
+// through device-coherent accesses (relaxed agent-scope atomics: sc1 loads and
+// stores, coherent across the XCDs' L2 caches).  The writer waits for its
+// stores to be acknowledged (vmcnt 0) before the workgroup bumps the arrival
+// counter, so no device-wide fence -- an L2 write-back plus invalidate on this
+// chip -- is needed.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev2(float* p, float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_dev2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Publish this workgroup's partial (already stored with st_dev*) and report
+// whether it is the last of `expected` workgroups to arrive at `counter`.  The
+// last one resets the counter to zero for the next launch.  Call with every
+// thread of the workgroup.
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected, int* flag) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == expected - 1;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -126,20 +126,12 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs ga, Epi epi) 
 
   // ---- K splits: publish, count arrivals, the last workgroup sums in order
   if (ga.splits > 1) {
-    const size_t stride = (size_t)ga.n_groups * MT * 256;
-    float2* pbase = reinterpret_cast<float2*>(ga.part) + (size_t)g * MT * 256 + tid;
+    const size_t stride = (size_t)ga.n_groups * MT * 256 * 2;   // floats per split
+    float* pbase = ga.part + ((size_t)g * MT * 256 + tid) * 2;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) pbase[s * stride + mt * 256] = make_float2(v0[mt], v1[mt]);
-    if (RMS && tid < 16 * MT) ga.ss_part[((size_t)s * ga.n_groups + g) * 64 + tid] = ssum;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned old = atomicAdd(&ga.counters[g], 1u);
-      last_flag = (old == (unsigned)(ga.splits - 1));
-    }
-    __syncthreads();
-    if (!last_flag) return;
-    __threadfence();
+    for (int mt = 0; mt < MT; ++mt) st_dev2(pbase + s * stride + mt * 512, v0[mt], v1[mt]);
+    if (RMS && tid < 16 * MT) st_dev(&ga.ss_part[((size_t)s * ga.n_groups + g) * 64 + tid], ssum);
+    if (!arrive_last(&ga.counters[g], (unsigned)ga.splits, &last_flag)) return;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       v0[mt] = 0.f;
@@ -149,14 +141,12 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs ga, Epi epi) 
     for (int s2 = 0; s2 < ga.splits; ++s2) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const float2 p = pbase[s2 * stride + mt * 256];
+        const float2 p = ld_dev2(pbase + s2 * stride + mt * 512);
         v0[mt] += p.x;
         v1[mt] += p.y;
       }
-      if (RMS && tid < 16 * MT)
-        ssum += ga.ss_part[((size_t)s2 * ga.n_groups + g) * 64 + tid];
+      if (RMS && tid < 16 * MT) ssum += ld_dev(&ga.ss_part[((size_t)s2 * ga.n_groups + g) * 64 + tid]);
     }
-    if (tid == 0) atomicExch(&ga.counters[g], 0u);
   }
 
   if (RMS) {
