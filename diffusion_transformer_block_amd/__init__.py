@@ -22,6 +22,7 @@ from ._lib import (BLK_EHIP, BLK_EINVAL, BLK_ESIZE, BLK_ESTATE, BLK_EUNSUPPORTED
 
 __all__ = ["BlkConfig", "BlkError", "make_config", "blk_prepare_weights", "blk_forward",
            "flow_denoise", "blk_last_error", "blk_release", "blk_version", "EXPORTS",
+           "blk_set_execution_mode", "EXEC_AUTO", "EXEC_PER_OPERATOR", "EXEC_PERSISTENT",
            "forward_workspace_bytes", "flow_workspace_bytes", "packed_bytes"]
 
 
@@ -181,3 +182,12 @@ def blk_release() -> None:
 
 def blk_version() -> int:
     return load().blk_version()
+
+
+EXEC_AUTO, EXEC_PER_OPERATOR, EXEC_PERSISTENT = 0, 1, 2
+
+
+def blk_set_execution_mode(mode: int) -> None:
+    """0: persistent stage kernel where it applies (default); 1: one kernel per
+    operator; 2: persistent kernel only."""
+    check("blk_set_execution_mode", load().blk_set_execution_mode(mode))

@@ -18,7 +18,7 @@ ERROR_NAMES = {BLK_EINVAL: "BLK_EINVAL", BLK_EUNSUPPORTED: "BLK_EUNSUPPORTED",
 
 # every function include/blk.h declares
 EXPORTS = ("blk_prepare_weights", "blk_forward", "flow_denoise", "blk_last_error",
-           "blk_release", "blk_version")
+           "blk_release", "blk_version", "blk_set_execution_mode")
 
 
 class BlkConfig(ctypes.Structure):
@@ -69,6 +69,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.blk_release.restype = None
     lib.blk_version.argtypes = []
     lib.blk_version.restype = c_int
+    lib.blk_set_execution_mode.argtypes = [c_int]
+    lib.blk_set_execution_mode.restype = c_int
     _lib = lib
     return lib
 

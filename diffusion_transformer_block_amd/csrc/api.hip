@@ -16,6 +16,7 @@
 #include "../../include/blk.h"
 #include "common.h"
 #include "internal.h"
+#include "stage.h"
 
 using namespace blk;
 
@@ -158,6 +159,7 @@ int lookup(const void* packed, const blk_config& cfg, PackRecord* out) {
 struct BlockWs {
   size_t q, o, h, a, r1, r2, part, ss, att_o, att_ml;
   size_t ctr_qkv, ctr_o, ctr_gu, ctr_d, ctr_att;
+  size_t xb0, xb1, flags, sync;
   size_t total;
 };
 
@@ -189,6 +191,12 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
                   std::max(skinny_ss_floats(m, D, ggu), skinny_ss_floats(m, F, gd)));
   }
   part = std::max(part, extra_part);
+  if ((int)M <= kSkinnyMaxM && M > 0) {
+    const int m = (int)M;
+    part = std::max(part, std::max(std::max(stage_part_floats(m, D, gq), stage_part_floats(m, Hq * d, go)),
+                                   std::max(stage_part_floats(m, D, ggu), stage_part_floats(m, F, gd))));
+    ss = std::max(ss, (size_t)64 * std::max(std::max(stage_split(m, D) * gq, stage_split(m, D) * ggu), 1));
+  }
   w.part = off;
   off += align_up(part * 4);
   w.ss = off;
@@ -207,6 +215,14 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
   off += align_up((size_t)gd * 4);
   w.ctr_att = off;
   off += align_up(attn_counters(B, T, P, Hq, Hkv, d) * 4);
+  w.xb0 = off;
+  off += align_up(M * D * 2);
+  w.xb1 = off;
+  off += align_up(M * D * 2);
+  w.flags = off;
+  off += align_up((size_t)kPhCount * kStageMaxFlags * 4);
+  w.sync = off;
+  off += align_up(4 * 4);
   w.total = off;
   return w;
 }
@@ -218,6 +234,106 @@ T* at(void* base, size_t off) {
 template <class T>
 const T* at(const void* base, size_t off) {
   return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
+}
+
+// ---------------------------------------------------------------- persistent stage plan
+int g_exec_mode = 0;   // 0 auto, 1 per-operator kernels, 2 persistent stage kernel only
+
+// Whether auto mode takes the persistent stage kernel.  It does not yet: on the
+// 64-token block the graph of per-operator kernels measures faster.
+bool want_persistent() { return g_exec_mode == 2; }
+
+// Fills the shapes, phase maps and attention plan of a stage launch; false if
+// the persistent kernel does not cover this shape (the caller falls back to
+// one kernel per operator).
+bool stage_plan(const blk_config& c, int B, int T, int P, int flow_N, int nwg, StageArgs& sa) {
+  const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const int M = B * T;
+  if (nwg <= 0 || M <= 0 || M > kSkinnyMaxM) return false;
+  if (D % 128 != 0 || F % 128 != 0 || (Hq * d) % 128 != 0) return false;
+  if (flow_N > 0 && flow_N + 1 != M) return false;
+  sa.split_qkv = stage_split(M, D);
+  sa.split_o = stage_split(M, Hq * d);
+  sa.split_gu = stage_split(M, D);
+  sa.split_d = stage_split(M, F);
+  sa.split_w3 = stage_split(M, D);
+  for (int sp : {sa.split_qkv, sa.split_o, sa.split_gu, sa.split_d, sa.split_w3})
+    if (sp < 1) return false;
+  const int G_q = (Hq + 2 * Hkv) * d / 32, G_o = D / 32, G_gu = F / 16, G_d = D / 32;
+  const int gq = G_q * sa.split_qkv, n_o = G_o * sa.split_o, n_gu = G_gu * sa.split_gu,
+            n_d = G_d * sa.split_d, n_w3 = G_o * sa.split_w3;
+  int splits = 1, kps = 0;
+  attn_plan(B, T, P, Hq, Hkv, d, &splits, &kps);
+  const int n_rbt = B * Hkv * (((Hq / Hkv) * T + 63) / 64);
+  const int n_att = n_rbt * splits;
+  const int n_emb = (flow_N + 1 + 3) / 4;
+  for (int n : {gq, n_o, n_gu, n_d, n_w3, n_att, n_emb, flow_N})
+    if (n > kStageMaxFlags) return false;
+  sa.B = B;
+  sa.T = T;
+  sa.P = P;
+  sa.M = M;
+  sa.D = D;
+  sa.F = F;
+  sa.Hq = Hq;
+  sa.Hkv = Hkv;
+  sa.d = d;
+  sa.eps = c.rms_eps;
+  sa.att_splits = splits;
+  sa.att_kps = kps;
+  sa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+  int w0 = 0;
+  auto map = [&](int type, int n_tasks, int n_flags) {
+    PhaseMap& m = sa.ph[type];
+    m.n_tasks = n_tasks;
+    m.n_flags = n_flags;
+    m.nw = std::max(1, std::min(n_tasks, nwg));
+    m.w0 = w0 % nwg;
+    w0 = (w0 + n_tasks) % nwg;
+  };
+  if (flow_N > 0) {
+    map(kPhEMB, n_emb, n_emb);
+    map(kPhW3, n_w3, G_o);
+  }
+  map(kPhQKV, gq, G_q);
+  map(kPhATT, n_att, n_rbt);
+  map(kPhO, n_o, G_o);
+  map(kPhGU, n_gu, G_gu);
+  map(kPhD, n_d, G_d);
+  if (flow_N > 0) map(kPhVEL, flow_N, flow_N);
+  return true;
+}
+
+void stage_fill_common(StageArgs& sa, const Layout& lay, const void* packed, void* ws,
+                       const BlockWs& w) {
+  sa.packed = reinterpret_cast<const uint8_t*>(packed);
+  sa.layer0 = lay.layer0;
+  sa.layer_bytes = lay.layer_bytes;
+  sa.off_qkv = lay.wqkv;
+  sa.off_o = lay.wo;
+  sa.off_gu = lay.wgu;
+  sa.off_d = lay.wd;
+  sa.cos_t = at<float>(packed, lay.rope_cos);
+  sa.sin_t = at<float>(packed, lay.rope_sin);
+  sa.xb[0] = at<bf16_t>(ws, w.xb0);
+  sa.xb[1] = at<bf16_t>(ws, w.xb1);
+  sa.q = at<bf16_t>(ws, w.q);
+  sa.o = at<bf16_t>(ws, w.o);
+  sa.h = at<bf16_t>(ws, w.h);
+  sa.a = at<bf16_t>(ws, w.a);
+  sa.part_o = at<float>(ws, w.att_o);
+  sa.part_ml = at<float>(ws, w.att_ml);
+  sa.att_ctr = at<unsigned>(ws, w.ctr_att);
+  sa.part = at<float>(ws, w.part);
+  sa.ss_part = at<float>(ws, w.ss);
+  sa.ctr_qkv = at<unsigned>(ws, w.ctr_qkv);
+  sa.ctr_o = at<unsigned>(ws, w.ctr_o);
+  sa.ctr_gu = at<unsigned>(ws, w.ctr_gu);
+  sa.ctr_d = at<unsigned>(ws, w.ctr_d);
+  sa.flags = at<unsigned>(ws, w.flags);
+  sa.epoch = at<unsigned>(ws, w.sync);
+  sa.done_ctr = at<unsigned>(ws, w.sync) + 1;
+  sa.abort_word = at<unsigned>(ws, w.sync) + 2;
 }
 
 // ---------------------------------------------------------------- block driver
@@ -458,6 +574,13 @@ const char* blk_last_error(void) { return g_err.c_str(); }
 
 int blk_version(void) { return 1; }
 
+int blk_set_execution_mode(int mode) {
+  g_err.clear();
+  if (mode < 0 || mode > 2) return fail(BLK_EINVAL, "execution mode %d not in {0, 1, 2}", mode);
+  g_exec_mode = mode;
+  return BLK_OK;
+}
+
 void blk_release(void) {
   {
     std::lock_guard<std::mutex> lk(g_graph_mu);
@@ -604,6 +727,28 @@ int blk_forward(const blk_config* cfg, const void* packed, int layer, int batch,
   }
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
+  if (want_persistent()) {
+    StageArgs sa{};
+    const int nwg = stage_grid(cfg->head_dim, batch * tokens);
+    if (stage_plan(*cfg, batch, tokens, prefix, 0, nwg, sa)) {
+      stage_fill_common(sa, rec.lay, packed, ws, w);
+      sa.flow = 0;
+      sa.n_layers = 1;
+      sa.layer_first = layer;
+      sa.n_steps = 1;
+      sa.x = x;
+      sa.y = y;
+      sa.kn = k_new;
+      sa.vn = v_new;
+      sa.new_stride = new_stride;
+      sa.kp[0] = k_prefix;
+      sa.vp[0] = v_prefix;
+      sa.prefix_stride = prefix_stride;
+      HIP_TRY(launch_stage(sa, nwg, st));
+      return BLK_OK;
+    }
+    if (g_exec_mode == 2) return fail(BLK_EUNSUPPORTED, "the persistent stage kernel does not cover this shape");
+  }
   BlockIO io{x, k_prefix, v_prefix, prefix_stride, y, k_new, v_new, new_stride};
   enqueue_block(*cfg, rec.lay, packed, layer, batch, tokens, prefix, io, ws, w, st);
   HIP_TRY(hipGetLastError());
@@ -659,6 +804,7 @@ int flow_denoise(const blk_config* cfg, const void* packed, int n_layers, int n_
     key.ptrs.push_back(prefix > 0 ? k_prefix[l] : nullptr);
     key.ptrs.push_back(prefix > 0 ? v_prefix[l] : nullptr);
   }
+  key.ptrs.push_back(reinterpret_cast<const void*>((uintptr_t)g_exec_mode));
   key.ptrs.push_back(noise);
   key.ptrs.push_back(state);
   key.ptrs.push_back(actions);
@@ -680,10 +826,54 @@ int flow_denoise(const blk_config* cfg, const void* packed, int n_layers, int n_
     HIP_TRY(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
     GraphEntry e;
     (void)hipGetLastError();
+    StageArgs sa{};
+    const int nwg = want_persistent() ? stage_grid(cfg->head_dim, lay.n_actions + 1) : 0;
+    const bool use_stage = nwg > 0 && n_layers <= kStageMaxLayers &&
+                           stage_plan(*cfg, 1, lay.n_actions + 1, prefix, lay.n_actions, nwg, sa);
+    if (!use_stage && g_exec_mode == 2) {
+      (void)hipStreamDestroy(cs);
+      return fail(BLK_EUNSUPPORTED, "the persistent stage kernel does not cover this shape");
+    }
+    if (use_stage) {
+      stage_fill_common(sa, lay, packed, ws, fw.blk);
+      sa.flow = 1;
+      sa.n_layers = n_layers;
+      sa.layer_first = 0;
+      sa.n_steps = n_steps;
+      sa.xb[0] = at<bf16_t>(ws, fw.x0);
+      sa.xb[1] = at<bf16_t>(ws, fw.x1);
+      sa.kn = at<bf16_t>(ws, fw.kn);
+      sa.vn = at<bf16_t>(ws, fw.vn);
+      sa.new_stride = 0;
+      for (int l = 0; l < n_layers; ++l) {
+        sa.kp[l] = kp[l];
+        sa.vp[l] = vp[l];
+      }
+      sa.prefix_stride = 0;
+      sa.N = lay.n_actions;
+      sa.A = lay.action_dim;
+      sa.w_fused = at<float>(packed, lay.h_wfused);
+      sa.table = at<float>(packed, lay.h_table);
+      sa.dt = at<float>(packed, lay.h_dt);
+      sa.w3 = at<uint8_t>(packed, lay.h_w3);
+      sa.b3 = at<float>(packed, lay.h_b3);
+      sa.ws_f = at<float>(packed, lay.h_ws);
+      sa.bs = at<float>(packed, lay.h_bs);
+      sa.w_out = at<float>(packed, lay.h_wout);
+      sa.b_out = at<float>(packed, lay.h_bout);
+      sa.noise = noise;
+      sa.state = state;
+      sa.actions = actions;
+      sa.z = at<bf16_t>(ws, fw.z);
+    }
     hipError_t err = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
     if (err == hipSuccess) {
-      enqueue_flow(*cfg, lay, packed, n_layers, n_steps, prefix, kp.data(), vp.data(), noise,
-                   state, actions, ws, fw, cs);
+      if (use_stage) {
+        (void)launch_stage(sa, nwg, cs);
+      } else {
+        enqueue_flow(*cfg, lay, packed, n_layers, n_steps, prefix, kp.data(), vp.data(), noise,
+                     state, actions, ws, fw, cs);
+      }
       hipError_t launch_err = hipGetLastError();
       err = hipStreamEndCapture(cs, &e.graph);
       if (err == hipSuccess) err = launch_err;

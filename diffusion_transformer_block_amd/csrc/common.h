@@ -63,6 +63,28 @@ __device__ __forceinline__ float2 ld_dev2(const float* p) {
 }
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Activations (bf16) produced by one workgroup and read by another within the
+// same kernel: coherent 16-byte loads (two 8-byte agent-scope loads) and
+// coherent 2-byte stores.
+__device__ __forceinline__ uint4 ld_act16(const bf16_t* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
+}
+__device__ __forceinline__ float ld_act(const bf16_t* p) {
+  return bf2f(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void st_act(bf16_t* p, float v) {
+  __hip_atomic_store(p, f2bf(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_act_bits(bf16_t* p, bf16_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_f32c(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Publish this workgroup's partial (already stored with st_dev*) and report
 // whether it is the last of `expected` workgroups to arrive at `counter`.  The
 // last one resets the counter to zero for the next launch.  Call with every

@@ -23,145 +23,16 @@
 //    fragments) loaded straight into registers one step ahead; 2 x 2 waves of
 //    64 x 64 each.
 #include "common.h"
+#include "gemm_dev.h"
 #include "internal.h"
 
 namespace blk {
 
-__device__ __forceinline__ float sumsq8(uint4 v) {
-  float s = 0.f;
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = __uint_as_float(w[i] << 16);
-    const float hi = __uint_as_float(w[i] & 0xffff0000u);
-    s = fmaf(lo, lo, s);
-    s = fmaf(hi, hi, s);
-  }
-  return s;
-}
-
 // ============================================================================ skinny
-template <int MT, int UK, bool RMS, class Epi>
+template <int MT, bool RMS, class Epi>
 __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs ga, Epi epi) {
-  __shared__ __attribute__((aligned(16))) float red[4][MT * 512];
-  __shared__ float ssr[4][16 * MT];
-  __shared__ float rrow[16 * MT];
-  __shared__ int last_flag;
-
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
-  const int g = blockIdx.x, s = blockIdx.y;
-  const int KT = ga.K >> 5;
-  const int KTS = KT / ga.splits;
-  const int KW = KTS >> 2;
-  const int kt0 = s * KTS + w * KW;
-
-  const bf16_t* arow[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int row = min(16 * mt + lr, ga.M - 1);
-    arow[mt] = ga.A + (size_t)row * ga.lda + (size_t)kt0 * 32 + 8 * lg;
-  }
-  const uint4* bp = reinterpret_cast<const uint4*>(ga.Bp + frag_offset(g, kt0, 0, KT)) + l;
-
-  f32x4 acc[MT][2];
-  float ss[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    acc[mt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    ss[mt] = 0.f;
-  }
-
-  for (int u = 0; u < KW; u += UK) {
-    uint4 bv[UK][2];
-    uint4 av[UK][MT];
-#pragma unroll
-    for (int q = 0; q < UK; ++q) {
-      bv[q][0] = ld_stream(bp + (u + q) * 128);
-      bv[q][1] = ld_stream(bp + (u + q) * 128 + 64);
-    }
-#pragma unroll
-    for (int q = 0; q < UK; ++q)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        av[q][mt] = *reinterpret_cast<const uint4*>(arow[mt] + (u + q) * 32);
-#pragma unroll
-    for (int q = 0; q < UK; ++q)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (RMS) ss[mt] += sumsq8(av[q][mt]);
-        acc[mt][0] = mfma16(as_bf16x8(av[q][mt]), as_bf16x8(bv[q][0]), acc[mt][0]);
-        acc[mt][1] = mfma16(as_bf16x8(av[q][mt]), as_bf16x8(bv[q][1]), acc[mt][1]);
-      }
-  }
-
-  // ---- reduce the four waves' K ranges through LDS
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<f32x4*>(&red[w][((mt * 2 + i) * 64 + l) * 4]) = acc[mt][i];
-  if (RMS) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      float v = ss[mt];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      if (lg == 0) ssr[w][16 * mt + lr] = v;
-    }
-  }
-  __syncthreads();
-
-  float v0[MT], v1[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int i0 = ((mt * 2 + 0) * 64 + (tid >> 2)) * 4 + (tid & 3);
-    const int i1 = ((mt * 2 + 1) * 64 + (tid >> 2)) * 4 + (tid & 3);
-    v0[mt] = ((red[0][i0] + red[1][i0]) + red[2][i0]) + red[3][i0];
-    v1[mt] = ((red[0][i1] + red[1][i1]) + red[2][i1]) + red[3][i1];
-  }
-  float ssum = 0.f;
-  if (RMS && tid < 16 * MT) ssum = ((ssr[0][tid] + ssr[1][tid]) + ssr[2][tid]) + ssr[3][tid];
-
-  // ---- K splits: publish, count arrivals, the last workgroup sums in order
-  if (ga.splits > 1) {
-    const size_t stride = (size_t)ga.n_groups * MT * 256 * 2;   // floats per split
-    float* pbase = ga.part + ((size_t)g * MT * 256 + tid) * 2;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) st_dev2(pbase + s * stride + mt * 512, v0[mt], v1[mt]);
-    if (RMS && tid < 16 * MT) st_dev(&ga.ss_part[((size_t)s * ga.n_groups + g) * 64 + tid], ssum);
-    if (!arrive_last(&ga.counters[g], (unsigned)ga.splits, &last_flag)) return;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      v0[mt] = 0.f;
-      v1[mt] = 0.f;
-    }
-    ssum = 0.f;
-    for (int s2 = 0; s2 < ga.splits; ++s2) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const float2 p = ld_dev2(pbase + s2 * stride + mt * 512);
-        v0[mt] += p.x;
-        v1[mt] += p.y;
-      }
-      if (RMS && tid < 16 * MT) ssum += ld_dev(&ga.ss_part[((size_t)s2 * ga.n_groups + g) * 64 + tid]);
-    }
-  }
-
-  if (RMS) {
-    if (tid < 16 * MT) rrow[tid] = rsqrtf(ssum / (float)ga.K + ga.eps);
-    __syncthreads();
-  }
-  const int c = (tid >> 2) & 15;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = 16 * mt + 4 * (tid >> 6) + (tid & 3);
-    if (m < ga.M) {
-      const float r = RMS ? rrow[m] : (ga.r ? ga.r[m] : 1.f);
-      epi.store(m, g, c, v0[mt], v1[mt], r);
-    }
-  }
+  __shared__ SkinnySmem sm;
+  skinny_task<MT, RMS>(ga, epi, blockIdx.x, blockIdx.y, sm, NoWait{});
 }
 
 int skinny_splits(int M, int K, int n_groups) {
@@ -189,30 +60,20 @@ size_t skinny_ss_floats(int M, int K, int n_groups) {
   return (size_t)s * n_groups * 64;
 }
 
-template <int MT, int UK, bool RMS, class Epi>
-static void skinny_go(const GemmArgs& ga, const Epi& e, hipStream_t st) {
-  skinny_gemm_kernel<MT, UK, RMS, Epi><<<dim3(ga.n_groups, ga.splits), 256, 0, st>>>(ga, e);
-}
-
 template <int MT, bool RMS, class Epi>
-static void skinny_uk(const GemmArgs& ga, const Epi& e, int UK, hipStream_t st) {
-  if (UK == 4) skinny_go<MT, 4, RMS>(ga, e, st);
-  else if (UK == 2) skinny_go<MT, 2, RMS>(ga, e, st);
-  else skinny_go<MT, 1, RMS>(ga, e, st);
+static void skinny_go(const GemmArgs& ga, const Epi& e, hipStream_t st) {
+  skinny_gemm_kernel<MT, RMS, Epi><<<dim3(ga.n_groups, ga.splits), 256, 0, st>>>(ga, e);
 }
 
 template <bool RMS, class Epi>
 static void launch_skinny(GemmArgs ga, const Epi& e, hipStream_t st) {
   ga.splits = skinny_splits(ga.M, ga.K, ga.n_groups);
-  const int KW = (ga.K / 32) / ga.splits / 4;
-  // the unroll must divide the per-wave k-tile count exactly
-  const int UK = (KW % 4 == 0) ? 4 : (KW % 2 == 0) ? 2 : 1;
   const int MT = (ga.M + 15) / 16;
   switch (MT) {
-    case 1: skinny_uk<1, RMS>(ga, e, UK, st); break;
-    case 2: skinny_uk<2, RMS>(ga, e, UK, st); break;
-    case 3: skinny_uk<3, RMS>(ga, e, UK, st); break;
-    default: skinny_uk<4, RMS>(ga, e, UK, st); break;
+    case 1: skinny_go<1, RMS>(ga, e, st); break;
+    case 2: skinny_go<2, RMS>(ga, e, st); break;
+    case 3: skinny_go<3, RMS>(ga, e, st); break;
+    default: skinny_go<4, RMS>(ga, e, st); break;
   }
 }
 

@@ -38,6 +38,9 @@ void launch_copy_f32(const float* in, size_t n, float* out, hipStream_t st);
 // Each epilogue receives one output pair: row m, group g, column c < 16 inside
 // the group's tiles, the fp32 sums v0 (tile 0) and v1 (tile 1), and the row
 // scale r (the RMS statistic, or 1 when the GEMM has no norm ahead of it).
+// store1 takes a single tile i of group g (only for plain column groups).
+// Loads of activations and all stores are device-coherent, so a consumer
+// workgroup of the same persistent kernel can read them.
 
 // Fused QKV: scale by r, rotate (Q, K) pairs, scatter into Q / K_new / V_new.
 struct EpiQKV {
@@ -69,13 +72,13 @@ struct EpiQKV {
       } else {
         dst = kn + (size_t)b * new_stride + ((size_t)t * Hkv + (head - Hq)) * d;
       }
-      dst[j] = f2bf(lo);
-      dst[j + half] = f2bf(hi);
+      st_act(dst + j, lo);
+      st_act(dst + j + half, hi);
     } else {
       const int col0 = 32 * (g - n_rot_groups) + c;
       bf16_t* base = vn + (size_t)b * new_stride + (size_t)t * Hkv * d;
-      base[col0] = f2bf(v0);       // V row layout [Hkv][d] is contiguous in col
-      base[col0 + 16] = f2bf(v1);
+      st_act(base + col0, v0);       // V row layout [Hkv][d] is contiguous in col
+      st_act(base + col0 + 16, v1);
     }
   }
 };
@@ -87,8 +90,12 @@ struct EpiResidual {
   int ld;
   __device__ __forceinline__ void store(int m, int g, int c, float v0, float v1, float) const {
     const size_t o = (size_t)m * ld + 32 * g + c;
-    out[o] = f2bf(bf2f(res[o]) + v0);
-    out[o + 16] = f2bf(bf2f(res[o + 16]) + v1);
+    st_act(out + o, ld_act(res + o) + v0);
+    st_act(out + o + 16, ld_act(res + o + 16) + v1);
+  }
+  __device__ __forceinline__ void store1(int m, int g, int i, int c, float v, float) const {
+    const size_t o = (size_t)m * ld + 32 * g + 16 * i + c;
+    st_act(out + o, ld_act(res + o) + v);
   }
 };
 
@@ -97,7 +104,7 @@ struct EpiGateUp {
   bf16_t* out;
   int ld;
   __device__ __forceinline__ void store(int m, int g, int c, float v0, float v1, float r) const {
-    out[(size_t)m * ld + 16 * g + c] = f2bf(silu(v0 * r) * (v1 * r));
+    st_act(out + (size_t)m * ld + 16 * g + c, silu(v0 * r) * (v1 * r));
   }
 };
 
@@ -110,8 +117,12 @@ struct EpiBias {
   __device__ __forceinline__ void store(int m, int g, int c, float v0, float v1, float) const {
     const int n = 32 * g + c;
     bf16_t* o = out + (size_t)(m + row_off) * ld + n;
-    o[0] = f2bf(v0 + bias[n]);
-    o[16] = f2bf(v1 + bias[n + 16]);
+    st_act(o, v0 + bias[n]);
+    st_act(o + 16, v1 + bias[n + 16]);
+  }
+  __device__ __forceinline__ void store1(int m, int g, int i, int c, float v, float) const {
+    const int n = 32 * g + 16 * i + c;
+    st_act(out + (size_t)(m + row_off) * ld + n, v + bias[n]);
   }
 };
 

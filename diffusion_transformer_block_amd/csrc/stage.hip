@@ -1,0 +1,497 @@
+// Persistent stage kernel for small chunks (M = B * T <= 64 rows).
+//
+// [TR] TileRT article: at decode-sized work, kernel launches, cross-kernel
+// barriers and memory round trips between operators dominate ("execution
+// gaps"); the remedy is one resident kernel that runs the whole operator
+// sequence as tile tasks.  [RT] reading note on "Running VLAs at Real-time
+// Speed" §3 (graph capture) and §6.2 (the action expert is memory bound).
+//
+// One launch runs a whole program -- one block stage ([PS] a stage is one
+// block at one denoise step), several layers, or the full flow-matching loop
+// ([RT] §2: 10 steps x 18 layers plus the suffix embedding and the velocity
+// head) -- on one workgroup per compute unit.  Each operator is a phase made of
+// independent tasks:
+//   QKV  one 32-column group of the fused QKV matrix, full K, RMS + RoPE epilogue
+//   ATT  one 64-row block x key slice of chunk attention (split slices combine
+//        in the last-arriving workgroup)
+//   O    one 16-column tile of W_o, full K, residual epilogue
+//   GU   one gate/up group, full K, RMS + SiLU-gate epilogue
+//   D    one 16-column tile of W_down, full K, residual epilogue
+//   EMB, W3, VEL  the flow head (embedding, its linear, velocity + Euler step)
+// Task t of a phase runs on workgroup (w0 + t mod nw); the phases' workgroup
+// sets are rotated so that consecutive phases start on different units.
+//
+// Hand-off: a task's outputs are written with device-coherent stores; after
+// they are acknowledged the workgroup writes the task's flag = the phase's
+// epoch.  A workgroup entering a phase polls (one wave, coherent loads, one
+// flag per lane) until every task of the previous phase has published, which
+// orders each phase after all earlier ones.  Epochs grow monotonically across
+// launches (the last workgroup to finish advances the base), so flags never
+// need clearing and a replayed graph stays correct.  Every wait is bounded: on
+// time-out the workgroup raises an abort word that all other waits also watch,
+// so the grid always drains; a workspace with the abort word set makes later
+// launches return at once.
+#include "attn_dev.h"
+#include "common.h"
+#include "gemm_dev.h"
+#include "internal.h"
+#include "stage.h"
+
+namespace blk {
+
+constexpr unsigned kMaxSpins = 1u << 22;   // ~ seconds of polling
+
+__device__ __forceinline__ unsigned ld_u32c(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_u32c(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave 0 polls flags[0 .. n) until all equal `want`; returns false on abort.
+__device__ bool wait_flags(const unsigned* flags, int n, unsigned want, unsigned* abort_word,
+                           int* ok_sh) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    unsigned spins = 0;
+    int ok = 1;
+    for (;;) {
+      bool ready = true;
+      for (int i = lane; i < n; i += 64) ready &= ld_u32c(flags + i) == want;
+      if (__all(ready)) break;
+      if (ld_u32c(abort_word) != 0u) {
+        ok = 0;
+        break;
+      }
+      if (++spins > kMaxSpins) {
+        if (lane == 0) st_u32c(abort_word, 1u);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (lane == 0) *ok_sh = ok;
+  }
+  __syncthreads();
+  return *ok_sh != 0;
+}
+
+// All of this workgroup's task outputs are acknowledged, then publish.
+__device__ __forceinline__ void signal_flag(unsigned* flag, unsigned value) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) st_u32c(flag, value);
+}
+
+// ---------------------------------------------------------------- flow head tasks
+struct FlowSmem {
+  float xs[8192];
+  float red[256];
+  float vin[4][64];
+  float wsum[4];
+};
+
+// Per-step view of the flow head.
+struct FlowTask {
+  const float* a_in;      // actions at this step's start (noise at step 0)
+  const float* state;
+  const float* w_fused;   // [A][D] W1 W2a
+  const float* bias;      // [D] time table row of this step
+  const float* ws_f;      // [A][D]
+  const float* bs;
+  bf16_t* z;              // [N][D]
+  bf16_t* x0;             // X row 0 (state token)
+  const bf16_t* X;        // [N + 1][D] output of the last layer
+  const float* w_out;     // [D][A] (final gain folded)
+  const float* b_out;
+  float* actions;         // [N][A]
+  float dt;
+  int N, A, D;
+  float eps;
+};
+
+// rows [4t, 4t + 4) of [z rows 0..N-1 ; state row N]
+__device__ void emb_task(const FlowTask& f, int t, FlowSmem& fs) {
+  const int r0 = 4 * t;
+  const int nr = min(4, f.N + 1 - r0);
+  __syncthreads();
+  for (int i = threadIdx.x; i < nr * f.A; i += 256) {
+    const int rr = i / f.A, k = i - rr * f.A;
+    const int r = r0 + rr;
+    fs.vin[rr][k] = r < f.N ? ld_f32c(f.a_in + (size_t)r * f.A + k) : f.state[k];
+  }
+  __syncthreads();
+  for (int n = threadIdx.x; n < f.D; n += 256) {
+    for (int rr = 0; rr < nr; ++rr) {
+      const int r = r0 + rr;
+      if (r < f.N) {
+        float acc = f.bias[n];
+        for (int k = 0; k < f.A; ++k) acc = fmaf(fs.vin[rr][k], f.w_fused[(size_t)k * f.D + n], acc);
+        st_act(f.z + (size_t)r * f.D + n, silu(acc));
+      } else {
+        float acc = f.bs[n];
+        for (int k = 0; k < f.A; ++k) acc = fmaf(fs.vin[rr][k], f.ws_f[(size_t)k * f.D + n], acc);
+        st_act(f.x0 + n, acc);
+      }
+    }
+  }
+}
+
+// action row i: v = RMS(X[i+1]) . W_out' + b_out; actions[i] = a_in[i] + dt v
+__device__ void vel_task(const FlowTask& f, int i, FlowSmem& fs) {
+  const int tid = threadIdx.x;
+  const bf16_t* xr = f.X + (size_t)(i + 1) * f.D;
+  __syncthreads();
+  float ss = 0.f;
+  for (int k = tid; k < f.D; k += 256) {
+    const float v = ld_act(xr + k);
+    fs.xs[k] = v;
+    ss = fmaf(v, v, ss);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((tid & 63) == 0) fs.wsum[tid >> 6] = ss;
+  __syncthreads();
+  const float r = rsqrtf(((fs.wsum[0] + fs.wsum[1]) + (fs.wsum[2] + fs.wsum[3])) / (float)f.D + f.eps);
+  const int nsl = 256 / f.A;
+  const int col = tid % f.A, sl = tid / f.A;
+  float acc = 0.f;
+  if (sl < nsl) {
+    const int kper = (f.D + nsl - 1) / nsl;
+    const int k0 = sl * kper, k1 = min(f.D, k0 + kper);
+    for (int k = k0; k < k1; ++k) acc = fmaf(fs.xs[k], f.w_out[(size_t)k * f.A + col], acc);
+  }
+  fs.red[tid] = acc;
+  __syncthreads();
+  if (tid < f.A) {
+    float v = 0.f;
+    for (int q = 0; q < nsl; ++q) v += fs.red[q * f.A + tid];
+    v = v * r + f.b_out[tid];
+    const float a = ld_f32c(f.a_in + (size_t)i * f.A + tid);
+    __hip_atomic_store(f.actions + (size_t)i * f.A + tid, a + f.dt * v, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ---------------------------------------------------------------- tasks
+// Each task runs in its own (non-inlined) function so that its register
+// allocation does not inherit the pressure of the others; it receives small
+// argument structs by value (the kernel's large argument block never escapes).
+// `wait` performs the wait for the producing step; a GEMM task calls it after
+// issuing its weight loads.  Return: true if the task completed its outputs.
+
+template <int MT, bool RMS, class Epi, class W>
+__device__ __noinline__ bool gemm_run(GemmArgs ga, Epi e, int g, int s, SkinnySmem& sm, W& wait) {
+  return skinny_task<MT, RMS>(ga, e, g, s, sm, wait);
+}
+
+template <int HD, class W>
+__device__ __noinline__ bool attn_run(AttnArgs aa, int qb, int bh, int split, AttnSmem<HD>& sm,
+                                      W& wait) {
+  if (!wait()) return false;
+  return attn_task<HD>(aa, qb, bh, split, sm);
+}
+
+template <class W>
+__device__ __noinline__ bool emb_run(FlowTask f, int t, FlowSmem& fs, W& wait) {
+  if (!wait()) return false;
+  emb_task(f, t, fs);
+  return true;
+}
+
+template <class W>
+__device__ __noinline__ bool vel_run(FlowTask f, int t, FlowSmem& fs, W& wait) {
+  if (!wait()) return false;
+  vel_task(f, t, fs);
+  return true;
+}
+
+// ---------------------------------------------------------------- the kernel
+template <int MT, int HD>
+__global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ unsigned e0_sh;
+  __shared__ int ok_sh;
+  SkinnySmem& gsm = *reinterpret_cast<SkinnySmem*>(smem);
+  AttnSmem<HD>& asm_ = *reinterpret_cast<AttnSmem<HD>*>(smem);
+  FlowSmem& fsm = *reinterpret_cast<FlowSmem*>(smem);
+
+  if (threadIdx.x == 0) {
+    e0_sh = ld_u32c(sa.epoch);
+    ok_sh = ld_u32c(sa.abort_word) == 0u;
+  }
+  __syncthreads();
+  if (!ok_sh) return;
+  const unsigned e0 = e0_sh;
+  unsigned phi = 0;
+  int prev = -1;
+  const int nwg = gridDim.x;
+  unsigned* const flags = sa.flags;
+  unsigned* const abort_word = sa.abort_word;
+
+  // Runs this workgroup's tasks of phase `type`.  task(t, wait) returns the
+  // flag index to publish (or -1); wait() waits once per phase for every task
+  // of the previous phase.  Returns false if the grid aborted.
+  auto phase = [&](int type, auto&& task) -> bool {
+    ++phi;
+    const PhaseMap pm = sa.ph[type];
+    const int my = (int)((blockIdx.x + nwg - pm.w0) % nwg);
+    bool waited = prev < 0, alive = true;
+    const unsigned* pflags = flags + (prev < 0 ? 0 : prev) * kStageMaxFlags;
+    const int pn = prev < 0 ? 0 : sa.ph[prev].n_flags;
+    const unsigned want = e0 + phi - 1;
+    int* okp = &ok_sh;
+    auto wait = [&waited, &alive, pflags, pn, want, abort_word, okp]() -> bool {
+      if (!waited) {
+        waited = true;
+        alive = wait_flags(pflags, pn, want, abort_word, okp);
+      }
+      return alive;
+    };
+    if (my < pm.nw) {
+      for (int t = my; t < pm.n_tasks; t += pm.nw) {
+        const int fl = task(t, wait);
+        if (!alive) return false;
+        if (fl >= 0) signal_flag(flags + type * kStageMaxFlags + fl, e0 + phi);
+      }
+    }
+    prev = type;
+    return true;
+  };
+
+  const int D = sa.D, F = sa.F, d = sa.d, Hq = sa.Hq, Hkv = sa.Hkv, M = sa.M;
+  const int n_rb = ((Hq / Hkv) * sa.T + 63) / 64;
+
+  auto run_layer = [&](int layer, const bf16_t* in, bf16_t* out, const bf16_t* kp,
+                       const bf16_t* vp) -> bool {
+    const uint8_t* lw = sa.packed + sa.layer0 + (size_t)layer * sa.layer_bytes;
+    GemmArgs base{};
+    base.M = M;
+    base.eps = sa.eps;
+    base.part = sa.part;
+    base.ss_part = sa.ss_part;
+    if (!phase(kPhQKV, [&](int t, auto& wait) {
+          GemmArgs ga = base;
+          ga.A = in;
+          ga.lda = D;
+          ga.K = D;
+          ga.Bp = lw + sa.off_qkv;
+          ga.n_groups = (Hq + 2 * Hkv) * d / 32;
+          ga.splits = sa.split_qkv;
+          ga.counters = sa.ctr_qkv;
+          const int g = t / ga.splits;
+          EpiQKV e{sa.q, sa.kn, sa.vn, sa.new_stride, sa.cos_t, sa.sin_t, sa.T, sa.P, Hq, Hkv, d};
+          return gemm_run<MT, true>(ga, e, g, t - g * ga.splits, gsm, wait) ? g : -1;
+        }))
+      return false;
+    if (!phase(kPhATT, [&](int t, auto& wait) {
+          AttnArgs aa{};
+          aa.q = sa.q;
+          aa.kp = kp;
+          aa.vp = vp;
+          aa.prefix_stride = sa.prefix_stride;
+          aa.kn = sa.kn;
+          aa.vn = sa.vn;
+          aa.new_stride = sa.new_stride;
+          aa.o = sa.o;
+          aa.B = sa.B;
+          aa.T = sa.T;
+          aa.P = sa.P;
+          aa.Hq = Hq;
+          aa.Hkv = Hkv;
+          aa.d = d;
+          aa.splits = sa.att_splits;
+          aa.keys_per_split = sa.att_kps;
+          aa.scale_log2 = sa.scale_log2;
+          aa.part_o = sa.part_o;
+          aa.part_ml = sa.part_ml;
+          aa.counters = sa.att_ctr;
+          const int rb = t / aa.splits, split = t - rb * aa.splits;
+          const int bh = rb / n_rb, qb = rb - bh * n_rb;
+          return attn_run<HD>(aa, qb, bh, split, asm_, wait) ? rb : -1;
+        }))
+      return false;
+    if (!phase(kPhO, [&](int t, auto& wait) {
+          GemmArgs ga = base;
+          ga.A = sa.o;
+          ga.lda = Hq * d;
+          ga.K = Hq * d;
+          ga.Bp = lw + sa.off_o;
+          ga.n_groups = D / 32;
+          ga.splits = sa.split_o;
+          ga.counters = sa.ctr_o;
+          const int g = t / ga.splits;
+          return gemm_run<MT, false>(ga, EpiResidual{in, sa.h, D}, g, t - g * ga.splits, gsm, wait) ? g : -1;
+        }))
+      return false;
+    if (!phase(kPhGU, [&](int t, auto& wait) {
+          GemmArgs ga = base;
+          ga.A = sa.h;
+          ga.lda = D;
+          ga.K = D;
+          ga.Bp = lw + sa.off_gu;
+          ga.n_groups = F / 16;
+          ga.splits = sa.split_gu;
+          ga.counters = sa.ctr_gu;
+          const int g = t / ga.splits;
+          return gemm_run<MT, true>(ga, EpiGateUp{sa.a, F}, g, t - g * ga.splits, gsm, wait) ? g : -1;
+        }))
+      return false;
+    return phase(kPhD, [&](int t, auto& wait) {
+      GemmArgs ga = base;
+      ga.A = sa.a;
+      ga.lda = F;
+      ga.K = F;
+      ga.Bp = lw + sa.off_d;
+      ga.n_groups = D / 32;
+      ga.splits = sa.split_d;
+      ga.counters = sa.ctr_d;
+      const int g = t / ga.splits;
+      return gemm_run<MT, false>(ga, EpiResidual{sa.h, out, D}, g, t - g * ga.splits, gsm, wait) ? g : -1;
+    });
+  };
+
+  bool ok = true;
+  if (!sa.flow) {
+    for (int li = 0; li < sa.n_layers && ok; ++li) {
+      const bf16_t* in = li == 0 ? sa.x : sa.xb[(li - 1) & 1];
+      bf16_t* out = li == sa.n_layers - 1 ? sa.y : sa.xb[li & 1];
+      ok = run_layer(sa.layer_first + li, in, out, sa.kp[0], sa.vp[0]);
+    }
+  } else {
+    for (int s = 0; s < sa.n_steps && ok; ++s) {
+      FlowTask f{};
+      f.a_in = s == 0 ? sa.noise : sa.actions;
+      f.state = sa.state;
+      f.w_fused = sa.w_fused;
+      f.bias = sa.table + (size_t)s * D;
+      f.ws_f = sa.ws_f;
+      f.bs = sa.bs;
+      f.z = sa.z;
+      f.x0 = sa.xb[0];
+      f.X = sa.xb[sa.n_layers & 1];
+      f.w_out = sa.w_out;
+      f.b_out = sa.b_out;
+      f.actions = sa.actions;
+      f.dt = sa.dt[s];
+      f.N = sa.N;
+      f.A = sa.A;
+      f.D = D;
+      f.eps = sa.eps;
+      ok = phase(kPhEMB, [&](int t, auto& wait) { return emb_run(f, t, fsm, wait) ? t : -1; });
+      if (ok)
+        ok = phase(kPhW3, [&](int t, auto& wait) {
+          GemmArgs ga{};
+          ga.A = sa.z;
+          ga.lda = D;
+          ga.M = sa.N;
+          ga.K = D;
+          ga.Bp = sa.w3;
+          ga.n_groups = D / 32;
+          ga.splits = sa.split_w3;
+          ga.part = sa.part;
+          ga.counters = sa.ctr_o;
+          const int g = t / ga.splits;
+          return gemm_run<MT, false>(ga, EpiBias{sa.b3, sa.xb[0], D, 1}, g, t - g * ga.splits, gsm, wait) ? g : -1;
+        });
+      for (int l = 0; l < sa.n_layers && ok; ++l)
+        ok = run_layer(l, sa.xb[l & 1], sa.xb[(l + 1) & 1], sa.kp[l], sa.vp[l]);
+      if (ok) ok = phase(kPhVEL, [&](int t, auto& wait) { return vel_run(f, t, fsm, wait) ? t : -1; });
+    }
+  }
+  if (!ok) return;
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(sa.done_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == (unsigned)nwg - 1u) {
+      st_u32c(sa.done_ctr, 0u);
+      st_u32c(sa.epoch, e0 + phi);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- host side
+template <int MT, int HD>
+static hipError_t go(const StageArgs& sa, int nwg, size_t smem, hipStream_t st) {
+  stage_kernel<MT, HD><<<nwg, 256, smem, st>>>(sa);
+  return hipGetLastError();
+}
+
+// Raises the kernel's dynamic LDS limit (outside any stream capture) and
+// returns how many of its workgroups fit on one compute unit.
+template <int MT, int HD>
+static int prepare(size_t smem) {
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&stage_kernel<MT, HD>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+    return 0;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stage_kernel<MT, HD>, 256, smem) != hipSuccess)
+    return 0;
+  return n;
+}
+
+template <int HD>
+static int prepare_mt(int mt, size_t smem) {
+  switch (mt) {
+    case 1: return prepare<1, HD>(smem);
+    case 2: return prepare<2, HD>(smem);
+    case 3: return prepare<3, HD>(smem);
+    default: return prepare<4, HD>(smem);
+  }
+}
+
+int stage_grid(int head_dim, int rows) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  const size_t smem = stage_smem_bytes(head_dim);
+  const int mt = (rows + 15) / 16;
+  const int occ = head_dim == 64 ? prepare_mt<64>(mt, smem)
+                  : head_dim == 128 ? prepare_mt<128>(mt, smem)
+                                    : prepare_mt<256>(mt, smem);
+  return occ >= 1 ? cus : 0;
+}
+
+int stage_split(int M, int K) {
+  const int KT = K / 32;
+  int s = 1;
+  while ((size_t)M * K * 2 / s > 131072 && KT % (8 * s) == 0) s *= 2;
+  while (KT / (4 * s) > kMaxPrefetch && KT % (8 * s) == 0) s *= 2;
+  return s;
+}
+
+size_t stage_part_floats(int M, int K, int n_groups) {
+  const int s = stage_split(M, K);
+  return s > 1 ? (size_t)s * n_groups * ((M + 15) / 16) * 256 * 2 : 0;
+}
+
+size_t stage_smem_bytes(int head_dim) {
+  size_t att = head_dim == 64    ? sizeof(AttnSmem<64>)
+               : head_dim == 128 ? sizeof(AttnSmem<128>)
+                                 : sizeof(AttnSmem<256>);
+  size_t m = sizeof(SkinnySmem);
+  if (att > m) m = att;
+  if (sizeof(FlowSmem) > m) m = sizeof(FlowSmem);
+  return (m + 255) / 256 * 256;
+}
+
+template <int MT>
+static hipError_t go_hd(const StageArgs& sa, int nwg, size_t smem, hipStream_t st) {
+  switch (sa.d) {
+    case 64: return go<MT, 64>(sa, nwg, smem, st);
+    case 128: return go<MT, 128>(sa, nwg, smem, st);
+    default: return go<MT, 256>(sa, nwg, smem, st);
+  }
+}
+
+hipError_t launch_stage(const StageArgs& sa, int nwg, hipStream_t st) {
+  const size_t smem = stage_smem_bytes(sa.d);
+  const int rows = sa.flow ? sa.N + 1 : sa.M;
+  switch ((rows + 15) / 16) {
+    case 1: return go_hd<1>(sa, nwg, smem, st);
+    case 2: return go_hd<2>(sa, nwg, smem, st);
+    case 3: return go_hd<3>(sa, nwg, smem, st);
+    default: return go_hd<4>(sa, nwg, smem, st);
+  }
+}
+
+}  // namespace blk

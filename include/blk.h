@@ -19,6 +19,9 @@
  *        the product (§4.3); gated FFN, bias/residual/activation epilogues
  *        and precomputed RMS statistics (§5); graph capture of a fixed
  *        sequence of GPU work with stable shapes and addresses (§3).
+ *   [TR] TileRT article: at decode-sized work the gaps between kernels
+ *        (launches, barriers, memory round trips) dominate; one resident
+ *        kernel runs the operator sequence as tile tasks.
  *
  * Conventions for every call:
  *   - Matrices are row-major [in, out] (row-vector convention y = x W).
@@ -192,6 +195,21 @@ void blk_release(void);
 
 /* Library ABI version (bumped when a signature or a layout changes). */
 int blk_version(void);
+
+/*
+ * blk_set_execution_mode -- how blk_forward and flow_denoise run a small chunk
+ * (B*T <= 64 rows), process-wide:
+ *   0 (default) automatic: the path this library version measures fastest
+ *     for the shape (at present one kernel per operator everywhere);
+ *   1 always one kernel per operator;
+ *   2 the persistent stage kernel: one launch for the whole block or the whole
+ *     denoise loop, its workgroups handing off through flags in the workspace
+ *     ([TR]-style execution without launch gaps); BLK_EUNSUPPORTED where it
+ *     does not cover the shape.
+ * Results agree within rounding.  Large chunks always use per-operator kernels.
+ * Errors: BLK_EINVAL for another value.
+ */
+int blk_set_execution_mode(int mode);
 
 #ifdef __cplusplus
 }

@@ -298,3 +298,50 @@ def test_flow_rejects_wrong_step_count():
     with pytest.raises(blk.BlkError) as ei:
         blk.flow_denoise(cfg, packed, flow.n_steps - 1, kp, vp, head["noise"], head["state"])
     assert ei.value.code == blk.BLK_ESTATE
+
+
+# ---------------------------------------------------------------- both execution paths
+@pytest.fixture
+def exec_mode():
+    import diffusion_transformer_block_amd as blk
+    yield blk.blk_set_execution_mode
+    blk.blk_set_execution_mode(blk.EXEC_AUTO)
+
+
+@pytest.mark.parametrize("mode", [1, 2], ids=["per_operator", "persistent"])
+@pytest.mark.parametrize("shape", [s_ for s_ in (synth.TINY, synth.AE_BLOCK,
+                                                        synth.small_shape("gqa_1x37", batch=1),
+                                                        synth.small_shape("mha_2x32", n_q_heads=2, n_kv_heads=2,
+                                                                          head_dim=128, batch=2, tokens=32,
+                                                                          prefix=100, hidden=256, ffn=512))],
+                         ids=lambda s: s.name)
+def test_block_each_execution_path(exec_mode, mode, shape):
+    exec_mode(mode)
+    check_block(shape, synth.block_case(shape))
+
+
+def test_paths_agree_on_ae_block(exec_mode):
+    """The persistent kernel and the per-operator kernels reduce in different
+    orders; their outputs agree to bf16 rounding."""
+    shape = synth.AE_BLOCK
+    case = synth.block_case(shape)
+    exec_mode(1)
+    y1, k1, v1 = gpu_block(shape, case)
+    exec_mode(2)
+    y2, k2, v2 = gpu_block(shape, case)
+    for a, b in ((y1, y2), (k1, k2), (v1, v2)):
+        assert max_err_ratio(a, b) <= 1e-2
+
+
+@pytest.mark.parametrize("mode", [1, 2], ids=["per_operator", "persistent"])
+def test_flow_each_execution_path(exec_mode, mode):
+    import diffusion_transformer_block_amd as blk
+    flow = synth.FLOW
+    exec_mode(mode)
+    case, cfg, packed, kp, vp, head = flow_inputs(flow, 3)
+    acts = blk.flow_denoise(cfg, packed, flow.n_steps, kp, vp, head["noise"], head["state"])
+    torch.cuda.synchronize()
+    ref = oracle_flow(flow, case, 3)
+    err = max_err_ratio(acts.cpu().numpy(), ref)
+    say(f"  flow 3 layers, mode {mode}: err {err:.2e}")
+    assert err <= LOOP_TOL
