@@ -15,7 +15,9 @@
 
 #include "../../include/blk.h"
 #include "common.h"
+#include "attn_small.h"
 #include "internal.h"
+#include "skinny.h"
 #include "stage.h"
 
 using namespace blk;
@@ -58,8 +60,8 @@ int check_config(const blk_config* c) {
     return fail(BLK_EUNSUPPORTED, "head_dim %d not in {64, 128, 256}", d);
   if (c->hidden % 128 != 0 || c->hidden > 16384)
     return fail(BLK_EUNSUPPORTED, "hidden %d must be a multiple of 128 and <= 16384", c->hidden);
-  if (c->ffn % 64 != 0 || c->ffn > 65536)
-    return fail(BLK_EUNSUPPORTED, "ffn %d must be a multiple of 64 and <= 65536", c->ffn);
+  if (c->ffn % 128 != 0 || c->ffn > 65536)
+    return fail(BLK_EUNSUPPORTED, "ffn %d must be a multiple of 128 and <= 65536", c->ffn);
   if (c->n_q_heads % c->n_kv_heads != 0)
     return fail(BLK_EUNSUPPORTED, "n_q_heads %d is not a multiple of n_kv_heads %d",
                 c->n_q_heads, c->n_kv_heads);
@@ -159,6 +161,7 @@ int lookup(const void* packed, const blk_config& cfg, PackRecord* out) {
 struct BlockWs {
   size_t q, o, h, a, r1, r2, part, ss, att_o, att_ml;
   size_t ctr_qkv, ctr_o, ctr_gu, ctr_d, ctr_att;
+  size_t sm_att_o, sm_att_ml, ctr_sm_att;   // small-chunk attention partials
   size_t xb0, xb1, flags, sync;
   size_t total;
 };
@@ -169,15 +172,21 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
   const size_t M = (size_t)B * T;
   const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const int gq = (Hq + 2 * Hkv) * d / 32, go = D / 32, ggu = F / 16, gd = D / 32;
+  // small chunks keep activations in operand order, padded to 16-row tiles
+  const bool small = M > 0 && (int)M <= kSkinnyMaxM;
+  const size_t Mp = small ? (size_t)16 * mt_of((int)M) : M;
+  const size_t q_rows = small ? std::max(Mp * Hq,
+                                         (size_t)B * Hkv * 16 * (((Hq / Hkv) * (size_t)T + 15) / 16))
+                              : M * Hq;
   size_t off = base;
   w.q = off;
-  off += align_up(M * Hq * d * 2);
+  off += align_up(q_rows * d * 2);
   w.o = off;
-  off += align_up(M * Hq * d * 2);
+  off += align_up(Mp * Hq * d * 2);
   w.h = off;
-  off += align_up(M * D * 2);
+  off += align_up(Mp * D * 2);
   w.a = off;
-  off += align_up(M * F * 2);
+  off += align_up(Mp * F * 2);
   w.r1 = off;
   off += align_up(M * 4);
   w.r2 = off;
@@ -191,6 +200,13 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
                   std::max(skinny_ss_floats(m, D, ggu), skinny_ss_floats(m, F, gd)));
   }
   part = std::max(part, extra_part);
+  if (small) {
+    const int m = (int)M;
+    for (size_t v : {sk_part_floats(m, D, gq, true), sk_part_floats(m, D, gq, false),
+                     sk_part_floats(m, Hq * d, go, false), sk_part_floats(m, D, ggu, false),
+                     sk_part_floats(m, F, gd, false)})
+      part = std::max(part, v);
+  }
   if ((int)M <= kSkinnyMaxM && M > 0) {
     const int m = (int)M;
     part = std::max(part, std::max(std::max(stage_part_floats(m, D, gq), stage_part_floats(m, Hq * d, go)),
@@ -215,6 +231,12 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
   off += align_up((size_t)gd * 4);
   w.ctr_att = off;
   off += align_up(attn_counters(B, T, P, Hq, Hkv, d) * 4);
+  w.sm_att_o = off;
+  off += align_up(small ? attn_sm_part_o_elems(B, T, P, Hq, Hkv, d) * 2 : 0);
+  w.sm_att_ml = off;
+  off += align_up(small ? attn_sm_part_ml_floats(B, T, P, Hq, Hkv, d) * 4 : 0);
+  w.ctr_sm_att = off;
+  off += align_up(small ? attn_sm_counters(B, T, Hq, Hkv) * 4 : 0);
   w.xb0 = off;
   off += align_up(M * D * 2);
   w.xb1 = off;
@@ -348,12 +370,118 @@ struct BlockIO {
   int64_t new_stride;
 };
 
+// Whether every skinny GEMM of a small chunk has a valid split (a row-major
+// block input is staged whole per workgroup, which bounds its K range).
+bool small_plan_ok(const blk_config& c, int M, bool x_rowmajor) {
+  const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  return sk_splits(M, D, (Hq + 2 * Hkv) * d / 32, x_rowmajor) >= 1 &&
+         sk_splits(M, Hq * d, D / 32, false) >= 1 && sk_splits(M, D, F / 16, false) >= 1 &&
+         sk_splits(M, F, D / 32, false) >= 1;
+}
+
+// Small chunk (B * T <= 64 rows): one launch per operator, activations in
+// operand order.  x (block input, also the first residual) and y (block
+// output) are row-major caller buffers for a single block, or operand-order
+// rows inside the denoise loop (x_frag / y_frag).
+void enqueue_block_small(const blk_config& c, const Layout& lay, const void* packed, int layer,
+                         int B, int T, int P, const BlockIO& io, bool x_frag, bool y_frag, void* ws,
+                         const BlockWs& w, hipStream_t st) {
+  const int M = B * T, MT = mt_of(M);
+  const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const uint8_t* lw = at<uint8_t>(packed, lay.layer0 + (size_t)layer * lay.layer_bytes);
+  bf16_t* q = at<bf16_t>(ws, w.q);
+  bf16_t* o = at<bf16_t>(ws, w.o);
+  bf16_t* h = at<bf16_t>(ws, w.h);
+  bf16_t* a = at<bf16_t>(ws, w.a);
+  SkArgs base{};
+  base.M = M;
+  base.eps = c.rms_eps;
+  base.part = at<float>(ws, w.part);
+
+  // 1. RMS(x) -> fused QKV GEMM with row scale and RoPE epilogue
+  {
+    SkArgs ga = base;
+    ga.A = io.x;
+    ga.lda = D;
+    ga.K = D;
+    ga.Bp = lw + lay.wqkv;
+    ga.n_groups = (Hq + 2 * Hkv) * d / 32;
+    ga.splits = sk_splits(M, D, ga.n_groups, !x_frag);
+    ga.counters = at<unsigned>(ws, w.ctr_qkv);
+    EpiQkvS e{q, io.kn, io.vn, io.new_stride, at<float>(packed, lay.rope_cos),
+              at<float>(packed, lay.rope_sin), T, P, Hq, Hkv, d};
+    launch_sk_qkv(ga, !x_frag, e, st);
+  }
+  // 2. attention over [prefix ; own]
+  {
+    AttnSmArgs aa{};
+    aa.q = q;
+    aa.kp = io.kp;
+    aa.vp = io.vp;
+    aa.prefix_stride = io.prefix_stride;
+    aa.kn = io.kn;
+    aa.vn = io.vn;
+    aa.new_stride = io.new_stride;
+    aa.o = o;
+    aa.B = B;
+    aa.T = T;
+    aa.P = P;
+    aa.Hq = Hq;
+    aa.Hkv = Hkv;
+    attn_sm_plan(B, T, P, Hq, Hkv, &aa.splits, &aa.kps);
+    aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    aa.part_o = at<bf16_t>(ws, w.sm_att_o);
+    aa.part_ml = at<float>(ws, w.sm_att_ml);
+    aa.counters = at<unsigned>(ws, w.ctr_sm_att);
+    launch_attn_sm(aa, d, st);
+  }
+  // 3. h = x + O W_o
+  {
+    SkArgs ga = base;
+    ga.A = o;
+    ga.K = Hq * d;
+    ga.Bp = lw + lay.wo;
+    ga.n_groups = D / 32;
+    ga.splits = sk_splits(M, ga.K, ga.n_groups, false);
+    ga.counters = at<unsigned>(ws, w.ctr_o);
+    EpiResidS e{io.x, x_frag ? 1 : 0, MT, nullptr, h, 1, MT, 0, D};
+    launch_sk_resid(ga, e, st);
+  }
+  // 4. RMS(h) -> gate/up GEMM with SiLU(gate) * up epilogue
+  {
+    SkArgs ga = base;
+    ga.A = h;
+    ga.K = D;
+    ga.Bp = lw + lay.wgu;
+    ga.n_groups = F / 16;
+    ga.splits = sk_splits(M, D, ga.n_groups, false);
+    ga.counters = at<unsigned>(ws, w.ctr_gu);
+    launch_sk_gateup(ga, EpiGateUpS{a, MT}, st);
+  }
+  // 5. y = h + a W_d
+  {
+    SkArgs ga = base;
+    ga.A = a;
+    ga.K = F;
+    ga.Bp = lw + lay.wd;
+    ga.n_groups = D / 32;
+    ga.splits = sk_splits(M, F, ga.n_groups, false);
+    ga.counters = at<unsigned>(ws, w.ctr_d);
+    EpiResidS e{h, 1, MT, nullptr, io.y, y_frag ? 1 : 0, MT, 0, D};
+    launch_sk_resid(ga, e, st);
+  }
+}
+
 void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, int layer, int B,
                    int T, int P, const BlockIO& io, void* ws, const BlockWs& w, hipStream_t st) {
   const int M = B * T;
+  if (M <= kSkinnyMaxM) {
+    enqueue_block_small(c, lay, packed, layer, B, T, P, io, false, false, ws, w, st);
+    return;
+  }
   const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const uint8_t* lw = at<uint8_t>(packed, lay.layer0 + (size_t)layer * lay.layer_bytes);
-  const bool skinny = M <= kSkinnyMaxM;
+  const bool skinny = false;
   bf16_t* q = at<bf16_t>(ws, w.q);
   bf16_t* o = at<bf16_t>(ws, w.o);
   bf16_t* h = at<bf16_t>(ws, w.h);
@@ -462,18 +590,21 @@ FlowWs flow_ws_layout(const blk_config& c, int N, int P) {
   const int T = N + 1;
   const size_t D = c.hidden;
   size_t off = 0;
+  // X and z rows in operand order, padded to 16-row tiles
   f.x0 = off;
-  off += align_up((size_t)T * D * 2);
+  off += align_up((size_t)16 * mt_of(T) * D * 2);
   f.x1 = off;
-  off += align_up((size_t)T * D * 2);
+  off += align_up((size_t)16 * mt_of(T) * D * 2);
   f.z = off;
-  off += align_up((size_t)N * D * 2);
+  off += align_up((size_t)16 * mt_of(N) * D * 2);
   f.kn = off;
   off += align_up((size_t)T * c.n_kv_heads * c.head_dim * 2);
   f.vn = off;
   off += align_up((size_t)T * c.n_kv_heads * c.head_dim * 2);
   // the embedding's W3 GEMM (N rows, K = D, D/32 groups) shares the split-K scratch
-  f.blk = block_ws_layout(c, 1, T, P, off, skinny_part_floats(N, (int)D, (int)D / 32));
+  f.blk = block_ws_layout(c, 1, T, P, off,
+                          std::max(skinny_part_floats(N, (int)D, (int)D / 32),
+                                   sk_part_floats(N, (int)D, (int)D / 32, false)));
   f.total = f.blk.total;
   return f;
 }
@@ -499,22 +630,24 @@ void enqueue_flow(const blk_config& c, const Layout& lay, const void* packed, in
                      A,
                      D};
     launch_flow_embed(ea, st);
-    GemmArgs ga{};
-    ga.A = z;
-    ga.lda = D;
-    ga.M = N;
-    ga.K = D;
-    ga.Bp = at<uint8_t>(packed, lay.h_w3);
-    ga.n_groups = D / 32;
-    ga.part = at<float>(ws, fw.blk.part);
-    ga.ss_part = at<float>(ws, fw.blk.ss);
-    ga.counters = at<unsigned>(ws, fw.blk.ctr_o);  // W3 is D x D like W_o's group count
-    launch_gemm_bias(ga, EpiBias{at<float>(packed, lay.h_b3), X[0], D, 1}, st);
+    {
+      SkArgs ga{};
+      ga.A = z;
+      ga.M = N;
+      ga.K = D;
+      ga.Bp = at<uint8_t>(packed, lay.h_w3);
+      ga.n_groups = D / 32;
+      ga.splits = sk_splits(N, D, ga.n_groups, false);
+      ga.part = at<float>(ws, fw.blk.part);
+      ga.counters = at<unsigned>(ws, fw.blk.ctr_o);  // W3 has W_o's group count (D / 32)
+      EpiResidS e{nullptr, 0, 0, at<float>(packed, lay.h_b3), X[0], 1, mt_of(T), 1, D};
+      launch_sk_resid(ga, e, st);
+    }
     int cur = 0;
     for (int l = 0; l < n_layers; ++l) {
       BlockIO io{X[cur],  kp[l],  vp[l], 0, X[cur ^ 1], at<bf16_t>(ws, fw.kn),
                  at<bf16_t>(ws, fw.vn), 0};
-      enqueue_block(c, lay, packed, l, 1, T, P, io, ws, fw.blk, st);
+      enqueue_block_small(c, lay, packed, l, 1, T, P, io, true, true, ws, fw.blk, st);
       cur ^= 1;
     }
     FlowVelArgs va{X[cur],
@@ -718,6 +851,12 @@ int blk_forward(const blk_config* cfg, const void* packed, int layer, int batch,
   if (batch == 0 || tokens == 0) return BLK_OK;
   if (!x || !y || !k_new || !v_new) return fail(BLK_EINVAL, "x, y, k_new and v_new must be non-NULL");
   if (prefix > 0 && (!k_prefix || !v_prefix)) return fail(BLK_EINVAL, "prefix K/V is NULL with prefix > 0");
+  for (const void* p : {(const void*)x, (const void*)y, (const void*)k_new, (const void*)v_new,
+                        (const void*)k_prefix, (const void*)v_prefix})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+      return fail(BLK_EINVAL, "x, y, k_new, v_new, k_prefix and v_prefix must be 16-byte aligned");
+  if (prefix_stride % 8 != 0 || new_stride % 8 != 0)
+    return fail(BLK_EINVAL, "prefix_stride and new_stride must be multiples of 8 elements");
   const int64_t kvrow = (int64_t)cfg->n_kv_heads * cfg->head_dim;
   if (batch > 1) {
     if (prefix > 0 && prefix_stride < (int64_t)prefix * kvrow)
@@ -725,6 +864,8 @@ int blk_forward(const blk_config* cfg, const void* packed, int layer, int batch,
     if (new_stride < (int64_t)tokens * kvrow)
       return fail(BLK_EINVAL, "new_stride smaller than one stream's tokens");
   }
+  if (batch * tokens <= kSkinnyMaxM && !small_plan_ok(*cfg, batch * tokens, true))
+    return fail(BLK_EUNSUPPORTED, "hidden %d too wide for a %d-row chunk", cfg->hidden, batch * tokens);
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
   if (want_persistent()) {
@@ -789,7 +930,12 @@ int flow_denoise(const blk_config* cfg, const void* packed, int n_layers, int n_
     if (!k_prefix || !v_prefix) return fail(BLK_EINVAL, "k_prefix / v_prefix arrays are NULL");
     for (int l = 0; l < n_layers; ++l)
       if (!k_prefix[l] || !v_prefix[l]) return fail(BLK_EINVAL, "prefix pointer of layer %d is NULL", l);
+    for (int l = 0; l < n_layers; ++l)
+      if (reinterpret_cast<uintptr_t>(k_prefix[l]) % 16 || reinterpret_cast<uintptr_t>(v_prefix[l]) % 16)
+        return fail(BLK_EINVAL, "prefix buffers must be 16-byte aligned");
   }
+  if (!small_plan_ok(*cfg, T, false) || sk_splits(lay.n_actions, cfg->hidden, cfg->hidden / 32, false) < 1)
+    return fail(BLK_EUNSUPPORTED, "hidden %d too wide for the denoise loop", cfg->hidden);
   hipStream_t st = (hipStream_t)stream;
   int dev = 0;
   HIP_TRY(hipGetDevice(&dev));

@@ -102,6 +102,88 @@ __device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected
   return *flag != 0;
 }
 
+// ---------------------------------------------------------------- buffer resources
+// Raw buffer accesses through a descriptor whose record count bounds the
+// access: a load past the end returns zero, a store past the end is dropped.
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  const int n = bytes > 0x7fffffffu ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+// 16 bytes, device-coherent (sc1): data written by other workgroups of the
+// same launch
+__device__ __forceinline__ uint4 buf_ld_act(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+// 16 bytes, streaming (nt): weights and caches read once
+__device__ __forceinline__ uint4 buf_ld_stream(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+// device-coherent 16 / 8-byte stores (sc1)
+__device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, int off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4v{v.x, v.y, v.z, v.w}, r, off, 0, 16);
+}
+__device__ __forceinline__ void buf_st8(__amdgpu_buffer_rsrc_t r, int off, uint32_t lo, uint32_t hi) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2v{lo, hi}, r, off, 0, 16);
+}
+__device__ __forceinline__ float buf_ld4_act(__amdgpu_buffer_rsrc_t r, int off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 16));
+}
+__device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, int off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 16);
+}
+// Device-coherent 16 / 8-byte accesses through per-lane pointers, as relaxed
+// agent-scope 64-bit atomics (global loads / stores with sc1).  A buffer
+// descriptor must be wave-uniform, so the raw buffer forms above only serve
+// accesses whose base is uniform.
+__device__ __forceinline__ uint2 ld8c(const void* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+}
+__device__ __forceinline__ uint4 ld16c(const void* p) {
+  const uint2 a = ld8c(p);
+  const uint2 b = ld8c(reinterpret_cast<const char*>(p) + 8);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+__device__ __forceinline__ void st8c(void* p, uint32_t lo, uint32_t hi) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), (uint64_t)lo | ((uint64_t)hi << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st16c(void* p, uint4 v) {
+  st8c(p, v.x, v.y);
+  st8c(reinterpret_cast<char*>(p) + 8, v.z, v.w);
+}
+
+__device__ __forceinline__ uint4 pack8(const float* v) {
+  return make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
+}
+__device__ __forceinline__ void unpack8(uint4 u, float* v) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// ---------------------------------------------------------------- operand-order activations
+// A small activation matrix X [M <= 64][K] (bf16) that a skinny MFMA GEMM
+// reads as its row operand is stored in operand order: k-tile kt (32 columns)
+// and row tile mt (16 rows) form one 1 KiB fragment at element
+// ((kt * MT + mt) * 64 + lane) * 8, MT = ceil(M / 16), where lane
+// r % 16 + 16 * ((c % 32) / 8) holds X[r][c .. c + 7] for c % 8 == 0.  A wave
+// reads a fragment with one fully contiguous 16-byte load per lane (a
+// row-major [M][K] matrix would need 16 rows x 64 bytes per load instead).
+__host__ __device__ inline size_t fa_index(int r, int c, int MT) {
+  return ((size_t)((c >> 5) * MT + (r >> 4)) * 64 + (r & 15) + 16 * ((c >> 3) & 3)) * 8 + (c & 7);
+}
+__host__ __device__ inline int mt_of(int M) { return (M + 15) >> 4; }
+
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

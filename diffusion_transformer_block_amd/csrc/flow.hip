@@ -16,7 +16,8 @@ namespace blk {
 
 // Block (row, column tile): rows 0..N-1 -> z[row] = SiLU(a[row] W_fused + bias);
 // row N -> X row 0 = state Ws + bs (the state token, constant over steps but
-// recomputed here so the loop needs no other kernel).
+// recomputed here so the loop needs no other kernel).  z ([N][D]) and X
+// ([N + 1][D]) are in the skinny GEMMs' operand order (fa_index).
 __global__ __launch_bounds__(256) void flow_embed_kernel(FlowEmbedArgs a) {
   __shared__ float vin[64];
   const int row = blockIdx.y;
@@ -29,11 +30,11 @@ __global__ __launch_bounds__(256) void flow_embed_kernel(FlowEmbedArgs a) {
   if (state_row) {
     float acc = a.bs[n];
     for (int k = 0; k < a.A; ++k) acc = fmaf(vin[k], a.ws[(size_t)k * a.D + n], acc);
-    a.x0[n] = f2bf(acc);
+    a.x0[fa_index(0, n, mt_of(a.N + 1))] = f2bf(acc);
   } else {
     float acc = a.bias_row[n];
     for (int k = 0; k < a.A; ++k) acc = fmaf(vin[k], a.w_fused[(size_t)k * a.D + n], acc);
-    a.z[(size_t)row * a.D + n] = f2bf(silu(acc));
+    a.z[fa_index(row, n, mt_of(a.N))] = f2bf(silu(acc));
   }
 }
 
@@ -43,17 +44,18 @@ void launch_flow_embed(const FlowEmbedArgs& a, hipStream_t st) {
 
 // One block per action row i: r = RMS(X[i + 1]); v[a] = r sum_k X[i+1][k] W_out'[k][a]
 // + b_out[a]; a_out[i][a] = a_in[i][a] + dt v[a].  256 threads = (A columns)
-// x (256 / A) slices of k, reduced through LDS in a fixed order.
+// x (256 / A) slices of k, reduced through LDS in a fixed order.  X is in
+// operand order (fa_index, N + 1 rows).
 __global__ __launch_bounds__(256) void flow_velocity_kernel(FlowVelArgs a) {
   __shared__ float xs[8192];
   __shared__ float red[256];
   __shared__ float wsum[4];
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
-  const bf16_t* xr = a.X + (size_t)(i + 1) * a.D;
+  const int MT = mt_of(a.N + 1);
   float ss = 0.f;
   for (int k = tid; k < a.D; k += 256) {
-    const float v = bf2f(xr[k]);
+    const float v = bf2f(a.X[fa_index(i + 1, k, MT)]);
     xs[k] = v;
     ss = fmaf(v, v, ss);
   }

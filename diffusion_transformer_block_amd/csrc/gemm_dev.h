@@ -35,23 +35,6 @@ struct SkinnySmem {
 
 constexpr int kMaxPrefetch = 16;   // weight k-tiles per wave held in registers
 
-typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
-  const int n = bytes > 0x7fffffffu ? 0x7fffffff : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
-}
-// 16 bytes, device-coherent (sc1): activations written by other workgroups
-__device__ __forceinline__ uint4 buf_ld_act(__amdgpu_buffer_rsrc_t r, int off) {
-  const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-// 16 bytes, streaming (nt): weights read once
-__device__ __forceinline__ uint4 buf_ld_stream(__amdgpu_buffer_rsrc_t r, int off) {
-  const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
 __device__ __forceinline__ float sumsq8(uint4 v) {
   float s = 0.f;
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};

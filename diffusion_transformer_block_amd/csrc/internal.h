@@ -185,6 +185,26 @@ size_t attn_part_ml_floats(int B, int T, int P, int Hq, int Hkv, int d);
 size_t attn_counters(int B, int T, int P, int Hq, int Hkv, int d);
 void launch_attention(const AttnArgs& a, hipStream_t st);
 
+// ---------------------------------------------------------------- small-chunk path
+// (M = B * T <= 64): activations in operand order, see skinny.h / attn_small.h
+struct SkArgs;
+struct EpiQkvS;
+struct EpiResidS;
+struct EpiGateUpS;
+struct AttnSmArgs;
+int device_cus();
+// K splits of a skinny GEMM (-1: no valid split, row-major input too wide)
+int sk_splits(int M, int K, int n_groups, bool a_rowmajor);
+size_t sk_part_floats(int M, int K, int n_groups, bool a_rowmajor);
+void launch_sk_qkv(const SkArgs& ga, bool a_rowmajor, const EpiQkvS& e, hipStream_t st);
+void launch_sk_resid(const SkArgs& ga, const EpiResidS& e, hipStream_t st);
+void launch_sk_gateup(const SkArgs& ga, const EpiGateUpS& e, hipStream_t st);
+void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps);
+size_t attn_sm_part_o_elems(int B, int T, int P, int Hq, int Hkv, int d);
+size_t attn_sm_part_ml_floats(int B, int T, int P, int Hq, int Hkv, int d);
+size_t attn_sm_counters(int B, int T, int Hq, int Hkv);
+void launch_attn_sm(const AttnSmArgs& a, int head_dim, hipStream_t st);
+
 // ---------------------------------------------------------------- flow head
 struct FlowEmbedArgs {
   const float* act;        // [N][A] current actions

@@ -1,0 +1,397 @@
+// Skinny GEMM (M <= 64 rows) of the small-chunk path, as a device task shared
+// by the standalone kernels and the persistent stage kernel.
+//
+// [RT] = reading note on "Running VLAs at Real-time Speed" (Ma et al.,
+// arXiv:2510.26742v1).  §5: bias / residual / activation merged into the GEMM
+// tail; the gated FFN's two up-projections share one load of their input; the
+// RMS statistic is consumed fused as a row scale; a partial split-K balances
+// skinny shapes over the compute units; §6.2: at few tokens a GEMM is bound by
+// reading its bf16 weights.
+//
+// One task = one 32-column group g of a packed weight (both 16-column tiles,
+// as the fused QKV and gate/up epilogues need) over the K-range of split s.
+//  * Weights: fragments (g, kt, 0..1), 1 KiB each, one 16-byte streaming load
+//    per lane.
+//  * Activations: in operand order (fa_index in common.h: one contiguous
+//    1 KiB load per fragment), or row-major (the block's input, owned by the
+//    caller), which the workgroup first stages through LDS with row-contiguous
+//    16-byte loads, writing the fragments in operand order; the lane slot is
+//    XOR-swizzled with the k-tile so that both the staging writes and the
+//    operand reads are free of bank conflicts.
+//  * The four waves split the K-range; each keeps a ring of NB k-tiles of
+//    loads in flight ahead of its MFMAs (weights of the first NB k-tiles are
+//    issued before the task's wait, since they do not depend on earlier work).
+//  * The waves' tiles meet in LDS and are summed in a fixed order; K splits
+//    publish fp32 tiles and the last split to arrive (device counter, reset by
+//    it) sums all of them in split order, so results do not depend on timing.
+//  * With RMS the waves also sum x^2 of the rows they load (the statistic
+//    costs no extra pass) and the epilogue gets r = (mean x^2 + eps)^-1/2.
+//  * The epilogue reads the summed 64 x 32 tile from LDS in the order it
+//    stores (row-contiguous 16-byte stores).
+#pragma once
+#include "common.h"
+
+namespace blk {
+
+constexpr int kTileRow = 36;        // floats per row of the LDS result tile (32 + 4 pad)
+constexpr int kSkMaxStage = 128;    // KiB of row-major activations staged per workgroup
+constexpr int kSkMaxSplits = 16;
+
+struct SkArgs {
+  const bf16_t* A;      // activations, operand order (MT = ceil(M/16)), or row-major (lda)
+  int lda;              // row-major only
+  int M, K;
+  const uint8_t* Bp;    // packed weight fragments
+  int n_groups;
+  int splits;           // K splits (KT % (4 splits) == 0)
+  float eps;            // RMS epsilon
+  float* part;          // [splits][n_groups][64 * 32] tiles, then [splits][n_groups][64] x^2 sums
+  unsigned* counters;   // [n_groups], zero on entry and on exit
+};
+
+template <bool AROW>
+struct SkSmem {
+  union {
+    uint4 astage[AROW ? kSkMaxStage * 64 : 1];  // row-major activations in operand order
+    f32x4 red[4][4 * 2 * 64];                  // per-wave accumulators in MFMA C order
+  };
+  float tile[64 * kTileRow];                   // summed tile [row][col]
+  float ss[4][64];
+  float rrow[64];
+  int last_flag;
+};
+
+struct NoWait {
+  __device__ __forceinline__ bool operator()() const { return true; }
+};
+
+__device__ __forceinline__ float sumsq8(uint4 v) {
+  float x[8];
+  unpack8(v, x);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s = fmaf(x[i], x[i], s);
+  return s;
+}
+
+// operand-order slot of (k-tile u, row tile mt, lane) in the LDS staging area
+__device__ __forceinline__ int stage_slot(int u, int mt, int lane, int MT) {
+  return (u * MT + mt) * 64 + (lane & 48) + ((lane & 15) ^ (u & 15));
+}
+
+// Runs one task and stores its outputs through `epi` (see the epilogues
+// below).  `wait()` is called after the first weight loads are issued and
+// before anything that depends on earlier work; it returns false to abandon
+// the task.  Returns false when this workgroup did not run the epilogue
+// (abandoned, or it only published a split partial).
+template <int MT, int NB, bool RMS, bool AROW, class Epi, class Wait>
+__device__ bool sk_task(const SkArgs& ga, const Epi& epi, int g, int s, SkSmem<AROW>& sm,
+                        Wait&& wait) {
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+  const int l = tid & 63, lr = l & 15;
+  const int KT = ga.K >> 5;
+  const int KTS = KT / ga.splits;
+  const int KW = KTS >> 2;             // k-tiles per wave, a multiple of NB
+  const int kb = s * KTS;              // first k-tile of this split
+  const int uw = w * KW;               // first k-tile of this wave, relative to kb
+
+  // ---- weights of the first NB k-tiles (independent of earlier work)
+  const __amdgpu_buffer_rsrc_t rb =
+      make_rsrc(ga.Bp + frag_offset(g, 0, 0, KT), (size_t)KT * 2 * kFragBytes);
+  const int boff = (kb + uw) * 2 * kFragBytes + l * 16;
+  uint4 bw[NB][2];
+  auto issue_w = [&](int b, int u) {
+    bw[b][0] = buf_ld_stream(rb, boff + u * 2 * kFragBytes);
+    bw[b][1] = buf_ld_stream(rb, boff + u * 2 * kFragBytes + kFragBytes);
+  };
+#pragma unroll
+  for (int b = 0; b < NB; ++b) issue_w(b, b);
+  if (!wait()) return false;
+  const typename Epi::Pre pre = epi.prefetch(g, ga.M);
+
+  // ---- activations
+  uint4 av[NB][MT];
+  __amdgpu_buffer_rsrc_t ra;
+  int aoff = 0;
+  if (AROW) {
+    // stage rows [0, M) x k-tiles [kb, kb + KTS) in operand order
+    const int nck = KTS * 4;                       // 16-byte chunks per row
+    const int total = ga.M * nck;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(ga.A, (size_t)ga.M * ga.lda * 2);
+    for (int i0 = 0; i0 < total; i0 += 256 * 16) {
+      uint4 v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int i = i0 + j * 256 + tid;
+        const int r = i / nck, c = i - r * nck;
+        v[j] = buf_ld_act(rx, i < total ? (r * ga.lda + kb * 32 + c * 8) * 2 : 0x7ffffff0);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int i = i0 + j * 256 + tid;
+        if (i < total) {
+          const int r = i / nck, c = i - r * nck;
+          sm.astage[stage_slot(c >> 2, r >> 4, (r & 15) + 16 * (c & 3), MT)] = v[j];
+        }
+      }
+    }
+    __syncthreads();
+  } else {
+    ra = make_rsrc(ga.A, (size_t)KT * MT * kFragBytes);
+    aoff = ((kb + uw) * MT * 64 + l) * 16;
+  }
+  auto issue_a = [&](int b, int u) {
+    if (!AROW) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) av[b][mt] = buf_ld_act(ra, aoff + (u * MT + mt) * kFragBytes);
+    }
+  };
+  auto get_a = [&](int b, int u, int mt) -> uint4 {
+    if (AROW) return sm.astage[stage_slot(uw + u, mt, l, MT)];
+    return av[b][mt];
+  };
+
+  f32x4 acc[MT][2];
+  float ss[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    acc[mt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ss[mt] = 0.f;
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) issue_a(b, b);
+  for (int u0 = 0; u0 < KW; u0 += NB) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int u = u0 + b;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint4 a = get_a(b, u, mt);
+        if (RMS) ss[mt] += sumsq8(a);
+        acc[mt][0] = mfma16(as_bf16x8(a), as_bf16x8(bw[b][0]), acc[mt][0]);
+        acc[mt][1] = mfma16(as_bf16x8(a), as_bf16x8(bw[b][1]), acc[mt][1]);
+      }
+      if (u + NB < KW) {
+        issue_w(b, u + NB);
+        issue_a(b, u + NB);
+      }
+    }
+  }
+
+  // ---- the four waves' tiles -> summed tile [row][col] in LDS
+  __syncthreads();   // staging reads (and a previous task's readers) are done
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) sm.red[w][(mt * 2 + i) * 64 + l] = acc[mt][i];
+  if (RMS) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float v = ss[mt];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (l < 16) sm.ss[w][16 * mt + lr] = v;
+    }
+  }
+  __syncthreads();
+  for (int sl = tid; sl < MT * 128; sl += 256) {
+    const f32x4 v = ((sm.red[0][sl] + sm.red[1][sl]) + sm.red[2][sl]) + sm.red[3][sl];
+    const int mt = sl >> 7, i = (sl >> 6) & 1, ll = sl & 63;
+    const int row = 16 * mt + 4 * (ll >> 4), col = 16 * i + (ll & 15);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sm.tile[(row + j) * kTileRow + col] = v[j];
+  }
+  float ssum = 0.f;
+  if (RMS && tid < 16 * MT) ssum = ((sm.ss[0][tid] + sm.ss[1][tid]) + sm.ss[2][tid]) + sm.ss[3][tid];
+  __syncthreads();
+
+  // ---- K splits: publish, last arriver sums every split in order
+  if (ga.splits > 1) {
+    const int r = tid >> 2, c0 = (tid & 3) * 8;
+    const size_t tile_floats = 64 * 32;
+    const size_t ss_base = (size_t)ga.splits * ga.n_groups * tile_floats;
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc(ga.part, (ss_base + (size_t)ga.splits * ga.n_groups * 64) * 4);
+    const int toff = (int)(((size_t)g * tile_floats + r * 32 + c0) * 4);
+    const int tstride = (int)((size_t)ga.n_groups * tile_floats * 4);
+    const int soff = (int)((ss_base + (size_t)g * 64 + tid) * 4);
+    const int sstride = ga.n_groups * 64 * 4;
+    {
+      const float* tp = &sm.tile[r * kTileRow + c0];
+      buf_st16(rp, toff + s * tstride, *reinterpret_cast<const uint4*>(tp));
+      buf_st16(rp, toff + s * tstride + 16, *reinterpret_cast<const uint4*>(tp + 4));
+      if (RMS && tid < 64) buf_st4(rp, soff + s * sstride, ssum);
+    }
+    if (!arrive_last(&ga.counters[g], (unsigned)ga.splits, &sm.last_flag)) return false;
+    uint4 pv[kSkMaxSplits][2];
+    float ps[kSkMaxSplits];
+#pragma unroll
+    for (int sp = 0; sp < kSkMaxSplits; ++sp)
+      if (sp < ga.splits) {
+        pv[sp][0] = buf_ld_act(rp, toff + sp * tstride);
+        pv[sp][1] = buf_ld_act(rp, toff + sp * tstride + 16);
+        ps[sp] = RMS && tid < 64 ? buf_ld4_act(rp, soff + sp * sstride) : 0.f;
+      }
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    ssum = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < kSkMaxSplits; ++sp)
+      if (sp < ga.splits) {
+        const uint32_t u[8] = {pv[sp][0].x, pv[sp][0].y, pv[sp][0].z, pv[sp][0].w,
+                               pv[sp][1].x, pv[sp][1].y, pv[sp][1].z, pv[sp][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += __uint_as_float(u[e]);
+        ssum += ps[sp];
+      }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm.tile[r * kTileRow + c0 + e] = v[e];
+  }
+  if (RMS) {
+    if (tid < 64) sm.rrow[tid] = rsqrtf(ssum / (float)ga.K + ga.eps);
+  }
+  if (RMS || ga.splits > 1) __syncthreads();
+  epi.run(sm.tile, sm.rrow, RMS, g, ga.M, pre);
+  return true;
+}
+
+// ============================================================================ epilogues
+// Each epilogue is called by all 256 threads with the summed tile
+// tile[row * kTileRow + col] (row < 64, col < 32 = the group's two 16-column
+// tiles) and the row scale rrow (used when `rms`).  prefetch() runs right
+// after the task's wait, so its loads overlap the activation loads.  All
+// stores are device-coherent.
+
+// Attention operand order of Q (written by the QKV epilogue, read by the
+// attention): for stream b and kv head hk the rows are ar = t G + gh over the
+// G = Hq / Hkv query heads sharing that kv head; row tile ar / 16 and the
+// 32-column slice ks of the head dimension form one 1 KiB fragment, lane
+// ar % 16 + 16 ((dd % 32) / 8) holding 8 consecutive dd.
+__host__ __device__ inline size_t qa_index(int bh, int n_rt, int KS, int ar, int dd) {
+  return ((((size_t)bh * n_rt + (ar >> 4)) * KS + (dd >> 5)) * 64 + (ar & 15) + 16 * ((dd >> 3) & 3)) * 8 +
+         (dd & 7);
+}
+
+// Fused QKV: row scale, RoPE on the rotated (Q, K) groups (column j with
+// j + d/2 in one group), Q into the attention operand order, K_new and V_new
+// row-major ([T][Hkv][d] per stream at b * new_stride).
+struct EpiQkvS {
+  bf16_t* q;
+  bf16_t* kn;
+  bf16_t* vn;
+  int64_t new_stride;
+  const float* cos_t;   // [max_pos][d/2]
+  const float* sin_t;
+  int T, P, Hq, Hkv, d;
+  struct Pre {};
+  __device__ Pre prefetch(int, int) const { return {}; }
+  __device__ void run(const float* tile, const float* rrow, bool rms, int g, int M, const Pre&) const {
+    const int t = threadIdx.x;
+    const int r = t >> 2;
+    if (r >= M) return;
+    const float rs = rms ? rrow[r] : 1.f;
+    const int b = r / T, tt = r - b * T;
+    const int gpr = d >> 5, n_rot_groups = (Hq + Hkv) * gpr;
+    const float* tr = tile + r * kTileRow;
+    if (g < n_rot_groups) {
+      const int q4 = (t & 3) * 4;
+      const int head = g / gpr;
+      const int half = d >> 1;
+      const int j0 = 16 * (g - head * gpr) + q4;
+      const size_t ti = (size_t)(P + tt) * half + j0;
+      const float4 cs = *reinterpret_cast<const float4*>(cos_t + ti);
+      const float4 sn = *reinterpret_cast<const float4*>(sin_t + ti);
+      const float c4[4] = {cs.x, cs.y, cs.z, cs.w}, s4[4] = {sn.x, sn.y, sn.z, sn.w};
+      float lo[4], hi[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v0 = tr[q4 + i] * rs, v1 = tr[16 + q4 + i] * rs;
+        lo[i] = v0 * c4[i] - v1 * s4[i];
+        hi[i] = v0 * s4[i] + v1 * c4[i];
+      }
+      if (head < Hq) {
+        const int G = Hq / Hkv;
+        const int hk = head / G, gh = head - hk * G;
+        const int n_rt = (G * T + 15) >> 4;
+        const int ar = tt * G + gh, bh = b * Hkv + hk;
+        st8c(q + qa_index(bh, n_rt, d >> 5, ar, j0), pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
+        st8c(q + qa_index(bh, n_rt, d >> 5, ar, j0 + half), pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
+      } else {
+        bf16_t* dst = kn + (size_t)b * new_stride + ((size_t)tt * Hkv + (head - Hq)) * d;
+        st8c(dst + j0, pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
+        st8c(dst + j0 + half, pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
+      }
+    } else {
+      const int c0 = (t & 3) * 8;
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = tr[c0 + i] * rs;
+      bf16_t* dst = vn + (size_t)b * new_stride + (size_t)tt * Hkv * d + 32 * (g - n_rot_groups) + c0;
+      st16c(dst, pack8(v));
+    }
+  }
+};
+
+// out[row_off + m][n] = acc (+ res[m][n]) (+ bias[n]) for the group's 32
+// columns n = 32 g + c: O and down projections (residual), the flow
+// embedding's W3 (bias).  res and out are each in operand order (MT of their
+// own row count) or row-major with leading dimension N.
+struct EpiResidS {
+  const bf16_t* res;    // may be NULL
+  int res_frag, res_MT;
+  const float* bias;    // may be NULL
+  bf16_t* out;
+  int out_frag, out_MT, row_off;
+  int N;
+  struct Pre {
+    uint4 v;
+  };
+  __device__ Pre prefetch(int g, int M) const {
+    const int t = threadIdx.x, ln = t & 63;
+    const int r = 16 * (t >> 6) + (ln & 15), c = 32 * g + 8 * (ln >> 4);
+    Pre p{make_uint4(0, 0, 0, 0)};
+    if (res && r < M) p.v = ld16c(res + (res_frag ? fa_index(r, c, res_MT) : (size_t)r * N + c));
+    return p;
+  }
+  __device__ void run(const float* tile, const float*, bool, int g, int M, const Pre& p) const {
+    const int t = threadIdx.x, ln = t & 63;
+    const int r = 16 * (t >> 6) + (ln & 15), cl = 8 * (ln >> 4), c = 32 * g + cl;
+    if (r >= M) return;
+    float v[8], rv[8];
+    unpack8(p.v, rv);
+    const float* tr = tile + r * kTileRow + cl;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = tr[i] + rv[i];
+    if (bias) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] += bias[c + i];
+    }
+    const int ro = r + row_off;
+    st16c(out + (out_frag ? fa_index(ro, c, out_MT) : (size_t)ro * N + c), pack8(v));
+  }
+};
+
+// a[m][j] = SiLU(r * gate) * (r * up) for j = 16 g + c: tile 0 holds the gate
+// columns, tile 1 the up columns of the same j; a is in operand order.
+struct EpiGateUpS {
+  bf16_t* out;
+  int MT;
+  struct Pre {};
+  __device__ Pre prefetch(int, int) const { return {}; }
+  __device__ void run(const float* tile, const float* rrow, bool rms, int g, int M, const Pre&) const {
+    const int t = threadIdx.x;
+    if (t >= 128) return;
+    const int q = t & 31;
+    const int r = 16 * (t >> 5) + (q & 15), hf = q >> 4;
+    if (r >= M) return;
+    const float rs = rms ? rrow[r] : 1.f;
+    const float* tr = tile + r * kTileRow + 8 * hf;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = silu(tr[i] * rs) * (tr[16 + i] * rs);
+    st16c(out + fa_index(r, 16 * g + 8 * hf, MT), pack8(v));
+  }
+};
+
+}  // namespace blk

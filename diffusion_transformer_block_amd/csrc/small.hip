@@ -1,0 +1,178 @@
+// Standalone kernels of the small-chunk path (M = B * T <= 64 rows): the
+// skinny GEMM with its epilogues and the chunk attention, one launch per
+// operator, plus the planners that pick their splits.  The device code lives
+// in skinny.h and attn_small.h, shared with the persistent stage kernel.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "attn_small.h"
+#include "common.h"
+#include "internal.h"
+#include "skinny.h"
+
+namespace blk {
+
+// ============================================================================ planners
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Per-workgroup cost model of a skinny GEMM task: its operand bytes at the
+// rate one compute unit sustains from L2 / HBM (about 100 GB/s measured with
+// 16-byte loads), plus a fixed price for a K split's hand-off (publish, count,
+// reload: three dependent memory round trips).
+constexpr double kCuBytesPerUs = 100e3;
+constexpr double kSplitUs = 2.0;
+
+int sk_splits(int M, int K, int n_groups, bool a_rowmajor) {
+  const int KT = K / 32, MT = mt_of(M);
+  const int n_cu = device_cus();
+  int best = -1;
+  double best_t = 1e30;
+  for (int s = 1; s <= kSkMaxSplits; s *= 2) {
+    if (KT % (4 * s) != 0) break;
+    if (s > 1 && n_groups * s > n_cu) break;
+    if (a_rowmajor && (KT / s) * MT > kSkMaxStage) continue;
+    const double bytes = (double)(2 + MT) * (KT / s) * kFragBytes;
+    const double t = bytes / kCuBytesPerUs + (s > 1 ? kSplitUs : 0.0);
+    if (t < best_t) {
+      best_t = t;
+      best = s;
+    }
+  }
+  return best;
+}
+
+size_t sk_part_floats(int M, int K, int n_groups, bool a_rowmajor) {
+  const int s = sk_splits(M, K, n_groups, a_rowmajor);
+  if (s <= 1) return 0;
+  return (size_t)s * n_groups * (64 * 32 + 64);
+}
+
+static int sk_nb(int KW) {
+  if (KW % 8 == 0) return 8;
+  if (KW % 4 == 0) return 4;
+  if (KW % 2 == 0) return 2;
+  return 1;
+}
+
+void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps) {
+  const int G = Hq / Hkv;
+  const int n_rbt = B * Hkv * ((G * T + 63) / 64);
+  const int L = P + T;
+  int s = std::max(1, std::min(kAttnMaxSplits, (48 + n_rbt - 1) / n_rbt));
+  s = std::min(s, (L + 31) / 32);
+  int k = (L + s - 1) / s;
+  k = (k + 31) / 32 * 32;
+  *kps = k;
+  *splits = (L + k - 1) / k;
+}
+
+size_t attn_sm_part_o_elems(int B, int T, int P, int Hq, int Hkv, int d) {
+  int s = 1, k = 32;
+  attn_sm_plan(B, T, P, Hq, Hkv, &s, &k);
+  if (s <= 1) return 0;
+  const int n_rbt = B * Hkv * ((Hq / Hkv * T + 63) / 64);
+  return (size_t)s * n_rbt * 64 * d;
+}
+size_t attn_sm_part_ml_floats(int B, int T, int P, int Hq, int Hkv, int d) {
+  return attn_sm_part_o_elems(B, T, P, Hq, Hkv, d) / d * 2;
+}
+size_t attn_sm_counters(int B, int T, int Hq, int Hkv) {
+  return (size_t)B * Hkv * ((Hq / Hkv * T + 63) / 64);
+}
+
+// ============================================================================ skinny GEMM
+template <int MT, int NB, bool RMS, bool AROW, class Epi>
+__global__ __launch_bounds__(256) void sk_kernel(SkArgs ga, Epi epi) {
+  extern __shared__ __attribute__((aligned(16))) char sk_dsm[];
+  sk_task<MT, NB, RMS, AROW>(ga, epi, blockIdx.x, blockIdx.y, *reinterpret_cast<SkSmem<AROW>*>(sk_dsm),
+                             NoWait{});
+}
+
+template <int MT, int NB, bool RMS, bool AROW, class Epi>
+static void sk_go(const SkArgs& ga, const Epi& e, hipStream_t st) {
+  auto kern = sk_kernel<MT, NB, RMS, AROW, Epi>;
+  const size_t smem = sizeof(SkSmem<AROW>);
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(ga.n_groups, ga.splits), dim3(256), smem, st, ga, e);
+}
+
+template <int MT, bool RMS, bool AROW, class Epi>
+static void sk_go_nb(const SkArgs& ga, const Epi& e, hipStream_t st) {
+  switch (sk_nb(ga.K / 32 / ga.splits / 4)) {
+    case 8: sk_go<MT, 8, RMS, AROW>(ga, e, st); break;
+    case 4: sk_go<MT, 4, RMS, AROW>(ga, e, st); break;
+    case 2: sk_go<MT, 2, RMS, AROW>(ga, e, st); break;
+    default: sk_go<MT, 1, RMS, AROW>(ga, e, st); break;
+  }
+}
+
+template <bool RMS, bool AROW, class Epi>
+static void sk_launch(const SkArgs& ga, const Epi& e, hipStream_t st) {
+  switch (mt_of(ga.M)) {
+    case 1: sk_go_nb<1, RMS, AROW>(ga, e, st); break;
+    case 2: sk_go_nb<2, RMS, AROW>(ga, e, st); break;
+    case 3: sk_go_nb<3, RMS, AROW>(ga, e, st); break;
+    default: sk_go_nb<4, RMS, AROW>(ga, e, st); break;
+  }
+}
+
+void launch_sk_qkv(const SkArgs& ga, bool a_rowmajor, const EpiQkvS& e, hipStream_t st) {
+  if (a_rowmajor) sk_launch<true, true>(ga, e, st);
+  else sk_launch<true, false>(ga, e, st);
+}
+void launch_sk_resid(const SkArgs& ga, const EpiResidS& e, hipStream_t st) {
+  sk_launch<false, false>(ga, e, st);
+}
+void launch_sk_gateup(const SkArgs& ga, const EpiGateUpS& e, hipStream_t st) {
+  sk_launch<true, false>(ga, e, st);
+}
+
+// ============================================================================ attention
+template <int HD>
+__global__ __launch_bounds__(256) void attn_sm_kernel(AttnSmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char at_dsm[];
+  attn_sm_task<HD>(a, blockIdx.z, blockIdx.y, blockIdx.x, *reinterpret_cast<AttnSmSmem<HD>*>(at_dsm),
+                   NoWait{});
+}
+
+template <int HD>
+static void attn_sm_go(const AttnSmArgs& a, hipStream_t st) {
+  auto kern = attn_sm_kernel<HD>;
+  const size_t smem = sizeof(AttnSmSmem<HD>);
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    attr_set = true;
+  }
+  const int G = a.Hq / a.Hkv;
+  const dim3 grid(a.splits, (G * a.T + 63) / 64, a.B * a.Hkv);
+  hipLaunchKernelGGL(kern, grid, dim3(256), smem, st, a);
+}
+
+void launch_attn_sm(const AttnSmArgs& a, int head_dim, hipStream_t st) {
+  switch (head_dim) {
+    case 64: attn_sm_go<64>(a, st); break;
+    case 128: attn_sm_go<128>(a, st); break;
+    default: attn_sm_go<256>(a, st); break;
+  }
+}
+
+}  // namespace blk

@@ -62,7 +62,7 @@ extern "C" {
 #define BLK_EHIP (-5)         /* a HIP runtime call failed (message has the reason)  */
 
 /* Shape of one block.  Supported: head_dim in {64, 128, 256}; hidden % 128 == 0;
- * ffn % 64 == 0; n_q_heads % n_kv_heads == 0; 1 <= max_pos <= 1<<20. */
+ * ffn % 128 == 0; n_q_heads % n_kv_heads == 0; 1 <= max_pos <= 1<<20. */
 typedef struct blk_config {
   int32_t hidden;      /* D: model width                                         */
   int32_t ffn;         /* F: gated-FFN width                                      */
@@ -149,11 +149,14 @@ int blk_prepare_weights(const blk_config* cfg, const blk_layer_src* layers, int 
  *           new_stride = prefix_stride) to append the chunk to the cache.
  *   ws      device workspace of *ws_bytes bytes (query with ws == NULL);
  *           zero-filled before its first use.
+ * x, y, k_new, v_new, k_prefix and v_prefix must be 16-byte aligned and both
+ * strides multiples of 8 elements (the kernels move 16-byte vectors).
  * Computes y = h + FFN(RMSNorm(h) g2), h = x + Attn(RoPE(Q), [K_p; RoPE(K)],
  * [V_p; V]) W_o with Q, K, V = RMSNorm(x) g1 [W_q|W_k|W_v]; chunk token t is at
  * position P + t; no attention mask (every query sees all P + T keys).
  * `packed` must come from blk_prepare_weights with an identical cfg; `layer`
- * selects the layer.  Errors: BLK_EINVAL, BLK_EUNSUPPORTED (P + T > max_pos),
+ * selects the layer.  Errors: BLK_EINVAL (also misaligned buffers or strides),
+ * BLK_EUNSUPPORTED (P + T > max_pos),
  * BLK_ESIZE (ws too small), BLK_ESTATE (packed unknown / cfg differs), BLK_EHIP.
  */
 int blk_forward(const blk_config* cfg, const void* packed, int layer, int batch, int tokens,
