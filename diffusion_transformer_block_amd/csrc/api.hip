@@ -161,7 +161,7 @@ int lookup(const void* packed, const blk_config& cfg, PackRecord* out) {
 struct BlockWs {
   size_t q, o, h, a, r1, r2, part, ss, att_o, att_ml;
   size_t ctr_qkv, ctr_o, ctr_gu, ctr_d, ctr_att;
-  size_t sm_att_o, sm_att_ml, ctr_sm_att;   // small-chunk attention partials
+  size_t sm_att_o, sm_att_ml;   // small-chunk attention key-slice partials
   size_t xb0, xb1, flags, sync;
   size_t total;
 };
@@ -176,7 +176,7 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
   const bool small = M > 0 && (int)M <= kSkinnyMaxM;
   const size_t Mp = small ? (size_t)16 * mt_of((int)M) : M;
   const size_t q_rows = small ? std::max(Mp * Hq,
-                                         (size_t)B * Hkv * 16 * (((Hq / Hkv) * (size_t)T + 15) / 16))
+                                         (size_t)B * Hkv * 32 * (((Hq / Hkv) * (size_t)T + 31) / 32))
                               : M * Hq;
   size_t off = base;
   w.q = off;
@@ -235,8 +235,6 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
   off += align_up(small ? attn_sm_part_o_elems(B, T, P, Hq, Hkv, d) * 2 : 0);
   w.sm_att_ml = off;
   off += align_up(small ? attn_sm_part_ml_floats(B, T, P, Hq, Hkv, d) * 4 : 0);
-  w.ctr_sm_att = off;
-  off += align_up(small ? attn_sm_counters(B, T, Hq, Hkv) * 4 : 0);
   w.xb0 = off;
   off += align_up(M * D * 2);
   w.xb1 = off;
@@ -432,7 +430,6 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     aa.part_o = at<bf16_t>(ws, w.sm_att_o);
     aa.part_ml = at<float>(ws, w.sm_att_ml);
-    aa.counters = at<unsigned>(ws, w.ctr_sm_att);
     launch_attn_sm(aa, d, st);
   }
   // 3. h = x + O W_o

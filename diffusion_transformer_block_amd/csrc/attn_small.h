@@ -10,25 +10,31 @@
 //
 // The rows of one (stream b, kv head hk) are the G = Hq / Hkv query heads of
 // each of the T tokens, row ar = t G + gh; they all read that kv head's keys,
-// so one K/V tile serves 64 rows (16 per wave).  A task takes 64 rows and one
-// slice of the keys:
-//  * K / V tiles of 32 keys are loaded with row-contiguous 16-byte loads two
-//    tiles ahead of use and staged through double-buffered LDS;
-//  * S^T = K Q^T on MFMA, K rows as the A operand (LDS), Q^T as the B operand
-//    held in registers (the QKV epilogue stores Q in exactly that operand
-//    order, qa_index), so a lane ends up with 4 keys of one row;
+// so one K/V tile serves 64 rows.  A task takes 64 rows and one slice of the
+// keys, in steps of 64 keys:
+//  * K / V tiles are loaded with row-contiguous 16-byte loads one step ahead
+//    and staged through double-buffered LDS;
+//  * wave w takes 32 query rows (w % 2) and one 32-key half (w / 2) of every
+//    step, with 32 x 32 x 16 MFMAs (twice the operand reuse of 16 x 16 tiles:
+//    the LDS reads, not the MFMAs, bound this loop);
+//  * S^T = K Q^T: K rows as the A operand (LDS), Q^T as the B operand held in
+//    registers (the QKV epilogue stores Q in exactly that operand order,
+//    qa_index), so a lane holds 16 keys of one query row;
 //  * online softmax per row in base 2 (scores pre-scaled by log2(e)/sqrt(d));
-//  * O^T += V^T P^T on MFMA: P^T is the B operand straight from the score
-//    registers (slot e of lane group lg is key 4 lg + e, or 16 + 4 lg + e - 4
-//    for e >= 4), V^T the A operand read out of the row-major V tile with
-//    ds_read_b64_tr_b16, which hands lane i of each 16-lane group element
-//    i % 4 of the 8 bytes at lane 4 k + i / 4 (k < 4): pointing lane i at
-//    key 4 lg + i / 4, dims 4 (i % 4) .. + 3 yields V[4 lg + k][i] -- the
-//    same key order as P^T;
-//  * one key slice writes the normalised rows straight into the O
-//    projection's operand order; several slices publish bf16 partials
-//    normalised by their own sum plus (max, sum), and the last slice to arrive
-//    (device counter, reset by it) combines all of them in slice order.
+//    the output is rescaled only when a row's max grows by more than 2^8;
+//  * O^T += V^T P^T: P^T is the B operand straight from the score registers
+//    (slot e of the u-th 16-key step is S^T value 8 u + e, keys
+//    16 u + 4 (l/32) + e or 16 u + 8 + 4 (l/32) + e - 4), V^T the A operand
+//    read out of the row-major V tile with ds_read_b64_tr_b16, which hands
+//    lane i of each 16-lane group element i % 4 of the 8 bytes at lane
+//    4 k + i / 4 (k < 4): pointing lane i at key row 4 k' + i / 4, dims
+//    4 (i % 4) .. + 3 yields V[key k][dim i] in that key order;
+//  * the two key halves meet in LDS; one key slice then writes the normalised
+//    rows straight into the O projection's operand order; several slices
+//    publish bf16 partials normalised by their own sum plus (max, sum), which
+//    a separate merge step (attn_combine_task, one thread per 16 output
+//    bytes, all slices' loads in flight together) combines in slice order.
+//    Many small slices keep every workgroup to about one memory round trip.
 #pragma once
 #include "common.h"
 #include "skinny.h"
@@ -51,16 +57,16 @@ struct AttnSmArgs {
   float scale_log2;       // log2(e) / sqrt(d)
   bf16_t* part_o;         // [splits][n_rbt][64][d] (normalised partials)
   float* part_ml;         // [splits][n_rbt][64][2] (max, sum)
-  unsigned* counters;     // [n_rbt]
 };
 
-constexpr int kAttnMaxSplits = 8;
+constexpr int kAttnMaxSplits = 16;
 
 template <int HD>
 struct AttnSmSmem {
-  bf16_t k[2][32 * (HD + 8)];
-  bf16_t v[2][32 * (HD + 16)];
-  int last_flag;
+  bf16_t k[2][64 * (HD + 8)];        // K tiles; after the key loop: the block's rows [64][HD + 8]
+  bf16_t v[2][64 * (HD + 16)];       // V tiles; after the key loop: the second key half's partials
+  float2 ml[64];                     // per row (max, sum) of this slice
+  float2 ml2[64];                    // second key half's (max, sum)
 };
 
 __device__ __forceinline__ uint2 lds_tr16(const bf16_t* p) {
@@ -69,150 +75,180 @@ __device__ __forceinline__ uint2 lds_tr16(const bf16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // One task: stream x kv head bh, 64-row block rb, key slice ks.  Returns true
-// if this workgroup wrote the block's final rows.
+// if this workgroup wrote the block's final rows (a single key slice).
 template <int HD, class Wait>
 __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSmSmem<HD>& sm,
                              Wait&& wait) {
   constexpr int KROW = HD + 8, VROW = HD + 16;
-  constexpr int NKS = HD / 32;                 // 32-wide k-steps of S^T
-  constexpr int NDT = HD / 16;                 // 16-row tiles of O^T
+  constexpr int NDS = HD / 16;                 // 16-wide d steps of S^T (32x32x16)
+  constexpr int NDT = HD / 32;                 // 32-row d tiles of O^T
   constexpr int CPR = HD / 8;                  // 16-byte chunks per key row
-  constexpr int NCH = 32 * CPR / 256;          // chunks per thread per tile (K or V)
+  constexpr int NCH = 64 * CPR / 256;          // chunks per thread per 64-key tile (K or V)
+  constexpr int IPT = 64 * CPR / 256;          // (row, chunk) items per thread of a 64-row block
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
-  const int l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int l = tid & 63;
+  const int rp = w & 1, kh = w >> 1;           // 32-row half of the block, 32-key half of a tile
   const int b = bh / a.Hkv, hk = bh - b * a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int rows = G * a.T;
-  const int n_rt = (rows + 15) >> 4;
+  const int n_rt = (rows + 31) >> 5;           // 32-row tiles of this (stream, kv head)
   const int L = a.P + a.T;
   const int key_begin = ks * a.kps;
   const int key_end = min(L, key_begin + a.kps);
-  const int n_tiles = (key_end - key_begin + 31) >> 5;
-
-  const bf16_t* kpb = a.kp ? a.kp + (size_t)b * a.prefix_stride + (size_t)hk * HD : nullptr;
-  const bf16_t* vpb = a.vp ? a.vp + (size_t)b * a.prefix_stride + (size_t)hk * HD : nullptr;
-  const bf16_t* knb = a.kn + (size_t)b * a.new_stride + (size_t)hk * HD;
-  const bf16_t* vnb = a.vn + (size_t)b * a.new_stride + (size_t)hk * HD;
+  const int n_tiles = (key_end - key_begin + 63) >> 6;
   const int kvrow = a.Hkv * HD;
-  // K (h = 0) / V (h = 1) chunk c of key `key`; zero past the slice
-  auto ld_kv = [&](int h, int key, int c) -> uint4 {
-    if (key >= key_end) return make_uint4(0, 0, 0, 0);
-    if (key < a.P) {
-      const bf16_t* p = (h ? vpb : kpb) + (size_t)key * kvrow + 8 * c;
-      return *reinterpret_cast<const uint4*>(p);
-    }
-    return ld16c((h ? vnb : knb) + (size_t)(key - a.P) * kvrow + 8 * c);
-  };
-  uint4 reg[2][2][NCH];   // [ring slot][K, V][chunk]
-  auto load_tile = [&](int slot, int tile) {
-    const int base = key_begin + 32 * tile;
+
+  // K / V sources: prefix (caller's cache, read once) and the chunk's own rows
+  // (written by the QKV step, possibly earlier in the same launch: coherent)
+  const __amdgpu_buffer_rsrc_t rkp =
+      make_rsrc(a.kp ? a.kp + (size_t)b * a.prefix_stride + (size_t)hk * HD : a.kn, (size_t)a.P * kvrow * 2);
+  const __amdgpu_buffer_rsrc_t rvp =
+      make_rsrc(a.vp ? a.vp + (size_t)b * a.prefix_stride + (size_t)hk * HD : a.vn, (size_t)a.P * kvrow * 2);
+  const __amdgpu_buffer_rsrc_t rkn = make_rsrc(a.kn + (size_t)b * a.new_stride + (size_t)hk * HD, (size_t)a.T * kvrow * 2);
+  const __amdgpu_buffer_rsrc_t rvn = make_rsrc(a.vn + (size_t)b * a.new_stride + (size_t)hk * HD, (size_t)a.T * kvrow * 2);
+  uint4 reg[2][NCH];   // one tile in flight: [K, V][chunk]
+  auto load_tile = [&](int tile) {
+    const int base = key_begin + 64 * tile;
+    const bool all_prefix = base + 64 <= a.P;   // uniform
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int idx = tid + 256 * j;
       const int kk = idx / CPR, c = idx - kk * CPR;
-      reg[slot][0][j] = ld_kv(0, base + kk, c);
-      reg[slot][1][j] = ld_kv(1, base + kk, c);
+      const int key = base + kk;
+      if (all_prefix) {
+        const int off = (key * kvrow + 8 * c) * 2;
+        reg[0][j] = buf_ld_stream(rkp, off);
+        reg[1][j] = buf_ld_stream(rvp, off);
+      } else if (key >= key_end) {
+        reg[0][j] = make_uint4(0, 0, 0, 0);
+        reg[1][j] = make_uint4(0, 0, 0, 0);
+      } else if (key < a.P) {
+        const int off = (key * kvrow + 8 * c) * 2;
+        reg[0][j] = buf_ld_stream(rkp, off);
+        reg[1][j] = buf_ld_stream(rvp, off);
+      } else {
+        const int off = ((key - a.P) * kvrow + 8 * c) * 2;
+        reg[0][j] = buf_ld_act(rkn, off);
+        reg[1][j] = buf_ld_act(rvn, off);
+      }
     }
   };
-  auto store_tile = [&](int slot, int buf) {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int idx = tid + 256 * j;
       const int kk = idx / CPR, c = idx - kk * CPR;
-      *reinterpret_cast<uint4*>(&sm.k[buf][kk * KROW + 8 * c]) = reg[slot][0][j];
-      *reinterpret_cast<uint4*>(&sm.v[buf][kk * VROW + 8 * c]) = reg[slot][1][j];
+      *reinterpret_cast<uint4*>(&sm.k[buf][kk * KROW + 8 * c]) = reg[0][j];
+      *reinterpret_cast<uint4*>(&sm.v[buf][kk * VROW + 8 * c]) = reg[1][j];
     }
   };
 
-  // prefix tiles do not depend on earlier work: start them before the wait
-  const bool pre0 = key_begin + 32 <= a.P, pre1 = key_begin + 64 <= a.P;
-  if (n_tiles > 0 && pre0) load_tile(0, 0);
-  if (n_tiles > 1 && pre1) load_tile(1, 1);
+  // the first tile, if wholly in the prefix, does not depend on earlier work
+  // and starts before the wait
+  const bool pre0 = key_begin + 64 <= a.P;
+  if (n_tiles > 0 && pre0) load_tile(0);
   if (!wait()) return false;
-  if (n_tiles > 0 && !pre0) load_tile(0, 0);
-  if (n_tiles > 1 && !pre1) load_tile(1, 1);
+  if (n_tiles > 0 && !pre0) load_tile(0);
 
-  // this wave's 16 query rows: Q^T fragments (B operand), one per k-step
-  const int rt = min(4 * rb + w, n_rt - 1);
+  // this wave's 32 query rows: Q^T fragments (B operand), one per d step
+  const int rt = min(2 * rb + rp, n_rt - 1);
   const __amdgpu_buffer_rsrc_t rq =
-      make_rsrc(a.q + (size_t)(bh * n_rt + rt) * NKS * 512, (size_t)NKS * kFragBytes);
-  uint4 qf[NKS];
+      make_rsrc(a.q + (size_t)(bh * n_rt + rt) * NDS * 512, (size_t)NDS * kFragBytes);
+  uint4 qf[NDS];
 #pragma unroll
-  for (int s = 0; s < NKS; ++s) qf[s] = buf_ld_act(rq, s * kFragBytes + l * 16);
+  for (int s = 0; s < NDS; ++s) qf[s] = buf_ld_act(rq, s * kFragBytes + l * 16);
 
-  f32x4 o[NDT];
+  f32x16 o[NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
+  // running reference max (may trail the true max by up to 2^8, see below) and sum
   float m_run = -INFINITY, l_run = 0.f;
 
   __syncthreads();   // a previous task's readers of sm are done
   if (n_tiles > 0) {
-    store_tile(0, 0);
-    if (n_tiles > 2) load_tile(0, 2);
+    store_tile(0);
+    if (n_tiles > 1) load_tile(1);
   }
   __syncthreads();
 
-  // one 32-key tile; CUR (= it & 1) is a compile-time constant so that the
-  // register ring stays in registers
+  // lane roles: query row l % 32 of this wave's 32 rows; S^T keys
+  // 32 kh + 8 (v/4) + 4 (l/32) + v%4 of the 64-key tile, v < 16
+  const int hl = l >> 5;
+  const int p16 = l & 15;
+  // V^T operand (transposed LDS reads): d = 32 dt + 16 ((l/16) % 2) + 4 (p16 % 4),
+  // key rows 32 kh + 16 u + 4 hl + p16 / 4 (+ 8 for the second read)
+  const int vt_off = (32 * kh + 4 * hl + (p16 >> 2)) * VROW + 16 * ((l >> 4) & 1) + 4 * (p16 & 3);
+
   auto step = [&](int it, auto cur_c) {
-    constexpr int cur = decltype(cur_c)::value;
-    const int base = key_begin + 32 * it;
-    // ---- S^T: lane holds S[row lr][key 16 mt + 4 lg + j]
-    f32x4 s[2];
+    constexpr int cur = decltype(cur_c)::value;   // LDS buffer of tile it
+    const int base = key_begin + 64 * it + 32 * kh;
+    // ---- S^T (32 keys x 32 rows)
+    f32x16 sacc;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+    const bf16_t* kr = &sm.k[cur][(32 * kh + (l & 31)) * KROW + 8 * hl];
 #pragma unroll
-      for (int ksx = 0; ksx < NKS; ++ksx) {
-        const uint4 kf = *reinterpret_cast<const uint4*>(&sm.k[cur][(16 * mt + lr) * KROW + 32 * ksx + 8 * lg]);
-        s[mt] = mfma16(as_bf16x8(kf), as_bf16x8(qf[ksx]), s[mt]);
-      }
-    }
-    float x[8];
+    for (int s = 0; s < NDS; ++s)
+      sacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(kr + 16 * s)), as_bf16x8(qf[s]), sacc);
+    // ---- online softmax in base 2
+    float x[16];
     float mloc = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = base + 16 * mt + 4 * lg + j;
-        const float v = key < key_end ? s[mt][j] * a.scale_log2 : -INFINITY;
-        x[mt * 4 + j] = v;
-        mloc = fmaxf(mloc, v);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+    for (int v = 0; v < 16; ++v) {
+      const int key = base + 8 * (v >> 2) + 4 * hl + (v & 3);
+      x[v] = key < key_end ? sacc[v] * a.scale_log2 : -INFINITY;
+      mloc = fmaxf(mloc, x[v]);
+    }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = exp2f(m_run - m_new);
+    // Rescale only when some row's max grew past the reference by more than
+    // 2^8 (exp2 of scores against a stale reference stays <= 256: exact
+    // enough in bf16 and far from fp32 overflow); otherwise keep it.
+    const bool grow = mloc > m_run + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mloc : m_run;
+      const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] = o[dt] * alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    // masked keys (and rows that have seen no key yet) contribute exactly 0
     float psum = 0.f;
-    uint32_t pw[4];
+    uint32_t pw[8];
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const float p0 = exp2f(x[e] - m_new);
-      const float p1 = exp2f(x[e + 1] - m_new);
+    for (int v = 0; v < 16; v += 2) {
+      const float p0 = x[v] == -INFINITY ? 0.f : exp2f(x[v] - m_run);
+      const float p1 = x[v + 1] == -INFINITY ? 0.f : exp2f(x[v + 1] - m_run);
       psum += p0 + p1;
-      pw[e / 2] = pack2(p0, p1);
+      pw[v / 2] = pack2(p0, p1);
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    const bf16x8 pb = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
-
-    // ---- O^T += V^T P^T
-    const bf16_t* vt = &sm.v[cur][(4 * lg + (lr >> 2)) * VROW + 4 * (lr & 3)];
+    l_run += psum;
+    // ---- O^T += V^T P^T, two 16-key steps (P^T slots e <-> S^T values 8 u + e)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const uint2 lo = lds_tr16(vt + 16 * dt);
-      const uint2 hi = lds_tr16(vt + 16 * VROW + 16 * dt);
-      o[dt] = o[dt] * alpha;
-      o[dt] = mfma16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, o[dt]);
+    for (int u = 0; u < 2; ++u) {
+      const bf16x8 pb = as_bf16x8(make_uint4(pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]));
+      const bf16_t* vt = &sm.v[cur][vt_off + 16 * u * VROW];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint2 lo = lds_tr16(vt + 32 * dt);
+        const uint2 hi = lds_tr16(vt + 8 * VROW + 32 * dt);
+        o[dt] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, o[dt]);
+      }
     }
-    // ---- stage the next tile (its buffer was last read one tile ago) and
-    //      start the loads of the tile after the next; tile t sits in ring
-    //      slot t & 1
+    // ---- stage the next tile into the other buffer (last read one tile ago)
+    //      and start the loads of the tile after it
     if (it + 1 < n_tiles) {
-      store_tile(cur ^ 1, cur ^ 1);
-      if (it + 3 < n_tiles) load_tile(cur ^ 1, it + 3);
+      store_tile(cur ^ 1);
+      if (it + 2 < n_tiles) load_tile(it + 2);
     }
     __syncthreads();
   };
@@ -221,96 +257,141 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
     if (it + 1 < n_tiles) step(it + 1, std::integral_constant<int, 1>{});
   }
 
-  float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  // ---- merge the two key halves: kh = 1 parks (m, l, O^T) in LDS, kh = 0
+  //      combines and writes normalised rows [64][HD + 8] (bf16) plus stats
+  float l_tot = l_run + __shfl_xor(l_run, 32);   // the two lanes of a row share m_run
+  float* park = reinterpret_cast<float*>(sm.v[0]);   // [2 row halves][32 rows][HD + 4] fp32
+  constexpr int PROW = HD + 4;
+  const int row32 = l & 31;
+  if (kh == 1) {
+    float* dst = park + (rp * 32 + row32) * PROW;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * q + 4 * hl) =
+            make_float4(o[dt][4 * q], o[dt][4 * q + 1], o[dt][4 * q + 2], o[dt][4 * q + 3]);
+    if (hl == 0) sm.ml2[rp * 32 + row32] = make_float2(m_run, l_tot);
+  }
+  __syncthreads();
+  bf16_t* rowt = sm.k[0];
+  if (kh == 0) {
+    const float2 o2 = sm.ml2[rp * 32 + row32];
+    const float mm = fmaxf(m_run, o2.x);
+    const float a1 = m_run == -INFINITY ? 0.f : exp2f(m_run - mm);
+    const float a2 = o2.x == -INFINITY ? 0.f : exp2f(o2.x - mm);
+    const float lsum = l_tot * a1 + o2.y * a2;
+    const float inv = 1.f / lsum;
+    const float* src = park + (rp * 32 + row32) * PROW;
+    bf16_t* dst = rowt + (rp * 32 + row32) * KROW;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d0 = 32 * dt + 8 * q + 4 * hl;
+        const float4 p2 = *reinterpret_cast<const float4*>(src + d0);
+        *reinterpret_cast<uint2*>(dst + d0) =
+            make_uint2(pack2((o[dt][4 * q] * a1 + p2.x * a2) * inv, (o[dt][4 * q + 1] * a1 + p2.y * a2) * inv),
+                       pack2((o[dt][4 * q + 2] * a1 + p2.z * a2) * inv, (o[dt][4 * q + 3] * a1 + p2.w * a2) * inv));
+      }
+    if (hl == 0) sm.ml[rp * 32 + row32] = make_float2(mm, lsum);
+  }
+  __syncthreads();
 
   const int n_rb = (rows + 63) >> 6;
   const int rb_id = bh * n_rb + rb;
-  const int MTo = mt_of(a.B * a.T);
-  const int arow = 64 * rb + 16 * w + lr;
 
   if (a.splits == 1) {
-    if (arow < rows) {
-      const float inv = 1.f / l_tot;
-      const int t = arow / G, h = hk * G + (arow - t * G);
-      const int m = b * a.T + t;
+    const int MTo = mt_of(a.B * a.T);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o, (size_t)MTo * 16 * a.Hq * HD * 2);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        st8c(a.o + fa_index(m, h * HD + 16 * dt + 4 * lg, MTo), pack2(o[dt][0] * inv, o[dt][1] * inv),
-             pack2(o[dt][2] * inv, o[dt][3] * inv));
+    for (int p = 0; p < IPT; ++p) {
+      const int i = tid + 256 * p, row = i / CPR, c = i - row * CPR;
+      const int ar = 64 * rb + row;
+      if (ar < rows) {
+        const int t = ar / G, h = hk * G + (ar - t * G);
+        buf_st16(ro, (int)(fa_index(b * a.T + t, h * HD + 8 * c, MTo) * 2),
+                 *reinterpret_cast<const uint4*>(rowt + row * KROW + 8 * c));
+      }
     }
     return true;
   }
 
-  // ---- several key slices: publish (o / l, m, l); the last combines
+  // ---- several key slices: publish the normalised rows and (max, sum) with
+  //      row-contiguous stores; attn_combine_task merges the slices
   const int n_rbt = a.B * a.Hkv * n_rb;
-  {
-    const float inv = 1.f / l_tot;
-    bf16_t* po = a.part_o + (((size_t)ks * n_rbt + rb_id) * 64 + 16 * w + lr) * HD + 4 * lg;
+  const size_t slab = (size_t)64 * HD;     // bf16 per (slice, row block)
+  const __amdgpu_buffer_rsrc_t rpo = make_rsrc(a.part_o + ((size_t)ks * n_rbt + rb_id) * slab, slab * 2);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-      st8c(po + 16 * dt, pack2(o[dt][0] * inv, o[dt][1] * inv), pack2(o[dt][2] * inv, o[dt][3] * inv));
-    if (lg == 0)
-      st8c(a.part_ml + (((size_t)ks * n_rbt + rb_id) * 64 + 16 * w + lr) * 2, __float_as_uint(m_run),
-           __float_as_uint(l_tot));
+  for (int p = 0; p < IPT; ++p) {
+    const int i = tid + 256 * p, row = i / CPR, c = i - row * CPR;
+    buf_st16(rpo, (row * HD + 8 * c) * 2, *reinterpret_cast<const uint4*>(rowt + row * KROW + 8 * c));
   }
-  if (!arrive_last(&a.counters[rb_id], (unsigned)a.splits, &sm.last_flag)) return false;
+  if (tid < 64) {
+    const __amdgpu_buffer_rsrc_t rpm = make_rsrc(a.part_ml + ((size_t)ks * n_rbt + rb_id) * 128, 512);
+    buf_st8(rpm, tid * 8, __float_as_uint(sm.ml[tid].x), __float_as_uint(sm.ml[tid].y));
+  }
+  return false;
+}
 
-  // 4 threads per row, HD / 4 columns each, in two halves; all slices' loads
-  // of a half are in flight together
-  constexpr int QC = HD / 4, HC = QC / 16;   // 16-byte chunks per half
-  const int row = tid >> 2, qq = tid & 3;
-  const int arow2 = 64 * rb + row;
-  if (arow2 < rows) {
-    float mx = -INFINITY;
-    float2 ml[kAttnMaxSplits];
+// Items of the key-slice merge: one per (row block, row, 16-byte chunk).
+__host__ __device__ inline int attn_combine_items(int B, int T, int Hq, int Hkv, int HD) {
+  return B * Hkv * ((Hq / Hkv * T + 63) / 64) * 64 * (HD / 8);
+}
+
+// Merges the key slices of attn_sm_task for the 256 items of workgroup-sized
+// task `task`: o = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m),
+// in slice order, stored in the O projection's operand order.
+template <int HD>
+__device__ void attn_combine_task(const AttnSmArgs& a, int task) {
+  constexpr int CPR = HD / 8;
+  const int G = a.Hq / a.Hkv;
+  const int rows = G * a.T;
+  const int n_rb = (rows + 63) >> 6;
+  const int n_rbt = a.B * a.Hkv * n_rb;
+  const int i = task * 256 + (int)threadIdx.x;
+  if (i >= n_rbt * 64 * CPR) return;
+  const int rb_id = i / (64 * CPR), rem = i - rb_id * 64 * CPR;
+  const int row = rem / CPR, c = rem - row * CPR;
+  const int bh = rb_id / n_rb, rb = rb_id - bh * n_rb;
+  const int b = bh / a.Hkv, hk = bh - b * a.Hkv;
+  const int ar = 64 * rb + row;
+  if (ar >= rows) return;
+  const size_t slab = (size_t)64 * HD;
+  const __amdgpu_buffer_rsrc_t rpo = make_rsrc(a.part_o, (size_t)a.splits * n_rbt * slab * 2);
+  const __amdgpu_buffer_rsrc_t rpm = make_rsrc(a.part_ml, (size_t)a.splits * n_rbt * 512);
+  float2 ml[kAttnMaxSplits];
+  uint4 pv[kAttnMaxSplits];
 #pragma unroll
-    for (int sp = 0; sp < kAttnMaxSplits; ++sp)
-      if (sp < a.splits) {
-        const uint2 u = ld8c(a.part_ml + (((size_t)sp * n_rbt + rb_id) * 64 + row) * 2);
-        ml[sp] = make_float2(__uint_as_float(u.x), __uint_as_float(u.y));
-        mx = fmaxf(mx, ml[sp].x);
-      }
-    float den = 0.f, wgt[kAttnMaxSplits];
-#pragma unroll
-    for (int sp = 0; sp < kAttnMaxSplits; ++sp)
-      if (sp < a.splits) {
-        wgt[sp] = ml[sp].y * exp2f(ml[sp].x - mx);
-        den += wgt[sp];
-      }
-    const float inv = 1.f / den;
-    const int t = arow2 / G, h = hk * G + (arow2 - t * G);
-    const int m = b * a.T + t;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int c0 = qq * QC + hf * (QC / 2);
-      uint4 pv[kAttnMaxSplits][HC];
-#pragma unroll
-      for (int sp = 0; sp < kAttnMaxSplits; ++sp)
-        if (sp < a.splits) {
-          const bf16_t* po = a.part_o + (((size_t)sp * n_rbt + rb_id) * 64 + row) * HD + c0;
-#pragma unroll
-          for (int c = 0; c < HC; ++c) pv[sp][c] = ld16c(po + 8 * c);
-        }
-#pragma unroll
-      for (int c = 0; c < HC; ++c) {
-        float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int sp = 0; sp < kAttnMaxSplits; ++sp)
-          if (sp < a.splits) {
-            float x[8];
-            unpack8(pv[sp][c], x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] = fmaf(wgt[sp], x[e], f[e]);
-          }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] *= inv;
-        st16c(a.o + fa_index(m, h * HD + c0 + 8 * c, MTo), pack8(f));
-      }
+  for (int sp = 0; sp < kAttnMaxSplits; ++sp)
+    if (sp < a.splits) {
+      const u32x2v u = __builtin_amdgcn_raw_buffer_load_b64(rpm, ((sp * n_rbt + rb_id) * 64 + row) * 8, 0, 16);
+      ml[sp] = make_float2(__uint_as_float(u[0]), __uint_as_float(u[1]));
+      pv[sp] = buf_ld_act(rpo, (int)((((size_t)sp * n_rbt + rb_id) * 64 + row) * HD + 8 * c) * 2);
     }
-  }
-  return true;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < kAttnMaxSplits; ++sp)
+    if (sp < a.splits) mx = fmaxf(mx, ml[sp].x);
+  float den = 0.f;
+  float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sp = 0; sp < kAttnMaxSplits; ++sp)
+    if (sp < a.splits) {
+      const float wgt = ml[sp].x == -INFINITY ? 0.f : ml[sp].y * exp2f(ml[sp].x - mx);
+      den += wgt;
+      float x[8];
+      unpack8(pv[sp], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = fmaf(wgt, x[e], f[e]);
+    }
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] *= inv;
+  const int t = ar / G, h = hk * G + (ar - t * G);
+  const int MTo = mt_of(a.B * a.T);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o, (size_t)MTo * 16 * a.Hq * HD * 2);
+  buf_st16(ro, (int)(fa_index(b * a.T + t, h * HD + 8 * c, MTo) * 2), pack8(f));
 }
 
 }  // namespace blk

@@ -202,7 +202,6 @@ void launch_sk_gateup(const SkArgs& ga, const EpiGateUpS& e, hipStream_t st);
 void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps);
 size_t attn_sm_part_o_elems(int B, int T, int P, int Hq, int Hkv, int d);
 size_t attn_sm_part_ml_floats(int B, int T, int P, int Hq, int Hkv, int d);
-size_t attn_sm_counters(int B, int T, int Hq, int Hkv);
 void launch_attn_sm(const AttnSmArgs& a, int head_dim, hipStream_t st);
 
 // ---------------------------------------------------------------- flow head

@@ -265,11 +265,11 @@ __device__ bool sk_task(const SkArgs& ga, const Epi& epi, int g, int s, SkSmem<A
 
 // Attention operand order of Q (written by the QKV epilogue, read by the
 // attention): for stream b and kv head hk the rows are ar = t G + gh over the
-// G = Hq / Hkv query heads sharing that kv head; row tile ar / 16 and the
-// 32-column slice ks of the head dimension form one 1 KiB fragment, lane
-// ar % 16 + 16 ((dd % 32) / 8) holding 8 consecutive dd.
-__host__ __device__ inline size_t qa_index(int bh, int n_rt, int KS, int ar, int dd) {
-  return ((((size_t)bh * n_rt + (ar >> 4)) * KS + (dd >> 5)) * 64 + (ar & 15) + 16 * ((dd >> 3) & 3)) * 8 +
+// G = Hq / Hkv query heads sharing that kv head; row tile ar / 32 and the
+// 16-column slice dd / 16 form one 1 KiB fragment, lane ar % 32 + 32 ((dd % 16) / 8)
+// holding 8 consecutive dd (the B operand of a 32 x 32 x 16 MFMA).
+__host__ __device__ inline size_t qa_index(int bh, int n_rt, int NDS, int ar, int dd) {
+  return ((((size_t)bh * n_rt + (ar >> 5)) * NDS + (dd >> 4)) * 64 + (ar & 31) + 32 * ((dd >> 3) & 1)) * 8 +
          (dd & 7);
 }
 
@@ -313,10 +313,10 @@ struct EpiQkvS {
       if (head < Hq) {
         const int G = Hq / Hkv;
         const int hk = head / G, gh = head - hk * G;
-        const int n_rt = (G * T + 15) >> 4;
+        const int n_rt = (G * T + 31) >> 5;
         const int ar = tt * G + gh, bh = b * Hkv + hk;
-        st8c(q + qa_index(bh, n_rt, d >> 5, ar, j0), pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
-        st8c(q + qa_index(bh, n_rt, d >> 5, ar, j0 + half), pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
+        st8c(q + qa_index(bh, n_rt, d >> 4, ar, j0), pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
+        st8c(q + qa_index(bh, n_rt, d >> 4, ar, j0 + half), pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
       } else {
         bf16_t* dst = kn + (size_t)b * new_stride + ((size_t)tt * Hkv + (head - Hq)) * d;
         st8c(dst + j0, pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));

@@ -66,11 +66,15 @@ static int sk_nb(int KW) {
   return 1;
 }
 
+// Key slices per 64-row block: enough workgroups (about 96) that each takes
+// one or two 64-key steps -- one memory round trip for its K/V -- and the
+// merge kernel spreads the combine over every row; slices are multiples of
+// 32 keys (a wave's half of a step).
 void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps) {
   const int G = Hq / Hkv;
   const int n_rbt = B * Hkv * ((G * T + 63) / 64);
   const int L = P + T;
-  int s = std::max(1, std::min(kAttnMaxSplits, (48 + n_rbt - 1) / n_rbt));
+  int s = std::max(1, std::min(kAttnMaxSplits, (96 + n_rbt - 1) / n_rbt));
   s = std::min(s, (L + 31) / 32);
   int k = (L + s - 1) / s;
   k = (k + 31) / 32 * 32;
@@ -87,9 +91,6 @@ size_t attn_sm_part_o_elems(int B, int T, int P, int Hq, int Hkv, int d) {
 }
 size_t attn_sm_part_ml_floats(int B, int T, int P, int Hq, int Hkv, int d) {
   return attn_sm_part_o_elems(B, T, P, Hq, Hkv, d) / d * 2;
-}
-size_t attn_sm_counters(int B, int T, int Hq, int Hkv) {
-  return (size_t)B * Hkv * ((Hq / Hkv * T + 63) / 64);
 }
 
 // ============================================================================ skinny GEMM
@@ -153,6 +154,11 @@ __global__ __launch_bounds__(256) void attn_sm_kernel(AttnSmArgs a) {
 }
 
 template <int HD>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnSmArgs a) {
+  attn_combine_task<HD>(a, blockIdx.x);
+}
+
+template <int HD>
 static void attn_sm_go(const AttnSmArgs& a, hipStream_t st) {
   auto kern = attn_sm_kernel<HD>;
   const size_t smem = sizeof(AttnSmSmem<HD>);
@@ -165,6 +171,10 @@ static void attn_sm_go(const AttnSmArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const dim3 grid(a.splits, (G * a.T + 63) / 64, a.B * a.Hkv);
   hipLaunchKernelGGL(kern, grid, dim3(256), smem, st, a);
+  if (a.splits > 1) {
+    const int items = attn_combine_items(a.B, a.T, a.Hq, a.Hkv, HD);
+    hipLaunchKernelGGL(attn_combine_kernel<HD>, dim3((items + 255) / 256), dim3(256), 0, st, a);
+  }
 }
 
 void launch_attn_sm(const AttnSmArgs& a, int head_dim, hipStream_t st) {
