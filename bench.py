@@ -49,6 +49,8 @@ def parse():
                     default="all", help="restrict the run (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rotate", type=int, default=16, help="weight copies in rotation")
+    ap.add_argument("--exec-mode", choices=["auto", "per_operator", "persistent"], default="auto",
+                    help="blk_set_execution_mode for the small-chunk workloads")
     return ap.parse_args()
 
 
@@ -279,6 +281,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    import diffusion_transformer_block_amd as blk
+    blk.blk_set_execution_mode({"auto": blk.EXEC_AUTO, "per_operator": blk.EXEC_PER_OPERATOR,
+                                "persistent": blk.EXEC_PERSISTENT}[args.exec_mode])
     rotate = max(1, args.rotate)
     steps = max(rotate, (args.steps // rotate) * rotate)
     shape = synth.AE_BLOCK

@@ -207,12 +207,6 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
                      sk_part_floats(m, F, gd, false)})
       part = std::max(part, v);
   }
-  if ((int)M <= kSkinnyMaxM && M > 0) {
-    const int m = (int)M;
-    part = std::max(part, std::max(std::max(stage_part_floats(m, D, gq), stage_part_floats(m, Hq * d, go)),
-                                   std::max(stage_part_floats(m, D, ggu), stage_part_floats(m, F, gd))));
-    ss = std::max(ss, (size_t)64 * std::max(std::max(stage_split(m, D) * gq, stage_split(m, D) * ggu), 1));
-  }
   w.part = off;
   off += align_up(part * 4);
   w.ss = off;
@@ -236,9 +230,9 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
   w.sm_att_ml = off;
   off += align_up(small ? attn_sm_part_ml_floats(B, T, P, Hq, Hkv, d) * 4 : 0);
   w.xb0 = off;
-  off += align_up(M * D * 2);
+  off += align_up(Mp * D * 2);
   w.xb1 = off;
-  off += align_up(M * D * 2);
+  off += align_up(Mp * D * 2);
   w.flags = off;
   off += align_up((size_t)kPhCount * kStageMaxFlags * 4);
   w.sync = off;
@@ -263,31 +257,31 @@ int g_exec_mode = 0;   // 0 auto, 1 per-operator kernels, 2 persistent stage ker
 // 64-token block the graph of per-operator kernels measures faster.
 bool want_persistent() { return g_exec_mode == 2; }
 
-// Fills the shapes, phase maps and attention plan of a stage launch; false if
-// the persistent kernel does not cover this shape (the caller falls back to
-// one kernel per operator).
+// Fills the shapes, splits, phase maps and attention plan of a stage launch;
+// false if the persistent kernel does not cover this shape.
 bool stage_plan(const blk_config& c, int B, int T, int P, int flow_N, int nwg, StageArgs& sa) {
   const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const int M = B * T;
   if (nwg <= 0 || M <= 0 || M > kSkinnyMaxM) return false;
-  if (D % 128 != 0 || F % 128 != 0 || (Hq * d) % 128 != 0) return false;
   if (flow_N > 0 && flow_N + 1 != M) return false;
-  sa.split_qkv = stage_split(M, D);
-  sa.split_o = stage_split(M, Hq * d);
-  sa.split_gu = stage_split(M, D);
-  sa.split_d = stage_split(M, F);
-  sa.split_w3 = stage_split(M, D);
+  const int G_q = (Hq + 2 * Hkv) * d / 32, G_o = D / 32, G_gu = F / 16, G_d = D / 32;
+  // a block's first layer reads the caller's row-major input (staged per
+  // workgroup), which bounds the QKV split; later layers can use the same
+  sa.split_qkv = sk_splits(M, D, G_q, true);
+  sa.split_o = sk_splits(M, Hq * d, G_o, false);
+  sa.split_gu = sk_splits(M, D, G_gu, false);
+  sa.split_d = sk_splits(M, F, G_d, false);
+  sa.split_w3 = flow_N > 0 ? sk_splits(flow_N, D, G_o, false) : 1;
   for (int sp : {sa.split_qkv, sa.split_o, sa.split_gu, sa.split_d, sa.split_w3})
     if (sp < 1) return false;
-  const int G_q = (Hq + 2 * Hkv) * d / 32, G_o = D / 32, G_gu = F / 16, G_d = D / 32;
-  const int gq = G_q * sa.split_qkv, n_o = G_o * sa.split_o, n_gu = G_gu * sa.split_gu,
-            n_d = G_d * sa.split_d, n_w3 = G_o * sa.split_w3;
-  int splits = 1, kps = 0;
-  attn_plan(B, T, P, Hq, Hkv, d, &splits, &kps);
+  int splits = 1, kps = 32;
+  attn_sm_plan(B, T, P, Hq, Hkv, &splits, &kps);
   const int n_rbt = B * Hkv * (((Hq / Hkv) * T + 63) / 64);
   const int n_att = n_rbt * splits;
+  const int n_cmb = splits > 1 ? (attn_combine_items(B, T, Hq, Hkv, d) + 255) / 256 : 0;
   const int n_emb = (flow_N + 1 + 3) / 4;
-  for (int n : {gq, n_o, n_gu, n_d, n_w3, n_att, n_emb, flow_N})
+  for (int n : {G_q * sa.split_qkv, n_att, n_cmb, G_o * sa.split_o, G_gu * sa.split_gu, G_d * sa.split_d,
+                G_o * sa.split_w3, n_emb, flow_N})
     if (n > kStageMaxFlags) return false;
   sa.B = B;
   sa.T = T;
@@ -301,6 +295,7 @@ bool stage_plan(const blk_config& c, int B, int T, int P, int flow_N, int nwg, S
   sa.eps = c.rms_eps;
   sa.att_splits = splits;
   sa.att_kps = kps;
+  sa.att_merge_tasks = n_cmb;
   sa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
   int w0 = 0;
   auto map = [&](int type, int n_tasks, int n_flags) {
@@ -313,13 +308,14 @@ bool stage_plan(const blk_config& c, int B, int T, int P, int flow_N, int nwg, S
   };
   if (flow_N > 0) {
     map(kPhEMB, n_emb, n_emb);
-    map(kPhW3, n_w3, G_o);
+    map(kPhW3, G_o * sa.split_w3, G_o);
   }
-  map(kPhQKV, gq, G_q);
-  map(kPhATT, n_att, n_rbt);
-  map(kPhO, n_o, G_o);
-  map(kPhGU, n_gu, G_gu);
-  map(kPhD, n_d, G_d);
+  map(kPhQKV, G_q * sa.split_qkv, G_q);
+  map(kPhATT, n_att, n_att);
+  if (n_cmb > 0) map(kPhCMB, n_cmb, n_cmb);
+  map(kPhO, G_o * sa.split_o, G_o);
+  map(kPhGU, G_gu * sa.split_gu, G_gu);
+  map(kPhD, G_d * sa.split_d, G_d);
   if (flow_N > 0) map(kPhVEL, flow_N, flow_N);
   return true;
 }
@@ -341,11 +337,9 @@ void stage_fill_common(StageArgs& sa, const Layout& lay, const void* packed, voi
   sa.o = at<bf16_t>(ws, w.o);
   sa.h = at<bf16_t>(ws, w.h);
   sa.a = at<bf16_t>(ws, w.a);
-  sa.part_o = at<float>(ws, w.att_o);
-  sa.part_ml = at<float>(ws, w.att_ml);
-  sa.att_ctr = at<unsigned>(ws, w.ctr_att);
+  sa.att_part_o = at<bf16_t>(ws, w.sm_att_o);
+  sa.att_part_ml = at<float>(ws, w.sm_att_ml);
   sa.part = at<float>(ws, w.part);
-  sa.ss_part = at<float>(ws, w.ss);
   sa.ctr_qkv = at<unsigned>(ws, w.ctr_qkv);
   sa.ctr_o = at<unsigned>(ws, w.ctr_o);
   sa.ctr_gu = at<unsigned>(ws, w.ctr_gu);
@@ -593,7 +587,7 @@ FlowWs flow_ws_layout(const blk_config& c, int N, int P) {
   f.x1 = off;
   off += align_up((size_t)16 * mt_of(T) * D * 2);
   f.z = off;
-  off += align_up((size_t)16 * mt_of(N) * D * 2);
+  off += align_up((size_t)16 * mt_of(T) * D * 2);   // row tiles of X (>= those of z's N rows)
   f.kn = off;
   off += align_up((size_t)T * c.n_kv_heads * c.head_dim * 2);
   f.vn = off;

@@ -6,7 +6,7 @@
 
 namespace blk {
 
-enum StagePhase : int { kPhQKV = 0, kPhATT, kPhO, kPhGU, kPhD, kPhEMB, kPhW3, kPhVEL, kPhCount };
+enum StagePhase : int { kPhQKV = 0, kPhATT, kPhCMB, kPhO, kPhGU, kPhD, kPhEMB, kPhW3, kPhVEL, kPhCount };
 constexpr int kStageMaxLayers = 64;
 constexpr int kStageMaxFlags = 1024;   // tasks (flags) per phase
 
@@ -28,11 +28,12 @@ struct StageArgs {
   size_t layer0, layer_bytes, off_qkv, off_o, off_gu, off_d;
   const float* cos_t;
   const float* sin_t;
-  // activations
-  const bf16_t* x;          // block mode input [M][D]
-  bf16_t* y;                // block mode output [M][D]
-  bf16_t* xb[2];            // [M][D] ping-pong (flow: X)
-  bf16_t* q;
+  // activations: x / y are the caller's row-major block input / output (block
+  // mode); everything else is in the skinny GEMMs' operand order
+  const bf16_t* x;
+  bf16_t* y;
+  bf16_t* xb[2];            // layer inputs / outputs between layers (flow: X)
+  bf16_t* q;                // attention operand order
   bf16_t* o;
   bf16_t* h;
   bf16_t* a;
@@ -45,17 +46,15 @@ struct StageArgs {
   // K splits of the GEMM steps (last arriver reduces) and their scratch
   int split_qkv, split_o, split_gu, split_d, split_w3;
   float* part;
-  float* ss_part;
   unsigned* ctr_qkv;
   unsigned* ctr_o;
   unsigned* ctr_gu;
   unsigned* ctr_d;
-  // attention plan and split scratch
-  int att_splits, att_kps;
+  // attention: key slices and their partials, merge tasks
+  int att_splits, att_kps, att_merge_tasks;
   float scale_log2;
-  float* part_o;
-  float* part_ml;
-  unsigned* att_ctr;
+  bf16_t* att_part_o;
+  float* att_part_ml;
   // flow head
   int N, A;
   const float* w_fused;
@@ -80,9 +79,6 @@ struct StageArgs {
 };
 
 size_t stage_smem_bytes(int head_dim);
-// K split of a stage GEMM step: keeps each task's activation slice near 128 KiB.
-int stage_split(int M, int K);
-size_t stage_part_floats(int M, int K, int n_groups);
 // Workgroups of the persistent grid (one per compute unit when a workgroup fits),
 // 0 if the kernel cannot be resident on every unit.
 int stage_grid(int head_dim, int rows);

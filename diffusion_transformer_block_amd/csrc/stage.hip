@@ -10,16 +10,22 @@
 // block at one denoise step), several layers, or the full flow-matching loop
 // ([RT] §2: 10 steps x 18 layers plus the suffix embedding and the velocity
 // head) -- on one workgroup per compute unit.  Each operator is a phase made of
-// independent tasks:
-//   QKV  one 32-column group of the fused QKV matrix, full K, RMS + RoPE epilogue
-//   ATT  one 64-row block x key slice of chunk attention (split slices combine
-//        in the last-arriving workgroup)
-//   O    one 16-column tile of W_o, full K, residual epilogue
-//   GU   one gate/up group, full K, RMS + SiLU-gate epilogue
-//   D    one 16-column tile of W_down, full K, residual epilogue
+// independent tasks (the device tasks of skinny.h / attn_small.h, the same
+// code the per-operator kernels run):
+//   QKV  one 32-column group (x K split) of the fused QKV matrix, RMS + RoPE
+//   ATT  one 64-row block x key slice of chunk attention
+//   CMB  merge of the key slices (256 output chunks per task), if sliced
+//   O    one 32-column group (x K split) of W_o, residual epilogue
+//   GU   one gate/up group, RMS + SiLU-gate epilogue
+//   D    one 32-column group (x K split) of W_down, residual epilogue
 //   EMB, W3, VEL  the flow head (embedding, its linear, velocity + Euler step)
 // Task t of a phase runs on workgroup (w0 + t mod nw); the phases' workgroup
 // sets are rotated so that consecutive phases start on different units.
+//
+// Overlap: a GEMM task issues its weight loads -- at these shapes its whole
+// weight slice -- before it waits for the producing phase, and a workgroup
+// with no task in a phase moves straight on to the next one, so weight
+// streaming of later phases runs under the current one.
 //
 // Hand-off: a task's outputs are written with device-coherent stores; after
 // they are acknowledged the workgroup writes the task's flag = the phase's
@@ -31,10 +37,12 @@
 // time-out the workgroup raises an abort word that all other waits also watch,
 // so the grid always drains; a workspace with the abort word set makes later
 // launches return at once.
-#include "attn_dev.h"
+#include <type_traits>
+
+#include "attn_small.h"
 #include "common.h"
-#include "gemm_dev.h"
 #include "internal.h"
+#include "skinny.h"
 #include "stage.h"
 
 namespace blk {
@@ -91,7 +99,8 @@ struct FlowSmem {
   float wsum[4];
 };
 
-// Per-step view of the flow head.
+// Per-step view of the flow head; z ([N][D]) and X ([N + 1][D]) are in the
+// skinny GEMMs' operand order.
 struct FlowTask {
   const float* a_in;      // actions at this step's start (noise at step 0)
   const float* state;
@@ -99,14 +108,15 @@ struct FlowTask {
   const float* bias;      // [D] time table row of this step
   const float* ws_f;      // [A][D]
   const float* bs;
-  bf16_t* z;              // [N][D]
-  bf16_t* x0;             // X row 0 (state token)
-  const bf16_t* X;        // [N + 1][D] output of the last layer
+  bf16_t* z;
+  bf16_t* x0;             // X (the state token goes to row 0)
+  const bf16_t* X;        // output of the last layer
   const float* w_out;     // [D][A] (final gain folded)
   const float* b_out;
   float* actions;         // [N][A]
   float dt;
   int N, A, D;
+  int MTz;                // row tiles of z's operand order (those of X, so W3 can share MT)
   float eps;
 };
 
@@ -114,6 +124,7 @@ struct FlowTask {
 __device__ void emb_task(const FlowTask& f, int t, FlowSmem& fs) {
   const int r0 = 4 * t;
   const int nr = min(4, f.N + 1 - r0);
+  const int MTz = f.MTz, MTx = mt_of(f.N + 1);
   __syncthreads();
   for (int i = threadIdx.x; i < nr * f.A; i += 256) {
     const int rr = i / f.A, k = i - rr * f.A;
@@ -127,11 +138,11 @@ __device__ void emb_task(const FlowTask& f, int t, FlowSmem& fs) {
       if (r < f.N) {
         float acc = f.bias[n];
         for (int k = 0; k < f.A; ++k) acc = fmaf(fs.vin[rr][k], f.w_fused[(size_t)k * f.D + n], acc);
-        st_act(f.z + (size_t)r * f.D + n, silu(acc));
+        st_act(f.z + fa_index(r, n, MTz), silu(acc));
       } else {
         float acc = f.bs[n];
         for (int k = 0; k < f.A; ++k) acc = fmaf(fs.vin[rr][k], f.ws_f[(size_t)k * f.D + n], acc);
-        st_act(f.x0 + n, acc);
+        st_act(f.x0 + fa_index(0, n, MTx), acc);
       }
     }
   }
@@ -140,11 +151,11 @@ __device__ void emb_task(const FlowTask& f, int t, FlowSmem& fs) {
 // action row i: v = RMS(X[i+1]) . W_out' + b_out; actions[i] = a_in[i] + dt v
 __device__ void vel_task(const FlowTask& f, int i, FlowSmem& fs) {
   const int tid = threadIdx.x;
-  const bf16_t* xr = f.X + (size_t)(i + 1) * f.D;
+  const int MTx = mt_of(f.N + 1);
   __syncthreads();
   float ss = 0.f;
   for (int k = tid; k < f.D; k += 256) {
-    const float v = ld_act(xr + k);
+    const float v = ld_act(f.X + fa_index(i + 1, k, MTx));
     fs.xs[k] = v;
     ss = fmaf(v, v, ss);
   }
@@ -177,33 +188,43 @@ __device__ void vel_task(const FlowTask& f, int i, FlowSmem& fs) {
 // Each task runs in its own (non-inlined) function so that its register
 // allocation does not inherit the pressure of the others; it receives small
 // argument structs by value (the kernel's large argument block never escapes).
-// `wait` performs the wait for the producing step; a GEMM task calls it after
-// issuing its weight loads.  Return: true if the task completed its outputs.
+// `wait` performs the wait for the producing phase.  Return: true if this
+// workgroup completed the task's outputs (false also when it only published a
+// split partial; the phase checks separately whether the grid aborted).
 
-template <int MT, bool RMS, class Epi, class W>
-__device__ __noinline__ bool gemm_run(GemmArgs ga, Epi e, int g, int s, SkinnySmem& sm, W& wait) {
-  return skinny_task<MT, RMS>(ga, e, g, s, sm, wait);
+template <int MT, int NB, bool RMS, bool AROW, class Epi, class W>
+__device__ __noinline__ bool sk_run(SkArgs ga, Epi e, int g, int s, uint8_t* smem, W& wait) {
+  return sk_task<MT, NB, RMS, AROW>(ga, e, g, s, *reinterpret_cast<SkSmem<AROW>*>(smem), wait);
+}
+
+template <int MT, bool RMS, bool AROW, class Epi, class W>
+__device__ __forceinline__ bool sk_dispatch(const SkArgs& ga, const Epi& e, int g, int s, uint8_t* smem,
+                                            W& wait) {
+  const int KW = ga.K / 32 / ga.splits / 4;
+  if (KW % 8 == 0) return sk_run<MT, 8, RMS, AROW>(ga, e, g, s, smem, wait);
+  if (KW % 4 == 0) return sk_run<MT, 4, RMS, AROW>(ga, e, g, s, smem, wait);
+  if (KW % 2 == 0) return sk_run<MT, 2, RMS, AROW>(ga, e, g, s, smem, wait);
+  return sk_run<MT, 1, RMS, AROW>(ga, e, g, s, smem, wait);
 }
 
 template <int HD, class W>
-__device__ __noinline__ bool attn_run(AttnArgs aa, int qb, int bh, int split, AttnSmem<HD>& sm,
-                                      W& wait) {
-  if (!wait()) return false;
-  return attn_task<HD>(aa, qb, bh, split, sm);
+__device__ __noinline__ void attn_run(AttnSmArgs aa, int bh, int rb, int ks, uint8_t* smem, W& wait) {
+  (void)attn_sm_task<HD>(aa, bh, rb, ks, *reinterpret_cast<AttnSmSmem<HD>*>(smem), wait);
+}
+
+template <int HD, class W>
+__device__ __noinline__ void cmb_run(AttnSmArgs aa, int t, W& wait) {
+  if (wait()) attn_combine_task<HD>(aa, t);
 }
 
 template <class W>
-__device__ __noinline__ bool emb_run(FlowTask f, int t, FlowSmem& fs, W& wait) {
-  if (!wait()) return false;
-  emb_task(f, t, fs);
-  return true;
+__device__ __noinline__ void emb_run(FlowTask f, int t, FlowSmem& fs, W& wait) {
+  if (wait()) emb_task(f, t, fs);
 }
 
 template <class W>
-__device__ __noinline__ bool vel_run(FlowTask f, int t, FlowSmem& fs, W& wait) {
-  if (!wait()) return false;
-  vel_task(f, t, fs);
-  return true;
+__device__ __noinline__ void vel_run(FlowTask f, int t, FlowSmem& fs, W& wait) {
+  if (wait()) vel_task(f, t, fs);
 }
 
 // ---------------------------------------------------------------- the kernel
@@ -212,8 +233,6 @@ __global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ unsigned e0_sh;
   __shared__ int ok_sh;
-  SkinnySmem& gsm = *reinterpret_cast<SkinnySmem*>(smem);
-  AttnSmem<HD>& asm_ = *reinterpret_cast<AttnSmem<HD>*>(smem);
   FlowSmem& fsm = *reinterpret_cast<FlowSmem*>(smem);
 
   if (threadIdx.x == 0) {
@@ -260,18 +279,20 @@ __global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
   };
 
   const int D = sa.D, F = sa.F, d = sa.d, Hq = sa.Hq, Hkv = sa.Hkv, M = sa.M;
+  const int MTm = mt_of(M);
   const int n_rb = ((Hq / Hkv) * sa.T + 63) / 64;
 
-  auto run_layer = [&](int layer, const bf16_t* in, bf16_t* out, const bf16_t* kp,
-                       const bf16_t* vp) -> bool {
+  // in_frag: the layer input (and first residual) is in operand order;
+  // out_frag: likewise for its output
+  auto run_layer = [&](int layer, const bf16_t* in, bool in_frag, bf16_t* out, bool out_frag,
+                       const bf16_t* kp, const bf16_t* vp) -> bool {
     const uint8_t* lw = sa.packed + sa.layer0 + (size_t)layer * sa.layer_bytes;
-    GemmArgs base{};
+    SkArgs base{};
     base.M = M;
     base.eps = sa.eps;
     base.part = sa.part;
-    base.ss_part = sa.ss_part;
     if (!phase(kPhQKV, [&](int t, auto& wait) {
-          GemmArgs ga = base;
+          SkArgs ga = base;
           ga.A = in;
           ga.lda = D;
           ga.K = D;
@@ -280,83 +301,89 @@ __global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
           ga.splits = sa.split_qkv;
           ga.counters = sa.ctr_qkv;
           const int g = t / ga.splits;
-          EpiQKV e{sa.q, sa.kn, sa.vn, sa.new_stride, sa.cos_t, sa.sin_t, sa.T, sa.P, Hq, Hkv, d};
-          return gemm_run<MT, true>(ga, e, g, t - g * ga.splits, gsm, wait) ? g : -1;
+          EpiQkvS e{sa.q, sa.kn, sa.vn, sa.new_stride, sa.cos_t, sa.sin_t, sa.T, sa.P, Hq, Hkv, d};
+          const bool done = in_frag ? sk_dispatch<MT, true, false>(ga, e, g, t - g * ga.splits, smem, wait)
+                                    : sk_dispatch<MT, true, true>(ga, e, g, t - g * ga.splits, smem, wait);
+          return done ? g : -1;
         }))
       return false;
+    AttnSmArgs aa{};
+    aa.q = sa.q;
+    aa.kp = kp;
+    aa.vp = vp;
+    aa.prefix_stride = sa.prefix_stride;
+    aa.kn = sa.kn;
+    aa.vn = sa.vn;
+    aa.new_stride = sa.new_stride;
+    aa.o = sa.o;
+    aa.B = sa.B;
+    aa.T = sa.T;
+    aa.P = sa.P;
+    aa.Hq = Hq;
+    aa.Hkv = Hkv;
+    aa.splits = sa.att_splits;
+    aa.kps = sa.att_kps;
+    aa.scale_log2 = sa.scale_log2;
+    aa.part_o = sa.att_part_o;
+    aa.part_ml = sa.att_part_ml;
     if (!phase(kPhATT, [&](int t, auto& wait) {
-          AttnArgs aa{};
-          aa.q = sa.q;
-          aa.kp = kp;
-          aa.vp = vp;
-          aa.prefix_stride = sa.prefix_stride;
-          aa.kn = sa.kn;
-          aa.vn = sa.vn;
-          aa.new_stride = sa.new_stride;
-          aa.o = sa.o;
-          aa.B = sa.B;
-          aa.T = sa.T;
-          aa.P = sa.P;
-          aa.Hq = Hq;
-          aa.Hkv = Hkv;
-          aa.d = d;
-          aa.splits = sa.att_splits;
-          aa.keys_per_split = sa.att_kps;
-          aa.scale_log2 = sa.scale_log2;
-          aa.part_o = sa.part_o;
-          aa.part_ml = sa.part_ml;
-          aa.counters = sa.att_ctr;
-          const int rb = t / aa.splits, split = t - rb * aa.splits;
-          const int bh = rb / n_rb, qb = rb - bh * n_rb;
-          return attn_run<HD>(aa, qb, bh, split, asm_, wait) ? rb : -1;
+          const int rbt = t / aa.splits, ks = t - rbt * aa.splits;
+          const int bh = rbt / n_rb, rb = rbt - bh * n_rb;
+          attn_run<HD>(aa, bh, rb, ks, smem, wait);
+          return t;
+        }))
+      return false;
+    if (aa.splits > 1 && !phase(kPhCMB, [&](int t, auto& wait) {
+          cmb_run<HD>(aa, t, wait);
+          return t;
         }))
       return false;
     if (!phase(kPhO, [&](int t, auto& wait) {
-          GemmArgs ga = base;
+          SkArgs ga = base;
           ga.A = sa.o;
-          ga.lda = Hq * d;
           ga.K = Hq * d;
           ga.Bp = lw + sa.off_o;
           ga.n_groups = D / 32;
           ga.splits = sa.split_o;
           ga.counters = sa.ctr_o;
           const int g = t / ga.splits;
-          return gemm_run<MT, false>(ga, EpiResidual{in, sa.h, D}, g, t - g * ga.splits, gsm, wait) ? g : -1;
+          EpiResidS e{in, in_frag ? 1 : 0, MTm, nullptr, sa.h, 1, MTm, 0, D};
+          return sk_dispatch<MT, false, false>(ga, e, g, t - g * ga.splits, smem, wait) ? g : -1;
         }))
       return false;
     if (!phase(kPhGU, [&](int t, auto& wait) {
-          GemmArgs ga = base;
+          SkArgs ga = base;
           ga.A = sa.h;
-          ga.lda = D;
           ga.K = D;
           ga.Bp = lw + sa.off_gu;
           ga.n_groups = F / 16;
           ga.splits = sa.split_gu;
           ga.counters = sa.ctr_gu;
           const int g = t / ga.splits;
-          return gemm_run<MT, true>(ga, EpiGateUp{sa.a, F}, g, t - g * ga.splits, gsm, wait) ? g : -1;
+          return sk_dispatch<MT, true, false>(ga, EpiGateUpS{sa.a, MTm}, g, t - g * ga.splits, smem, wait) ? g : -1;
         }))
       return false;
     return phase(kPhD, [&](int t, auto& wait) {
-      GemmArgs ga = base;
+      SkArgs ga = base;
       ga.A = sa.a;
-      ga.lda = F;
       ga.K = F;
       ga.Bp = lw + sa.off_d;
       ga.n_groups = D / 32;
       ga.splits = sa.split_d;
       ga.counters = sa.ctr_d;
       const int g = t / ga.splits;
-      return gemm_run<MT, false>(ga, EpiResidual{sa.h, out, D}, g, t - g * ga.splits, gsm, wait) ? g : -1;
+      EpiResidS e{sa.h, 1, MTm, nullptr, out, out_frag ? 1 : 0, MTm, 0, D};
+      return sk_dispatch<MT, false, false>(ga, e, g, t - g * ga.splits, smem, wait) ? g : -1;
     });
   };
 
   bool ok = true;
   if (!sa.flow) {
     for (int li = 0; li < sa.n_layers && ok; ++li) {
-      const bf16_t* in = li == 0 ? sa.x : sa.xb[(li - 1) & 1];
-      bf16_t* out = li == sa.n_layers - 1 ? sa.y : sa.xb[li & 1];
-      ok = run_layer(sa.layer_first + li, in, out, sa.kp[0], sa.vp[0]);
+      const bool first = li == 0, last = li == sa.n_layers - 1;
+      const bf16_t* in = first ? sa.x : sa.xb[(li - 1) & 1];
+      bf16_t* out = last ? sa.y : sa.xb[li & 1];
+      ok = run_layer(sa.layer_first + li, in, !first, out, !last, sa.kp[0], sa.vp[0]);
     }
   } else {
     for (int s = 0; s < sa.n_steps && ok; ++s) {
@@ -377,13 +404,16 @@ __global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
       f.N = sa.N;
       f.A = sa.A;
       f.D = D;
+      f.MTz = mt_of(sa.N + 1);
       f.eps = sa.eps;
-      ok = phase(kPhEMB, [&](int t, auto& wait) { return emb_run(f, t, fsm, wait) ? t : -1; });
+      ok = phase(kPhEMB, [&](int t, auto& wait) {
+        emb_run(f, t, fsm, wait);
+        return t;
+      });
       if (ok)
         ok = phase(kPhW3, [&](int t, auto& wait) {
-          GemmArgs ga{};
+          SkArgs ga{};
           ga.A = sa.z;
-          ga.lda = D;
           ga.M = sa.N;
           ga.K = D;
           ga.Bp = sa.w3;
@@ -392,11 +422,16 @@ __global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
           ga.part = sa.part;
           ga.counters = sa.ctr_o;
           const int g = t / ga.splits;
-          return gemm_run<MT, false>(ga, EpiBias{sa.b3, sa.xb[0], D, 1}, g, t - g * ga.splits, gsm, wait) ? g : -1;
+          EpiResidS e{nullptr, 0, 0, sa.b3, sa.xb[0], 1, mt_of(sa.N + 1), 1, D};
+          return sk_dispatch<MT, false, false>(ga, e, g, t - g * ga.splits, smem, wait) ? g : -1;
         });
       for (int l = 0; l < sa.n_layers && ok; ++l)
-        ok = run_layer(l, sa.xb[l & 1], sa.xb[(l + 1) & 1], sa.kp[l], sa.vp[l]);
-      if (ok) ok = phase(kPhVEL, [&](int t, auto& wait) { return vel_run(f, t, fsm, wait) ? t : -1; });
+        ok = run_layer(l, sa.xb[l & 1], true, sa.xb[(l + 1) & 1], true, sa.kp[l], sa.vp[l]);
+      if (ok)
+        ok = phase(kPhVEL, [&](int t, auto& wait) {
+          vel_run(f, t, fsm, wait);
+          return t;
+        });
     }
   }
   if (!ok) return;
@@ -440,9 +475,7 @@ static int prepare_mt(int mt, size_t smem) {
 }
 
 int stage_grid(int head_dim, int rows) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  const int cus = device_cus();
   const size_t smem = stage_smem_bytes(head_dim);
   const int mt = (rows + 15) / 16;
   const int occ = head_dim == 64 ? prepare_mt<64>(mt, smem)
@@ -451,24 +484,11 @@ int stage_grid(int head_dim, int rows) {
   return occ >= 1 ? cus : 0;
 }
 
-int stage_split(int M, int K) {
-  const int KT = K / 32;
-  int s = 1;
-  while ((size_t)M * K * 2 / s > 131072 && KT % (8 * s) == 0) s *= 2;
-  while (KT / (4 * s) > kMaxPrefetch && KT % (8 * s) == 0) s *= 2;
-  return s;
-}
-
-size_t stage_part_floats(int M, int K, int n_groups) {
-  const int s = stage_split(M, K);
-  return s > 1 ? (size_t)s * n_groups * ((M + 15) / 16) * 256 * 2 : 0;
-}
-
 size_t stage_smem_bytes(int head_dim) {
-  size_t att = head_dim == 64    ? sizeof(AttnSmem<64>)
-               : head_dim == 128 ? sizeof(AttnSmem<128>)
-                                 : sizeof(AttnSmem<256>);
-  size_t m = sizeof(SkinnySmem);
+  size_t att = head_dim == 64    ? sizeof(AttnSmSmem<64>)
+               : head_dim == 128 ? sizeof(AttnSmSmem<128>)
+                                 : sizeof(AttnSmSmem<256>);
+  size_t m = sizeof(SkSmem<true>);
   if (att > m) m = att;
   if (sizeof(FlowSmem) > m) m = sizeof(FlowSmem);
   return (m + 255) / 256 * 256;
