@@ -159,7 +159,7 @@ int lookup(const void* packed, const blk_config& cfg, PackRecord* out) {
 
 // ---------------------------------------------------------------- workspace layout
 struct BlockWs {
-  size_t q, o, h, a, r1, r2, part, ss, att_o, att_ml;
+  size_t q, o, h, a, r1, r2, part, att_o, att_ml;
   size_t ctr_qkv, ctr_o, ctr_gu, ctr_d, ctr_att;
   size_t sm_att_o, sm_att_ml;   // small-chunk attention key-slice partials
   size_t xb0, xb1, flags, sync;
@@ -191,14 +191,7 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
   off += align_up(M * 4);
   w.r2 = off;
   off += align_up(M * 4);
-  size_t part = 0, ss = 0;
-  if ((int)M <= kSkinnyMaxM && M > 0) {
-    const int m = (int)M;
-    part = std::max(std::max(skinny_part_floats(m, D, gq), skinny_part_floats(m, Hq * d, go)),
-                    std::max(skinny_part_floats(m, D, ggu), skinny_part_floats(m, F, gd)));
-    ss = std::max(std::max(skinny_ss_floats(m, D, gq), skinny_ss_floats(m, Hq * d, go)),
-                  std::max(skinny_ss_floats(m, D, ggu), skinny_ss_floats(m, F, gd)));
-  }
+  size_t part = 0;
   part = std::max(part, extra_part);
   if (small) {
     const int m = (int)M;
@@ -209,8 +202,6 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
   }
   w.part = off;
   off += align_up(part * 4);
-  w.ss = off;
-  off += align_up(ss * 4);
   w.att_o = off;
   off += align_up(attn_part_o_floats(B, T, P, Hq, Hkv, d) * 4);
   w.att_ml = off;
@@ -267,21 +258,31 @@ bool stage_plan(const blk_config& c, int B, int T, int P, int flow_N, int nwg, S
   const int G_q = (Hq + 2 * Hkv) * d / 32, G_o = D / 32, G_gu = F / 16, G_d = D / 32;
   // a block's first layer reads the caller's row-major input (staged per
   // workgroup), which bounds the QKV split; later layers can use the same
-  sa.split_qkv = sk_splits(M, D, G_q, true);
-  sa.split_o = sk_splits(M, Hq * d, G_o, false);
-  sa.split_gu = sk_splits(M, D, G_gu, false);
-  sa.split_d = sk_splits(M, F, G_d, false);
-  sa.split_w3 = flow_N > 0 ? sk_splits(flow_N, D, G_o, false) : 1;
-  for (int sp : {sa.split_qkv, sa.split_o, sa.split_gu, sa.split_d, sa.split_w3})
-    if (sp < 1) return false;
+  const SkPlan p_qkv = sk_plan(M, D, G_q, true), p_o = sk_plan(M, Hq * d, G_o, false),
+               p_gu = sk_plan(M, D, G_gu, false), p_d = sk_plan(M, F, G_d, false),
+               p_w3 = flow_N > 0 ? sk_plan(flow_N, D, G_o, false) : SkPlan{1, 1};
+  for (const SkPlan& p : {p_qkv, p_o, p_gu, p_d, p_w3})
+    if (p.splits < 1) return false;
+  sa.split_qkv = p_qkv.splits;
+  sa.split_o = p_o.splits;
+  sa.split_gu = p_gu.splits;
+  sa.split_d = p_d.splits;
+  sa.split_w3 = p_w3.splits;
+  sa.gpw_qkv = p_qkv.gpw;
+  sa.gpw_o = p_o.gpw;
+  sa.gpw_gu = p_gu.gpw;
+  sa.gpw_d = p_d.gpw;
+  sa.gpw_w3 = p_w3.gpw;
   int splits = 1, kps = 32;
   attn_sm_plan(B, T, P, Hq, Hkv, &splits, &kps);
   const int n_rbt = B * Hkv * (((Hq / Hkv) * T + 63) / 64);
   const int n_att = n_rbt * splits;
   const int n_cmb = splits > 1 ? (attn_combine_items(B, T, Hq, Hkv, d) + 255) / 256 : 0;
   const int n_emb = (flow_N + 1 + 3) / 4;
-  for (int n : {G_q * sa.split_qkv, n_att, n_cmb, G_o * sa.split_o, G_gu * sa.split_gu, G_d * sa.split_d,
-                G_o * sa.split_w3, n_emb, flow_N})
+  // tasks of a GEMM phase: (group block, split); one flag per group block
+  auto nt = [](int G, const SkPlan& p) { return G / p.gpw * p.splits; };
+  for (int n : {nt(G_q, p_qkv), n_att, n_cmb, nt(G_o, p_o), nt(G_gu, p_gu), nt(G_d, p_d), nt(G_o, p_w3),
+                n_emb, flow_N})
     if (n > kStageMaxFlags) return false;
   sa.B = B;
   sa.T = T;
@@ -308,14 +309,14 @@ bool stage_plan(const blk_config& c, int B, int T, int P, int flow_N, int nwg, S
   };
   if (flow_N > 0) {
     map(kPhEMB, n_emb, n_emb);
-    map(kPhW3, G_o * sa.split_w3, G_o);
+    map(kPhW3, nt(G_o, p_w3), G_o / p_w3.gpw);
   }
-  map(kPhQKV, G_q * sa.split_qkv, G_q);
+  map(kPhQKV, nt(G_q, p_qkv), G_q / p_qkv.gpw);
   map(kPhATT, n_att, n_att);
   if (n_cmb > 0) map(kPhCMB, n_cmb, n_cmb);
-  map(kPhO, G_o * sa.split_o, G_o);
-  map(kPhGU, G_gu * sa.split_gu, G_gu);
-  map(kPhD, G_d * sa.split_d, G_d);
+  map(kPhO, nt(G_o, p_o), G_o / p_o.gpw);
+  map(kPhGU, nt(G_gu, p_gu), G_gu / p_gu.gpw);
+  map(kPhD, nt(G_d, p_d), G_d / p_d.gpw);
   if (flow_N > 0) map(kPhVEL, flow_N, flow_N);
   return true;
 }
@@ -366,9 +367,9 @@ struct BlockIO {
 // block input is staged whole per workgroup, which bounds its K range).
 bool small_plan_ok(const blk_config& c, int M, bool x_rowmajor) {
   const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
-  return sk_splits(M, D, (Hq + 2 * Hkv) * d / 32, x_rowmajor) >= 1 &&
-         sk_splits(M, Hq * d, D / 32, false) >= 1 && sk_splits(M, D, F / 16, false) >= 1 &&
-         sk_splits(M, F, D / 32, false) >= 1;
+  return sk_plan(M, D, (Hq + 2 * Hkv) * d / 32, x_rowmajor).splits >= 1 &&
+         sk_plan(M, Hq * d, D / 32, false).splits >= 1 && sk_plan(M, D, F / 16, false).splits >= 1 &&
+         sk_plan(M, F, D / 32, false).splits >= 1;
 }
 
 // Small chunk (B * T <= 64 rows): one launch per operator, activations in
@@ -398,11 +399,12 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     ga.K = D;
     ga.Bp = lw + lay.wqkv;
     ga.n_groups = (Hq + 2 * Hkv) * d / 32;
-    ga.splits = sk_splits(M, D, ga.n_groups, !x_frag);
+    const SkPlan p = sk_plan(M, D, ga.n_groups, !x_frag);
+    ga.splits = p.splits;
     ga.counters = at<unsigned>(ws, w.ctr_qkv);
     EpiQkvS e{q, io.kn, io.vn, io.new_stride, at<float>(packed, lay.rope_cos),
               at<float>(packed, lay.rope_sin), T, P, Hq, Hkv, d};
-    launch_sk_qkv(ga, !x_frag, e, st);
+    launch_sk_qkv(ga, p.gpw, !x_frag, e, st);
   }
   // 2. attention over [prefix ; own]
   {
@@ -433,10 +435,11 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     ga.K = Hq * d;
     ga.Bp = lw + lay.wo;
     ga.n_groups = D / 32;
-    ga.splits = sk_splits(M, ga.K, ga.n_groups, false);
+    const SkPlan p = sk_plan(M, ga.K, ga.n_groups, false);
+    ga.splits = p.splits;
     ga.counters = at<unsigned>(ws, w.ctr_o);
     EpiResidS e{io.x, x_frag ? 1 : 0, MT, nullptr, h, 1, MT, 0, D};
-    launch_sk_resid(ga, e, st);
+    launch_sk_resid(ga, p.gpw, e, st);
   }
   // 4. RMS(h) -> gate/up GEMM with SiLU(gate) * up epilogue
   {
@@ -445,9 +448,10 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     ga.K = D;
     ga.Bp = lw + lay.wgu;
     ga.n_groups = F / 16;
-    ga.splits = sk_splits(M, D, ga.n_groups, false);
+    const SkPlan p = sk_plan(M, D, ga.n_groups, false);
+    ga.splits = p.splits;
     ga.counters = at<unsigned>(ws, w.ctr_gu);
-    launch_sk_gateup(ga, EpiGateUpS{a, MT}, st);
+    launch_sk_gateup(ga, p.gpw, EpiGateUpS{a, MT}, st);
   }
   // 5. y = h + a W_d
   {
@@ -456,10 +460,11 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     ga.K = F;
     ga.Bp = lw + lay.wd;
     ga.n_groups = D / 32;
-    ga.splits = sk_splits(M, F, ga.n_groups, false);
+    const SkPlan p = sk_plan(M, F, ga.n_groups, false);
+    ga.splits = p.splits;
     ga.counters = at<unsigned>(ws, w.ctr_d);
     EpiResidS e{h, 1, MT, nullptr, io.y, y_frag ? 1 : 0, MT, 0, D};
-    launch_sk_resid(ga, e, st);
+    launch_sk_resid(ga, p.gpw, e, st);
   }
 }
 
@@ -472,7 +477,6 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
   }
   const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const uint8_t* lw = at<uint8_t>(packed, lay.layer0 + (size_t)layer * lay.layer_bytes);
-  const bool skinny = false;
   bf16_t* q = at<bf16_t>(ws, w.q);
   bf16_t* o = at<bf16_t>(ws, w.o);
   bf16_t* h = at<bf16_t>(ws, w.h);
@@ -482,9 +486,6 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
 
   GemmArgs base{};
   base.M = M;
-  base.eps = c.rms_eps;
-  base.part = at<float>(ws, w.part);
-  base.ss_part = at<float>(ws, w.ss);
 
   // 1. RMS(x) -> fused QKV GEMM with row scale and RoPE epilogue
   {
@@ -494,13 +495,8 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     ga.K = D;
     ga.Bp = lw + lay.wqkv;
     ga.n_groups = (Hq + 2 * Hkv) * d / 32;
-    ga.counters = at<unsigned>(ws, w.ctr_qkv);
-    if (skinny) {
-      ga.rms_fused = 1;
-    } else {
-      launch_rms_rows(io.x, M, D, c.rms_eps, r1, st);
-      ga.r = r1;
-    }
+    launch_rms_rows(io.x, M, D, c.rms_eps, r1, st);
+    ga.r = r1;
     EpiQKV e{q, io.kn, io.vn, io.new_stride, at<float>(packed, lay.rope_cos),
              at<float>(packed, lay.rope_sin), T, P, Hq, Hkv, d};
     launch_gemm_qkv(ga, e, st);
@@ -537,7 +533,6 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     ga.K = Hq * d;
     ga.Bp = lw + lay.wo;
     ga.n_groups = D / 32;
-    ga.counters = at<unsigned>(ws, w.ctr_o);
     launch_gemm_residual(ga, EpiResidual{io.x, h, D}, st);
   }
   // 4. RMS(h) -> gate/up GEMM with SiLU(gate) * up epilogue
@@ -548,13 +543,8 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     ga.K = D;
     ga.Bp = lw + lay.wgu;
     ga.n_groups = F / 16;
-    ga.counters = at<unsigned>(ws, w.ctr_gu);
-    if (skinny) {
-      ga.rms_fused = 1;
-    } else {
-      launch_rms_rows(h, M, D, c.rms_eps, r2, st);
-      ga.r = r2;
-    }
+    launch_rms_rows(h, M, D, c.rms_eps, r2, st);
+    ga.r = r2;
     launch_gemm_gateup(ga, EpiGateUp{a, F}, st);
   }
   // 5. y = h + a W_d
@@ -565,7 +555,6 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     ga.K = F;
     ga.Bp = lw + lay.wd;
     ga.n_groups = D / 32;
-    ga.counters = at<unsigned>(ws, w.ctr_d);
     launch_gemm_residual(ga, EpiResidual{h, io.y, D}, st);
   }
 }
@@ -593,9 +582,7 @@ FlowWs flow_ws_layout(const blk_config& c, int N, int P) {
   f.vn = off;
   off += align_up((size_t)T * c.n_kv_heads * c.head_dim * 2);
   // the embedding's W3 GEMM (N rows, K = D, D/32 groups) shares the split-K scratch
-  f.blk = block_ws_layout(c, 1, T, P, off,
-                          std::max(skinny_part_floats(N, (int)D, (int)D / 32),
-                                   sk_part_floats(N, (int)D, (int)D / 32, false)));
+  f.blk = block_ws_layout(c, 1, T, P, off, sk_part_floats(N, (int)D, (int)D / 32, false));
   f.total = f.blk.total;
   return f;
 }
@@ -628,11 +615,12 @@ void enqueue_flow(const blk_config& c, const Layout& lay, const void* packed, in
       ga.K = D;
       ga.Bp = at<uint8_t>(packed, lay.h_w3);
       ga.n_groups = D / 32;
-      ga.splits = sk_splits(N, D, ga.n_groups, false);
+      const SkPlan p = sk_plan(N, D, ga.n_groups, false);
+      ga.splits = p.splits;
       ga.part = at<float>(ws, fw.blk.part);
       ga.counters = at<unsigned>(ws, fw.blk.ctr_o);  // W3 has W_o's group count (D / 32)
       EpiResidS e{nullptr, 0, 0, at<float>(packed, lay.h_b3), X[0], 1, mt_of(T), 1, D};
-      launch_sk_resid(ga, e, st);
+      launch_sk_resid(ga, p.gpw, e, st);
     }
     int cur = 0;
     for (int l = 0; l < n_layers; ++l) {
@@ -925,7 +913,7 @@ int flow_denoise(const blk_config* cfg, const void* packed, int n_layers, int n_
       if (reinterpret_cast<uintptr_t>(k_prefix[l]) % 16 || reinterpret_cast<uintptr_t>(v_prefix[l]) % 16)
         return fail(BLK_EINVAL, "prefix buffers must be 16-byte aligned");
   }
-  if (!small_plan_ok(*cfg, T, false) || sk_splits(lay.n_actions, cfg->hidden, cfg->hidden / 32, false) < 1)
+  if (!small_plan_ok(*cfg, T, false) || sk_plan(lay.n_actions, cfg->hidden, cfg->hidden / 32, false).splits < 1)
     return fail(BLK_EUNSUPPORTED, "hidden %d too wide for the denoise loop", cfg->hidden);
   hipStream_t st = (hipStream_t)stream;
   int dev = 0;

@@ -9,73 +9,17 @@
 // split-K balances skinny shapes over the compute units.  §6.2: at few tokens
 // a GEMM is bound by reading its bf16 weights.
 //
-// Two kernels:
-//  * skinny_gemm (M <= 64 rows): each workgroup streams a contiguous run of
-//    weight fragments for one 32-column group and one K split, with 16-byte
-//    coalesced loads issued UK k-tiles ahead; the four waves split the run and
-//    reduce through LDS; K splits reduce through a float32 scratch buffer and
-//    the last-arriving workgroup of a group (device-scope arrival counter,
-//    reset by that workgroup) sums the splits in a fixed order and runs the
-//    epilogue.  With RMS fused, every workgroup also sums x^2 over its K
-//    slice of the rows it already loaded, so the statistic costs no extra pass.
-//  * tiled_gemm (large M): 128 x 128 output tile per workgroup, K step 64,
+// The large-chunk GEMM (M > 64 rows; chunks of <= 64 rows run the skinny
+// GEMM of skinny.h):
+//  * tiled_gemm: 128 x 128 output tile per workgroup, K step 64,
 //    A (activations) staged through double-buffered LDS, B (packed weight
 //    fragments) loaded straight into registers one step ahead; 2 x 2 waves of
 //    64 x 64 each.
 #include "common.h"
-#include "gemm_dev.h"
 #include "internal.h"
+#include "skinny.h"
 
 namespace blk {
-
-// ============================================================================ skinny
-template <int MT, bool RMS, class Epi>
-__global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs ga, Epi epi) {
-  __shared__ SkinnySmem sm;
-  skinny_task<MT, RMS>(ga, epi, blockIdx.x, blockIdx.y, sm, NoWait{});
-}
-
-int skinny_splits(int M, int K, int n_groups) {
-  (void)M;
-  const int KT = K / 32;
-  int best = 1;
-  for (int s = 1; s <= 64; s *= 2) {
-    if (KT % (4 * s) != 0) break;
-    if (n_groups * s > 512) break;
-    best = s;
-  }
-  return best;
-}
-
-size_t skinny_part_floats(int M, int K, int n_groups) {
-  const int s = skinny_splits(M, K, n_groups);
-  if (s == 1) return 0;
-  const int MT = (M + 15) / 16;
-  return (size_t)s * n_groups * MT * 256 * 2;
-}
-
-size_t skinny_ss_floats(int M, int K, int n_groups) {
-  const int s = skinny_splits(M, K, n_groups);
-  if (s == 1) return 0;
-  return (size_t)s * n_groups * 64;
-}
-
-template <int MT, bool RMS, class Epi>
-static void skinny_go(const GemmArgs& ga, const Epi& e, hipStream_t st) {
-  skinny_gemm_kernel<MT, RMS, Epi><<<dim3(ga.n_groups, ga.splits), 256, 0, st>>>(ga, e);
-}
-
-template <bool RMS, class Epi>
-static void launch_skinny(GemmArgs ga, const Epi& e, hipStream_t st) {
-  ga.splits = skinny_splits(ga.M, ga.K, ga.n_groups);
-  const int MT = (ga.M + 15) / 16;
-  switch (MT) {
-    case 1: skinny_go<1, RMS>(ga, e, st); break;
-    case 2: skinny_go<2, RMS>(ga, e, st); break;
-    case 3: skinny_go<3, RMS>(ga, e, st); break;
-    default: skinny_go<4, RMS>(ga, e, st); break;
-  }
-}
 
 // ============================================================================ tiled
 template <class Epi>
@@ -193,32 +137,14 @@ static void launch_tiled(const GemmArgs& ga, const Epi& e, hipStream_t st) {
 }
 
 // ============================================================================ dispatch
-void launch_gemm_qkv(const GemmArgs& ga, const EpiQKV& e, hipStream_t st) {
-  if (ga.M <= kSkinnyMaxM) {
-    if (ga.rms_fused) launch_skinny<true>(ga, e, st);
-    else launch_skinny<false>(ga, e, st);
-  } else {
-    launch_tiled(ga, e, st);
-  }
-}
+void launch_gemm_qkv(const GemmArgs& ga, const EpiQKV& e, hipStream_t st) { launch_tiled(ga, e, st); }
 void launch_gemm_residual(const GemmArgs& ga, const EpiResidual& e, hipStream_t st) {
-  if (ga.M <= kSkinnyMaxM) launch_skinny<false>(ga, e, st);
-  else launch_tiled(ga, e, st);
+  launch_tiled(ga, e, st);
 }
-void launch_gemm_gateup(const GemmArgs& ga, const EpiGateUp& e, hipStream_t st) {
-  if (ga.M <= kSkinnyMaxM) {
-    if (ga.rms_fused) launch_skinny<true>(ga, e, st);
-    else launch_skinny<false>(ga, e, st);
-  } else {
-    launch_tiled(ga, e, st);
-  }
-}
-void launch_gemm_bias(const GemmArgs& ga, const EpiBias& e, hipStream_t st) {
-  if (ga.M <= kSkinnyMaxM) launch_skinny<false>(ga, e, st);
-  else launch_tiled(ga, e, st);
-}
+void launch_gemm_gateup(const GemmArgs& ga, const EpiGateUp& e, hipStream_t st) { launch_tiled(ga, e, st); }
 
 // ============================================================================ RMS rows
+// r[m] = (sum_k x[m][k]^2 / K + eps)^-1/2, one wave per row
 __global__ __launch_bounds__(256) void rms_rows_kernel(const bf16_t* __restrict__ x, int M, int K,
                                                        float eps, float* __restrict__ r) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);

@@ -108,24 +108,6 @@ struct EpiGateUp {
   }
 };
 
-// out[m + row_off][n] = acc + bias[n] (flow embedding's linear after SiLU).
-struct EpiBias {
-  const float* bias;
-  bf16_t* out;
-  int ld;
-  int row_off;
-  __device__ __forceinline__ void store(int m, int g, int c, float v0, float v1, float) const {
-    const int n = 32 * g + c;
-    bf16_t* o = out + (size_t)(m + row_off) * ld + n;
-    st_act(o, v0 + bias[n]);
-    st_act(o + 16, v1 + bias[n + 16]);
-  }
-  __device__ __forceinline__ void store1(int m, int g, int i, int c, float v, float) const {
-    const int n = 32 * g + 16 * i + c;
-    st_act(out + (size_t)(m + row_off) * ld + n, v + bias[n]);
-  }
-};
-
 // ---------------------------------------------------------------- GEMM launch
 struct GemmArgs {
   const bf16_t* A;      // activations [M][K], row-major, leading dimension lda
@@ -133,29 +115,16 @@ struct GemmArgs {
   int M, K;
   const uint8_t* Bp;    // packed weight fragments
   int n_groups;
-  // row scale: fused RMS of A's rows (rms_fused), else r (may be NULL = 1)
-  int rms_fused;
-  float eps;
+  // row scale r (the RMS statistic; may be NULL = 1)
   const float* r;
-  // split-K (skinny kernel): partial sums, partial sums of squares, counters
-  int splits;
-  float* part;          // [splits][n_groups][MT*256] float2
-  float* ss_part;       // [splits][n_groups][64]
-  unsigned* counters;   // [n_groups], zero on entry, zero on exit
 };
 
-enum EpiKind { kEpiQKV, kEpiResidual, kEpiGateUp, kEpiBias };
-
-// Chooses between the skinny (M <= 64, split-K) and the tiled (large M) kernel.
+// The large-chunk (M > 64) tiled GEMMs.
 void launch_gemm_qkv(const GemmArgs& ga, const EpiQKV& e, hipStream_t st);
 void launch_gemm_residual(const GemmArgs& ga, const EpiResidual& e, hipStream_t st);
 void launch_gemm_gateup(const GemmArgs& ga, const EpiGateUp& e, hipStream_t st);
-void launch_gemm_bias(const GemmArgs& ga, const EpiBias& e, hipStream_t st);
 
-// Split-K factor and scratch sizes of the skinny kernel for a GEMM shape.
-int skinny_splits(int M, int K, int n_groups);
-size_t skinny_part_floats(int M, int K, int n_groups);   // floats of `part`
-size_t skinny_ss_floats(int M, int K, int n_groups);     // floats of `ss_part`
+// Chunks of at most this many rows (B * T) take the small-chunk path.
 constexpr int kSkinnyMaxM = 64;
 
 // ---------------------------------------------------------------- RMS statistics
@@ -193,12 +162,17 @@ struct EpiResidS;
 struct EpiGateUpS;
 struct AttnSmArgs;
 int device_cus();
-// K splits of a skinny GEMM (-1: no valid split, row-major input too wide)
-int sk_splits(int M, int K, int n_groups, bool a_rowmajor);
+// Plan of a skinny GEMM: K splits and 32-column groups per workgroup
+// (splits = -1: no valid plan, a row-major input too wide to stage)
+struct SkPlan {
+  int splits, gpw;
+};
+SkPlan sk_plan(int M, int K, int n_groups, bool a_rowmajor);
 size_t sk_part_floats(int M, int K, int n_groups, bool a_rowmajor);
-void launch_sk_qkv(const SkArgs& ga, bool a_rowmajor, const EpiQkvS& e, hipStream_t st);
-void launch_sk_resid(const SkArgs& ga, const EpiResidS& e, hipStream_t st);
-void launch_sk_gateup(const SkArgs& ga, const EpiGateUpS& e, hipStream_t st);
+int sk_nb(int KW, int gpw, int MT);
+void launch_sk_qkv(const SkArgs& ga, int gpw, bool a_rowmajor, const EpiQkvS& e, hipStream_t st);
+void launch_sk_resid(const SkArgs& ga, int gpw, const EpiResidS& e, hipStream_t st);
+void launch_sk_gateup(const SkArgs& ga, int gpw, const EpiGateUpS& e, hipStream_t st);
 void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps);
 size_t attn_sm_part_o_elems(int B, int T, int P, int Hq, int Hkv, int d);
 size_t attn_sm_part_ml_floats(int B, int T, int P, int Hq, int Hkv, int d);

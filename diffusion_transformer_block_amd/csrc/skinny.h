@@ -8,8 +8,11 @@
 // skinny shapes over the compute units; §6.2: at few tokens a GEMM is bound by
 // reading its bf16 weights.
 //
-// One task = one 32-column group g of a packed weight (both 16-column tiles,
-// as the fused QKV and gate/up epilogues need) over the K-range of split s.
+// One task = GPW (1 or 2) consecutive 32-column groups of a packed weight
+// (a group holds both 16-column tiles, as the fused QKV and gate/up epilogues
+// need) over the K-range of split s.  Two groups per workgroup halve the
+// number of workgroups that each read the whole activation slab -- those
+// re-reads, all served by L2, bound the widest GEMMs otherwise.
 //  * Weights: fragments (g, kt, 0..1), 1 KiB each, one 16-byte streaming load
 //    per lane.
 //  * Activations: in operand order (fa_index in common.h: one contiguous
@@ -33,9 +36,16 @@
 
 namespace blk {
 
-constexpr int kTileRow = 36;        // floats per row of the LDS result tile (32 + 4 pad)
 constexpr int kSkMaxStage = 128;    // KiB of row-major activations staged per workgroup
 constexpr int kSkMaxSplits = 16;
+constexpr int kSkMaxGpw = 2;        // 32-column groups per workgroup
+// Two groups per workgroup measured slower on every 64-row shape of the AE
+// block (the per-unit operand stream, not the L2 re-reads, binds), so plans
+// keep one; the two-group variant stays available to the kernels.
+constexpr int kSkPlanMaxGpw = 1;
+
+// row stride (floats) of the LDS result tile of GPW groups: 32 GPW + 4 pad
+__host__ __device__ constexpr int sk_tile_stride(int gpw) { return 32 * gpw + 4; }
 
 struct SkArgs {
   const bf16_t* A;      // activations, operand order (MT = ceil(M/16)), or row-major (lda)
@@ -46,16 +56,16 @@ struct SkArgs {
   int splits;           // K splits (KT % (4 splits) == 0)
   float eps;            // RMS epsilon
   float* part;          // [splits][n_groups][64 * 32] tiles, then [splits][n_groups][64] x^2 sums
-  unsigned* counters;   // [n_groups], zero on entry and on exit
+  unsigned* counters;   // [n_groups / GPW], zero on entry and on exit
 };
 
-template <bool AROW>
+template <bool AROW, int GPW>
 struct SkSmem {
   union {
     uint4 astage[AROW ? kSkMaxStage * 64 : 1];  // row-major activations in operand order
-    f32x4 red[4][4 * 2 * 64];                  // per-wave accumulators in MFMA C order
+    f32x4 red[4][4 * GPW * 2 * 64];            // per-wave accumulators in MFMA C order
   };
-  float tile[64 * kTileRow];                   // summed tile [row][col]
+  float tile[64 * sk_tile_stride(GPW)];        // summed tile [row][col]
   float ss[4][64];
   float rrow[64];
   int last_flag;
@@ -79,14 +89,16 @@ __device__ __forceinline__ int stage_slot(int u, int mt, int lane, int MT) {
   return (u * MT + mt) * 64 + (lane & 48) + ((lane & 15) ^ (u & 15));
 }
 
-// Runs one task and stores its outputs through `epi` (see the epilogues
-// below).  `wait()` is called after the first weight loads are issued and
-// before anything that depends on earlier work; it returns false to abandon
-// the task.  Returns false when this workgroup did not run the epilogue
-// (abandoned, or it only published a split partial).
-template <int MT, int NB, bool RMS, bool AROW, class Epi, class Wait>
-__device__ bool sk_task(const SkArgs& ga, const Epi& epi, int g, int s, SkSmem<AROW>& sm,
+// Runs one task -- groups [GPW gb, GPW gb + GPW) over split s -- and stores
+// its outputs through `epi` (see the epilogues below).  `wait()` is called
+// after the first weight loads are issued and before anything that depends on
+// earlier work; it returns false to abandon the task.  Returns false when
+// this workgroup did not run the epilogue (abandoned, or it only published a
+// split partial).
+template <int MT, int NB, int GPW, bool RMS, bool AROW, class Epi, class Wait>
+__device__ bool sk_task(const SkArgs& ga, const Epi& epi, int gb, int s, SkSmem<AROW, GPW>& sm,
                         Wait&& wait) {
+  constexpr int TS = sk_tile_stride(GPW);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int l = tid & 63, lr = l & 15;
@@ -95,44 +107,71 @@ __device__ bool sk_task(const SkArgs& ga, const Epi& epi, int g, int s, SkSmem<A
   const int KW = KTS >> 2;             // k-tiles per wave, a multiple of NB
   const int kb = s * KTS;              // first k-tile of this split
   const int uw = w * KW;               // first k-tile of this wave, relative to kb
+  const int g0 = gb * GPW;
+  const int ng = min(GPW, ga.n_groups - g0);
 
-  // ---- weights of the first NB k-tiles (independent of earlier work)
+  // ---- weights of the first NB k-tiles (independent of earlier work); the
+  //      groups' fragments are contiguous, [group][kt][tile]
   const __amdgpu_buffer_rsrc_t rb =
-      make_rsrc(ga.Bp + frag_offset(g, 0, 0, KT), (size_t)KT * 2 * kFragBytes);
+      make_rsrc(ga.Bp + frag_offset(g0, 0, 0, KT), (size_t)ng * KT * 2 * kFragBytes);
   const int boff = (kb + uw) * 2 * kFragBytes + l * 16;
-  uint4 bw[NB][2];
+  uint4 bw[NB][GPW][2];
   auto issue_w = [&](int b, int u) {
-    bw[b][0] = buf_ld_stream(rb, boff + u * 2 * kFragBytes);
-    bw[b][1] = buf_ld_stream(rb, boff + u * 2 * kFragBytes + kFragBytes);
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+      const int o = boff + (j * KT + u) * 2 * kFragBytes;
+      bw[b][j][0] = buf_ld_stream(rb, o);
+      bw[b][j][1] = buf_ld_stream(rb, o + kFragBytes);
+    }
   };
 #pragma unroll
   for (int b = 0; b < NB; ++b) issue_w(b, b);
   if (!wait()) return false;
-  const typename Epi::Pre pre = epi.prefetch(g, ga.M);
+  typename Epi::Pre pre[GPW];
+#pragma unroll
+  for (int j = 0; j < GPW; ++j) pre[j] = epi.prefetch(g0 + min(j, ng - 1), ga.M);
 
   // ---- activations
   uint4 av[NB][MT];
   __amdgpu_buffer_rsrc_t ra;
   int aoff = 0;
   if (AROW) {
-    // stage rows [0, M) x k-tiles [kb, kb + KTS) in operand order
+    // stage rows [0, M) x k-tiles [kb, kb + KTS) in operand order: one batch
+    // of at most 32 row-contiguous 16-byte loads per thread (the slab is at
+    // most kSkMaxStage KiB), rows past M clamped to M - 1 and not stored
     const int nck = KTS * 4;                       // 16-byte chunks per row
-    const int total = ga.M * nck;
+    const int nl = (ga.M * nck + 255) >> 8;        // loads per thread, <= 32 (uniform)
+    const int dr = 256 / nck, dc = 256 - dr * nck; // (row, chunk) step per load
+    const int r0 = tid / nck, c0 = tid - r0 * nck;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(ga.A, (size_t)ga.M * ga.lda * 2);
-    for (int i0 = 0; i0 < total; i0 += 256 * 16) {
-      uint4 v[16];
+    uint4 v[32];
+    {
+      int r = r0, c = c0;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int i = i0 + j * 256 + tid;
-        const int r = i / nck, c = i - r * nck;
-        v[j] = buf_ld_act(rx, i < total ? (r * ga.lda + kb * 32 + c * 8) * 2 : 0x7ffffff0);
+      for (int j = 0; j < 32; ++j) {
+        if (j < nl) {
+          v[j] = buf_ld_act(rx, (min(r, ga.M - 1) * ga.lda + kb * 32 + c * 8) * 2);
+          r += dr;
+          c += dc;
+          if (c >= nck) {
+            c -= nck;
+            ++r;
+          }
+        }
       }
+    }
+    {
+      int r = r0, c = c0;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int i = i0 + j * 256 + tid;
-        if (i < total) {
-          const int r = i / nck, c = i - r * nck;
-          sm.astage[stage_slot(c >> 2, r >> 4, (r & 15) + 16 * (c & 3), MT)] = v[j];
+      for (int j = 0; j < 32; ++j) {
+        if (j < nl) {
+          if (r < ga.M) sm.astage[stage_slot(c >> 2, r >> 4, (r & 15) + 16 * (c & 3), MT)] = v[j];
+          r += dr;
+          c += dc;
+          if (c >= nck) {
+            c -= nck;
+            ++r;
+          }
         }
       }
     }
@@ -152,12 +191,15 @@ __device__ bool sk_task(const SkArgs& ga, const Epi& epi, int g, int s, SkSmem<A
     return av[b][mt];
   };
 
-  f32x4 acc[MT][2];
+  f32x4 acc[MT][GPW][2];
   float ss[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    acc[mt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+      acc[mt][j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[mt][j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     ss[mt] = 0.f;
   }
 #pragma unroll
@@ -170,8 +212,11 @@ __device__ bool sk_task(const SkArgs& ga, const Epi& epi, int g, int s, SkSmem<A
       for (int mt = 0; mt < MT; ++mt) {
         const uint4 a = get_a(b, u, mt);
         if (RMS) ss[mt] += sumsq8(a);
-        acc[mt][0] = mfma16(as_bf16x8(a), as_bf16x8(bw[b][0]), acc[mt][0]);
-        acc[mt][1] = mfma16(as_bf16x8(a), as_bf16x8(bw[b][1]), acc[mt][1]);
+#pragma unroll
+        for (int j = 0; j < GPW; ++j) {
+          acc[mt][j][0] = mfma16(as_bf16x8(a), as_bf16x8(bw[b][j][0]), acc[mt][j][0]);
+          acc[mt][j][1] = mfma16(as_bf16x8(a), as_bf16x8(bw[b][j][1]), acc[mt][j][1]);
+        }
       }
       if (u + NB < KW) {
         issue_w(b, u + NB);
@@ -185,7 +230,9 @@ __device__ bool sk_task(const SkArgs& ga, const Epi& epi, int g, int s, SkSmem<A
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) sm.red[w][(mt * 2 + i) * 64 + l] = acc[mt][i];
+    for (int j = 0; j < GPW; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) sm.red[w][((mt * GPW + j) * 2 + i) * 64 + l] = acc[mt][j][i];
   if (RMS) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -196,12 +243,13 @@ __device__ bool sk_task(const SkArgs& ga, const Epi& epi, int g, int s, SkSmem<A
     }
   }
   __syncthreads();
-  for (int sl = tid; sl < MT * 128; sl += 256) {
+  for (int sl = tid; sl < MT * GPW * 128; sl += 256) {
     const f32x4 v = ((sm.red[0][sl] + sm.red[1][sl]) + sm.red[2][sl]) + sm.red[3][sl];
-    const int mt = sl >> 7, i = (sl >> 6) & 1, ll = sl & 63;
-    const int row = 16 * mt + 4 * (ll >> 4), col = 16 * i + (ll & 15);
+    const int q = sl >> 6, ll = sl & 63;           // q = (mt * GPW + j) * 2 + i
+    const int i = q & 1, j = (q >> 1) % GPW, mt = (q >> 1) / GPW;
+    const int row = 16 * mt + 4 * (ll >> 4), col = 32 * j + 16 * i + (ll & 15);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sm.tile[(row + j) * kTileRow + col] = v[j];
+    for (int jj = 0; jj < 4; ++jj) sm.tile[(row + jj) * TS + col] = v[jj];
   }
   float ssum = 0.f;
   if (RMS && tid < 16 * MT) ssum = ((sm.ss[0][tid] + sm.ss[1][tid]) + sm.ss[2][tid]) + sm.ss[3][tid];
@@ -214,52 +262,68 @@ __device__ bool sk_task(const SkArgs& ga, const Epi& epi, int g, int s, SkSmem<A
     const size_t ss_base = (size_t)ga.splits * ga.n_groups * tile_floats;
     const __amdgpu_buffer_rsrc_t rp =
         make_rsrc(ga.part, (ss_base + (size_t)ga.splits * ga.n_groups * 64) * 4);
-    const int toff = (int)(((size_t)g * tile_floats + r * 32 + c0) * 4);
-    const int tstride = (int)((size_t)ga.n_groups * tile_floats * 4);
-    const int soff = (int)((ss_base + (size_t)g * 64 + tid) * 4);
+    const int tstride = (int)((size_t)ga.n_groups * tile_floats * 4);   // bytes between splits
+    const int soff = (int)((ss_base + (size_t)g0 * 64 + tid) * 4);
     const int sstride = ga.n_groups * 64 * 4;
-    {
-      const float* tp = &sm.tile[r * kTileRow + c0];
-      buf_st16(rp, toff + s * tstride, *reinterpret_cast<const uint4*>(tp));
-      buf_st16(rp, toff + s * tstride + 16, *reinterpret_cast<const uint4*>(tp + 4));
-      if (RMS && tid < 64) buf_st4(rp, soff + s * sstride, ssum);
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+      const int toff = (int)(((size_t)(g0 + j) * tile_floats + r * 32 + c0) * 4);
+      const float* tp = &sm.tile[r * TS + 32 * j + c0];
+      if (j < ng) {
+        buf_st16(rp, toff + s * tstride, *reinterpret_cast<const uint4*>(tp));
+        buf_st16(rp, toff + s * tstride + 16, *reinterpret_cast<const uint4*>(tp + 4));
+      }
     }
-    if (!arrive_last(&ga.counters[g], (unsigned)ga.splits, &sm.last_flag)) return false;
-    uint4 pv[kSkMaxSplits][2];
-    float ps[kSkMaxSplits];
+    if (RMS && tid < 64) buf_st4(rp, soff + s * sstride, ssum);
+    if (!arrive_last(&ga.counters[gb], (unsigned)ga.splits, &sm.last_flag)) return false;
 #pragma unroll
-    for (int sp = 0; sp < kSkMaxSplits; ++sp)
-      if (sp < ga.splits) {
-        pv[sp][0] = buf_ld_act(rp, toff + sp * tstride);
-        pv[sp][1] = buf_ld_act(rp, toff + sp * tstride + 16);
-        ps[sp] = RMS && tid < 64 ? buf_ld4_act(rp, soff + sp * sstride) : 0.f;
-      }
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    ssum = 0.f;
+    for (int j = 0; j < GPW; ++j) {
+      if (j >= ng) break;
+      const int toff = (int)(((size_t)(g0 + j) * tile_floats + r * 32 + c0) * 4);
+      uint4 pv[kSkMaxSplits][2];
 #pragma unroll
-    for (int sp = 0; sp < kSkMaxSplits; ++sp)
-      if (sp < ga.splits) {
-        const uint32_t u[8] = {pv[sp][0].x, pv[sp][0].y, pv[sp][0].z, pv[sp][0].w,
-                               pv[sp][1].x, pv[sp][1].y, pv[sp][1].z, pv[sp][1].w};
+      for (int sp = 0; sp < kSkMaxSplits; ++sp)
+        if (sp < ga.splits) {
+          pv[sp][0] = buf_ld_act(rp, toff + sp * tstride);
+          pv[sp][1] = buf_ld_act(rp, toff + sp * tstride + 16);
+        }
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] += __uint_as_float(u[e]);
-        ssum += ps[sp];
-      }
+      for (int sp = 0; sp < kSkMaxSplits; ++sp)
+        if (sp < ga.splits) {
+          const uint32_t u[8] = {pv[sp][0].x, pv[sp][0].y, pv[sp][0].z, pv[sp][0].w,
+                                 pv[sp][1].x, pv[sp][1].y, pv[sp][1].z, pv[sp][1].w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sm.tile[r * kTileRow + c0 + e] = v[e];
+          for (int e = 0; e < 8; ++e) v[e] += __uint_as_float(u[e]);
+        }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm.tile[r * TS + 32 * j + c0 + e] = v[e];
+    }
+    if (RMS) {
+      float ps[kSkMaxSplits];
+#pragma unroll
+      for (int sp = 0; sp < kSkMaxSplits; ++sp)
+        if (sp < ga.splits) ps[sp] = tid < 64 ? buf_ld4_act(rp, soff + sp * sstride) : 0.f;
+      ssum = 0.f;
+#pragma unroll
+      for (int sp = 0; sp < kSkMaxSplits; ++sp)
+        if (sp < ga.splits) ssum += ps[sp];
+    }
   }
   if (RMS) {
     if (tid < 64) sm.rrow[tid] = rsqrtf(ssum / (float)ga.K + ga.eps);
   }
   if (RMS || ga.splits > 1) __syncthreads();
-  epi.run(sm.tile, sm.rrow, RMS, g, ga.M, pre);
+#pragma unroll
+  for (int j = 0; j < GPW; ++j)
+    if (j < ng) epi.run(sm.tile + 32 * j, TS, sm.rrow, RMS, g0 + j, ga.M, pre[j]);
   return true;
 }
 
 // ============================================================================ epilogues
-// Each epilogue is called by all 256 threads with the summed tile
-// tile[row * kTileRow + col] (row < 64, col < 32 = the group's two 16-column
-// tiles) and the row scale rrow (used when `rms`).  prefetch() runs right
+// Each epilogue is called by all 256 threads with the summed tile of its
+// group, tile[row * ts + col] (row < 64, col < 32 = the group's two 16-column
+// tiles), and the row scale rrow (used when `rms`).  prefetch() runs right
 // after the task's wait, so its loads overlap the activation loads.  All
 // stores are device-coherent.
 
@@ -286,14 +350,14 @@ struct EpiQkvS {
   int T, P, Hq, Hkv, d;
   struct Pre {};
   __device__ Pre prefetch(int, int) const { return {}; }
-  __device__ void run(const float* tile, const float* rrow, bool rms, int g, int M, const Pre&) const {
+  __device__ void run(const float* tile, int ts, const float* rrow, bool rms, int g, int M, const Pre&) const {
     const int t = threadIdx.x;
     const int r = t >> 2;
     if (r >= M) return;
     const float rs = rms ? rrow[r] : 1.f;
     const int b = r / T, tt = r - b * T;
     const int gpr = d >> 5, n_rot_groups = (Hq + Hkv) * gpr;
-    const float* tr = tile + r * kTileRow;
+    const float* tr = tile + r * ts;
     if (g < n_rot_groups) {
       const int q4 = (t & 3) * 4;
       const int head = g / gpr;
@@ -354,13 +418,13 @@ struct EpiResidS {
     if (res && r < M) p.v = ld16c(res + (res_frag ? fa_index(r, c, res_MT) : (size_t)r * N + c));
     return p;
   }
-  __device__ void run(const float* tile, const float*, bool, int g, int M, const Pre& p) const {
+  __device__ void run(const float* tile, int ts, const float*, bool, int g, int M, const Pre& p) const {
     const int t = threadIdx.x, ln = t & 63;
     const int r = 16 * (t >> 6) + (ln & 15), cl = 8 * (ln >> 4), c = 32 * g + cl;
     if (r >= M) return;
     float v[8], rv[8];
     unpack8(p.v, rv);
-    const float* tr = tile + r * kTileRow + cl;
+    const float* tr = tile + r * ts + cl;
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = tr[i] + rv[i];
     if (bias) {
@@ -379,14 +443,14 @@ struct EpiGateUpS {
   int MT;
   struct Pre {};
   __device__ Pre prefetch(int, int) const { return {}; }
-  __device__ void run(const float* tile, const float* rrow, bool rms, int g, int M, const Pre&) const {
+  __device__ void run(const float* tile, int ts, const float* rrow, bool rms, int g, int M, const Pre&) const {
     const int t = threadIdx.x;
     if (t >= 128) return;
     const int q = t & 31;
     const int r = 16 * (t >> 5) + (q & 15), hf = q >> 4;
     if (r >= M) return;
     const float rs = rms ? rrow[r] : 1.f;
-    const float* tr = tile + r * kTileRow + 8 * hf;
+    const float* tr = tile + r * ts + 8 * hf;
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = silu(tr[i] * rs) * (tr[16 + i] * rs);

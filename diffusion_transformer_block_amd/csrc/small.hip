@@ -27,42 +27,54 @@ int device_cus() {
   return cached[dev];
 }
 
-// Per-workgroup cost model of a skinny GEMM task: its operand bytes at the
-// rate one compute unit sustains from L2 / HBM (about 100 GB/s measured with
-// 16-byte loads), plus a fixed price for a K split's hand-off (publish, count,
-// reload: three dependent memory round trips).
-constexpr double kCuBytesPerUs = 100e3;
-constexpr double kSplitUs = 2.0;
+// Cost model of a skinny GEMM plan (K splits x 32-column groups per
+// workgroup), from measurements on this chip with 16-byte loads:
+//  * one compute unit streams about 90 GB/s of operands;
+//  * the activation slab, re-read by every workgroup from L2, is served at
+//    about 9.4 TB/s in aggregate;
+//  * the weights stream from HBM at about 5 TB/s;
+//  * a K split's hand-off (publish, count, reload) costs about 2 us;
+//  * workgroups beyond one per compute unit run in further rounds.
+constexpr double kCuBytesPerUs = 90e3, kL2BytesPerUs = 9.4e6, kHbmBytesPerUs = 5e6, kSplitUs = 2.0;
 
-int sk_splits(int M, int K, int n_groups, bool a_rowmajor) {
+SkPlan sk_plan(int M, int K, int n_groups, bool a_rowmajor) {
   const int KT = K / 32, MT = mt_of(M);
   const int n_cu = device_cus();
-  int best = -1;
+  SkPlan best{-1, 1};
   double best_t = 1e30;
-  for (int s = 1; s <= kSkMaxSplits; s *= 2) {
-    if (KT % (4 * s) != 0) break;
-    if (s > 1 && n_groups * s > n_cu) break;
-    if (a_rowmajor && (KT / s) * MT > kSkMaxStage) continue;
-    const double bytes = (double)(2 + MT) * (KT / s) * kFragBytes;
-    const double t = bytes / kCuBytesPerUs + (s > 1 ? kSplitUs : 0.0);
-    if (t < best_t) {
-      best_t = t;
-      best = s;
+  for (int gpw = 1; gpw <= kSkPlanMaxGpw; ++gpw) {
+    if (n_groups % gpw != 0) continue;
+    for (int s = 1; s <= kSkMaxSplits; s *= 2) {
+      if (KT % (4 * s) != 0) break;
+      const int n_wg = n_groups / gpw * s;
+      if (s > 1 && n_wg > n_cu) break;
+      if (a_rowmajor && (KT / s) * MT > kSkMaxStage) continue;
+      const double per_wg = (double)(2 * gpw + MT) * (KT / s) * kFragBytes;
+      const double a_all = (double)n_wg * MT * (KT / s) * kFragBytes;
+      const double w_all = 2.0 * n_groups * KT * kFragBytes;
+      double t = std::max(per_wg / kCuBytesPerUs, std::max(a_all / kL2BytesPerUs, w_all / kHbmBytesPerUs));
+      t *= (n_wg + n_cu - 1) / n_cu;
+      if (s > 1) t += kSplitUs;
+      if (t < best_t - 1e-9) {
+        best_t = t;
+        best = SkPlan{s, gpw};
+      }
     }
   }
   return best;
 }
 
 size_t sk_part_floats(int M, int K, int n_groups, bool a_rowmajor) {
-  const int s = sk_splits(M, K, n_groups, a_rowmajor);
-  if (s <= 1) return 0;
-  return (size_t)s * n_groups * (64 * 32 + 64);
+  const SkPlan p = sk_plan(M, K, n_groups, a_rowmajor);
+  if (p.splits <= 1) return 0;
+  return (size_t)p.splits * n_groups * (64 * 32 + 64);
 }
 
-static int sk_nb(int KW) {
-  if (KW % 8 == 0) return 8;
-  if (KW % 4 == 0) return 4;
-  if (KW % 2 == 0) return 2;
+// k-tiles in flight per wave: a divisor of the wave's k-tiles whose loads
+// (2 GPW weight + MT activation fragments per k-tile) fit in 192 registers
+int sk_nb(int KW, int gpw, int MT) {
+  for (int nb = 8; nb > 1; nb >>= 1)
+    if (KW % nb == 0 && nb * (2 * gpw + MT) <= 48) return nb;
   return 1;
 }
 
@@ -94,55 +106,64 @@ size_t attn_sm_part_ml_floats(int B, int T, int P, int Hq, int Hkv, int d) {
 }
 
 // ============================================================================ skinny GEMM
-template <int MT, int NB, bool RMS, bool AROW, class Epi>
+template <int MT, int NB, int GPW, bool RMS, bool AROW, class Epi>
 __global__ __launch_bounds__(256) void sk_kernel(SkArgs ga, Epi epi) {
   extern __shared__ __attribute__((aligned(16))) char sk_dsm[];
-  sk_task<MT, NB, RMS, AROW>(ga, epi, blockIdx.x, blockIdx.y, *reinterpret_cast<SkSmem<AROW>*>(sk_dsm),
-                             NoWait{});
+  sk_task<MT, NB, GPW, RMS, AROW>(ga, epi, blockIdx.x, blockIdx.y,
+                                  *reinterpret_cast<SkSmem<AROW, GPW>*>(sk_dsm), NoWait{});
 }
 
-template <int MT, int NB, bool RMS, bool AROW, class Epi>
+template <int MT, int NB, int GPW, bool RMS, bool AROW, class Epi>
 static void sk_go(const SkArgs& ga, const Epi& e, hipStream_t st) {
-  auto kern = sk_kernel<MT, NB, RMS, AROW, Epi>;
-  const size_t smem = sizeof(SkSmem<AROW>);
+  auto kern = sk_kernel<MT, NB, GPW, RMS, AROW, Epi>;
+  const size_t smem = sizeof(SkSmem<AROW, GPW>);
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(ga.n_groups, ga.splits), dim3(256), smem, st, ga, e);
+  hipLaunchKernelGGL(kern, dim3((ga.n_groups + GPW - 1) / GPW, ga.splits), dim3(256), smem, st, ga, e);
+}
+
+template <int MT, int GPW, bool RMS, bool AROW, class Epi>
+static void sk_go_nb(const SkArgs& ga, const Epi& e, hipStream_t st) {
+  switch (sk_nb(ga.K / 32 / ga.splits / 4, GPW, MT)) {
+    case 8: sk_go<MT, 8, GPW, RMS, AROW>(ga, e, st); break;
+    case 4: sk_go<MT, 4, GPW, RMS, AROW>(ga, e, st); break;
+    case 2: sk_go<MT, 2, GPW, RMS, AROW>(ga, e, st); break;
+    default: sk_go<MT, 1, GPW, RMS, AROW>(ga, e, st); break;
+  }
 }
 
 template <int MT, bool RMS, bool AROW, class Epi>
-static void sk_go_nb(const SkArgs& ga, const Epi& e, hipStream_t st) {
-  switch (sk_nb(ga.K / 32 / ga.splits / 4)) {
-    case 8: sk_go<MT, 8, RMS, AROW>(ga, e, st); break;
-    case 4: sk_go<MT, 4, RMS, AROW>(ga, e, st); break;
-    case 2: sk_go<MT, 2, RMS, AROW>(ga, e, st); break;
-    default: sk_go<MT, 1, RMS, AROW>(ga, e, st); break;
+static void sk_go_gpw(const SkArgs& ga, int gpw, const Epi& e, hipStream_t st) {
+  if constexpr (kSkPlanMaxGpw >= 2) {
+    if (gpw == 2) return sk_go_nb<MT, 2, RMS, AROW>(ga, e, st);
   }
+  (void)gpw;
+  sk_go_nb<MT, 1, RMS, AROW>(ga, e, st);
 }
 
 template <bool RMS, bool AROW, class Epi>
-static void sk_launch(const SkArgs& ga, const Epi& e, hipStream_t st) {
+static void sk_launch(const SkArgs& ga, int gpw, const Epi& e, hipStream_t st) {
   switch (mt_of(ga.M)) {
-    case 1: sk_go_nb<1, RMS, AROW>(ga, e, st); break;
-    case 2: sk_go_nb<2, RMS, AROW>(ga, e, st); break;
-    case 3: sk_go_nb<3, RMS, AROW>(ga, e, st); break;
-    default: sk_go_nb<4, RMS, AROW>(ga, e, st); break;
+    case 1: sk_go_gpw<1, RMS, AROW>(ga, gpw, e, st); break;
+    case 2: sk_go_gpw<2, RMS, AROW>(ga, gpw, e, st); break;
+    case 3: sk_go_gpw<3, RMS, AROW>(ga, gpw, e, st); break;
+    default: sk_go_gpw<4, RMS, AROW>(ga, gpw, e, st); break;
   }
 }
 
-void launch_sk_qkv(const SkArgs& ga, bool a_rowmajor, const EpiQkvS& e, hipStream_t st) {
-  if (a_rowmajor) sk_launch<true, true>(ga, e, st);
-  else sk_launch<true, false>(ga, e, st);
+void launch_sk_qkv(const SkArgs& ga, int gpw, bool a_rowmajor, const EpiQkvS& e, hipStream_t st) {
+  if (a_rowmajor) sk_launch<true, true>(ga, gpw, e, st);
+  else sk_launch<true, false>(ga, gpw, e, st);
 }
-void launch_sk_resid(const SkArgs& ga, const EpiResidS& e, hipStream_t st) {
-  sk_launch<false, false>(ga, e, st);
+void launch_sk_resid(const SkArgs& ga, int gpw, const EpiResidS& e, hipStream_t st) {
+  sk_launch<false, false>(ga, gpw, e, st);
 }
-void launch_sk_gateup(const SkArgs& ga, const EpiGateUpS& e, hipStream_t st) {
-  sk_launch<true, false>(ga, e, st);
+void launch_sk_gateup(const SkArgs& ga, int gpw, const EpiGateUpS& e, hipStream_t st) {
+  sk_launch<true, false>(ga, gpw, e, st);
 }
 
 // ============================================================================ attention

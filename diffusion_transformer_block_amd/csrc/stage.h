@@ -45,6 +45,7 @@ struct StageArgs {
   int64_t prefix_stride;
   // K splits of the GEMM steps (last arriver reduces) and their scratch
   int split_qkv, split_o, split_gu, split_d, split_w3;
+  int gpw_qkv, gpw_o, gpw_gu, gpw_d, gpw_w3;   // 32-column groups per task
   float* part;
   unsigned* ctr_qkv;
   unsigned* ctr_o;

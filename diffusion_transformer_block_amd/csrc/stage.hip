@@ -12,12 +12,12 @@
 // head) -- on one workgroup per compute unit.  Each operator is a phase made of
 // independent tasks (the device tasks of skinny.h / attn_small.h, the same
 // code the per-operator kernels run):
-//   QKV  one 32-column group (x K split) of the fused QKV matrix, RMS + RoPE
+//   QKV  one or two 32-column groups (x K split) of the fused QKV matrix, RMS + RoPE
 //   ATT  one 64-row block x key slice of chunk attention
 //   CMB  merge of the key slices (256 output chunks per task), if sliced
-//   O    one 32-column group (x K split) of W_o, residual epilogue
-//   GU   one gate/up group, RMS + SiLU-gate epilogue
-//   D    one 32-column group (x K split) of W_down, residual epilogue
+//   O    one or two 32-column groups (x K split) of W_o, residual epilogue
+//   GU   one or two gate/up groups (x K split), RMS + SiLU-gate epilogue
+//   D    one or two 32-column groups (x K split) of W_down, residual epilogue
 //   EMB, W3, VEL  the flow head (embedding, its linear, velocity + Euler step)
 // Task t of a phase runs on workgroup (w0 + t mod nw); the phases' workgroup
 // sets are rotated so that consecutive phases start on different units.
@@ -192,19 +192,32 @@ __device__ void vel_task(const FlowTask& f, int i, FlowSmem& fs) {
 // workgroup completed the task's outputs (false also when it only published a
 // split partial; the phase checks separately whether the grid aborted).
 
-template <int MT, int NB, bool RMS, bool AROW, class Epi, class W>
-__device__ __noinline__ bool sk_run(SkArgs ga, Epi e, int g, int s, uint8_t* smem, W& wait) {
-  return sk_task<MT, NB, RMS, AROW>(ga, e, g, s, *reinterpret_cast<SkSmem<AROW>*>(smem), wait);
+template <int MT, int NB, int GPW, bool RMS, bool AROW, class Epi, class W>
+__device__ __noinline__ bool sk_run(SkArgs ga, Epi e, int gb, int s, uint8_t* smem, W& wait) {
+  return sk_task<MT, NB, GPW, RMS, AROW>(ga, e, gb, s, *reinterpret_cast<SkSmem<AROW, GPW>*>(smem), wait);
 }
 
-template <int MT, bool RMS, bool AROW, class Epi, class W>
-__device__ __forceinline__ bool sk_dispatch(const SkArgs& ga, const Epi& e, int g, int s, uint8_t* smem,
-                                            W& wait) {
+template <int MT, int GPW, bool RMS, bool AROW, class Epi, class W>
+__device__ __forceinline__ bool sk_dispatch_nb(const SkArgs& ga, const Epi& e, int gb, int s, uint8_t* smem,
+                                               W& wait) {
   const int KW = ga.K / 32 / ga.splits / 4;
-  if (KW % 8 == 0) return sk_run<MT, 8, RMS, AROW>(ga, e, g, s, smem, wait);
-  if (KW % 4 == 0) return sk_run<MT, 4, RMS, AROW>(ga, e, g, s, smem, wait);
-  if (KW % 2 == 0) return sk_run<MT, 2, RMS, AROW>(ga, e, g, s, smem, wait);
-  return sk_run<MT, 1, RMS, AROW>(ga, e, g, s, smem, wait);
+  constexpr int P = 2 * GPW + MT;   // fragments per k-tile; at most 48 in flight per lane
+  if (KW % 8 == 0 && 8 * P <= 48) return sk_run<MT, 8, GPW, RMS, AROW>(ga, e, gb, s, smem, wait);
+  if (KW % 4 == 0 && 4 * P <= 48) return sk_run<MT, 4, GPW, RMS, AROW>(ga, e, gb, s, smem, wait);
+  if (KW % 2 == 0) return sk_run<MT, 2, GPW, RMS, AROW>(ga, e, gb, s, smem, wait);
+  return sk_run<MT, 1, GPW, RMS, AROW>(ga, e, gb, s, smem, wait);
+}
+
+// task t of a GEMM phase = (group block t / splits, split t % splits)
+template <int MT, bool RMS, bool AROW, class Epi, class W>
+__device__ __forceinline__ bool sk_dispatch(const SkArgs& ga, int gpw, const Epi& e, int t, uint8_t* smem,
+                                            W& wait) {
+  const int gb = t / ga.splits, s = t - gb * ga.splits;
+  if constexpr (kSkPlanMaxGpw >= 2) {
+    if (gpw == 2) return sk_dispatch_nb<MT, 2, RMS, AROW>(ga, e, gb, s, smem, wait);
+  }
+  (void)gpw;
+  return sk_dispatch_nb<MT, 1, RMS, AROW>(ga, e, gb, s, smem, wait);
 }
 
 template <int HD, class W>
@@ -300,11 +313,10 @@ __global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
           ga.n_groups = (Hq + 2 * Hkv) * d / 32;
           ga.splits = sa.split_qkv;
           ga.counters = sa.ctr_qkv;
-          const int g = t / ga.splits;
           EpiQkvS e{sa.q, sa.kn, sa.vn, sa.new_stride, sa.cos_t, sa.sin_t, sa.T, sa.P, Hq, Hkv, d};
-          const bool done = in_frag ? sk_dispatch<MT, true, false>(ga, e, g, t - g * ga.splits, smem, wait)
-                                    : sk_dispatch<MT, true, true>(ga, e, g, t - g * ga.splits, smem, wait);
-          return done ? g : -1;
+          const bool done = in_frag ? sk_dispatch<MT, true, false>(ga, sa.gpw_qkv, e, t, smem, wait)
+                                    : sk_dispatch<MT, true, true>(ga, sa.gpw_qkv, e, t, smem, wait);
+          return done ? t / ga.splits : -1;
         }))
       return false;
     AttnSmArgs aa{};
@@ -346,9 +358,8 @@ __global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
           ga.n_groups = D / 32;
           ga.splits = sa.split_o;
           ga.counters = sa.ctr_o;
-          const int g = t / ga.splits;
           EpiResidS e{in, in_frag ? 1 : 0, MTm, nullptr, sa.h, 1, MTm, 0, D};
-          return sk_dispatch<MT, false, false>(ga, e, g, t - g * ga.splits, smem, wait) ? g : -1;
+          return sk_dispatch<MT, false, false>(ga, sa.gpw_o, e, t, smem, wait) ? t / ga.splits : -1;
         }))
       return false;
     if (!phase(kPhGU, [&](int t, auto& wait) {
@@ -359,8 +370,8 @@ __global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
           ga.n_groups = F / 16;
           ga.splits = sa.split_gu;
           ga.counters = sa.ctr_gu;
-          const int g = t / ga.splits;
-          return sk_dispatch<MT, true, false>(ga, EpiGateUpS{sa.a, MTm}, g, t - g * ga.splits, smem, wait) ? g : -1;
+          return sk_dispatch<MT, true, false>(ga, sa.gpw_gu, EpiGateUpS{sa.a, MTm}, t, smem, wait) ? t / ga.splits
+                                                                                                   : -1;
         }))
       return false;
     return phase(kPhD, [&](int t, auto& wait) {
@@ -371,9 +382,8 @@ __global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
       ga.n_groups = D / 32;
       ga.splits = sa.split_d;
       ga.counters = sa.ctr_d;
-      const int g = t / ga.splits;
       EpiResidS e{sa.h, 1, MTm, nullptr, out, out_frag ? 1 : 0, MTm, 0, D};
-      return sk_dispatch<MT, false, false>(ga, e, g, t - g * ga.splits, smem, wait) ? g : -1;
+      return sk_dispatch<MT, false, false>(ga, sa.gpw_d, e, t, smem, wait) ? t / ga.splits : -1;
     });
   };
 
@@ -421,9 +431,8 @@ __global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
           ga.splits = sa.split_w3;
           ga.part = sa.part;
           ga.counters = sa.ctr_o;
-          const int g = t / ga.splits;
           EpiResidS e{nullptr, 0, 0, sa.b3, sa.xb[0], 1, mt_of(sa.N + 1), 1, D};
-          return sk_dispatch<MT, false, false>(ga, e, g, t - g * ga.splits, smem, wait) ? g : -1;
+          return sk_dispatch<MT, false, false>(ga, sa.gpw_w3, e, t, smem, wait) ? t / ga.splits : -1;
         });
       for (int l = 0; l < sa.n_layers && ok; ++l)
         ok = run_layer(l, sa.xb[l & 1], true, sa.xb[(l + 1) & 1], true, sa.kp[l], sa.vp[l]);
@@ -488,7 +497,8 @@ size_t stage_smem_bytes(int head_dim) {
   size_t att = head_dim == 64    ? sizeof(AttnSmSmem<64>)
                : head_dim == 128 ? sizeof(AttnSmSmem<128>)
                                  : sizeof(AttnSmSmem<256>);
-  size_t m = sizeof(SkSmem<true>);
+  size_t m = sizeof(SkSmem<true, kSkPlanMaxGpw>);
+  if (sizeof(SkSmem<false, kSkPlanMaxGpw>) > m) m = sizeof(SkSmem<false, kSkPlanMaxGpw>);
   if (att > m) m = att;
   if (sizeof(FlowSmem) > m) m = sizeof(FlowSmem);
   return (m + 255) / 256 * 256;
