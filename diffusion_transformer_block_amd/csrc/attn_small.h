@@ -63,10 +63,11 @@ constexpr int kAttnMaxSplits = 16;
 
 template <int HD>
 struct AttnSmSmem {
-  bf16_t k[2][64 * (HD + 8)];        // K tiles; after the key loop: the block's rows [64][HD + 8]
-  bf16_t v[2][64 * (HD + 16)];       // V tiles; after the key loop: the second key half's partials
-  float2 ml[64];                     // per row (max, sum) of this slice
-  float2 ml2[64];                    // second key half's (max, sum)
+  // K / V tiles; after the key loop both arrays hold the two key halves'
+  // unnormalised rows [2][64][HD + 4] (fp32, fits in k and v together)
+  bf16_t k[2][64 * (HD + 8)];
+  bf16_t v[2][64 * (HD + 16)];
+  float2 mlh[2][64];                 // per key half and row: (max, sum)
 };
 
 __device__ __forceinline__ uint2 lds_tr16(const bf16_t* p) {
@@ -114,39 +115,44 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
   const __amdgpu_buffer_rsrc_t rkn = make_rsrc(a.kn + (size_t)b * a.new_stride + (size_t)hk * HD, (size_t)a.T * kvrow * 2);
   const __amdgpu_buffer_rsrc_t rvn = make_rsrc(a.vn + (size_t)b * a.new_stride + (size_t)hk * HD, (size_t)a.T * kvrow * 2);
   uint4 reg[2][NCH];   // one tile in flight: [K, V][chunk]
+  // thread tid moves 16-byte chunk c0 of key rows kk0 + j RPJ, j < NCH
+  constexpr int RPJ = 256 / CPR;               // key rows per pass of the workgroup
+  const int kk0 = tid / CPR, c0 = tid - kk0 * CPR;
   auto load_tile = [&](int tile) {
-    const int base = key_begin + 64 * tile;
-    const bool all_prefix = base + 64 <= a.P;   // uniform
+    const int base = key_begin + 64 * tile + kk0;
+    if (base - kk0 + 64 <= a.P) {   // wholly in the prefix (uniform)
+      const int off0 = (base * kvrow + 8 * c0) * 2;
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int idx = tid + 256 * j;
-      const int kk = idx / CPR, c = idx - kk * CPR;
-      const int key = base + kk;
-      if (all_prefix) {
-        const int off = (key * kvrow + 8 * c) * 2;
-        reg[0][j] = buf_ld_stream(rkp, off);
-        reg[1][j] = buf_ld_stream(rvp, off);
-      } else if (key >= key_end) {
-        reg[0][j] = make_uint4(0, 0, 0, 0);
-        reg[1][j] = make_uint4(0, 0, 0, 0);
-      } else if (key < a.P) {
-        const int off = (key * kvrow + 8 * c) * 2;
-        reg[0][j] = buf_ld_stream(rkp, off);
-        reg[1][j] = buf_ld_stream(rvp, off);
-      } else {
-        const int off = ((key - a.P) * kvrow + 8 * c) * 2;
-        reg[0][j] = buf_ld_act(rkn, off);
-        reg[1][j] = buf_ld_act(rvn, off);
+      for (int j = 0; j < NCH; ++j) {
+        reg[0][j] = buf_ld_stream(rkp, off0 + j * RPJ * kvrow * 2);
+        reg[1][j] = buf_ld_stream(rvp, off0 + j * RPJ * kvrow * 2);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int key = base + j * RPJ;
+        if (key >= key_end) {
+          reg[0][j] = make_uint4(0, 0, 0, 0);
+          reg[1][j] = make_uint4(0, 0, 0, 0);
+        } else if (key < a.P) {
+          const int off = (key * kvrow + 8 * c0) * 2;
+          reg[0][j] = buf_ld_stream(rkp, off);
+          reg[1][j] = buf_ld_stream(rvp, off);
+        } else {
+          const int off = ((key - a.P) * kvrow + 8 * c0) * 2;
+          reg[0][j] = buf_ld_act(rkn, off);
+          reg[1][j] = buf_ld_act(rvn, off);
+        }
       }
     }
   };
   auto store_tile = [&](int buf) {
+    bf16_t* kd = &sm.k[buf][kk0 * KROW + 8 * c0];
+    bf16_t* vd = &sm.v[buf][kk0 * VROW + 8 * c0];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int idx = tid + 256 * j;
-      const int kk = idx / CPR, c = idx - kk * CPR;
-      *reinterpret_cast<uint4*>(&sm.k[buf][kk * KROW + 8 * c]) = reg[0][j];
-      *reinterpret_cast<uint4*>(&sm.v[buf][kk * VROW + 8 * c]) = reg[1][j];
+      *reinterpret_cast<uint4*>(kd + j * RPJ * KROW) = reg[0][j];
+      *reinterpret_cast<uint4*>(vd + j * RPJ * VROW) = reg[1][j];
     }
   };
 
@@ -191,14 +197,33 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
   auto step = [&](int it, auto cur_c) {
     constexpr int cur = decltype(cur_c)::value;   // LDS buffer of tile it
     const int base = key_begin + 64 * it + 32 * kh;
-    // ---- S^T (32 keys x 32 rows)
-    f32x16 sacc;
+    // ---- S^T (32 keys x 32 rows): K fragments read from LDS in batches of
+    //      8 ahead of their MFMAs, two independent accumulation chains
+    f32x16 sacc, sacc2;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+    for (int v = 0; v < 16; ++v) {
+      sacc[v] = 0.f;
+      sacc2[v] = 0.f;
+    }
     const bf16_t* kr = &sm.k[cur][(32 * kh + (l & 31)) * KROW + 8 * hl];
+    constexpr int KB = NDS < 8 ? NDS : (HD >= 256 ? 4 : 8);   // registers bound the batch at HD 256
 #pragma unroll
-    for (int s = 0; s < NDS; ++s)
-      sacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(kr + 16 * s)), as_bf16x8(qf[s]), sacc);
+    for (int s0 = 0; s0 < NDS; s0 += KB) {
+      uint4 kf[KB];
+#pragma unroll
+      for (int s = 0; s < KB; ++s) kf[s] = *reinterpret_cast<const uint4*>(kr + 16 * (s0 + s));
+#pragma unroll
+      for (int s = 0; s < KB; s += 2) {
+        sacc = mfma32(as_bf16x8(kf[s]), as_bf16x8(qf[s0 + s]), sacc);
+        if (s + 1 < KB) {
+          if constexpr (HD >= 256)
+            sacc = mfma32(as_bf16x8(kf[s + 1]), as_bf16x8(qf[s0 + s + 1]), sacc);
+          else
+            sacc2 = mfma32(as_bf16x8(kf[s + 1]), as_bf16x8(qf[s0 + s + 1]), sacc2);
+        }
+      }
+    }
+    sacc += sacc2;
     // ---- online softmax in base 2
     float x[16];
     float mloc = -INFINITY;
@@ -237,11 +262,18 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
     for (int u = 0; u < 2; ++u) {
       const bf16x8 pb = as_bf16x8(make_uint4(pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]));
       const bf16_t* vt = &sm.v[cur][vt_off + 16 * u * VROW];
+      constexpr int VB = NDT < 4 ? NDT : 4;   // transposed reads issued ahead of their MFMAs
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const uint2 lo = lds_tr16(vt + 32 * dt);
-        const uint2 hi = lds_tr16(vt + 8 * VROW + 32 * dt);
-        o[dt] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, o[dt]);
+      for (int d0 = 0; d0 < NDT; d0 += VB) {
+        uint2 vlo[VB], vhi[VB];
+#pragma unroll
+        for (int dt = 0; dt < VB; ++dt) {
+          vlo[dt] = lds_tr16(vt + 32 * (d0 + dt));
+          vhi[dt] = lds_tr16(vt + 8 * VROW + 32 * (d0 + dt));
+        }
+#pragma unroll
+        for (int dt = 0; dt < VB; ++dt)
+          o[d0 + dt] = mfma32(as_bf16x8(make_uint4(vlo[dt].x, vlo[dt].y, vhi[dt].x, vhi[dt].y)), pb, o[d0 + dt]);
       }
     }
     // ---- stage the next tile into the other buffer (last read one tile ago)
@@ -257,79 +289,69 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
     if (it + 1 < n_tiles) step(it + 1, std::integral_constant<int, 1>{});
   }
 
-  // ---- merge the two key halves: kh = 1 parks (m, l, O^T) in LDS, kh = 0
-  //      combines and writes normalised rows [64][HD + 8] (bf16) plus stats
-  float l_tot = l_run + __shfl_xor(l_run, 32);   // the two lanes of a row share m_run
-  float* park = reinterpret_cast<float*>(sm.v[0]);   // [2 row halves][32 rows][HD + 4] fp32
+  // ---- merge the two key halves: every wave parks its unnormalised O^T rows
+  //      (fp32) and (max, sum) in LDS -- the K / V tiles are no longer read --
+  //      then all 256 threads combine 16-byte output chunks and store them
+  //      (one key slice: the O projection's operand order; several: this
+  //      slice's normalised bf16 partial and its (max, sum))
+  const float l_tot = l_run + __shfl_xor(l_run, 32);   // the two lanes of a row share m_run
   constexpr int PROW = HD + 4;
+  float* park = reinterpret_cast<float*>(&sm.k[0][0]);   // [2 key halves][64 rows][PROW]
   const int row32 = l & 31;
-  if (kh == 1) {
-    float* dst = park + (rp * 32 + row32) * PROW;
+  {
+    float* dst = park + (kh * 64 + rp * 32 + row32) * PROW + 4 * hl;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * q + 4 * hl) =
+        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * q) =
             make_float4(o[dt][4 * q], o[dt][4 * q + 1], o[dt][4 * q + 2], o[dt][4 * q + 3]);
-    if (hl == 0) sm.ml2[rp * 32 + row32] = make_float2(m_run, l_tot);
-  }
-  __syncthreads();
-  bf16_t* rowt = sm.k[0];
-  if (kh == 0) {
-    const float2 o2 = sm.ml2[rp * 32 + row32];
-    const float mm = fmaxf(m_run, o2.x);
-    const float a1 = m_run == -INFINITY ? 0.f : exp2f(m_run - mm);
-    const float a2 = o2.x == -INFINITY ? 0.f : exp2f(o2.x - mm);
-    const float lsum = l_tot * a1 + o2.y * a2;
-    const float inv = 1.f / lsum;
-    const float* src = park + (rp * 32 + row32) * PROW;
-    bf16_t* dst = rowt + (rp * 32 + row32) * KROW;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int d0 = 32 * dt + 8 * q + 4 * hl;
-        const float4 p2 = *reinterpret_cast<const float4*>(src + d0);
-        *reinterpret_cast<uint2*>(dst + d0) =
-            make_uint2(pack2((o[dt][4 * q] * a1 + p2.x * a2) * inv, (o[dt][4 * q + 1] * a1 + p2.y * a2) * inv),
-                       pack2((o[dt][4 * q + 2] * a1 + p2.z * a2) * inv, (o[dt][4 * q + 3] * a1 + p2.w * a2) * inv));
-      }
-    if (hl == 0) sm.ml[rp * 32 + row32] = make_float2(mm, lsum);
+    if (hl == 0) sm.mlh[kh][rp * 32 + row32] = make_float2(m_run, l_tot);
   }
   __syncthreads();
 
   const int n_rb = (rows + 63) >> 6;
   const int rb_id = bh * n_rb + rb;
-
-  if (a.splits == 1) {
-    const int MTo = mt_of(a.B * a.T);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o, (size_t)MTo * 16 * a.Hq * HD * 2);
-#pragma unroll
-    for (int p = 0; p < IPT; ++p) {
-      const int i = tid + 256 * p, row = i / CPR, c = i - row * CPR;
-      const int ar = 64 * rb + row;
-      if (ar < rows) {
-        const int t = ar / G, h = hk * G + (ar - t * G);
-        buf_st16(ro, (int)(fa_index(b * a.T + t, h * HD + 8 * c, MTo) * 2),
-                 *reinterpret_cast<const uint4*>(rowt + row * KROW + 8 * c));
-      }
-    }
-    return true;
-  }
-
-  // ---- several key slices: publish the normalised rows and (max, sum) with
-  //      row-contiguous stores; attn_combine_task merges the slices
   const int n_rbt = a.B * a.Hkv * n_rb;
   const size_t slab = (size_t)64 * HD;     // bf16 per (slice, row block)
-  const __amdgpu_buffer_rsrc_t rpo = make_rsrc(a.part_o + ((size_t)ks * n_rbt + rb_id) * slab, slab * 2);
+  const int MTo = mt_of(a.B * a.T);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o, (size_t)MTo * 16 * a.Hq * HD * 2);
+  const __amdgpu_buffer_rsrc_t rpo =
+      make_rsrc(a.part_o + ((size_t)ks * n_rbt + rb_id) * slab, a.splits > 1 ? slab * 2 : 0);
 #pragma unroll
   for (int p = 0; p < IPT; ++p) {
     const int i = tid + 256 * p, row = i / CPR, c = i - row * CPR;
-    buf_st16(rpo, (row * HD + 8 * c) * 2, *reinterpret_cast<const uint4*>(rowt + row * KROW + 8 * c));
+    const float2 h0 = sm.mlh[0][row], h1 = sm.mlh[1][row];
+    const float mm = fmaxf(h0.x, h1.x);
+    const float a0 = h0.x == -INFINITY ? 0.f : exp2f(h0.x - mm);
+    const float a1 = h1.x == -INFINITY ? 0.f : exp2f(h1.x - mm);
+    const float inv = 1.f / (h0.y * a0 + h1.y * a1);
+    const float* p0 = park + row * PROW + 8 * c;
+    const float* p1 = p0 + 64 * PROW;
+    const float4 x0 = *reinterpret_cast<const float4*>(p0), x1 = *reinterpret_cast<const float4*>(p0 + 4);
+    const float4 y0 = *reinterpret_cast<const float4*>(p1), y1 = *reinterpret_cast<const float4*>(p1 + 4);
+    const float f[8] = {(x0.x * a0 + y0.x * a1) * inv, (x0.y * a0 + y0.y * a1) * inv,
+                        (x0.z * a0 + y0.z * a1) * inv, (x0.w * a0 + y0.w * a1) * inv,
+                        (x1.x * a0 + y1.x * a1) * inv, (x1.y * a0 + y1.y * a1) * inv,
+                        (x1.z * a0 + y1.z * a1) * inv, (x1.w * a0 + y1.w * a1) * inv};
+    if (a.splits == 1) {
+      const int ar = 64 * rb + row;
+      if (ar < rows) {
+        const int t = ar / G, h = hk * G + (ar - t * G);
+        buf_st16(ro, (int)(fa_index(b * a.T + t, h * HD + 8 * c, MTo) * 2), pack8(f));
+      }
+    } else {
+      buf_st16(rpo, (row * HD + 8 * c) * 2, pack8(f));
+    }
   }
+  if (a.splits == 1) return true;
   if (tid < 64) {
+    const float2 h0 = sm.mlh[0][tid], h1 = sm.mlh[1][tid];
+    const float mm = fmaxf(h0.x, h1.x);
+    const float a0 = h0.x == -INFINITY ? 0.f : exp2f(h0.x - mm);
+    const float a1 = h1.x == -INFINITY ? 0.f : exp2f(h1.x - mm);
     const __amdgpu_buffer_rsrc_t rpm = make_rsrc(a.part_ml + ((size_t)ks * n_rbt + rb_id) * 128, 512);
-    buf_st8(rpm, tid * 8, __float_as_uint(sm.ml[tid].x), __float_as_uint(sm.ml[tid].y));
+    buf_st8(rpm, tid * 8, __float_as_uint(mm), __float_as_uint(h0.y * a0 + h1.y * a1));
   }
   return false;
 }

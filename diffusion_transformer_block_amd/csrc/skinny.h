@@ -32,6 +32,8 @@
 //  * The epilogue reads the summed 64 x 32 tile from LDS in the order it
 //    stores (row-contiguous 16-byte stores).
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 
 namespace blk {
@@ -124,59 +126,66 @@ __device__ bool sk_task(const SkArgs& ga, const Epi& epi, int gb, int s, SkSmem<
       bw[b][j][1] = buf_ld_stream(rb, o + kFragBytes);
     }
   };
+  // ---- activations: row-major input is staged through LDS; without a
+  //      producing step to wait for (a standalone launch) its loads go out
+  //      before the weights', so that writing the stage does not wait for the
+  //      slower weight stream (loads complete in issue order)
+  constexpr bool kEarlyStage = AROW && std::is_same<std::decay_t<Wait>, NoWait>::value;
+  // stage rows [0, M) x k-tiles [kb, kb + KTS) in operand order: one batch of
+  // at most 32 row-contiguous 16-byte loads per thread (the slab is at most
+  // kSkMaxStage KiB), rows past M clamped to M - 1 and not stored
+  const int nck = KTS * 4;                       // 16-byte chunks per row
+  const int nl = AROW ? (ga.M * nck + 255) >> 8 : 0;   // loads per thread, <= 32 (uniform)
+  const int dr = 256 / nck, dc = 256 - dr * nck; // (row, chunk) step per load
+  const int r0 = tid / nck, c0 = tid - r0 * nck;
+  uint4 sv[AROW ? 32 : 1];
+  auto stage_issue = [&]() {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(ga.A, (size_t)ga.M * ga.lda * 2);
+    int r = r0, c = c0;
+#pragma unroll
+    for (int j = 0; j < (AROW ? 32 : 0); ++j) {
+      if (j < nl) {
+        sv[j] = buf_ld_act(rx, (min(r, ga.M - 1) * ga.lda + kb * 32 + c * 8) * 2);
+        r += dr;
+        c += dc;
+        if (c >= nck) {
+          c -= nck;
+          ++r;
+        }
+      }
+    }
+  };
+  auto stage_write = [&]() {
+    int r = r0, c = c0;
+#pragma unroll
+    for (int j = 0; j < (AROW ? 32 : 0); ++j) {
+      if (j < nl) {
+        if (r < ga.M) sm.astage[stage_slot(c >> 2, r >> 4, (r & 15) + 16 * (c & 3), MT)] = sv[j];
+        r += dr;
+        c += dc;
+        if (c >= nck) {
+          c -= nck;
+          ++r;
+        }
+      }
+    }
+    __syncthreads();
+  };
+  if (kEarlyStage) stage_issue();
 #pragma unroll
   for (int b = 0; b < NB; ++b) issue_w(b, b);
   if (!wait()) return false;
   typename Epi::Pre pre[GPW];
 #pragma unroll
   for (int j = 0; j < GPW; ++j) pre[j] = epi.prefetch(g0 + min(j, ng - 1), ga.M);
-
-  // ---- activations
+  if (AROW) {
+    if (!kEarlyStage) stage_issue();
+    stage_write();
+  }
   uint4 av[NB][MT];
   __amdgpu_buffer_rsrc_t ra;
   int aoff = 0;
-  if (AROW) {
-    // stage rows [0, M) x k-tiles [kb, kb + KTS) in operand order: one batch
-    // of at most 32 row-contiguous 16-byte loads per thread (the slab is at
-    // most kSkMaxStage KiB), rows past M clamped to M - 1 and not stored
-    const int nck = KTS * 4;                       // 16-byte chunks per row
-    const int nl = (ga.M * nck + 255) >> 8;        // loads per thread, <= 32 (uniform)
-    const int dr = 256 / nck, dc = 256 - dr * nck; // (row, chunk) step per load
-    const int r0 = tid / nck, c0 = tid - r0 * nck;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(ga.A, (size_t)ga.M * ga.lda * 2);
-    uint4 v[32];
-    {
-      int r = r0, c = c0;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        if (j < nl) {
-          v[j] = buf_ld_act(rx, (min(r, ga.M - 1) * ga.lda + kb * 32 + c * 8) * 2);
-          r += dr;
-          c += dc;
-          if (c >= nck) {
-            c -= nck;
-            ++r;
-          }
-        }
-      }
-    }
-    {
-      int r = r0, c = c0;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        if (j < nl) {
-          if (r < ga.M) sm.astage[stage_slot(c >> 2, r >> 4, (r & 15) + 16 * (c & 3), MT)] = v[j];
-          r += dr;
-          c += dc;
-          if (c >= nck) {
-            c -= nck;
-            ++r;
-          }
-        }
-      }
-    }
-    __syncthreads();
-  } else {
+  if (!AROW) {
     ra = make_rsrc(ga.A, (size_t)KT * MT * kFragBytes);
     aoff = ((kb + uw) * MT * 64 + l) * 16;
   }
