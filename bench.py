@@ -36,6 +36,48 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 
 
+# kernels behind each operator of the 64-token stage
+OP_KERNELS = {
+    "qkv_rope": "sk_kernel<EpiQkvS> (RMS + fused QKV + RoPE)",
+    "attention": "attn_sm_kernel<256> + attn_combine_kernel<256>",
+    "o_proj": "sk_kernel<EpiResidS> (O projection + residual)",
+    "gate_up": "sk_kernel<EpiGateUpS> (RMS + gate/up + SiLU*up)",
+    "down": "sk_kernel<EpiResidS> (down projection + residual)",
+    "stage": "stage_kernel (persistent)",
+}
+
+# HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE on this
+# workload, scaled by the factor a plain copy kernel of known size gives, and
+# the SHA-256 of the kernel sources when the counters were taken: a changed
+# kernel reports null until it is profiled again.
+TRAFFIC = {
+    "qkv_rope": {"fetch": 6713549, "write": 622592, "bytes": 7336141, "sources": "a9c433870c5c4cdc"},
+    "attention": {"fetch": 7740621, "write": 4005888, "bytes": 11746509, "sources": "a9c433870c5c4cdc"},
+    "o_proj": {"fetch": 8750080, "write": 4465664, "bytes": 13215744, "sources": "a9c433870c5c4cdc"},
+    "gate_up": {"fetch": 18017280, "write": 1048576, "bytes": 19065856, "sources": "a9c433870c5c4cdc"},
+    "down": {"fetch": 14916813, "write": 4465664, "bytes": 19382477, "sources": "a9c433870c5c4cdc"},
+}
+TRAFFIC_FETCH_SCALE = 2.0   # FETCH_SIZE of a 256 MiB copy reads 128 MiB
+TRAFFIC_WRITE_SCALE = 1.0   # WRITE_SIZE of the same copy reads 256 MiB
+TRAFFIC_SOURCES = ("common.h", "skinny.h", "attn_small.h", "small.hip")
+
+
+def sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "diffusion_transformer_block_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_of(op):
+    t = TRAFFIC.get(op)
+    if not t or t["sources"] != sources_digest():
+        return None
+    return t["bytes"]
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -51,6 +93,9 @@ def parse():
     ap.add_argument("--rotate", type=int, default=16, help="weight copies in rotation")
     ap.add_argument("--exec-mode", choices=["auto", "per_operator", "persistent"], default="auto",
                     help="blk_set_execution_mode for the small-chunk workloads")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB 4 times (the known-size "
+                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -70,6 +115,29 @@ def block_flops(shape, P):
     gemm = 2 * M * (D * (Hq + 2 * Hkv) * d + Hq * d * D + 2 * D * F + F * D)
     att = 2 * 2 * shape.batch * Hq * shape.tokens * (P + shape.tokens) * d
     return gemm, att
+
+
+def operator_bytes(shape, P):
+    """Algorithmic HBM bytes of each operator of one block stage: its weights,
+    the activations it reads and the ones it writes (bf16)."""
+    D, F, d, Hq, Hkv = shape.hidden, shape.ffn, shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    M = shape.batch * shape.tokens
+    act = lambda n: 2 * M * n
+    kv_new = 2 * 2 * M * Hkv * d
+    wb, ob = block_bytes(shape, P)
+    return {
+        "stage": wb + ob,
+        "qkv_rope": 2 * D * (Hq + 2 * Hkv) * d + act(D) + act(Hq * d) + kv_new,
+        "attention": act(Hq * d) + 2 * 2 * shape.batch * P * Hkv * d + kv_new + act(Hq * d),
+        "o_proj": 2 * Hq * d * D + act(Hq * d) + act(D) + act(D),
+        "gate_up": 2 * 2 * D * F + act(D) + act(F),
+        "down": 2 * F * D + act(F) + act(D) + act(D),
+    }
+
+
+def percentiles(v, qs=(10, 50, 90)):
+    v = sorted(v)
+    return [v[min(len(v) - 1, max(0, round(q / 100 * (len(v) - 1))))] for q in qs]
 
 
 def config_of(blk, shape, max_pos=None):
@@ -127,13 +195,15 @@ def time_block(shape, steps, warmup, rotate):
         g.replay()
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(st)
-    for _ in range(n_rep):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep + 1)]
+    ev[0].record(st)
+    for r in range(n_rep):
         g.replay()
-    e1.record(st)
+        ev[r + 1].record(st)
     torch.cuda.synchronize()
-    us_graph = e0.elapsed_time(e1) * 1e3 / (n_rep * rotate)
+    us_graph = ev[0].elapsed_time(ev[-1]) * 1e3 / (n_rep * rotate)
+    per_rep = [ev[r].elapsed_time(ev[r + 1]) * 1e3 / rotate for r in range(n_rep)]
+    e0, e1 = ev[0], ev[-1]
 
     # eager (one C call per block, five launches each)
     for i in range(rotate):
@@ -146,9 +216,37 @@ def time_block(shape, steps, warmup, rotate):
     e1.record(st)
     torch.cuda.synchronize()
     us_eager = e0.elapsed_time(e1) * 1e3 / (n_rep * rotate)
-    del g, packs, kps, vps
+
+    # warm: the graph of `rotate` stages on one copy (weights MALL-resident)
+    gw = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gw):
+        for _ in range(rotate):
+            run(0)
+    for _ in range(4):
+        gw.replay()
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(n_rep):
+        gw.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    us_warm = e0.elapsed_time(e1) * 1e3 / (n_rep * rotate)
+
+    # per operator: HIP events the library records on this stream around each
+    # operator of eager (cold, rotated) stages
+    blk.blk_set_operator_timing(True)
+    try:
+        for r in range(n_rep):
+            for i in range(rotate):
+                run(i)
+        ops = blk.blk_operator_times()
+    finally:
+        blk.blk_set_operator_timing(False)
+    torch.cuda.synchronize()
+    del g, gw, packs, kps, vps
     torch.cuda.empty_cache()
-    return {"us": us_graph, "us_eager": us_eager, "timed_steps": n_rep * rotate}
+    return {"us": us_graph, "us_eager": us_eager, "us_warm": us_warm,
+            "us_p10_p50_p90": percentiles(per_rep), "timed_steps": n_rep * rotate, "ops": ops}
 
 
 def time_loop(warmup, reps=20):
@@ -284,6 +382,15 @@ def main():
     import diffusion_transformer_block_amd as blk
     blk.blk_set_execution_mode({"auto": blk.EXEC_AUTO, "per_operator": blk.EXEC_PER_OPERATOR,
                                 "persistent": blk.EXEC_PERSISTENT}[args.exec_mode])
+    if args.calib_copy > 0:
+        n = args.calib_copy * (1 << 20) // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calib_copy} MiB read + {args.calib_copy} MiB written, 4 times")
+        del src, dst
     rotate = max(1, args.rotate)
     steps = max(rotate, (args.steps // rotate) * rotate)
     shape = synth.AE_BLOCK
@@ -293,6 +400,15 @@ def main():
         r = time_block(shape, steps, args.warmup, rotate)
         wb, ob = block_bytes(shape, shape.prefix)
         gbs = (wb + ob) / (r["us"] * 1e-6) / 1e9
+        opb = operator_bytes(shape, shape.prefix)
+        operators = []
+        for name, (us, calls) in r["ops"].items():
+            ach = opb[name] / (us * 1e-6) / 1e9
+            operators.append({"operator": name, "kernels": OP_KERNELS[name], "us": round(us, 3),
+                              "calls": calls, "algorithmic_bytes": opb[name],
+                              "achieved_GBs": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4),
+                              "traffic": traffic_of(name)})
+        dom = max(operators, key=lambda o: o["us"])
         line.update({
             "value": round(r["us"], 3), "unit": "us", "n_gpus": 1, "steps": r["timed_steps"],
             "warmup": args.warmup, "ms_per_step": round(r["us"] / 1e3, 6),
@@ -304,13 +420,23 @@ def main():
                        "prefix": shape.prefix, "weight_copies": rotate,
                        "parallelism": "single GPU"},
             "eager_us": round(r["us_eager"], 3),
-            "roofline": {"bound": "hbm", "kernel": "block_stage (qkv_rope, attention, o_proj, "
-                         "gate_up, down: one graph-replayed sequence)",
-                         "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": wb + ob,
-                         "traffic": None},
+            "warm_us": round(r["us_warm"], 3),
+            "us_p10_p50_p90": [round(v, 3) for v in r["us_p10_p50_p90"]],
+            "roofline": {"bound": "hbm", "kernel": f"{dom['operator']}: {dom['kernels']}",
+                         "achieved": dom["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dom["frac"], "algorithmic_bytes": dom["algorithmic_bytes"],
+                         "us_per_launch": dom["us"], "timing": "HIP events on the launch stream",
+                         "traffic": traffic_of(dom["operator"])},
+            "stage_roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                               "algorithmic_bytes": wb + ob,
+                               "roofline_us": round((wb + ob) / (HBM_PEAK_GBS * 1e3), 3)},
+            "operators": operators,
         })
-        log(f"  {r['us']:.2f} us/stage graph, {r['us_eager']:.2f} us eager, {gbs:.0f} GB/s")
+        log(f"  {r['us']:.2f} us/stage graph, {r['us_eager']:.2f} us eager, "
+            f"{r['us_warm']:.2f} us warm, {gbs:.0f} GB/s")
+        for o in operators:
+            log(f"    {o['operator']:9s} {o['us']:7.2f} us  {o['achieved_GBs']:7.1f} GB/s")
     if args.only in ("all", "loop"):
         log("loop flow_18x10")
         line["loop"] = time_loop(args.warmup)

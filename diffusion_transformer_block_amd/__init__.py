@@ -17,13 +17,14 @@ import ctypes
 from ctypes import byref, c_double, c_size_t, c_void_p
 
 from ._lib import (BLK_EHIP, BLK_EINVAL, BLK_ESIZE, BLK_ESTATE, BLK_EUNSUPPORTED, BLK_OK,
-                   EXPORTS, HEAD_FIELDS, LAYER_FIELDS, BlkConfig, BlkError, FlowHeadSrc,
-                   LayerSrc, check, load)
+                   EXPORTS, HEAD_FIELDS, LAYER_FIELDS, OPERATORS, BlkConfig, BlkError,
+                   FlowHeadSrc, LayerSrc, check, load)
 
 __all__ = ["BlkConfig", "BlkError", "make_config", "blk_prepare_weights", "blk_forward",
            "flow_denoise", "blk_last_error", "blk_release", "blk_version", "EXPORTS",
            "blk_set_execution_mode", "EXEC_AUTO", "EXEC_PER_OPERATOR", "EXEC_PERSISTENT",
-           "forward_workspace_bytes", "flow_workspace_bytes", "packed_bytes"]
+           "forward_workspace_bytes", "flow_workspace_bytes", "packed_bytes",
+           "blk_set_operator_timing", "blk_operator_times", "OPERATORS"]
 
 
 def _torch():
@@ -188,6 +189,22 @@ EXEC_AUTO, EXEC_PER_OPERATOR, EXEC_PERSISTENT = 0, 1, 2
 
 
 def blk_set_execution_mode(mode: int) -> None:
-    """0: persistent stage kernel where it applies (default); 1: one kernel per
-    operator; 2: persistent kernel only."""
+    """0 (default): automatic (at present one kernel per operator); 1: one
+    kernel per operator; 2: the persistent stage kernel only."""
     check("blk_set_execution_mode", load().blk_set_execution_mode(mode))
+
+
+def blk_set_operator_timing(enable: bool) -> None:
+    """Bracket every operator of each blk_forward call with HIP events on its
+    stream (or stop); either call discards what was accumulated."""
+    check("blk_set_operator_timing", load().blk_set_operator_timing(1 if enable else 0))
+
+
+def blk_operator_times() -> dict:
+    """{operator name: (average microseconds per call, timed calls)} since
+    timing was enabled, for the operators that ran."""
+    n = len(OPERATORS)
+    avg = (c_double * n)()
+    calls = (ctypes.c_int * n)()
+    check("blk_operator_times", load().blk_operator_times(avg, calls, n))
+    return {OPERATORS[i]: (avg[i], calls[i]) for i in range(n) if calls[i] > 0}

@@ -18,7 +18,11 @@ ERROR_NAMES = {BLK_EINVAL: "BLK_EINVAL", BLK_EUNSUPPORTED: "BLK_EUNSUPPORTED",
 
 # every function include/blk.h declares
 EXPORTS = ("blk_prepare_weights", "blk_forward", "flow_denoise", "blk_last_error",
-           "blk_release", "blk_version", "blk_set_execution_mode")
+           "blk_release", "blk_version", "blk_set_execution_mode", "blk_set_operator_timing",
+           "blk_operator_times")
+
+# operator indices of blk_operator_times (BLK_OP_* in include/blk.h)
+OPERATORS = ("qkv_rope", "attention", "o_proj", "gate_up", "down", "stage")
 
 
 class BlkConfig(ctypes.Structure):
@@ -71,6 +75,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.blk_version.restype = c_int
     lib.blk_set_execution_mode.argtypes = [c_int]
     lib.blk_set_execution_mode.restype = c_int
+    lib.blk_set_operator_timing.argtypes = [c_int]
+    lib.blk_set_operator_timing.restype = c_int
+    lib.blk_operator_times.argtypes = [POINTER(c_double), POINTER(c_int), c_int]
+    lib.blk_operator_times.restype = c_int
     _lib = lib
     return lib
 

@@ -241,6 +241,51 @@ const T* at(const void* base, size_t off) {
   return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
 }
 
+// ---------------------------------------------------------------- operator timing
+// While on, blk_forward brackets each operator of the stage with HIP events on
+// the caller's stream (nothing else changes); blk_operator_times reads them.
+constexpr size_t kTimerMaxEvents = 6 * 4096;
+struct OpTimer {
+  bool on = false;
+  std::vector<hipEvent_t> pool;   // created on first use, reused after each read
+  size_t used = 0;
+  struct Rec {
+    int op;
+    size_t e0, e1;
+  };
+  std::vector<Rec> recs;
+  double sum_ms[BLK_N_OPS] = {};
+  int calls[BLK_N_OPS] = {};
+};
+OpTimer g_timer;
+std::mutex g_timer_mu;
+// Set by blk_forward for the duration of one enqueue when timing is on (the
+// stream may be the null stream, hence the separate flag).
+thread_local bool g_marking = false;
+thread_local hipStream_t g_mark_stream = nullptr;
+thread_local size_t g_mark_prev = 0;
+
+hipError_t timer_event(hipStream_t st, size_t* idx) {
+  if (g_timer.used == g_timer.pool.size()) {
+    // no system-scope fence (an L2 write-back per event) between the kernels
+    hipEvent_t e;
+    const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
+    if (r != hipSuccess) return r;
+    g_timer.pool.push_back(e);
+  }
+  *idx = g_timer.used++;
+  return hipEventRecord(g_timer.pool[*idx], st);
+}
+
+// End of operator `op` of the stage being enqueued (no-op unless timing).
+void op_done(int op) {
+  if (!g_marking) return;
+  size_t e;
+  if (timer_event(g_mark_stream, &e) != hipSuccess) return;
+  g_timer.recs.push_back({op, g_mark_prev, e});
+  g_mark_prev = e;
+}
+
 // ---------------------------------------------------------------- persistent stage plan
 int g_exec_mode = 0;   // 0 auto, 1 per-operator kernels, 2 persistent stage kernel only
 
@@ -405,6 +450,7 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     EpiQkvS e{q, io.kn, io.vn, io.new_stride, at<float>(packed, lay.rope_cos),
               at<float>(packed, lay.rope_sin), T, P, Hq, Hkv, d};
     launch_sk_qkv(ga, p.gpw, !x_frag, e, st);
+    op_done(BLK_OP_QKV);
   }
   // 2. attention over [prefix ; own]
   {
@@ -427,6 +473,7 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     aa.part_o = at<bf16_t>(ws, w.sm_att_o);
     aa.part_ml = at<float>(ws, w.sm_att_ml);
     launch_attn_sm(aa, d, st);
+    op_done(BLK_OP_ATTENTION);
   }
   // 3. h = x + O W_o
   {
@@ -440,6 +487,7 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     ga.counters = at<unsigned>(ws, w.ctr_o);
     EpiResidS e{io.x, x_frag ? 1 : 0, MT, nullptr, h, 1, MT, 0, D};
     launch_sk_resid(ga, p.gpw, e, st);
+    op_done(BLK_OP_O_PROJ);
   }
   // 4. RMS(h) -> gate/up GEMM with SiLU(gate) * up epilogue
   {
@@ -452,6 +500,7 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     ga.splits = p.splits;
     ga.counters = at<unsigned>(ws, w.ctr_gu);
     launch_sk_gateup(ga, p.gpw, EpiGateUpS{a, MT}, st);
+    op_done(BLK_OP_GATE_UP);
   }
   // 5. y = h + a W_d
   {
@@ -465,6 +514,7 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     ga.counters = at<unsigned>(ws, w.ctr_d);
     EpiResidS e{h, 1, MT, nullptr, io.y, y_frag ? 1 : 0, MT, 0, D};
     launch_sk_resid(ga, p.gpw, e, st);
+    op_done(BLK_OP_DOWN);
   }
 }
 
@@ -500,6 +550,7 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     EpiQKV e{q, io.kn, io.vn, io.new_stride, at<float>(packed, lay.rope_cos),
              at<float>(packed, lay.rope_sin), T, P, Hq, Hkv, d};
     launch_gemm_qkv(ga, e, st);
+    op_done(BLK_OP_QKV);
   }
   // 2. attention over [prefix ; own]
   {
@@ -524,6 +575,7 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     aa.part_ml = at<float>(ws, w.att_ml);
     aa.counters = at<unsigned>(ws, w.ctr_att);
     launch_attention(aa, st);
+    op_done(BLK_OP_ATTENTION);
   }
   // 3. h = x + O W_o
   {
@@ -534,6 +586,7 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     ga.Bp = lw + lay.wo;
     ga.n_groups = D / 32;
     launch_gemm_residual(ga, EpiResidual{io.x, h, D}, st);
+    op_done(BLK_OP_O_PROJ);
   }
   // 4. RMS(h) -> gate/up GEMM with SiLU(gate) * up epilogue
   {
@@ -546,6 +599,7 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     launch_rms_rows(h, M, D, c.rms_eps, r2, st);
     ga.r = r2;
     launch_gemm_gateup(ga, EpiGateUp{a, F}, st);
+    op_done(BLK_OP_GATE_UP);
   }
   // 5. y = h + a W_d
   {
@@ -556,6 +610,7 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     ga.Bp = lw + lay.wd;
     ga.n_groups = D / 32;
     launch_gemm_residual(ga, EpiResidual{h, io.y, D}, st);
+    op_done(BLK_OP_DOWN);
   }
 }
 
@@ -690,6 +745,40 @@ int blk_set_execution_mode(int mode) {
   g_err.clear();
   if (mode < 0 || mode > 2) return fail(BLK_EINVAL, "execution mode %d not in {0, 1, 2}", mode);
   g_exec_mode = mode;
+  return BLK_OK;
+}
+
+int blk_set_operator_timing(int enable) {
+  g_err.clear();
+  if (enable != 0 && enable != 1) return fail(BLK_EINVAL, "enable %d not in {0, 1}", enable);
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  g_timer.on = enable == 1;
+  g_timer.used = 0;
+  g_timer.recs.clear();
+  for (int i = 0; i < BLK_N_OPS; ++i) {
+    g_timer.sum_ms[i] = 0.0;
+    g_timer.calls[i] = 0;
+  }
+  return BLK_OK;
+}
+
+int blk_operator_times(double* avg_us, int* calls, int n) {
+  g_err.clear();
+  if (n < 0 || (n > 0 && (!avg_us || !calls))) return fail(BLK_EINVAL, "avg_us / calls NULL or n < 0");
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  if (!g_timer.recs.empty()) HIP_TRY(hipEventSynchronize(g_timer.pool[g_timer.recs.back().e1]));
+  for (const auto& r : g_timer.recs) {
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, g_timer.pool[r.e0], g_timer.pool[r.e1]));
+    g_timer.sum_ms[r.op] += ms;
+    g_timer.calls[r.op] += 1;
+  }
+  g_timer.recs.clear();
+  g_timer.used = 0;
+  for (int i = 0; i < n && i < BLK_N_OPS; ++i) {
+    calls[i] = g_timer.calls[i];
+    avg_us[i] = g_timer.calls[i] ? 1e3 * g_timer.sum_ms[i] / g_timer.calls[i] : 0.0;
+  }
   return BLK_OK;
 }
 
@@ -846,6 +935,23 @@ int blk_forward(const blk_config* cfg, const void* packed, int layer, int batch,
   if (batch * tokens <= kSkinnyMaxM && !small_plan_ok(*cfg, batch * tokens, true))
     return fail(BLK_EUNSUPPORTED, "hidden %d too wide for a %d-row chunk", cfg->hidden, batch * tokens);
   hipStream_t st = (hipStream_t)stream;
+  std::unique_lock<std::mutex> tlk(g_timer_mu, std::defer_lock);
+  if (g_timer.on) {
+    tlk.lock();
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing(st, &cs));
+    if (cs != hipStreamCaptureStatusNone)
+      return fail(BLK_ESTATE, "operator timing is on while the stream is being captured");
+    if (g_timer.used + BLK_N_OPS + 1 > kTimerMaxEvents)
+      return fail(BLK_ESIZE, "operator timing holds %zu events; read them with blk_operator_times",
+                  kTimerMaxEvents);
+    HIP_TRY(timer_event(st, &g_mark_prev));
+    g_mark_stream = st;
+    g_marking = true;
+  }
+  struct MarkReset {
+    ~MarkReset() { g_marking = false; }
+  } mark_reset;
   (void)hipGetLastError();
   if (want_persistent()) {
     StageArgs sa{};
@@ -865,6 +971,7 @@ int blk_forward(const blk_config* cfg, const void* packed, int layer, int batch,
       sa.vp[0] = v_prefix;
       sa.prefix_stride = prefix_stride;
       HIP_TRY(launch_stage(sa, nwg, st));
+      op_done(BLK_OP_STAGE);
       return BLK_OK;
     }
     if (g_exec_mode == 2) return fail(BLK_EUNSUPPORTED, "the persistent stage kernel does not cover this shape");

@@ -214,6 +214,40 @@ int blk_version(void);
  */
 int blk_set_execution_mode(int mode);
 
+/*
+ * Operator timing.  The operators of one block stage, in order:
+ */
+#define BLK_OP_QKV 0        /* RMS(x), fused QKV GEMM, RoPE epilogue              */
+#define BLK_OP_ATTENTION 1  /* chunk attention (and its key-slice merge)          */
+#define BLK_OP_O_PROJ 2     /* O projection + residual                            */
+#define BLK_OP_GATE_UP 3    /* RMS(h), gate/up GEMM, SiLU(gate) * up epilogue     */
+#define BLK_OP_DOWN 4       /* down projection + residual                         */
+#define BLK_OP_STAGE 5      /* the persistent stage kernel, as one operator       */
+#define BLK_N_OPS 6
+
+/*
+ * blk_set_operator_timing -- enable (1) or disable (0) operator timing,
+ * process-wide; either call discards what was accumulated.  While enabled,
+ * every blk_forward call records a HIP event (created without the system-scope
+ * fence, so no cache write-back is added) on its stream before its first
+ * kernel and after each operator's last kernel (the work itself is unchanged),
+ * so an operator's time is the interval between the event ahead of it and its
+ * own.  At most 4096 calls are held between reads (BLK_ESIZE from blk_forward
+ * beyond that); blk_forward on a stream under graph capture fails with
+ * BLK_ESTATE while timing is on.  flow_denoise records nothing.
+ * Errors: BLK_EINVAL for another value.
+ */
+int blk_set_operator_timing(int enable);
+
+/*
+ * blk_operator_times -- waits for the recorded events, adds their intervals
+ * to per-operator totals and writes, for operator i < min(n, BLK_N_OPS),
+ * avg_us[i] (host double, microseconds per call since timing was enabled) and
+ * calls[i] (host int, timed calls; 0 with avg_us[i] = 0 for an operator that
+ * never ran).  Errors: BLK_EINVAL (NULL arrays with n > 0, n < 0), BLK_EHIP.
+ */
+int blk_operator_times(double* avg_us, int* calls, int n);
+
 #ifdef __cplusplus
 }
 #endif

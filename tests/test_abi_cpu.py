@@ -157,3 +157,17 @@ def test_binding_raises_blk_error():
     with pytest.raises(blk.BlkError) as ei:
         blk.packed_bytes(cfg(head_dim=96), 1)
     assert ei.value.code == _lib.BLK_EUNSUPPORTED
+
+
+def test_operator_timing_arguments(lib):
+    assert lib.blk_set_operator_timing(2) == _lib.BLK_EINVAL
+    assert lib.blk_set_operator_timing(-1) == _lib.BLK_EINVAL
+    assert lib.blk_operator_times(None, None, 3) == _lib.BLK_EINVAL
+    assert lib.blk_operator_times(None, None, -1) == _lib.BLK_EINVAL
+    # nothing recorded: no device work, every operator reads as never run
+    blk.blk_set_operator_timing(True)
+    try:
+        assert blk.blk_operator_times() == {}
+    finally:
+        blk.blk_set_operator_timing(False)
+    assert len(_lib.OPERATORS) == 6

@@ -172,6 +172,37 @@ def test_block_is_deterministic():
             assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("shape", [synth.AE_BLOCK, synth.TINY,
+                                   synth.small_shape("tiled_1x150", tokens=150, prefix=70)],
+                         ids=lambda s: s.name)
+def test_operator_timing_changes_nothing(shape):
+    """Operator timing only adds events: the outputs are bit-identical and
+    every operator of the stage is timed once per call."""
+    import diffusion_transformer_block_amd as blk
+    case = synth.block_case(shape)
+    cfg = config_of(shape)
+    packed = blk.blk_prepare_weights(cfg, [synth.tree_to_device(case["weights"])])
+    x = stack_streams(case, "x")
+    kp, vp = stack_streams(case, "k_prefix"), stack_streams(case, "v_prefix")
+    ws = torch.zeros(blk.forward_workspace_bytes(cfg, shape.batch, shape.tokens, shape.prefix),
+                     dtype=torch.uint8, device="cuda")
+    ref = blk.blk_forward(cfg, packed, 0, x, kp, vp, ws=ws)
+    blk.blk_set_operator_timing(True)
+    try:
+        outs = [blk.blk_forward(cfg, packed, 0, x, kp, vp, ws=ws) for _ in range(3)]
+        times = blk.blk_operator_times()
+    finally:
+        blk.blk_set_operator_timing(False)
+    torch.cuda.synchronize()
+    for o in outs:
+        for a, b in zip(ref, o):
+            assert torch.equal(a, b)
+    assert set(times) == {"qkv_rope", "attention", "o_proj", "gate_up", "down"}
+    for name, (us, calls) in times.items():
+        assert calls == 3 and us > 0, (name, us, calls)
+    say(f"  {shape.name} operator us: " + ", ".join(f"{k} {v[0]:.1f}" for k, v in times.items()))
+
+
 def test_kv_append_into_cache():
     """k_new / v_new written straight into rows P..P+T-1 of the caller's cache."""
     import diffusion_transformer_block_amd as blk
