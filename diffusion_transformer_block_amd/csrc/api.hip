@@ -301,8 +301,8 @@ bool stage_plan(const blk_config& c, int B, int T, int P, int flow_N, int nwg, S
   if (nwg <= 0 || M <= 0 || M > kSkinnyMaxM) return false;
   if (flow_N > 0 && flow_N + 1 != M) return false;
   const int G_q = (Hq + 2 * Hkv) * d / 32, G_o = D / 32, G_gu = F / 16, G_d = D / 32;
-  // a block's first layer reads the caller's row-major input (staged per
-  // workgroup), which bounds the QKV split; later layers can use the same
+  // a block's first layer reads the caller's row-major input, later layers
+  // the operand-order buffers; both plan alike
   const SkPlan p_qkv = sk_plan(M, D, G_q, true), p_o = sk_plan(M, Hq * d, G_o, false),
                p_gu = sk_plan(M, D, G_gu, false), p_d = sk_plan(M, F, G_d, false),
                p_w3 = flow_N > 0 ? sk_plan(flow_N, D, G_o, false) : SkPlan{1, 1};
@@ -408,8 +408,7 @@ struct BlockIO {
   int64_t new_stride;
 };
 
-// Whether every skinny GEMM of a small chunk has a valid split (a row-major
-// block input is staged whole per workgroup, which bounds its K range).
+// Whether every skinny GEMM of a small chunk has a valid split.
 bool small_plan_ok(const blk_config& c, int M, bool x_rowmajor) {
   const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   return sk_plan(M, D, (Hq + 2 * Hkv) * d / 32, x_rowmajor).splits >= 1 &&

@@ -91,7 +91,6 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
   constexpr int NDT = HD / 32;                 // 32-row d tiles of O^T
   constexpr int CPR = HD / 8;                  // 16-byte chunks per key row
   constexpr int NCH = 64 * CPR / 256;          // chunks per thread per 64-key tile (K or V)
-  constexpr int IPT = 64 * CPR / 256;          // (row, chunk) items per thread of a 64-row block
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int l = tid & 63;
@@ -318,30 +317,53 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o, (size_t)MTo * 16 * a.Hq * HD * 2);
   const __amdgpu_buffer_rsrc_t rpo =
       make_rsrc(a.part_o + ((size_t)ks * n_rbt + rb_id) * slab, a.splits > 1 ? slab * 2 : 0);
+  // LPR = HD / 8 lanes share a row: lane c reads float4 c and LPR + c of
+  // both halves (adjacent lanes, adjacent 16 bytes: no LDS bank conflicts),
+  // combines each into four bf16 and swaps one 8-byte half with its
+  // neighbour, so even lane 2j ends with the row's 16-byte output chunk j and
+  // odd lane 2j + 1 with chunk LPR / 2 + j.  A wave covers 64 / LPR rows per
+  // pass, the workgroup's 4 waves the 64 rows in LPR / 4 passes.
+  constexpr int LPR = HD / 8, RPP = 64 / LPR, PASSES = LPR / 4;
+  const int c = l % LPR, odd = c & 1;
+  uint4 res[PASSES];
 #pragma unroll
-  for (int p = 0; p < IPT; ++p) {
-    const int i = tid + 256 * p, row = i / CPR, c = i - row * CPR;
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = (w + 4 * p) * RPP + l / LPR;
     const float2 h0 = sm.mlh[0][row], h1 = sm.mlh[1][row];
     const float mm = fmaxf(h0.x, h1.x);
     const float a0 = h0.x == -INFINITY ? 0.f : exp2f(h0.x - mm);
     const float a1 = h1.x == -INFINITY ? 0.f : exp2f(h1.x - mm);
     const float inv = 1.f / (h0.y * a0 + h1.y * a1);
-    const float* p0 = park + row * PROW + 8 * c;
+    const float s0 = a0 * inv, s1 = a1 * inv;
+    const float* p0 = park + row * PROW;
     const float* p1 = p0 + 64 * PROW;
-    const float4 x0 = *reinterpret_cast<const float4*>(p0), x1 = *reinterpret_cast<const float4*>(p0 + 4);
-    const float4 y0 = *reinterpret_cast<const float4*>(p1), y1 = *reinterpret_cast<const float4*>(p1 + 4);
-    const float f[8] = {(x0.x * a0 + y0.x * a1) * inv, (x0.y * a0 + y0.y * a1) * inv,
-                        (x0.z * a0 + y0.z * a1) * inv, (x0.w * a0 + y0.w * a1) * inv,
-                        (x1.x * a0 + y1.x * a1) * inv, (x1.y * a0 + y1.y * a1) * inv,
-                        (x1.z * a0 + y1.z * a1) * inv, (x1.w * a0 + y1.w * a1) * inv};
+    uint2 half[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int f4 = LPR * e + c;
+      const float4 x = *reinterpret_cast<const float4*>(p0 + 4 * f4);
+      const float4 y = *reinterpret_cast<const float4*>(p1 + 4 * f4);
+      half[e] = make_uint2(pack2(x.x * s0 + y.x * s1, x.y * s0 + y.y * s1),
+                           pack2(x.z * s0 + y.z * s1, x.w * s0 + y.w * s1));
+    }
+    const uint2 give = odd ? half[0] : half[1];
+    const uint2 got = make_uint2(__shfl_xor(give.x, 1), __shfl_xor(give.y, 1));
+    res[p] = odd ? make_uint4(got.x, got.y, half[1].x, half[1].y)
+                 : make_uint4(half[0].x, half[0].y, got.x, got.y);
+  }
+  // then all the stores (interleaved with the reads they would serialise them)
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = (w + 4 * p) * RPP + l / LPR;
+    const int ch = (c >> 1) + (odd ? LPR / 2 : 0);   // 16-byte chunk of the row
     if (a.splits == 1) {
       const int ar = 64 * rb + row;
       if (ar < rows) {
         const int t = ar / G, h = hk * G + (ar - t * G);
-        buf_st16(ro, (int)(fa_index(b * a.T + t, h * HD + 8 * c, MTo) * 2), pack8(f));
+        buf_st16(ro, (int)(fa_index(b * a.T + t, h * HD + 8 * ch, MTo) * 2), res[p]);
       }
     } else {
-      buf_st16(rpo, (row * HD + 8 * c) * 2, pack8(f));
+      buf_st16(rpo, (row * HD + 8 * ch) * 2, res[p]);
     }
   }
   if (a.splits == 1) return true;

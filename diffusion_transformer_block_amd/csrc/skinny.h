@@ -17,10 +17,10 @@
 //    per lane.
 //  * Activations: in operand order (fa_index in common.h: one contiguous
 //    1 KiB load per fragment), or row-major (the block's input, owned by the
-//    caller), which the workgroup first stages through LDS with row-contiguous
-//    16-byte loads, writing the fragments in operand order; the lane slot is
-//    XOR-swizzled with the k-tile so that both the staging writes and the
-//    operand reads are free of bank conflicts.
+//    caller), loaded straight into the same registers: lane l takes 16
+//    bytes of row l % 16 of the tile at column 8 (l / 16), four 64-byte row
+//    pieces per fragment, the rest of each 128-byte line served by L2 one
+//    k-tile later.  Either way the loads ride the weights' pipeline.
 //  * The four waves split the K-range; each keeps a ring of NB k-tiles of
 //    loads in flight ahead of its MFMAs (weights of the first NB k-tiles are
 //    issued before the task's wait, since they do not depend on earlier work).
@@ -38,7 +38,6 @@
 
 namespace blk {
 
-constexpr int kSkMaxStage = 128;    // KiB of row-major activations staged per workgroup
 constexpr int kSkMaxSplits = 16;
 constexpr int kSkMaxGpw = 2;        // 32-column groups per workgroup
 // Two groups per workgroup measured slower on every 64-row shape of the AE
@@ -63,10 +62,7 @@ struct SkArgs {
 
 template <bool AROW, int GPW>
 struct SkSmem {
-  union {
-    uint4 astage[AROW ? kSkMaxStage * 64 : 1];  // row-major activations in operand order
-    f32x4 red[4][4 * GPW * 2 * 64];            // per-wave accumulators in MFMA C order
-  };
+  f32x4 red[4][4 * GPW * 2 * 64];              // per-wave accumulators in MFMA C order
   float tile[64 * sk_tile_stride(GPW)];        // summed tile [row][col]
   float ss[4][64];
   float rrow[64];
@@ -84,11 +80,6 @@ __device__ __forceinline__ float sumsq8(uint4 v) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) s = fmaf(x[i], x[i], s);
   return s;
-}
-
-// operand-order slot of (k-tile u, row tile mt, lane) in the LDS staging area
-__device__ __forceinline__ int stage_slot(int u, int mt, int lane, int MT) {
-  return (u * MT + mt) * 64 + (lane & 48) + ((lane & 15) ^ (u & 15));
 }
 
 // Runs one task -- groups [GPW gb, GPW gb + GPW) over split s -- and stores
@@ -126,79 +117,35 @@ __device__ bool sk_task(const SkArgs& ga, const Epi& epi, int gb, int s, SkSmem<
       bw[b][j][1] = buf_ld_stream(rb, o + kFragBytes);
     }
   };
-  // ---- activations: row-major input is staged through LDS; without a
-  //      producing step to wait for (a standalone launch) its loads go out
-  //      before the weights', so that writing the stage does not wait for the
-  //      slower weight stream (loads complete in issue order)
-  constexpr bool kEarlyStage = AROW && std::is_same<std::decay_t<Wait>, NoWait>::value;
-  // stage rows [0, M) x k-tiles [kb, kb + KTS) in operand order: one batch of
-  // at most 32 row-contiguous 16-byte loads per thread (the slab is at most
-  // kSkMaxStage KiB), rows past M clamped to M - 1 and not stored
-  const int nck = KTS * 4;                       // 16-byte chunks per row
-  const int nl = AROW ? (ga.M * nck + 255) >> 8 : 0;   // loads per thread, <= 32 (uniform)
-  const int dr = 256 / nck, dc = 256 - dr * nck; // (row, chunk) step per load
-  const int r0 = tid / nck, c0 = tid - r0 * nck;
-  uint4 sv[AROW ? 32 : 1];
-  auto stage_issue = [&]() {
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(ga.A, (size_t)ga.M * ga.lda * 2);
-    int r = r0, c = c0;
-#pragma unroll
-    for (int j = 0; j < (AROW ? 32 : 0); ++j) {
-      if (j < nl) {
-        sv[j] = buf_ld_act(rx, (min(r, ga.M - 1) * ga.lda + kb * 32 + c * 8) * 2);
-        r += dr;
-        c += dc;
-        if (c >= nck) {
-          c -= nck;
-          ++r;
-        }
-      }
-    }
-  };
-  auto stage_write = [&]() {
-    int r = r0, c = c0;
-#pragma unroll
-    for (int j = 0; j < (AROW ? 32 : 0); ++j) {
-      if (j < nl) {
-        if (r < ga.M) sm.astage[stage_slot(c >> 2, r >> 4, (r & 15) + 16 * (c & 3), MT)] = sv[j];
-        r += dr;
-        c += dc;
-        if (c >= nck) {
-          c -= nck;
-          ++r;
-        }
-      }
-    }
-    __syncthreads();
-  };
-  if (kEarlyStage) stage_issue();
 #pragma unroll
   for (int b = 0; b < NB; ++b) issue_w(b, b);
   if (!wait()) return false;
   typename Epi::Pre pre[GPW];
 #pragma unroll
   for (int j = 0; j < GPW; ++j) pre[j] = epi.prefetch(g0 + min(j, ng - 1), ga.M);
-  if (AROW) {
-    if (!kEarlyStage) stage_issue();
-    stage_write();
-  }
+  // ---- activations: an A fragment is 16 bytes per lane either way -- one
+  //      contiguous 1 KiB fragment in operand order, or (row-major input)
+  //      16 bytes of row lr of each 16-row tile, rows past M clamped to
+  //      M - 1 (their results are never stored)
   uint4 av[NB][MT];
   __amdgpu_buffer_rsrc_t ra;
-  int aoff = 0;
-  if (!AROW) {
+  int aoff[MT];
+  if (AROW) {
+    ra = make_rsrc(ga.A, (size_t)ga.M * ga.lda * 2);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      aoff[mt] = (min(16 * mt + lr, ga.M - 1) * ga.lda + (kb + uw) * 32 + 8 * (l >> 4)) * 2;
+  } else {
     ra = make_rsrc(ga.A, (size_t)KT * MT * kFragBytes);
-    aoff = ((kb + uw) * MT * 64 + l) * 16;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) aoff[mt] = ((kb + uw) * MT * 64 + l) * 16 + mt * kFragBytes;
   }
   auto issue_a = [&](int b, int u) {
-    if (!AROW) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) av[b][mt] = buf_ld_act(ra, aoff + (u * MT + mt) * kFragBytes);
-    }
+    for (int mt = 0; mt < MT; ++mt)
+      av[b][mt] = buf_ld_act(ra, aoff[mt] + u * (AROW ? 64 : MT * kFragBytes));
   };
-  auto get_a = [&](int b, int u, int mt) -> uint4 {
-    if (AROW) return sm.astage[stage_slot(uw + u, mt, l, MT)];
-    return av[b][mt];
-  };
+  auto get_a = [&](int b, int, int mt) -> uint4 { return av[b][mt]; };
 
   f32x4 acc[MT][GPW][2];
   float ss[MT];
@@ -235,7 +182,7 @@ __device__ bool sk_task(const SkArgs& ga, const Epi& epi, int gb, int s, SkSmem<
   }
 
   // ---- the four waves' tiles -> summed tile [row][col] in LDS
-  __syncthreads();   // staging reads (and a previous task's readers) are done
+  __syncthreads();   // a previous task's readers of sm are done
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -357,9 +304,23 @@ struct EpiQkvS {
   const float* cos_t;   // [max_pos][d/2]
   const float* sin_t;
   int T, P, Hq, Hkv, d;
-  struct Pre {};
-  __device__ Pre prefetch(int, int) const { return {}; }
-  __device__ void run(const float* tile, int ts, const float* rrow, bool rms, int g, int M, const Pre&) const {
+  // this thread's cos / sin quadruple, loaded while the GEMM runs
+  struct Pre {
+    float4 cs, sn;
+  };
+  __device__ Pre prefetch(int g, int M) const {
+    const int t = threadIdx.x, r = t >> 2;
+    const int gpr = d >> 5;
+    Pre p{make_float4(1.f, 1.f, 1.f, 1.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+    if (r < M && g < (Hq + Hkv) * gpr) {
+      const int tt = r % T, head = g / gpr;
+      const size_t ti = (size_t)(P + tt) * (d >> 1) + 16 * (g - head * gpr) + (t & 3) * 4;
+      p.cs = *reinterpret_cast<const float4*>(cos_t + ti);
+      p.sn = *reinterpret_cast<const float4*>(sin_t + ti);
+    }
+    return p;
+  }
+  __device__ void run(const float* tile, int ts, const float* rrow, bool rms, int g, int M, const Pre& pf) const {
     const int t = threadIdx.x;
     const int r = t >> 2;
     if (r >= M) return;
@@ -372,10 +333,7 @@ struct EpiQkvS {
       const int head = g / gpr;
       const int half = d >> 1;
       const int j0 = 16 * (g - head * gpr) + q4;
-      const size_t ti = (size_t)(P + tt) * half + j0;
-      const float4 cs = *reinterpret_cast<const float4*>(cos_t + ti);
-      const float4 sn = *reinterpret_cast<const float4*>(sin_t + ti);
-      const float c4[4] = {cs.x, cs.y, cs.z, cs.w}, s4[4] = {sn.x, sn.y, sn.z, sn.w};
+      const float c4[4] = {pf.cs.x, pf.cs.y, pf.cs.z, pf.cs.w}, s4[4] = {pf.sn.x, pf.sn.y, pf.sn.z, pf.sn.w};
       float lo[4], hi[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {

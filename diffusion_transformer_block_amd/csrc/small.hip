@@ -28,16 +28,20 @@ int device_cus() {
 }
 
 // Cost model of a skinny GEMM plan (K splits x 32-column groups per
-// workgroup), from measurements on this chip with 16-byte loads:
+// workgroup), fitted to a sweep of every (split, groups) plan of the 64-row
+// O, down, gate/up and QKV shapes on this chip (within ~0.5 us of each):
 //  * one compute unit streams about 90 GB/s of operands;
 //  * the activation slab, re-read by every workgroup from L2, is served at
 //    about 9.4 TB/s in aggregate;
 //  * the weights stream from HBM at about 5 TB/s;
-//  * a K split's hand-off (publish, count, reload) costs about 2 us;
+//  * K splits add a hand-off (publish, count, reload in split order) of
+//    about 1 us plus 0.35 us per split;
 //  * workgroups beyond one per compute unit run in further rounds.
-constexpr double kCuBytesPerUs = 90e3, kL2BytesPerUs = 9.4e6, kHbmBytesPerUs = 5e6, kSplitUs = 2.0;
+constexpr double kCuBytesPerUs = 90e3, kL2BytesPerUs = 9.4e6, kHbmBytesPerUs = 5e6;
+constexpr double kSplitUs = 1.0, kSplitPerUs = 0.35;
 
 SkPlan sk_plan(int M, int K, int n_groups, bool a_rowmajor) {
+  (void)a_rowmajor;   // both activation layouts stream alike
   const int KT = K / 32, MT = mt_of(M);
   const int n_cu = device_cus();
   SkPlan best{-1, 1};
@@ -48,13 +52,12 @@ SkPlan sk_plan(int M, int K, int n_groups, bool a_rowmajor) {
       if (KT % (4 * s) != 0) break;
       const int n_wg = n_groups / gpw * s;
       if (s > 1 && n_wg > n_cu) break;
-      if (a_rowmajor && (KT / s) * MT > kSkMaxStage) continue;
       const double per_wg = (double)(2 * gpw + MT) * (KT / s) * kFragBytes;
       const double a_all = (double)n_wg * MT * (KT / s) * kFragBytes;
       const double w_all = 2.0 * n_groups * KT * kFragBytes;
       double t = std::max(per_wg / kCuBytesPerUs, std::max(a_all / kL2BytesPerUs, w_all / kHbmBytesPerUs));
       t *= (n_wg + n_cu - 1) / n_cu;
-      if (s > 1) t += kSplitUs;
+      if (s > 1) t += kSplitUs + kSplitPerUs * s;
       if (t < best_t - 1e-9) {
         best_t = t;
         best = SkPlan{s, gpw};
