@@ -903,6 +903,12 @@ int blk_forward(const blk_config* cfg, const void* packed, int layer, int batch,
     return fail(BLK_EUNSUPPORTED, "prefix + tokens = %ld exceeds max_pos %d",
                 (long)prefix + tokens, cfg->max_pos);
   if ((long)batch * tokens > (1L << 24)) return fail(BLK_EUNSUPPORTED, "batch * tokens too large");
+  {
+    // the large-chunk kernels address an activation matrix with 32-bit byte offsets
+    const long widest = std::max({(long)cfg->hidden, (long)cfg->ffn, (long)cfg->n_q_heads * cfg->head_dim});
+    if ((long)batch * tokens * widest > (1L << 30))
+      return fail(BLK_EUNSUPPORTED, "batch * tokens * max(hidden, ffn, Hq d) exceeds 2^30");
+  }
   const BlockWs w = block_ws_layout(*cfg, batch, tokens, prefix, 0);
   if (!ws) {
     *ws_bytes = w.total;

@@ -42,44 +42,68 @@ void launch_flow_embed(const FlowEmbedArgs& a, hipStream_t st) {
   flow_embed_kernel<<<dim3((a.D + 255) / 256, a.N + 1), 256, 0, st>>>(a);
 }
 
-// One block per action row i: r = RMS(X[i + 1]); v[a] = r sum_k X[i+1][k] W_out'[k][a]
-// + b_out[a]; a_out[i][a] = a_in[i][a] + dt v[a].  256 threads = (A columns)
-// x (256 / A) slices of k, reduced through LDS in a fixed order.  X is in
-// operand order (fa_index, N + 1 rows).
+// One block per action row i: r = RMS(X[i + 1]); v[c] = r sum_k X[i+1][k] W_out'[k][c]
+// + b_out[c]; a_out[i][c] = a_in[i][c] + dt v[c].  Thread t takes k = t, t + 256, ...
+// and up to 32 columns at a time in registers, so all of its loads are independent
+// (one memory round trip); the 256 partial rows are summed through LDS in a fixed
+// order.  X is in operand order (fa_index, N + 1 rows).
 __global__ __launch_bounds__(256) void flow_velocity_kernel(FlowVelArgs a) {
-  __shared__ float xs[8192];
-  __shared__ float red[256];
+  constexpr int CW = 32;              // columns per pass
+  __shared__ float red[256][CW + 1];
+  __shared__ float part[8][CW];
   __shared__ float wsum[4];
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
   const int MT = mt_of(a.N + 1);
+  const int nk = (a.D + 255) / 256;   // k values per thread (D <= 8192: <= 32)
+  float xk[32];
   float ss = 0.f;
-  for (int k = tid; k < a.D; k += 256) {
-    const float v = bf2f(a.X[fa_index(i + 1, k, MT)]);
-    xs[k] = v;
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int k = tid + 256 * j;
+    xk[j] = (j < nk && k < a.D) ? bf2f(a.X[fa_index(i + 1, k, MT)]) : 0.f;
+    ss = fmaf(xk[j], xk[j], ss);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
   if ((tid & 63) == 0) wsum[tid >> 6] = ss;
   __syncthreads();
   const float r = rsqrtf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) / (float)a.D + a.eps);
-  const int nsl = 256 / a.A;          // k slices
-  const int col = tid % a.A, sl = tid / a.A;
-  float acc = 0.f;
-  if (sl < nsl) {
-    const int kper = (a.D + nsl - 1) / nsl;
-    const int k0 = sl * kper, k1 = min(a.D, k0 + kper);
-    for (int k = k0; k < k1; ++k) acc = fmaf(xs[k], a.w_out[(size_t)k * a.A + col], acc);
-  }
-  red[tid] = acc;
-  __syncthreads();
-  if (tid < a.A) {
-    float v = 0.f;
-    for (int q = 0; q < nsl; ++q) v += red[q * a.A + tid];
-    v = v * r + a.b_out[tid];
-    const float dt = *a.dt;
-    a.a_out[(size_t)i * a.A + tid] = a.a_in[(size_t)i * a.A + tid] + dt * v;
+  const float dt = *a.dt;
+  for (int c0 = 0; c0 < a.A; c0 += CW) {
+    const int nc = min(CW, a.A - c0);
+    float acc[CW];
+#pragma unroll
+    for (int c = 0; c < CW; ++c) acc[c] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {   // unrolled: xk stays in registers
+      const int k = tid + 256 * j;
+      if (j < nk && k < a.D) {
+        const float* wr = a.w_out + (size_t)k * a.A + c0;
+#pragma unroll
+        for (int c = 0; c < CW; ++c)
+          if (c < nc) acc[c] = fmaf(xk[j], wr[c], acc[c]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CW; ++c) red[tid][c] = acc[c];
+    __syncthreads();
+    {
+      const int c = tid & (CW - 1), g = tid >> 5;
+      float v = 0.f;
+      for (int q = 0; q < 32; ++q) v += red[32 * g + q][c];
+      part[g][c] = v;
+    }
+    __syncthreads();
+    if (tid < nc) {
+      float v = 0.f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) v += part[g][tid];
+      v = v * r + a.b_out[c0 + tid];
+      const size_t o = (size_t)i * a.A + c0 + tid;
+      a.a_out[o] = a.a_in[o] + dt * v;
+    }
+    __syncthreads();
   }
 }
 

@@ -10,130 +10,191 @@
 // a GEMM is bound by reading its bf16 weights.
 //
 // The large-chunk GEMM (M > 64 rows; chunks of <= 64 rows run the skinny
-// GEMM of skinny.h):
-//  * tiled_gemm: 128 x 128 output tile per workgroup, K step 64,
-//    A (activations) staged through double-buffered LDS, B (packed weight
-//    fragments) loaded straight into registers one step ahead; 2 x 2 waves of
-//    64 x 64 each.
+// GEMM of skinny.h): 256 x 256 (or 128 x 128) output tiles, both operands
+// moved into LDS by the buffer-load DMA as MFMA fragments, 2 x 2 waves of
+// 16 x 16 x 32 MFMAs, XCD-aware tile order (big_gemm_kernel below).
 #include "common.h"
 #include "internal.h"
 #include "skinny.h"
 
 namespace blk {
 
-// ============================================================================ tiled
-template <class Epi>
-__global__ __launch_bounds__(256) void tiled_gemm_kernel(GemmArgs ga, Epi epi) {
-  constexpr int BM = 128, BK = 64, LDS_ROW = BK + 8;
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDS_ROW];
+// ============================================================================ large-chunk GEMM
+// LDS DMA of one 1 KiB fragment: lane l's 16 bytes at voffset land at lds + 16 l.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0,
+                                           0, 0);
+}
 
+// BM x BN output tile per workgroup (4 waves in a 2 x 2 grid), K steps of 64.
+// Each stage holds the tile's A and B operands in LDS as 1 KiB MFMA
+// fragments -- A (row-major activations) gathered by the DMA as 16 rows x
+// 64 bytes per fragment, B (packed weights) one contiguous fragment each --
+// in two buffers: a wave reads all of its fragments of the current stage
+// into registers, then issues the next stage's DMA (after its reads, so they
+// do not wait on it), then runs its MFMAs.
+template <int BM, int BN, class Epi>
+__global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int n_tm) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t big_dsm[];
+  constexpr int BK = 64;
+  constexpr int MTB = BM / 16;            // 16-row tiles per block
+  constexpr int GB = BN / 32;             // 32-column groups per block
+  constexpr int MTW = MTB / 2, GW = GB / 2;
+  constexpr int AFR = MTB * 2, BFR = GB * 4, NFR = AFR + BFR;
+  constexpr int STAGE = NFR * kFragBytes;
+  constexpr int PER = NFR / 4;            // fragments each wave moves per stage
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
   const int wm = w >> 1, wn = w & 1;
-  const int nb = blockIdx.x, mb = blockIdx.y;
-  const int KT = ga.K >> 5;
-  const int nsteps = ga.K / BK;
+  // The hardware deals workgroups round-robin over the 8 XCDs: give each XCD
+  // a contiguous run of tiles, taken in bands of GM row tiles with the column
+  // tiles outer, so the tiles an XCD runs at once share row and column blocks
+  // in its L2.
+  const int nwg = gridDim.x, id = blockIdx.x;
+  const int xcd = id & 7, jx = id >> 3, qx = nwg >> 3, rx = nwg & 7;
+  const int tile = xcd * qx + min(xcd, rx) + jx;
+  constexpr int GM = 4;
+  const int n_tn = nwg / n_tm;
+  const int band = tile / (GM * n_tn), tib = tile - band * GM * n_tn;
+  const int rows_b = min(GM, n_tm - band * GM);
+  const int tm = band * GM + tib % rows_b, tn = tib / rows_b;
+  const int m0 = tm * BM, g0 = tn * GB;
+  const int KT = ga.K >> 5, nk = ga.K / BK;
 
-  const bf16_t* ag[4];
-  int lds_off[4];
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(ga.A, (size_t)ga.M * ga.lda * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(ga.Bp, (size_t)ga.n_groups * KT * 2 * kFragBytes);
+  // this wave's fragments of a stage: f = w + 4 i (A fragments first); rows
+  // and groups past the matrix are clamped (their results are not stored)
+  int voff[PER];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int cidx = tid + 256 * q;
-    const int row = cidx >> 3, col = (cidx & 7) * 8;
-    const int grow = min(mb * BM + row, ga.M - 1);
-    ag[q] = ga.A + (size_t)grow * ga.lda + col;
-    lds_off[q] = row * LDS_ROW + col;
+  for (int i = 0; i < PER; ++i) {
+    const int f = w + 4 * i;
+    if (f < AFR) {
+      const int kt = f / MTB, mt = f - kt * MTB;
+      const int row = min(m0 + 16 * mt + (l & 15), ga.M - 1);
+      voff[i] = (row * ga.lda + 32 * kt + 8 * (l >> 4)) * 2;
+    } else {
+      const int fb = f - AFR, gg = fb >> 2, kt = (fb >> 1) & 1, ii = fb & 1;
+      voff[i] = (int)frag_offset(min(g0 + gg, ga.n_groups - 1), kt, ii, KT) + 16 * l;
+    }
   }
-  const uint4* bg[2];
+  auto issue = [&](int s, int buf) {
+    uint8_t* base = big_dsm + buf * STAGE;
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    const int gq = min(4 * nb + 2 * wn + gi, ga.n_groups - 1);
-    bg[gi] = reinterpret_cast<const uint4*>(ga.Bp + frag_offset(gq, 0, 0, KT)) + l;
-  }
+    for (int i = 0; i < PER; ++i) {
+      const int f = w + 4 * i;
+      if (f < AFR) dma16(ra, base + f * kFragBytes, voff[i] + s * BK * 2);
+      else dma16(rb, base + f * kFragBytes, voff[i] + s * 2 * 2 * kFragBytes);
+    }
+  };
 
-  uint4 areg[4], breg[2][2][2];
+  f32x4 acc[MTW][GW][2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) areg[q] = *reinterpret_cast<const uint4*>(ag[q]);
+  for (int a = 0; a < MTW; ++a)
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int i = 0; i < 2; ++i) breg[gi][kk][i] = bg[gi][(kk * 2 + i) * 64];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(&As[0][lds_off[q]]) = areg[q];
+    for (int b = 0; b < GW; ++b) {
+      acc[a][b][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[a][b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-
-  f32x4 acc[4][4];
+  for (int s = 0; s < nk; ++s) {
+    const int cur = s & 1;
+    const uint8_t* base = big_dsm + cur * STAGE;
+    uint4 af[2][MTW], bfv[2][GW][2];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int step = 0; step < nsteps; ++step) {
-    const int cur = step & 1;
-    const bool more = step + 1 < nsteps;
-    uint4 bnext[2][2][2];
-    if (more) {
+      for (int mt = 0; mt < MTW; ++mt)
+        af[kt][mt] =
+            *reinterpret_cast<const uint4*>(base + (kt * MTB + wm * MTW + mt) * kFragBytes + 16 * l);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        areg[q] = *reinterpret_cast<const uint4*>(ag[q] + (size_t)(step + 1) * BK);
+      for (int gg = 0; gg < GW; ++gg)
 #pragma unroll
-      for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-            bnext[gi][kk][i] = bg[gi][(((step + 1) * 2 + kk) * 2 + i) * 64];
+        for (int ii = 0; ii < 2; ++ii)
+          bfv[kt][gg][ii] = *reinterpret_cast<const uint4*>(
+              base + (AFR + (wn * GW + gg) * 4 + kt * 2 + ii) * kFragBytes + 16 * l);
     }
+    if (s + 1 < nk) issue(s + 1, cur ^ 1);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const uint4 af = *reinterpret_cast<const uint4*>(
-            &As[cur][(64 * wm + 16 * mt + lr) * LDS_ROW + 32 * kk + 8 * lg]);
+      for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
+        for (int gg = 0; gg < GW; ++gg)
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
-            acc[mt][2 * gi + i] =
-                mfma16(as_bf16x8(af), as_bf16x8(breg[gi][kk][i]), acc[mt][2 * gi + i]);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(&As[cur ^ 1][lds_off[q]]) = areg[q];
-#pragma unroll
-      for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int i = 0; i < 2; ++i) breg[gi][kk][i] = bnext[gi][kk][i];
-    }
-    __syncthreads();
+          for (int ii = 0; ii < 2; ++ii)
+            acc[mt][gg][ii] = mfma16(as_bf16x8(af[kt][mt]), as_bf16x8(bfv[kt][gg][ii]), acc[mt][gg][ii]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next stage has landed
+    __syncthreads();                                    // and every wave is done with this one
   }
 
+  // ---- epilogue, 32 rows of the wave's tile at a time: math() in the MFMA
+  //      layout into this wave's LDS region, then 16-byte row stores
+  constexpr int LROW = 32 * GW + 4;       // floats per staged row
+  constexpr int SC = Epi::SLOT_CHUNKS;
+  float* stg = reinterpret_cast<float*>(big_dsm) + w * 32 * LROW;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int pass = 0; pass < MTW / 2; ++pass) {
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      const int g = 4 * nb + 2 * wn + gi;
-      if (g >= ga.n_groups) continue;
+    for (int mh = 0; mh < 2; ++mh) {
+      const int mt = 2 * pass + mh;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int row = mb * BM + 64 * wm + 16 * mt + 4 * lg + j;
-        if (row < ga.M) {
-          const float r = ga.r ? ga.r[row] : 1.f;
-          epi.store(row, g, lr, acc[mt][2 * gi][j], acc[mt][2 * gi + 1][j], r);
+        const int rl = 16 * mh + 4 * (l >> 4) + j;
+        const int row = min(m0 + wm * (BM / 2) + 16 * mt + 4 * (l >> 4) + j, ga.M - 1);
+        const float r = ga.r ? ga.r[row] : 1.f;
+#pragma unroll
+        for (int gg = 0; gg < GW; ++gg) {
+          const int g = min(g0 + wn * GW + gg, ga.n_groups - 1);
+          const float2 o = epi.math(row, g, l & 15, acc[mt][gg][0][j], acc[mt][gg][1][j], r);
+          stg[rl * LROW + 32 * gg + (l & 15)] = o.x;
+          stg[rl * LROW + 32 * gg + 16 + (l & 15)] = o.y;
         }
       }
     }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 32 * GW * SC / 64; ++it) {
+      const int idx = it * 64 + l;
+      const int rl = idx / (GW * SC), rem = idx - rl * (GW * SC);
+      const int gg = rem / SC, qc = rem - gg * SC;
+      const int row = m0 + wm * (BM / 2) + 32 * pass + rl;
+      const int g = g0 + wn * GW + gg;
+      const float4 lo = *reinterpret_cast<const float4*>(&stg[rl * LROW + 32 * gg + 8 * qc]);
+      const float4 hi = *reinterpret_cast<const float4*>(&stg[rl * LROW + 32 * gg + 8 * qc + 4]);
+      const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      if (row < ga.M && g < ga.n_groups) epi.store8(row, g, qc, v);
+    }
+    __syncthreads();
+  }
 }
 
+template <int BM, int BN, class Epi>
+static void launch_big(const GemmArgs& ga, const Epi& e, hipStream_t st) {
+  constexpr int NFR = (BM / 16) * 2 + (BN / 32) * 4;
+  const size_t smem = 2 * (size_t)NFR * kFragBytes;
+  auto kern = big_gemm_kernel<BM, BN, Epi>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    attr_set = true;
+  }
+  const int n_tm = (ga.M + BM - 1) / BM, n_tn = (ga.n_groups + BN / 32 - 1) / (BN / 32);
+  hipLaunchKernelGGL(kern, dim3(n_tm * n_tn), dim3(256), smem, st, ga, e, n_tm);
+}
+
+// 256 x 256 tiles where they fill the chip (about one workgroup per compute
+// unit or more), 128 x 128 otherwise.
 template <class Epi>
 static void launch_tiled(const GemmArgs& ga, const Epi& e, hipStream_t st) {
-  dim3 grid((ga.n_groups + 3) / 4, (ga.M + 127) / 128);
-  tiled_gemm_kernel<Epi><<<grid, 256, 0, st>>>(ga, e);
+  const long big_tiles = (long)((ga.M + 255) / 256) * ((ga.n_groups + 7) / 8);
+  if (big_tiles >= (long)device_cus() * 15 / 16) launch_big<256, 256>(ga, e, st);
+  else launch_big<128, 128>(ga, e, st);
 }
 
 // ============================================================================ dispatch

@@ -35,15 +35,18 @@ void launch_widen(const bf16_t* in, const float* gain, int cols, size_t n, float
 void launch_copy_f32(const float* in, size_t n, float* out, hipStream_t st);
 
 // ---------------------------------------------------------------- GEMM epilogues
-// Each epilogue receives one output pair: row m, group g, column c < 16 inside
-// the group's tiles, the fp32 sums v0 (tile 0) and v1 (tile 1), and the row
-// scale r (the RMS statistic, or 1 when the GEMM has no norm ahead of it).
-// store1 takes a single tile i of group g (only for plain column groups).
-// Loads of activations and all stores are device-coherent, so a consumer
-// workgroup of the same persistent kernel can read them.
+// The large-chunk GEMM finishes a tile in two phases.  math() sees one output
+// pair in the MFMA layout -- row m, group g, column c < 16 inside the group's
+// two tiles, their fp32 sums v0 (tile 0) and v1 (tile 1), the row scale r (the
+// RMS statistic, or 1) -- and returns the group's output slots c and 16 + c
+// (fp32).  The slots go through LDS, and store8() then writes 8 consecutive
+// slots (8 q .. 8 q + 7, q < 4 of the group's 32; q < SLOT_CHUNKS) of row m
+// with one 16-byte store.  The stores are plain: the next kernel reads them.
 
-// Fused QKV: scale by r, rotate (Q, K) pairs, scatter into Q / K_new / V_new.
+// Fused QKV: scale by r, rotate (Q, K) pairs (slot c = column j, slot 16 + c
+// = column j + d/2 of the rotated head), scatter into Q / K_new / V_new.
 struct EpiQKV {
+  static constexpr int SLOT_CHUNKS = 4;
   bf16_t* q;            // [M][Hq d]
   bf16_t* kn;           // stream b at b * new_stride, [T][Hkv][d]
   bf16_t* vn;
@@ -52,59 +55,63 @@ struct EpiQKV {
   const float* sin_t;
   int T, P, Hq, Hkv, d;
 
-  __device__ __forceinline__ void store(int m, int g, int c, float v0, float v1, float r) const {
-    const int b = m / T, t = m - b * T;
-    const int gpr = d >> 5;
-    const int n_rot_groups = (Hq + Hkv) * d / 32;
+  __device__ __forceinline__ float2 math(int m, int g, int c, float v0, float v1, float r) const {
     v0 *= r;
     v1 *= r;
+    const int gpr = d >> 5;
+    if (g >= (Hq + Hkv) * gpr) return make_float2(v0, v1);
+    const int t = m % T;
+    const int j = 16 * (g % gpr) + c;  // < d/2
+    const size_t ti = (size_t)(P + t) * (d >> 1) + j;
+    const float cs = cos_t[ti], sn = sin_t[ti];
+    return make_float2(v0 * cs - v1 * sn, v0 * sn + v1 * cs);
+  }
+  __device__ __forceinline__ void store8(int m, int g, int qc, const float* v) const {
+    const int b = m / T, t = m - b * T;
+    const int gpr = d >> 5, n_rot_groups = (Hq + Hkv) * gpr;
+    bf16_t* dst;
     if (g < n_rot_groups) {
       const int head = g / gpr;
-      const int j = 16 * (g - head * gpr) + c;  // < d/2
-      const int half = d >> 1;
-      const size_t ti = (size_t)(P + t) * half + j;
-      const float cs = cos_t[ti], sn = sin_t[ti];
-      const float lo = v0 * cs - v1 * sn;
-      const float hi = v0 * sn + v1 * cs;
-      bf16_t* dst;
-      if (head < Hq) {
-        dst = q + (size_t)m * Hq * d + (size_t)head * d;
-      } else {
-        dst = kn + (size_t)b * new_stride + ((size_t)t * Hkv + (head - Hq)) * d;
-      }
-      st_act(dst + j, lo);
-      st_act(dst + j + half, hi);
+      const int col = 16 * (g - head * gpr) + (qc & 1) * 8 + (qc >> 1) * (d >> 1);
+      dst = head < Hq ? q + (size_t)m * Hq * d + (size_t)head * d + col
+                      : kn + (size_t)b * new_stride + ((size_t)t * Hkv + (head - Hq)) * d + col;
     } else {
-      const int col0 = 32 * (g - n_rot_groups) + c;
-      bf16_t* base = vn + (size_t)b * new_stride + (size_t)t * Hkv * d;
-      st_act(base + col0, v0);       // V row layout [Hkv][d] is contiguous in col
-      st_act(base + col0 + 16, v1);
+      dst = vn + (size_t)b * new_stride + (size_t)t * Hkv * d + 32 * (g - n_rot_groups) + 8 * qc;
     }
+    *reinterpret_cast<uint4*>(dst) = pack8(v);
   }
 };
 
 // out[m][n] = res[m][n] + acc (residual add; O projection and down projection).
 struct EpiResidual {
+  static constexpr int SLOT_CHUNKS = 4;
   const bf16_t* res;
   bf16_t* out;
   int ld;
-  __device__ __forceinline__ void store(int m, int g, int c, float v0, float v1, float) const {
-    const size_t o = (size_t)m * ld + 32 * g + c;
-    st_act(out + o, ld_act(res + o) + v0);
-    st_act(out + o + 16, ld_act(res + o + 16) + v1);
+  __device__ __forceinline__ float2 math(int, int, int, float v0, float v1, float) const {
+    return make_float2(v0, v1);
   }
-  __device__ __forceinline__ void store1(int m, int g, int i, int c, float v, float) const {
-    const size_t o = (size_t)m * ld + 32 * g + 16 * i + c;
-    st_act(out + o, ld_act(res + o) + v);
+  __device__ __forceinline__ void store8(int m, int g, int qc, const float* v) const {
+    const size_t o = (size_t)m * ld + 32 * g + 8 * qc;
+    float x[8];
+    unpack8(*reinterpret_cast<const uint4*>(res + o), x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] += v[e];
+    *reinterpret_cast<uint4*>(out + o) = pack8(x);
   }
 };
 
-// out[m][j] = SiLU(r * gate) * (r * up), j = 16 g + c (gate/up interleave).
+// out[m][j] = SiLU(r * gate) * (r * up), j = 16 g + c (gate/up interleave):
+// 16 slots per group.
 struct EpiGateUp {
+  static constexpr int SLOT_CHUNKS = 2;
   bf16_t* out;
   int ld;
-  __device__ __forceinline__ void store(int m, int g, int c, float v0, float v1, float r) const {
-    st_act(out + (size_t)m * ld + 16 * g + c, silu(v0 * r) * (v1 * r));
+  __device__ __forceinline__ float2 math(int, int, int, float v0, float v1, float r) const {
+    return make_float2(silu(v0 * r) * (v1 * r), 0.f);
+  }
+  __device__ __forceinline__ void store8(int m, int g, int qc, const float* v) const {
+    *reinterpret_cast<uint4*>(out + (size_t)m * ld + 16 * g + 8 * qc) = pack8(v);
   }
 };
 

@@ -156,7 +156,8 @@ int blk_prepare_weights(const blk_config* cfg, const blk_layer_src* layers, int 
  * position P + t; no attention mask (every query sees all P + T keys).
  * `packed` must come from blk_prepare_weights with an identical cfg; `layer`
  * selects the layer.  Errors: BLK_EINVAL (also misaligned buffers or strides),
- * BLK_EUNSUPPORTED (P + T > max_pos),
+ * BLK_EUNSUPPORTED (P + T > max_pos; batch * tokens * max(hidden, ffn, Hq d)
+ * above 2^30),
  * BLK_ESIZE (ws too small), BLK_ESTATE (packed unknown / cfg differs), BLK_EHIP.
  */
 int blk_forward(const blk_config* cfg, const void* packed, int layer, int batch, int tokens,
