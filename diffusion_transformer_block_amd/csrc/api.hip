@@ -159,8 +159,8 @@ int lookup(const void* packed, const blk_config& cfg, PackRecord* out) {
 
 // ---------------------------------------------------------------- workspace layout
 struct BlockWs {
-  size_t q, o, h, a, r1, r2, part, att_o, att_ml;
-  size_t ctr_qkv, ctr_o, ctr_gu, ctr_d, ctr_att;
+  size_t q, o, h, a, r1, r2, part;
+  size_t ctr_qkv, ctr_o, ctr_gu, ctr_d;
   size_t sm_att_o, sm_att_ml;   // small-chunk attention key-slice partials
   size_t xb0, xb1, flags, sync;
   size_t total;
@@ -172,12 +172,11 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
   const size_t M = (size_t)B * T;
   const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const int gq = (Hq + 2 * Hkv) * d / 32, go = D / 32, ggu = F / 16, gd = D / 32;
-  // small chunks keep activations in operand order, padded to 16-row tiles
+  // activations between operators are in operand order, padded to 16-row
+  // tiles; Q is in the attention's operand order (32-row tiles per kv head)
   const bool small = M > 0 && (int)M <= kSkinnyMaxM;
-  const size_t Mp = small ? (size_t)16 * mt_of((int)M) : M;
-  const size_t q_rows = small ? std::max(Mp * Hq,
-                                         (size_t)B * Hkv * 32 * (((Hq / Hkv) * (size_t)T + 31) / 32))
-                              : M * Hq;
+  const size_t Mp = (size_t)16 * mt_of((int)M);
+  const size_t q_rows = std::max(Mp * Hq, (size_t)B * Hkv * 32 * (((Hq / Hkv) * (size_t)T + 31) / 32));
   size_t off = base;
   w.q = off;
   off += align_up(q_rows * d * 2);
@@ -202,10 +201,6 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
   }
   w.part = off;
   off += align_up(part * 4);
-  w.att_o = off;
-  off += align_up(attn_part_o_floats(B, T, P, Hq, Hkv, d) * 4);
-  w.att_ml = off;
-  off += align_up(attn_part_ml_floats(B, T, P, Hq, Hkv, d) * 4);
   w.ctr_qkv = off;
   off += align_up((size_t)gq * 4);
   w.ctr_o = off;
@@ -214,12 +209,10 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
   off += align_up((size_t)ggu * 4);
   w.ctr_d = off;
   off += align_up((size_t)gd * 4);
-  w.ctr_att = off;
-  off += align_up(attn_counters(B, T, P, Hq, Hkv, d) * 4);
   w.sm_att_o = off;
-  off += align_up(small ? attn_sm_part_o_elems(B, T, P, Hq, Hkv, d) * 2 : 0);
+  off += align_up(attn_sm_part_o_elems(B, T, P, Hq, Hkv, d) * 2);
   w.sm_att_ml = off;
-  off += align_up(small ? attn_sm_part_ml_floats(B, T, P, Hq, Hkv, d) * 4 : 0);
+  off += align_up(attn_sm_part_ml_floats(B, T, P, Hq, Hkv, d) * 4);
   w.xb0 = off;
   off += align_up(Mp * D * 2);
   w.xb1 = off;
@@ -525,6 +518,7 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     return;
   }
   const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const int MT = mt_of(M);
   const uint8_t* lw = at<uint8_t>(packed, lay.layer0 + (size_t)layer * lay.layer_bytes);
   bf16_t* q = at<bf16_t>(ws, w.q);
   bf16_t* o = at<bf16_t>(ws, w.o);
@@ -536,7 +530,8 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
   GemmArgs base{};
   base.M = M;
 
-  // 1. RMS(x) -> fused QKV GEMM with row scale and RoPE epilogue
+  // 1. RMS(x) -> fused QKV GEMM with row scale and RoPE epilogue (Q in the
+  //    attention's operand order)
   {
     GemmArgs ga = base;
     ga.A = io.x;
@@ -544,16 +539,18 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     ga.K = D;
     ga.Bp = lw + lay.wqkv;
     ga.n_groups = (Hq + 2 * Hkv) * d / 32;
-    launch_rms_rows(io.x, M, D, c.rms_eps, r1, st);
+    launch_rms_rows(io.x, M, D, false, c.rms_eps, r1, st);
     ga.r = r1;
     EpiQKV e{q, io.kn, io.vn, io.new_stride, at<float>(packed, lay.rope_cos),
              at<float>(packed, lay.rope_sin), T, P, Hq, Hkv, d};
     launch_gemm_qkv(ga, e, st);
     op_done(BLK_OP_QKV);
   }
-  // 2. attention over [prefix ; own]
+  // 2. attention over [prefix ; own]: the chunk attention of the small path,
+  //    64 query rows per workgroup over all keys (or key slices and a merge
+  //    when there are few row blocks); O in operand order
   {
-    AttnArgs aa{};
+    AttnSmArgs aa{};
     aa.q = q;
     aa.kp = io.kp;
     aa.vp = io.vp;
@@ -567,16 +564,14 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     aa.P = P;
     aa.Hq = Hq;
     aa.Hkv = Hkv;
-    aa.d = d;
-    attn_plan(B, T, P, Hq, Hkv, d, &aa.splits, &aa.keys_per_split);
+    attn_sm_plan(B, T, P, Hq, Hkv, &aa.splits, &aa.kps);
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
-    aa.part_o = at<float>(ws, w.att_o);
-    aa.part_ml = at<float>(ws, w.att_ml);
-    aa.counters = at<unsigned>(ws, w.ctr_att);
-    launch_attention(aa, st);
+    aa.part_o = at<bf16_t>(ws, w.sm_att_o);
+    aa.part_ml = at<float>(ws, w.sm_att_ml);
+    launch_attn_sm(aa, d, st);
     op_done(BLK_OP_ATTENTION);
   }
-  // 3. h = x + O W_o
+  // 3. h = x + O W_o (h in operand order)
   {
     GemmArgs ga = base;
     ga.A = o;
@@ -584,7 +579,7 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     ga.K = Hq * d;
     ga.Bp = lw + lay.wo;
     ga.n_groups = D / 32;
-    launch_gemm_residual(ga, EpiResidual{io.x, h, D}, st);
+    launch_gemm_residual(ga, EpiResidual{io.x, 0, h, 1, D, MT}, st);
     op_done(BLK_OP_O_PROJ);
   }
   // 4. RMS(h) -> gate/up GEMM with SiLU(gate) * up epilogue
@@ -595,12 +590,12 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     ga.K = D;
     ga.Bp = lw + lay.wgu;
     ga.n_groups = F / 16;
-    launch_rms_rows(h, M, D, c.rms_eps, r2, st);
+    launch_rms_rows(h, M, D, true, c.rms_eps, r2, st);
     ga.r = r2;
-    launch_gemm_gateup(ga, EpiGateUp{a, F}, st);
+    launch_gemm_gateup(ga, EpiGateUp{a, MT}, st);
     op_done(BLK_OP_GATE_UP);
   }
-  // 5. y = h + a W_d
+  // 5. y = h + a W_d (y row-major, the caller's)
   {
     GemmArgs ga = base;
     ga.A = a;
@@ -608,7 +603,7 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     ga.K = F;
     ga.Bp = lw + lay.wd;
     ga.n_groups = D / 32;
-    launch_gemm_residual(ga, EpiResidual{h, io.y, D}, st);
+    launch_gemm_residual(ga, EpiResidual{h, 1, io.y, 0, D, MT}, st);
     op_done(BLK_OP_DOWN);
   }
 }

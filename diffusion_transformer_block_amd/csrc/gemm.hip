@@ -11,7 +11,7 @@
 //
 // The large-chunk GEMM (M > 64 rows; chunks of <= 64 rows run the skinny
 // GEMM of skinny.h): 256 x 256 (or 128 x 128) output tiles, both operands
-// moved into LDS by the buffer-load DMA as MFMA fragments, 2 x 2 waves of
+// moved into LDS by the load DMA as MFMA fragments, 2 x 2 waves of
 // 16 x 16 x 32 MFMAs, XCD-aware tile order (big_gemm_kernel below).
 #include "common.h"
 #include "internal.h"
@@ -19,21 +19,52 @@
 
 namespace blk {
 
-// ============================================================================ large-chunk GEMM
-// LDS DMA of one 1 KiB fragment: lane l's 16 bytes at voffset land at lds + 16 l.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0,
-                                           0, 0);
+__device__ __forceinline__ void EpiQKV::store8(int m, int g, int qc, const float* v) const {
+  const int b = m / T, t = m - b * T;
+  const int gpr = d >> 5, n_rot_groups = (Hq + Hkv) * gpr;
+  bf16_t* dst;
+  if (g < n_rot_groups) {
+    const int head = g / gpr;
+    const int col = 16 * (g - head * gpr) + (qc & 1) * 8 + (qc >> 1) * (d >> 1);
+    if (head < Hq) {
+      const int G = Hq / Hkv, hk = head / G, gh = head - hk * G;
+      dst = q + qa_index(b * Hkv + hk, (G * T + 31) >> 5, d >> 4, t * G + gh, col);
+    } else {
+      dst = kn + (size_t)b * new_stride + ((size_t)t * Hkv + (head - Hq)) * d + col;
+    }
+  } else {
+    dst = vn + (size_t)b * new_stride + (size_t)t * Hkv * d + 32 * (g - n_rot_groups) + 8 * qc;
+  }
+  *reinterpret_cast<uint4*>(dst) = pack8(v);
 }
 
-// BM x BN output tile per workgroup (4 waves in a 2 x 2 grid), K steps of 64.
-// Each stage holds the tile's A and B operands in LDS as 1 KiB MFMA
-// fragments -- A (row-major activations) gathered by the DMA as 16 rows x
-// 64 bytes per fragment, B (packed weights) one contiguous fragment each --
-// in two buffers: a wave reads all of its fragments of the current stage
-// into registers, then issues the next stage's DMA (after its reads, so they
-// do not wait on it), then runs its MFMAs.
-template <int BM, int BN, class Epi>
+// ============================================================================ large-chunk GEMM
+__device__ __forceinline__ unsigned lds_u32(const void* p) {
+  return (unsigned)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+// LDS DMA of one 1 KiB fragment: lane l's 16 bytes at gp land at LDS byte
+// address lds + 16 l.  Written as assembly so that the compiler adds no
+// waits of its own for it (it would wait for the DMA before every later LDS
+// read); the kernel waits (vmcnt) before a barrier hands the stage on.
+// (M0 is reserved to the compiler: no other code in these kernels uses it.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(unsigned lds, const void* gp) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(gp) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// BM x BN output tile per workgroup (4 waves in a 2 x 2 grid, each BM/2 x
+// BN/2 of 16 x 16 x 32 MFMAs), K steps of 64 in two LDS stages.  A stage holds
+// the tile's operands as 1 KiB MFMA fragments: B (packed weights) and, for
+// AFRAG, A (an operand-order activation, fa_index) one contiguous fragment
+// each; a row-major A is gathered as 16 rows x 64 bytes per fragment.  The
+// loop is software-pipelined: a wave reads its k-tile-1 fragments while its
+// k-tile-0 MFMAs run, and, after the barrier that publishes the next stage,
+// that stage's k-tile-0 fragments while its k-tile-1 MFMAs run; the DMA of
+// the stage after next goes out right after that barrier.
+template <int BM, int BN, bool AFRAG, class Epi>
 __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int n_tm) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t big_dsm[];
   constexpr int BK = 64;
@@ -61,34 +92,50 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   const int tm = band * GM + tib % rows_b, tn = tib / rows_b;
   const int m0 = tm * BM, g0 = tn * GB;
   const int KT = ga.K >> 5, nk = ga.K / BK;
+  const int MTa = mt_of(ga.M);
 
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(ga.A, (size_t)ga.M * ga.lda * 2);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(ga.Bp, (size_t)ga.n_groups * KT * 2 * kFragBytes);
   // this wave's fragments of a stage: f = w + 4 i (A fragments first); rows
   // and groups past the matrix are clamped (their results are not stored)
-  int voff[PER];
+  const uint8_t* gsrc[PER];
+  int gstep[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int f = w + 4 * i;
     if (f < AFR) {
       const int kt = f / MTB, mt = f - kt * MTB;
-      const int row = min(m0 + 16 * mt + (l & 15), ga.M - 1);
-      voff[i] = (row * ga.lda + 32 * kt + 8 * (l >> 4)) * 2;
+      if (AFRAG) {
+        const int rt = min(m0 / 16 + mt, MTa - 1);
+        gsrc[i] = reinterpret_cast<const uint8_t*>(ga.A) + ((size_t)kt * MTa + rt) * kFragBytes + 16 * l;
+        gstep[i] = 2 * MTa * kFragBytes;
+      } else {
+        const int row = min(m0 + 16 * mt + (l & 15), ga.M - 1);
+        gsrc[i] = reinterpret_cast<const uint8_t*>(ga.A) + ((size_t)row * ga.lda + 32 * kt + 8 * (l >> 4)) * 2;
+        gstep[i] = BK * 2;
+      }
     } else {
       const int fb = f - AFR, gg = fb >> 2, kt = (fb >> 1) & 1, ii = fb & 1;
-      voff[i] = (int)frag_offset(min(g0 + gg, ga.n_groups - 1), kt, ii, KT) + 16 * l;
+      gsrc[i] = ga.Bp + frag_offset(min(g0 + gg, ga.n_groups - 1), kt, ii, KT) + 16 * l;
+      gstep[i] = 2 * 2 * kFragBytes;
     }
   }
+  const unsigned lds0 = lds_u32(big_dsm);
   auto issue = [&](int s, int buf) {
-    uint8_t* base = big_dsm + buf * STAGE;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int f = w + 4 * i;
-      if (f < AFR) dma16(ra, base + f * kFragBytes, voff[i] + s * BK * 2);
-      else dma16(rb, base + f * kFragBytes, voff[i] + s * 2 * 2 * kFragBytes);
-    }
+    for (int i = 0; i < PER; ++i)
+      dma16(lds0 + buf * STAGE + (w + 4 * i) * kFragBytes, gsrc[i] + (size_t)s * gstep[i]);
   };
-
+  auto rd = [&](int buf, int kt, uint4 (&af)[MTW], uint4 (&bfv)[GW][2]) {
+    const uint8_t* base = big_dsm + buf * STAGE;
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+      af[mt] = *reinterpret_cast<const uint4*>(base + (kt * MTB + wm * MTW + mt) * kFragBytes + 16 * l);
+#pragma unroll
+    for (int gg = 0; gg < GW; ++gg)
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+        bfv[gg][ii] = *reinterpret_cast<const uint4*>(
+            base + (AFR + (wn * GW + gg) * 4 + kt * 2 + ii) * kFragBytes + 16 * l);
+  };
   f32x4 acc[MTW][GW][2];
 #pragma unroll
   for (int a = 0; a < MTW; ++a)
@@ -97,40 +144,38 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
       acc[a][b][0] = f32x4{0.f, 0.f, 0.f, 0.f};
       acc[a][b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-
-  issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    const int cur = s & 1;
-    const uint8_t* base = big_dsm + cur * STAGE;
-    uint4 af[2][MTW], bfv[2][GW][2];
+  auto mm = [&](const uint4 (&af)[MTW], const uint4 (&bfv)[GW][2]) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int mt = 0; mt < MTW; ++mt)
-        af[kt][mt] =
-            *reinterpret_cast<const uint4*>(base + (kt * MTB + wm * MTW + mt) * kFragBytes + 16 * l);
+    for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
       for (int gg = 0; gg < GW; ++gg)
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii)
-          bfv[kt][gg][ii] = *reinterpret_cast<const uint4*>(
-              base + (AFR + (wn * GW + gg) * 4 + kt * 2 + ii) * kFragBytes + 16 * l);
-    }
-    if (s + 1 < nk) issue(s + 1, cur ^ 1);
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int mt = 0; mt < MTW; ++mt)
-#pragma unroll
-        for (int gg = 0; gg < GW; ++gg)
-#pragma unroll
-          for (int ii = 0; ii < 2; ++ii)
-            acc[mt][gg][ii] = mfma16(as_bf16x8(af[kt][mt]), as_bf16x8(bfv[kt][gg][ii]), acc[mt][gg][ii]);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next stage has landed
-    __syncthreads();                                    // and every wave is done with this one
+          acc[mt][gg][ii] = mfma16(as_bf16x8(af[mt]), as_bf16x8(bfv[gg][ii]), acc[mt][gg][ii]);
+  };
+
+  // prologue: stages 0 and 1 in flight, stage 0 landed, its k-tile-0 fragments read
+  issue(0, 0);
+  if (nk > 1) {
+    issue(1, 1);
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
+  __syncthreads();
+  uint4 a0[MTW], b0[GW][2], a1[MTW], b1[GW][2];
+  rd(0, 0, a0, b0);
+  for (int s = 0; s < nk; ++s) {
+    const int b = s & 1;
+    rd(b, 1, a1, b1);
+    mm(a0, b0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // stage s + 1 landed
+    __syncthreads();                                    // and every wave has read stage s
+    if (s + 2 < nk) issue(s + 2, b);
+    if (s + 1 < nk) rd(b ^ 1, 0, a0, b0);
+    mm(a1, b1);
+  }
+  __syncthreads();
 
   // ---- epilogue, 32 rows of the wave's tile at a time: math() in the MFMA
   //      layout into this wave's LDS region, then 16-byte row stores
@@ -173,11 +218,11 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   }
 }
 
-template <int BM, int BN, class Epi>
+template <int BM, int BN, bool AFRAG, class Epi>
 static void launch_big(const GemmArgs& ga, const Epi& e, hipStream_t st) {
   constexpr int NFR = (BM / 16) * 2 + (BN / 32) * 4;
   const size_t smem = 2 * (size_t)NFR * kFragBytes;
-  auto kern = big_gemm_kernel<BM, BN, Epi>;
+  auto kern = big_gemm_kernel<BM, BN, AFRAG, Epi>;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -190,37 +235,41 @@ static void launch_big(const GemmArgs& ga, const Epi& e, hipStream_t st) {
 
 // 256 x 256 tiles where they fill the chip (about one workgroup per compute
 // unit or more), 128 x 128 otherwise.
-template <class Epi>
+template <bool AFRAG, class Epi>
 static void launch_tiled(const GemmArgs& ga, const Epi& e, hipStream_t st) {
   const long big_tiles = (long)((ga.M + 255) / 256) * ((ga.n_groups + 7) / 8);
-  if (big_tiles >= (long)device_cus() * 15 / 16) launch_big<256, 256>(ga, e, st);
-  else launch_big<128, 128>(ga, e, st);
+  if (big_tiles >= (long)device_cus() * 15 / 16) launch_big<256, 256, AFRAG>(ga, e, st);
+  else launch_big<128, 128, AFRAG>(ga, e, st);
 }
 
 // ============================================================================ dispatch
-void launch_gemm_qkv(const GemmArgs& ga, const EpiQKV& e, hipStream_t st) { launch_tiled(ga, e, st); }
+void launch_gemm_qkv(const GemmArgs& ga, const EpiQKV& e, hipStream_t st) { launch_tiled<false>(ga, e, st); }
 void launch_gemm_residual(const GemmArgs& ga, const EpiResidual& e, hipStream_t st) {
-  launch_tiled(ga, e, st);
+  launch_tiled<true>(ga, e, st);
 }
-void launch_gemm_gateup(const GemmArgs& ga, const EpiGateUp& e, hipStream_t st) { launch_tiled(ga, e, st); }
+void launch_gemm_gateup(const GemmArgs& ga, const EpiGateUp& e, hipStream_t st) { launch_tiled<true>(ga, e, st); }
 
 // ============================================================================ RMS rows
-// r[m] = (sum_k x[m][k]^2 / K + eps)^-1/2, one wave per row
+// r[m] = (sum_k x[m][k]^2 / K + eps)^-1/2, one wave per row; x row-major or,
+// with frag, in operand order (fa_index over mt_of(M) row tiles)
 __global__ __launch_bounds__(256) void rms_rows_kernel(const bf16_t* __restrict__ x, int M, int K,
-                                                       float eps, float* __restrict__ r) {
+                                                       int frag, float eps, float* __restrict__ r) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   if (row >= M) return;
-  const bf16_t* p = x + (size_t)row * K;
+  const int MT = mt_of(M);
   float s = 0.f;
-  for (int k = 8 * l; k < K; k += 512) s += sumsq8(*reinterpret_cast<const uint4*>(p + k));
+  for (int k = 8 * l; k < K; k += 512) {
+    const bf16_t* p = frag ? x + fa_index(row, k, MT) : x + (size_t)row * K + k;
+    s += sumsq8(*reinterpret_cast<const uint4*>(p));
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
   if (l == 0) r[row] = rsqrtf(s / (float)K + eps);
 }
 
-void launch_rms_rows(const bf16_t* x, int M, int K, float eps, float* r, hipStream_t st) {
-  rms_rows_kernel<<<(M + 3) / 4, 256, 0, st>>>(x, M, K, eps, r);
+void launch_rms_rows(const bf16_t* x, int M, int K, bool frag, float eps, float* r, hipStream_t st) {
+  rms_rows_kernel<<<(M + 3) / 4, 256, 0, st>>>(x, M, K, frag ? 1 : 0, eps, r);
 }
 
 }  // namespace blk

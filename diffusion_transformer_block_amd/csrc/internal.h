@@ -44,10 +44,11 @@ void launch_copy_f32(const float* in, size_t n, float* out, hipStream_t st);
 // with one 16-byte store.  The stores are plain: the next kernel reads them.
 
 // Fused QKV: scale by r, rotate (Q, K) pairs (slot c = column j, slot 16 + c
-// = column j + d/2 of the rotated head), scatter into Q / K_new / V_new.
+// = column j + d/2 of the rotated head), Q into the chunk attention's operand
+// order (qa_index in skinny.h), K_new / V_new row-major.
 struct EpiQKV {
   static constexpr int SLOT_CHUNKS = 4;
-  bf16_t* q;            // [M][Hq d]
+  bf16_t* q;
   bf16_t* kn;           // stream b at b * new_stride, [T][Hkv][d]
   bf16_t* vn;
   int64_t new_stride;
@@ -66,52 +67,44 @@ struct EpiQKV {
     const float cs = cos_t[ti], sn = sin_t[ti];
     return make_float2(v0 * cs - v1 * sn, v0 * sn + v1 * cs);
   }
-  __device__ __forceinline__ void store8(int m, int g, int qc, const float* v) const {
-    const int b = m / T, t = m - b * T;
-    const int gpr = d >> 5, n_rot_groups = (Hq + Hkv) * gpr;
-    bf16_t* dst;
-    if (g < n_rot_groups) {
-      const int head = g / gpr;
-      const int col = 16 * (g - head * gpr) + (qc & 1) * 8 + (qc >> 1) * (d >> 1);
-      dst = head < Hq ? q + (size_t)m * Hq * d + (size_t)head * d + col
-                      : kn + (size_t)b * new_stride + ((size_t)t * Hkv + (head - Hq)) * d + col;
-    } else {
-      dst = vn + (size_t)b * new_stride + (size_t)t * Hkv * d + 32 * (g - n_rot_groups) + 8 * qc;
-    }
-    *reinterpret_cast<uint4*>(dst) = pack8(v);
-  }
+  __device__ __forceinline__ void store8(int m, int g, int qc, const float* v) const;
 };
 
-// out[m][n] = res[m][n] + acc (residual add; O projection and down projection).
+// out = res + acc (residual add; O projection and down projection).  res and
+// out are each row-major [M][ld] or in operand order (fa_index, MT row tiles).
 struct EpiResidual {
   static constexpr int SLOT_CHUNKS = 4;
   const bf16_t* res;
+  int res_frag;
   bf16_t* out;
-  int ld;
+  int out_frag;
+  int ld, MT;
   __device__ __forceinline__ float2 math(int, int, int, float v0, float v1, float) const {
     return make_float2(v0, v1);
   }
   __device__ __forceinline__ void store8(int m, int g, int qc, const float* v) const {
-    const size_t o = (size_t)m * ld + 32 * g + 8 * qc;
+    const int c = 32 * g + 8 * qc;
+    const size_t ro = res_frag ? fa_index(m, c, MT) : (size_t)m * ld + c;
+    const size_t oo = out_frag ? fa_index(m, c, MT) : (size_t)m * ld + c;
     float x[8];
-    unpack8(*reinterpret_cast<const uint4*>(res + o), x);
+    unpack8(*reinterpret_cast<const uint4*>(res + ro), x);
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] += v[e];
-    *reinterpret_cast<uint4*>(out + o) = pack8(x);
+    *reinterpret_cast<uint4*>(out + oo) = pack8(x);
   }
 };
 
 // out[m][j] = SiLU(r * gate) * (r * up), j = 16 g + c (gate/up interleave):
-// 16 slots per group.
+// 16 slots per group, stored in operand order (fa_index, MT row tiles).
 struct EpiGateUp {
   static constexpr int SLOT_CHUNKS = 2;
   bf16_t* out;
-  int ld;
+  int MT;
   __device__ __forceinline__ float2 math(int, int, int, float v0, float v1, float r) const {
     return make_float2(silu(v0 * r) * (v1 * r), 0.f);
   }
   __device__ __forceinline__ void store8(int m, int g, int qc, const float* v) const {
-    *reinterpret_cast<uint4*>(out + (size_t)m * ld + 16 * g + 8 * qc) = pack8(v);
+    *reinterpret_cast<uint4*>(out + fa_index(m, 16 * g + 8 * qc, MT)) = pack8(v);
   }
 };
 
@@ -136,30 +129,8 @@ constexpr int kSkinnyMaxM = 64;
 
 // ---------------------------------------------------------------- RMS statistics
 // r[m] = (sum_k x[m][k]^2 / K + eps)^-1/2
-void launch_rms_rows(const bf16_t* x, int M, int K, float eps, float* r, hipStream_t st);
+void launch_rms_rows(const bf16_t* x, int M, int K, bool frag, float eps, float* r, hipStream_t st);
 
-// ---------------------------------------------------------------- attention
-struct AttnArgs {
-  const bf16_t* q;          // [B*T][Hq d]
-  const bf16_t* kp;         // stream b at b * prefix_stride, [P][Hkv][d]
-  const bf16_t* vp;
-  int64_t prefix_stride;
-  const bf16_t* kn;         // stream b at b * new_stride, [T][Hkv][d]
-  const bf16_t* vn;
-  int64_t new_stride;
-  bf16_t* o;                // [B*T][Hq d]
-  int B, T, P, Hq, Hkv, d;
-  int splits, keys_per_split;
-  float scale_log2;         // log2(e) / sqrt(d)
-  float* part_o;            // split partials
-  float* part_ml;
-  unsigned* counters;
-};
-void attn_plan(int B, int T, int P, int Hq, int Hkv, int d, int* splits, int* keys_per_split);
-size_t attn_part_o_floats(int B, int T, int P, int Hq, int Hkv, int d);
-size_t attn_part_ml_floats(int B, int T, int P, int Hq, int Hkv, int d);
-size_t attn_counters(int B, int T, int P, int Hq, int Hkv, int d);
-void launch_attention(const AttnArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- small-chunk path
 // (M = B * T <= 64): activations in operand order, see skinny.h / attn_small.h

@@ -171,10 +171,18 @@ void launch_sk_gateup(const SkArgs& ga, int gpw, const EpiGateUpS& e, hipStream_
 
 // ============================================================================ attention
 template <int HD>
-__global__ __launch_bounds__(256) void attn_sm_kernel(AttnSmArgs a) {
+__global__ __launch_bounds__(256) void attn_sm_kernel(AttnSmArgs a, int n_rb) {
   extern __shared__ __attribute__((aligned(16))) char at_dsm[];
-  attn_sm_task<HD>(a, blockIdx.z, blockIdx.y, blockIdx.x, *reinterpret_cast<AttnSmSmem<HD>*>(at_dsm),
-                   NoWait{});
+  // Tasks in the order (stream x kv head, key slice, row block), row block
+  // fastest; the hardware deals workgroups round-robin over the 8 XCDs, so
+  // hand each XCD a contiguous run of tasks: the row blocks that read the
+  // same K/V tiles then share one L2.
+  const int nwg = gridDim.x, id = blockIdx.x;
+  const int xcd = id & 7, jx = id >> 3, qx = nwg >> 3, rx = nwg & 7;
+  const int task = xcd * qx + min(xcd, rx) + jx;
+  const int rb = task % n_rb, rest = task / n_rb;
+  const int ks = rest % a.splits, bh = rest / a.splits;
+  attn_sm_task<HD>(a, bh, rb, ks, *reinterpret_cast<AttnSmSmem<HD>*>(at_dsm), NoWait{});
 }
 
 template <int HD>
@@ -193,8 +201,8 @@ static void attn_sm_go(const AttnSmArgs& a, hipStream_t st) {
     attr_set = true;
   }
   const int G = a.Hq / a.Hkv;
-  const dim3 grid(a.splits, (G * a.T + 63) / 64, a.B * a.Hkv);
-  hipLaunchKernelGGL(kern, grid, dim3(256), smem, st, a);
+  const int n_rb = (G * a.T + 63) / 64;
+  hipLaunchKernelGGL(kern, dim3(a.splits * n_rb * a.B * a.Hkv), dim3(256), smem, st, a, n_rb);
   if (a.splits > 1) {
     const int items = attn_combine_items(a.B, a.T, a.Hq, a.Hkv, HD);
     hipLaunchKernelGGL(attn_combine_kernel<HD>, dim3((items + 255) / 256), dim3(256), 0, st, a);
