@@ -312,7 +312,7 @@ bool stage_plan(const blk_config& c, int B, int T, int P, int flow_N, int nwg, S
   sa.gpw_d = p_d.gpw;
   sa.gpw_w3 = p_w3.gpw;
   int splits = 1, kps = 32;
-  attn_sm_plan(B, T, P, Hq, Hkv, &splits, &kps);
+  attn_sm_plan(B, T, P, Hq, Hkv, &splits, &kps, nullptr);
   const int n_rbt = B * Hkv * (((Hq / Hkv) * T + 63) / 64);
   const int n_att = n_rbt * splits;
   const int n_cmb = splits > 1 ? (attn_combine_items(B, T, Hq, Hkv, d) + 255) / 256 : 0;
@@ -460,7 +460,7 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     aa.P = P;
     aa.Hq = Hq;
     aa.Hkv = Hkv;
-    attn_sm_plan(B, T, P, Hq, Hkv, &aa.splits, &aa.kps);
+    attn_sm_plan(B, T, P, Hq, Hkv, &aa.splits, &aa.kps, &aa.long_rows);
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     aa.part_o = at<bf16_t>(ws, w.sm_att_o);
     aa.part_ml = at<float>(ws, w.sm_att_ml);
@@ -564,7 +564,7 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     aa.P = P;
     aa.Hq = Hq;
     aa.Hkv = Hkv;
-    attn_sm_plan(B, T, P, Hq, Hkv, &aa.splits, &aa.kps);
+    attn_sm_plan(B, T, P, Hq, Hkv, &aa.splits, &aa.kps, &aa.long_rows);
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     aa.part_o = at<bf16_t>(ws, w.sm_att_o);
     aa.part_ml = at<float>(ws, w.sm_att_ml);

@@ -57,6 +57,7 @@ struct AttnSmArgs {
   float scale_log2;       // log2(e) / sqrt(d)
   bf16_t* part_o;         // [splits][n_rbt][64][d] (normalised partials)
   float* part_ml;         // [splits][n_rbt][64][2] (max, sum)
+  int long_rows;          // 1: 128-row blocks over a single key slice (attn_sm_task LONG)
 };
 
 constexpr int kAttnMaxSplits = 16;
@@ -81,9 +82,14 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// One task: stream x kv head bh, 64-row block rb, key slice ks.  Returns true
+// One task: stream x kv head bh, row block rb, key slice ks.  Returns true
 // if this workgroup wrote the block's final rows (a single key slice).
-template <int HD, class Wait>
+// Row blocks are 64 rows: wave w takes 32 rows (w % 2) and one 32-key half
+// (w / 2) of every tile, and the halves merge at the end.  LONG (long key
+// runs, a single key slice only) makes them 128 rows: wave w takes 32 rows and
+// both key halves of every tile in turn, so a K/V tile serves twice the rows
+// and no merge is needed.
+template <int HD, bool LONG = false, class Wait>
 __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSmSmem<HD>& sm,
                              Wait&& wait) {
   constexpr int KROW = HD + 8, VROW = HD + 16;
@@ -94,7 +100,8 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int l = tid & 63;
-  const int rp = w & 1, kh = w >> 1;           // 32-row half of the block, 32-key half of a tile
+  const int rp = LONG ? w : (w & 1);          // 32-row tile of the block
+  const int kh_w = w >> 1;                     // the wave's 32-key half of a tile (not LONG)
   const int b = bh / a.Hkv, hk = bh - b * a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int rows = G * a.T;
@@ -163,7 +170,7 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
   if (n_tiles > 0 && !pre0) load_tile(0);
 
   // this wave's 32 query rows: Q^T fragments (B operand), one per d step
-  const int rt = min(2 * rb + rp, n_rt - 1);
+  const int rt = min((LONG ? 4 : 2) * rb + rp, n_rt - 1);
   const __amdgpu_buffer_rsrc_t rq =
       make_rsrc(a.q + (size_t)(bh * n_rt + rt) * NDS * 512, (size_t)NDS * kFragBytes);
   uint4 qf[NDS];
@@ -191,10 +198,14 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
   const int p16 = l & 15;
   // V^T operand (transposed LDS reads): d = 32 dt + 16 ((l/16) % 2) + 4 (p16 % 4),
   // key rows 32 kh + 16 u + 4 hl + p16 / 4 (+ 8 for the second read)
-  const int vt_off = (32 * kh + 4 * hl + (p16 >> 2)) * VROW + 16 * ((l >> 4) & 1) + 4 * (p16 & 3);
+  const int vt_off0 = (4 * hl + (p16 >> 2)) * VROW + 16 * ((l >> 4) & 1) + 4 * (p16 & 3);
 
   auto step = [&](int it, auto cur_c) {
     constexpr int cur = decltype(cur_c)::value;   // LDS buffer of tile it
+#pragma unroll
+    for (int khi = 0; khi < (LONG ? 2 : 1); ++khi) {
+    const int kh = LONG ? khi : kh_w;
+    const int vt_off = vt_off0 + 32 * kh * VROW;
     const int base = key_begin + 64 * it + 32 * kh;
     // ---- S^T (32 keys x 32 rows): K fragments read from LDS in batches of
     //      8 ahead of their MFMAs, two independent accumulation chains
@@ -275,6 +286,7 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
           o[d0 + dt] = mfma32(as_bf16x8(make_uint4(vlo[dt].x, vlo[dt].y, vhi[dt].x, vhi[dt].y)), pb, o[d0 + dt]);
       }
     }
+    }   // key halves
     // ---- stage the next tile into the other buffer (last read one tile ago)
     //      and start the loads of the tile after it
     if (it + 1 < n_tiles) {
@@ -295,6 +307,58 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
   //      slice's normalised bf16 partial and its (max, sum))
   const float l_tot = l_run + __shfl_xor(l_run, 32);   // the two lanes of a row share m_run
   constexpr int PROW = HD + 4;
+  if constexpr (LONG) {
+    // ---- every wave holds its rows' whole result: park them (fp32, with
+    //      1 / sum) in LDS and store the 128 rows in the O projection's
+    //      operand order, 16 bytes per lane as in the merge below
+    float* park = reinterpret_cast<float*>(&sm.k[0][0]);   // [128 rows][PROW]
+    float* inv_row = &sm.mlh[0][0].x;                        // [128]
+    const int row32 = l & 31;
+    {
+      float* dst = park + (32 * rp + row32) * PROW + 4 * hl;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(dst + 32 * dt + 8 * q) =
+              make_float4(o[dt][4 * q], o[dt][4 * q + 1], o[dt][4 * q + 2], o[dt][4 * q + 3]);
+      if (hl == 0) inv_row[32 * rp + row32] = 1.f / l_tot;
+    }
+    __syncthreads();
+    const int MTo = mt_of(a.B * a.T);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o, (size_t)MTo * 16 * a.Hq * HD * 2);
+    constexpr int LPR = HD / 8, RPP = 64 / LPR, PASSES = 128 / (4 * RPP);
+    const int c = l % LPR, odd = c & 1;
+    uint4 res[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = (w + 4 * p) * RPP + l / LPR;
+      const float inv = inv_row[row];
+      const float* p0 = park + row * PROW;
+      uint2 half[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float4 x = *reinterpret_cast<const float4*>(p0 + 4 * (LPR * e + c));
+        half[e] = make_uint2(pack2(x.x * inv, x.y * inv), pack2(x.z * inv, x.w * inv));
+      }
+      const uint2 give = odd ? half[0] : half[1];
+      const uint2 got = make_uint2(__shfl_xor(give.x, 1), __shfl_xor(give.y, 1));
+      res[p] = odd ? make_uint4(got.x, got.y, half[1].x, half[1].y)
+                   : make_uint4(half[0].x, half[0].y, got.x, got.y);
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = (w + 4 * p) * RPP + l / LPR;
+      const int ch = (c >> 1) + (odd ? LPR / 2 : 0);
+      const int ar = 128 * rb + row;
+      if (ar < rows) {
+        const int t = ar / G, h = hk * G + (ar - t * G);
+        buf_st16(ro, (int)(fa_index(b * a.T + t, h * HD + 8 * ch, MTo) * 2), res[p]);
+      }
+    }
+    return true;
+  }
+  const int kh = kh_w;
   float* park = reinterpret_cast<float*>(&sm.k[0][0]);   // [2 key halves][64 rows][PROW]
   const int row32 = l & 31;
   {

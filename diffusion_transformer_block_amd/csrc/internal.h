@@ -151,7 +151,8 @@ int sk_nb(int KW, int gpw, int MT);
 void launch_sk_qkv(const SkArgs& ga, int gpw, bool a_rowmajor, const EpiQkvS& e, hipStream_t st);
 void launch_sk_resid(const SkArgs& ga, int gpw, const EpiResidS& e, hipStream_t st);
 void launch_sk_gateup(const SkArgs& ga, int gpw, const EpiGateUpS& e, hipStream_t st);
-void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps);
+// long_rows: set to 1 for 128-row blocks over one key slice (NULL: 64-row blocks only)
+void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps, int* long_rows);
 size_t attn_sm_part_o_elems(int B, int T, int P, int Hq, int Hkv, int d);
 size_t attn_sm_part_ml_floats(int B, int T, int P, int Hq, int Hkv, int d);
 void launch_attn_sm(const AttnSmArgs& a, int head_dim, hipStream_t st);

@@ -85,10 +85,21 @@ int sk_nb(int KW, int gpw, int MT) {
 // one or two 64-key steps -- one memory round trip for its K/V -- and the
 // merge kernel spreads the combine over every row; slices are multiples of
 // 32 keys (a wave's half of a step).
-void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps) {
+void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps, int* long_rows) {
   const int G = Hq / Hkv;
   const int n_rbt = B * Hkv * ((G * T + 63) / 64);
   const int L = P + T;
+  // enough 128-row blocks to fill half the chip: one key slice each, 128 rows
+  // per K/V tile
+  // (long_rows == NULL: the caller runs 64-row blocks only)
+  const int n_rbt_long = B * Hkv * ((G * T + 127) / 128);
+  if (long_rows) *long_rows = 0;
+  if (long_rows && n_rbt_long >= device_cus() / 2) {
+    *splits = 1;
+    *kps = (L + 31) / 32 * 32;
+    *long_rows = 1;
+    return;
+  }
   int s = std::max(1, std::min(kAttnMaxSplits, (96 + n_rbt - 1) / n_rbt));
   s = std::min(s, (L + 31) / 32);
   int k = (L + s - 1) / s;
@@ -99,7 +110,7 @@ void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps) {
 
 size_t attn_sm_part_o_elems(int B, int T, int P, int Hq, int Hkv, int d) {
   int s = 1, k = 32;
-  attn_sm_plan(B, T, P, Hq, Hkv, &s, &k);
+  attn_sm_plan(B, T, P, Hq, Hkv, &s, &k, nullptr);
   if (s <= 1) return 0;
   const int n_rbt = B * Hkv * ((Hq / Hkv * T + 63) / 64);
   return (size_t)s * n_rbt * 64 * d;
@@ -170,7 +181,7 @@ void launch_sk_gateup(const SkArgs& ga, int gpw, const EpiGateUpS& e, hipStream_
 }
 
 // ============================================================================ attention
-template <int HD>
+template <int HD, bool LONG>
 __global__ __launch_bounds__(256) void attn_sm_kernel(AttnSmArgs a, int n_rb) {
   extern __shared__ __attribute__((aligned(16))) char at_dsm[];
   // Tasks in the order (stream x kv head, key slice, row block), row block
@@ -182,7 +193,7 @@ __global__ __launch_bounds__(256) void attn_sm_kernel(AttnSmArgs a, int n_rb) {
   const int task = xcd * qx + min(xcd, rx) + jx;
   const int rb = task % n_rb, rest = task / n_rb;
   const int ks = rest % a.splits, bh = rest / a.splits;
-  attn_sm_task<HD>(a, bh, rb, ks, *reinterpret_cast<AttnSmSmem<HD>*>(at_dsm), NoWait{});
+  attn_sm_task<HD, LONG>(a, bh, rb, ks, *reinterpret_cast<AttnSmSmem<HD>*>(at_dsm), NoWait{});
 }
 
 template <int HD>
@@ -190,9 +201,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnSmArgs a) {
   attn_combine_task<HD>(a, blockIdx.x);
 }
 
-template <int HD>
-static void attn_sm_go(const AttnSmArgs& a, hipStream_t st) {
-  auto kern = attn_sm_kernel<HD>;
+template <int HD, bool LONG>
+static void attn_sm_launch(const AttnSmArgs& a, hipStream_t st) {
+  auto kern = attn_sm_kernel<HD, LONG>;
   const size_t smem = sizeof(AttnSmSmem<HD>);
   static bool attr_set = false;
   if (!attr_set) {
@@ -201,8 +212,20 @@ static void attn_sm_go(const AttnSmArgs& a, hipStream_t st) {
     attr_set = true;
   }
   const int G = a.Hq / a.Hkv;
-  const int n_rb = (G * a.T + 63) / 64;
+  const int n_rb = (G * a.T + (LONG ? 127 : 63)) / (LONG ? 128 : 64);
   hipLaunchKernelGGL(kern, dim3(a.splits * n_rb * a.B * a.Hkv), dim3(256), smem, st, a, n_rb);
+}
+
+template <int HD>
+static void attn_sm_go(const AttnSmArgs& a, hipStream_t st) {
+  // (at HD 256 the 128-row variant spills; 64-row blocks over the one slice)
+  if constexpr (HD <= 128) {
+    if (a.long_rows) {
+      attn_sm_launch<HD, true>(a, st);
+      return;
+    }
+  }
+  attn_sm_launch<HD, false>(a, st);
   if (a.splits > 1) {
     const int items = attn_combine_items(a.B, a.T, a.Hq, a.Hkv, HD);
     hipLaunchKernelGGL(attn_combine_kernel<HD>, dim3((items + 255) / 256), dim3(256), 0, st, a);
