@@ -184,8 +184,8 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
   off += align_up(Mp * Hq * d * 2);
   w.h = off;
   off += align_up(Mp * D * 2);
-  w.a = off;
-  off += align_up(Mp * F * 2);
+  w.a = off;   // also x in operand order ahead of the large-chunk QKV step
+  off += align_up(Mp * std::max(F, D) * 2);
   w.r1 = off;
   off += align_up(M * 4);
   w.r2 = off;
@@ -534,12 +534,12 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
   //    attention's operand order)
   {
     GemmArgs ga = base;
-    ga.A = io.x;
+    ga.A = a;   // x in operand order (a is free until the gate/up step)
     ga.lda = D;
     ga.K = D;
     ga.Bp = lw + lay.wqkv;
     ga.n_groups = (Hq + 2 * Hkv) * d / 32;
-    launch_rms_rows(io.x, M, D, false, c.rms_eps, r1, st);
+    launch_rms_rows(io.x, M, D, false, c.rms_eps, r1, a, st);
     ga.r = r1;
     EpiQKV e{q, io.kn, io.vn, io.new_stride, at<float>(packed, lay.rope_cos),
              at<float>(packed, lay.rope_sin), T, P, Hq, Hkv, d};
@@ -590,7 +590,7 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     ga.K = D;
     ga.Bp = lw + lay.wgu;
     ga.n_groups = F / 16;
-    launch_rms_rows(h, M, D, true, c.rms_eps, r2, st);
+    launch_rms_rows(h, M, D, true, c.rms_eps, r2, nullptr, st);
     ga.r = r2;
     launch_gemm_gateup(ga, EpiGateUp{a, MT}, st);
     op_done(BLK_OP_GATE_UP);

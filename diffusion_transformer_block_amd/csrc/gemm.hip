@@ -243,7 +243,7 @@ static void launch_tiled(const GemmArgs& ga, const Epi& e, hipStream_t st) {
 }
 
 // ============================================================================ dispatch
-void launch_gemm_qkv(const GemmArgs& ga, const EpiQKV& e, hipStream_t st) { launch_tiled<false>(ga, e, st); }
+void launch_gemm_qkv(const GemmArgs& ga, const EpiQKV& e, hipStream_t st) { launch_tiled<true>(ga, e, st); }
 void launch_gemm_residual(const GemmArgs& ga, const EpiResidual& e, hipStream_t st) {
   launch_tiled<true>(ga, e, st);
 }
@@ -252,8 +252,10 @@ void launch_gemm_gateup(const GemmArgs& ga, const EpiGateUp& e, hipStream_t st) 
 // ============================================================================ RMS rows
 // r[m] = (sum_k x[m][k]^2 / K + eps)^-1/2, one wave per row; x row-major or,
 // with frag, in operand order (fa_index over mt_of(M) row tiles)
+// xf (may be NULL): a copy of a row-major x in operand order.
 __global__ __launch_bounds__(256) void rms_rows_kernel(const bf16_t* __restrict__ x, int M, int K,
-                                                       int frag, float eps, float* __restrict__ r) {
+                                                       int frag, float eps, float* __restrict__ r,
+                                                       bf16_t* __restrict__ xf) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   if (row >= M) return;
@@ -261,15 +263,18 @@ __global__ __launch_bounds__(256) void rms_rows_kernel(const bf16_t* __restrict_
   float s = 0.f;
   for (int k = 8 * l; k < K; k += 512) {
     const bf16_t* p = frag ? x + fa_index(row, k, MT) : x + (size_t)row * K + k;
-    s += sumsq8(*reinterpret_cast<const uint4*>(p));
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    if (xf) *reinterpret_cast<uint4*>(xf + fa_index(row, k, MT)) = v;
+    s += sumsq8(v);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
   if (l == 0) r[row] = rsqrtf(s / (float)K + eps);
 }
 
-void launch_rms_rows(const bf16_t* x, int M, int K, bool frag, float eps, float* r, hipStream_t st) {
-  rms_rows_kernel<<<(M + 3) / 4, 256, 0, st>>>(x, M, K, frag ? 1 : 0, eps, r);
+void launch_rms_rows(const bf16_t* x, int M, int K, bool frag, float eps, float* r, bf16_t* xf,
+                     hipStream_t st) {
+  rms_rows_kernel<<<(M + 3) / 4, 256, 0, st>>>(x, M, K, frag ? 1 : 0, eps, r, xf);
 }
 
 }  // namespace blk

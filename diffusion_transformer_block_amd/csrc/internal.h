@@ -119,7 +119,7 @@ struct GemmArgs {
   const float* r;
 };
 
-// The large-chunk (M > 64) tiled GEMMs.
+// The large-chunk (M > 64) GEMMs; A in operand order (fa_index).
 void launch_gemm_qkv(const GemmArgs& ga, const EpiQKV& e, hipStream_t st);
 void launch_gemm_residual(const GemmArgs& ga, const EpiResidual& e, hipStream_t st);
 void launch_gemm_gateup(const GemmArgs& ga, const EpiGateUp& e, hipStream_t st);
@@ -129,7 +129,9 @@ constexpr int kSkinnyMaxM = 64;
 
 // ---------------------------------------------------------------- RMS statistics
 // r[m] = (sum_k x[m][k]^2 / K + eps)^-1/2
-void launch_rms_rows(const bf16_t* x, int M, int K, bool frag, float eps, float* r, hipStream_t st);
+// xf (may be NULL) receives a row-major x in operand order.
+void launch_rms_rows(const bf16_t* x, int M, int K, bool frag, float eps, float* r, bf16_t* xf,
+                     hipStream_t st);
 
 
 // ---------------------------------------------------------------- small-chunk path
