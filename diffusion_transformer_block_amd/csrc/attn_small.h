@@ -86,9 +86,10 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // if this workgroup wrote the block's final rows (a single key slice).
 // Row blocks are 64 rows: wave w takes 32 rows (w % 2) and one 32-key half
 // (w / 2) of every tile, and the halves merge at the end.  LONG (long key
-// runs, a single key slice only) makes them 128 rows: wave w takes 32 rows and
-// both key halves of every tile in turn, so a K/V tile serves twice the rows
-// and no merge is needed.
+// runs) makes them 128 rows: wave w takes 32 rows and both key halves of
+// every tile in turn, so a K/V tile serves twice the rows and no merge is
+// needed; its slice partials go out per 64-row half, as the merge step reads
+// them.
 template <int HD, bool LONG = false, class Wait>
 __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSmSmem<HD>& sm,
                              Wait&& wait) {
@@ -323,6 +324,18 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
           *reinterpret_cast<float4*>(dst + 32 * dt + 8 * q) =
               make_float4(o[dt][4 * q], o[dt][4 * q + 1], o[dt][4 * q + 2], o[dt][4 * q + 3]);
       if (hl == 0) inv_row[32 * rp + row32] = 1.f / l_tot;
+      if (a.splits > 1 && hl == 0) {
+        // this slice's (max, sum) of the row, by 64-row block
+        const int row = 32 * rp + row32, ar = 128 * rb + row;
+        const int n_rb64 = (rows + 63) >> 6;
+        const int sub = __builtin_amdgcn_readfirstlane((128 * rb + 32 * rp) >> 6);   // wave-uniform
+        if (ar < rows) {
+          const size_t rb_id = (size_t)bh * n_rb64 + sub;
+          const __amdgpu_buffer_rsrc_t rpm = make_rsrc(
+              a.part_ml + ((size_t)ks * a.B * a.Hkv * n_rb64 + rb_id) * 128, 512);
+          buf_st8(rpm, (ar & 63) * 8, __float_as_uint(m_run), __float_as_uint(l_tot));
+        }
+      }
     }
     __syncthreads();
     const int MTo = mt_of(a.B * a.T);
@@ -352,11 +365,23 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
       const int ch = (c >> 1) + (odd ? LPR / 2 : 0);
       const int ar = 128 * rb + row;
       if (ar < rows) {
-        const int t = ar / G, h = hk * G + (ar - t * G);
-        buf_st16(ro, (int)(fa_index(b * a.T + t, h * HD + 8 * ch, MTo) * 2), res[p]);
+        if (a.splits == 1) {
+          const int t = ar / G, h = hk * G + (ar - t * G);
+          buf_st16(ro, (int)(fa_index(b * a.T + t, h * HD + 8 * ch, MTo) * 2), res[p]);
+        } else {
+          // the slice's normalised partial row, in its 64-row block's slab
+          const int n_rb64 = (rows + 63) >> 6;
+          // a wave's rows of a pass lie in one 64-row block (wave-uniform)
+          const int sub = __builtin_amdgcn_readfirstlane((128 * rb + (w + 4 * p) * RPP) >> 6);
+          const size_t rb_id = (size_t)bh * n_rb64 + sub;
+          const size_t slab = (size_t)64 * HD;
+          const __amdgpu_buffer_rsrc_t rpo = make_rsrc(
+              a.part_o + ((size_t)ks * a.B * a.Hkv * n_rb64 + rb_id) * slab, slab * 2);
+          buf_st16(rpo, ((ar & 63) * HD + 8 * ch) * 2, res[p]);
+        }
       }
     }
-    return true;
+    return a.splits == 1;
   }
   const int kh = kh_w;
   float* park = reinterpret_cast<float*>(&sm.k[0][0]);   // [2 key halves][64 rows][PROW]

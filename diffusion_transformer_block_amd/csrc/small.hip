@@ -89,14 +89,18 @@ void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps, i
   const int G = Hq / Hkv;
   const int n_rbt = B * Hkv * ((G * T + 63) / 64);
   const int L = P + T;
-  // enough 128-row blocks to fill half the chip: one key slice each, 128 rows
-  // per K/V tile
-  // (long_rows == NULL: the caller runs 64-row blocks only)
+  // many 128-row blocks (long chunks): 128 rows per K/V tile, and key slices
+  // only as far as needed for about two workgroups per compute unit, each
+  // slice at least 4 tiles (long_rows == NULL: the caller runs 64-row blocks)
   const int n_rbt_long = B * Hkv * ((G * T + 127) / 128);
   if (long_rows) *long_rows = 0;
-  if (long_rows && n_rbt_long >= device_cus() / 2) {
-    *splits = 1;
-    *kps = (L + 31) / 32 * 32;
+  if (long_rows && n_rbt_long >= 32) {
+    int s = std::max(1, std::min(kAttnMaxSplits, (2 * device_cus() + n_rbt_long / 2) / n_rbt_long));
+    s = std::max(1, std::min(s, L / 256));
+    int k = (L + s - 1) / s;
+    k = (k + 63) / 64 * 64;
+    *kps = k;
+    *splits = (L + k - 1) / k;
     *long_rows = 1;
     return;
   }
@@ -108,9 +112,13 @@ void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps, i
   *splits = (L + k - 1) / k;
 }
 
+// partials of the larger of the two plans (with and without 128-row blocks):
+// both index them by 64-row block
 size_t attn_sm_part_o_elems(int B, int T, int P, int Hq, int Hkv, int d) {
-  int s = 1, k = 32;
-  attn_sm_plan(B, T, P, Hq, Hkv, &s, &k, nullptr);
+  int s0 = 1, s1 = 1, k = 32, lr = 0;
+  attn_sm_plan(B, T, P, Hq, Hkv, &s0, &k, nullptr);
+  attn_sm_plan(B, T, P, Hq, Hkv, &s1, &k, &lr);
+  const int s = std::max(s0, s1);
   if (s <= 1) return 0;
   const int n_rbt = B * Hkv * ((Hq / Hkv * T + 63) / 64);
   return (size_t)s * n_rbt * 64 * d;
@@ -219,13 +227,14 @@ static void attn_sm_launch(const AttnSmArgs& a, hipStream_t st) {
 template <int HD>
 static void attn_sm_go(const AttnSmArgs& a, hipStream_t st) {
   // (at HD 256 the 128-row variant spills; 64-row blocks over the one slice)
+  bool launched = false;
   if constexpr (HD <= 128) {
     if (a.long_rows) {
       attn_sm_launch<HD, true>(a, st);
-      return;
+      launched = true;
     }
   }
-  attn_sm_launch<HD, false>(a, st);
+  if (!launched) attn_sm_launch<HD, false>(a, st);
   if (a.splits > 1) {
     const int items = attn_combine_items(a.B, a.T, a.Hq, a.Hkv, HD);
     hipLaunchKernelGGL(attn_combine_kernel<HD>, dim3((items + 255) / 256), dim3(256), 0, st, a);

@@ -109,6 +109,12 @@ def test_ae_block_peaked_softmax():
                       tokens=65, prefix=200, hidden=256, ffn=384),
     synth.small_shape("mqa_d256_1x64_longP", n_q_heads=2, n_kv_heads=1, head_dim=256, batch=1,
                       tokens=64, prefix=3001, hidden=256, ffn=512),
+    # 128-row attention blocks with key slices, GQA, ragged rows (1040 per kv head)
+    synth.small_shape("gqa_d64_1x520_long", n_q_heads=8, n_kv_heads=4, head_dim=64, batch=1,
+                      tokens=520, prefix=1500, hidden=512, ffn=1024),
+    # 128-row attention blocks, one key slice, d = 128, two streams
+    synth.small_shape("mha_d128_2x300_long", n_q_heads=16, n_kv_heads=16, head_dim=128, batch=2,
+                      tokens=300, prefix=900, hidden=512, ffn=1024),
 ], ids=lambda s: s.name)
 def test_small_shapes(shape):
     check_block(shape, synth.block_case(shape))
@@ -145,6 +151,37 @@ def test_attention_branch_alone(qk_std):
     # that the concentrated softmax passes on; 2e-2 max|delta| there.
     _branch_check(shape, case, w, f"attention branch (qk_std={qk_std})",
                   rel=1e-2 if qk_std is None else 2e-2)
+
+
+LONG_SHAPES = [
+    synth.small_shape("gqa_d64_1x520_long", n_q_heads=8, n_kv_heads=4, head_dim=64, batch=1,
+                      tokens=520, prefix=1500, hidden=512, ffn=1024),
+    synth.small_shape("mha_d128_2x300_long", n_q_heads=16, n_kv_heads=16, head_dim=128, batch=2,
+                      tokens=300, prefix=900, hidden=512, ffn=1024),
+]
+
+
+@pytest.mark.parametrize("shape", LONG_SHAPES, ids=lambda s: s.name)
+def test_attention_dominates_output(shape):
+    """The attention branch made the bulk of y: x scaled by 2^-6 (exact in
+    bf16; RMSNorm is scale-free, so Q, K, V are unchanged), the FFN off and
+    peaked logits, so that a wrong or missing attention output (key slices,
+    128-row blocks, their merge) shows at the block tolerance -- with the
+    residual at full scale, attention averaged over ~2000 keys sits below it.
+    Bound: 2e-2 max|y|, as for the peaked AE case (bf16 Q / K rounding)."""
+    case = synth.block_case(shape, 0.1)
+    w = dict(case["weights"])
+    w["w_down"] = synth.Bf16(np.zeros_like(w["w_down"].bits), np.zeros_like(w["w_down"].f32))
+    for st in case["streams"]:
+        xs = st["x"].f32 * np.float32(2.0 ** -6)
+        st["x"] = synth.Bf16(synth.f32_to_bf16_bits(xs), xs)
+    say(f"{shape.name}: B={shape.batch} T={shape.tokens} P={shape.prefix} (x / 64, FFN off)")
+    y, _, _ = gpu_block(shape, case, w)
+    for b in range(shape.batch):
+        ry, _, _ = oracle_block(shape, case, b, weights=w)
+        e = max_err_ratio(y[b], ry)
+        say(f"  stream {b}: y {e:.2e}")
+        assert e <= 2e-2
 
 
 def test_ffn_branch_alone():
