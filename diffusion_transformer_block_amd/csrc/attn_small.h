@@ -177,6 +177,10 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
   uint4 qf[NDS];
 #pragma unroll
   for (int s = 0; s < NDS; ++s) qf[s] = buf_ld_act(rq, s * kFragBytes + l * 16);
+  // Let Q land here, once: otherwise the compiler's wait for Q sits at the
+  // head of the key loop, where (counters being in order) it waits for each
+  // step's K/V prefetch as well.  (vmcnt(0); expcnt, lgkmcnt left free)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   f32x16 o[NDT];
 #pragma unroll
@@ -201,48 +205,58 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
   // key rows 32 kh + 16 u + 4 hl + p16 / 4 (+ 8 for the second read)
   const int vt_off0 = (4 * hl + (p16 >> 2)) * VROW + 16 * ((l >> 4) & 1) + 4 * (p16 & 3);
 
+  // key halves this wave takes of every tile: both (LONG) or its own
+  constexpr int NH = LONG ? 2 : 1;
   auto step = [&](int it, auto cur_c) {
     constexpr int cur = decltype(cur_c)::value;   // LDS buffer of tile it
+    // ---- S^T (32 keys x 32 rows) of each half: K fragments read from LDS in
+    //      batches ahead of their MFMAs; the halves' chains (and at HD < 256
+    //      two per half) are independent
+    f32x16 sacc[NH], sacc2[NH];
 #pragma unroll
-    for (int khi = 0; khi < (LONG ? 2 : 1); ++khi) {
-    const int kh = LONG ? khi : kh_w;
-    const int vt_off = vt_off0 + 32 * kh * VROW;
-    const int base = key_begin + 64 * it + 32 * kh;
-    // ---- S^T (32 keys x 32 rows): K fragments read from LDS in batches of
-    //      8 ahead of their MFMAs, two independent accumulation chains
-    f32x16 sacc, sacc2;
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      sacc[v] = 0.f;
-      sacc2[v] = 0.f;
-    }
-    const bf16_t* kr = &sm.k[cur][(32 * kh + (l & 31)) * KROW + 8 * hl];
+      for (int v = 0; v < 16; ++v) {
+        sacc[h][v] = 0.f;
+        sacc2[h][v] = 0.f;
+      }
     constexpr int KB = NDS < 8 ? NDS : (HD >= 256 ? 4 : 8);   // registers bound the batch at HD 256
 #pragma unroll
     for (int s0 = 0; s0 < NDS; s0 += KB) {
-      uint4 kf[KB];
+      uint4 kf[NH][KB];
 #pragma unroll
-      for (int s = 0; s < KB; ++s) kf[s] = *reinterpret_cast<const uint4*>(kr + 16 * (s0 + s));
+      for (int h = 0; h < NH; ++h) {
+        const int kh = LONG ? h : kh_w;
+        const bf16_t* kr = &sm.k[cur][(32 * kh + (l & 31)) * KROW + 8 * hl];
 #pragma unroll
-      for (int s = 0; s < KB; s += 2) {
-        sacc = mfma32(as_bf16x8(kf[s]), as_bf16x8(qf[s0 + s]), sacc);
-        if (s + 1 < KB) {
-          if constexpr (HD >= 256)
-            sacc = mfma32(as_bf16x8(kf[s + 1]), as_bf16x8(qf[s0 + s + 1]), sacc);
-          else
-            sacc2 = mfma32(as_bf16x8(kf[s + 1]), as_bf16x8(qf[s0 + s + 1]), sacc2);
-        }
+        for (int s = 0; s < KB; ++s) kf[h][s] = *reinterpret_cast<const uint4*>(kr + 16 * (s0 + s));
       }
+#pragma unroll
+      for (int s = 0; s < KB; s += 2)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          sacc[h] = mfma32(as_bf16x8(kf[h][s]), as_bf16x8(qf[s0 + s]), sacc[h]);
+          if (s + 1 < KB) {
+            if constexpr (HD >= 256)
+              sacc[h] = mfma32(as_bf16x8(kf[h][s + 1]), as_bf16x8(qf[s0 + s + 1]), sacc[h]);
+            else
+              sacc2[h] = mfma32(as_bf16x8(kf[h][s + 1]), as_bf16x8(qf[s0 + s + 1]), sacc2[h]);
+          }
+        }
     }
-    sacc += sacc2;
-    // ---- online softmax in base 2
-    float x[16];
+    // ---- online softmax in base 2, one update for all of the wave's keys
+    float x[NH][16];
     float mloc = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = base + 8 * (v >> 2) + 4 * hl + (v & 3);
-      x[v] = key < key_end ? sacc[v] * a.scale_log2 : -INFINITY;
-      mloc = fmaxf(mloc, x[v]);
+    for (int h = 0; h < NH; ++h) {
+      sacc[h] += sacc2[h];
+      const int base = key_begin + 64 * it + 32 * (LONG ? h : kh_w);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = base + 8 * (v >> 2) + 4 * hl + (v & 3);
+        x[h][v] = key < key_end ? sacc[h][v] * a.scale_log2 : -INFINITY;
+        mloc = fmaxf(mloc, x[h][v]);
+      }
     }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
     // Rescale only when some row's max grew past the reference by more than
@@ -259,35 +273,43 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
     }
     // masked keys (and rows that have seen no key yet) contribute exactly 0
     float psum = 0.f;
-    uint32_t pw[8];
+    uint32_t pw[NH][8];
 #pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      const float p0 = x[v] == -INFINITY ? 0.f : exp2f(x[v] - m_run);
-      const float p1 = x[v + 1] == -INFINITY ? 0.f : exp2f(x[v + 1] - m_run);
-      psum += p0 + p1;
-      pw[v / 2] = pack2(p0, p1);
-    }
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const float p0 = x[h][v] == -INFINITY ? 0.f : exp2f(x[h][v] - m_run);
+        const float p1 = x[h][v + 1] == -INFINITY ? 0.f : exp2f(x[h][v + 1] - m_run);
+        psum += p0 + p1;
+        pw[h][v / 2] = pack2(p0, p1);
+      }
     l_run += psum;
-    // ---- O^T += V^T P^T, two 16-key steps (P^T slots e <-> S^T values 8 u + e)
+    // ---- O^T += V^T P^T, two 16-key steps per half (P^T slots e <-> S^T
+    //      values 8 u + e)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const bf16x8 pb = as_bf16x8(make_uint4(pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]));
-      const bf16_t* vt = &sm.v[cur][vt_off + 16 * u * VROW];
-      constexpr int VB = NDT < 4 ? NDT : 4;   // transposed reads issued ahead of their MFMAs
+    for (int h = 0; h < NH; ++h) {
+      const int vt_off = vt_off0 + 32 * (LONG ? h : kh_w) * VROW;
 #pragma unroll
-      for (int d0 = 0; d0 < NDT; d0 += VB) {
-        uint2 vlo[VB], vhi[VB];
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8 pb =
+            as_bf16x8(make_uint4(pw[h][4 * u], pw[h][4 * u + 1], pw[h][4 * u + 2], pw[h][4 * u + 3]));
+        const bf16_t* vt = &sm.v[cur][vt_off + 16 * u * VROW];
+        constexpr int VB = NDT < 4 ? NDT : 4;   // transposed reads issued ahead of their MFMAs
 #pragma unroll
-        for (int dt = 0; dt < VB; ++dt) {
-          vlo[dt] = lds_tr16(vt + 32 * (d0 + dt));
-          vhi[dt] = lds_tr16(vt + 8 * VROW + 32 * (d0 + dt));
+        for (int d0 = 0; d0 < NDT; d0 += VB) {
+          uint2 vlo[VB], vhi[VB];
+#pragma unroll
+          for (int dt = 0; dt < VB; ++dt) {
+            vlo[dt] = lds_tr16(vt + 32 * (d0 + dt));
+            vhi[dt] = lds_tr16(vt + 8 * VROW + 32 * (d0 + dt));
+          }
+#pragma unroll
+          for (int dt = 0; dt < VB; ++dt)
+            o[d0 + dt] =
+                mfma32(as_bf16x8(make_uint4(vlo[dt].x, vlo[dt].y, vhi[dt].x, vhi[dt].y)), pb, o[d0 + dt]);
         }
-#pragma unroll
-        for (int dt = 0; dt < VB; ++dt)
-          o[d0 + dt] = mfma32(as_bf16x8(make_uint4(vlo[dt].x, vlo[dt].y, vhi[dt].x, vhi[dt].y)), pb, o[d0 + dt]);
       }
     }
-    }   // key halves
     // ---- stage the next tile into the other buffer (last read one tile ago)
     //      and start the loads of the tile after it
     if (it + 1 < n_tiles) {
