@@ -51,14 +51,14 @@ OP_KERNELS = {
 # the SHA-256 of the kernel sources when the counters were taken: a changed
 # kernel reports null until it is profiled again.
 TRAFFIC = {
-    "qkv_rope": {"fetch": 6713549, "write": 622592, "bytes": 7336141, "sources": "a9c433870c5c4cdc"},
-    "attention": {"fetch": 7740621, "write": 4005888, "bytes": 11746509, "sources": "a9c433870c5c4cdc"},
-    "o_proj": {"fetch": 8750080, "write": 4465664, "bytes": 13215744, "sources": "a9c433870c5c4cdc"},
-    "gate_up": {"fetch": 18017280, "write": 1048576, "bytes": 19065856, "sources": "a9c433870c5c4cdc"},
-    "down": {"fetch": 14916813, "write": 4465664, "bytes": 19382477, "sources": "a9c433870c5c4cdc"},
+    "qkv_rope": {"fetch": 6634845, "write": 622592, "bytes": 7257437, "sources": "66ff8585158c690d"},
+    "attention": {"fetch": 6363013, "write": 4087808, "bytes": 10450821, "sources": "66ff8585158c690d"},
+    "o_proj": {"fetch": 7705740, "write": 2364416, "bytes": 10070156, "sources": "66ff8585158c690d"},
+    "gate_up": {"fetch": 18015122, "write": 1048576, "bytes": 19063698, "sources": "66ff8585158c690d"},
+    "down": {"fetch": 13877588, "write": 2364416, "bytes": 16242004, "sources": "66ff8585158c690d"},
 }
-TRAFFIC_FETCH_SCALE = 2.0   # FETCH_SIZE of a 256 MiB copy reads 128 MiB
-TRAFFIC_WRITE_SCALE = 1.0   # WRITE_SIZE of the same copy reads 256 MiB
+TRAFFIC_FETCH_SCALE = 2.000   # FETCH_SIZE of a 256 MiB copy reads 128 MiB
+TRAFFIC_WRITE_SCALE = 1.000   # WRITE_SIZE of the same copy reads 256 MiB
 TRAFFIC_SOURCES = ("common.h", "skinny.h", "attn_small.h", "small.hip")
 
 
