@@ -189,8 +189,9 @@ void launch_sk_gateup(const SkArgs& ga, int gpw, const EpiGateUpS& e, hipStream_
 }
 
 // ============================================================================ attention
+// (128-row mode: registers capped for two workgroups per compute unit)
 template <int HD, bool LONG>
-__global__ __launch_bounds__(256) void attn_sm_kernel(AttnSmArgs a, int n_rb) {
+__global__ __launch_bounds__(256, LONG ? 2 : 1) void attn_sm_kernel(AttnSmArgs a, int n_rb) {
   extern __shared__ __attribute__((aligned(16))) char at_dsm[];
   // Tasks in the order (stream x kv head, key slice, row block), row block
   // fastest; the hardware deals workgroups round-robin over the 8 XCDs, so
