@@ -234,12 +234,15 @@ static void launch_big(const GemmArgs& ga, const Epi& e, hipStream_t st) {
 }
 
 // 256 x 256 tiles where they fill the chip (about one workgroup per compute
-// unit or more), 128 x 128 otherwise.
+// unit or more), else 128 x 128 where those do, else 128 x 64.
 template <bool AFRAG, class Epi>
 static void launch_tiled(const GemmArgs& ga, const Epi& e, hipStream_t st) {
-  const long big_tiles = (long)((ga.M + 255) / 256) * ((ga.n_groups + 7) / 8);
-  if (big_tiles >= (long)device_cus() * 15 / 16) launch_big<256, 256, AFRAG>(ga, e, st);
-  else launch_big<128, 128, AFRAG>(ga, e, st);
+  const long cus = device_cus();
+  const long t256 = (long)((ga.M + 255) / 256) * ((ga.n_groups + 7) / 8);
+  const long t128 = (long)((ga.M + 127) / 128) * ((ga.n_groups + 3) / 4);
+  if (t256 >= cus * 15 / 16) launch_big<256, 256, AFRAG>(ga, e, st);
+  else if (t128 >= cus * 15 / 16) launch_big<128, 128, AFRAG>(ga, e, st);
+  else launch_big<128, 64, AFRAG>(ga, e, st);
 }
 
 // ============================================================================ dispatch
