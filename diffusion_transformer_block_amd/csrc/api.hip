@@ -161,6 +161,7 @@ int lookup(const void* packed, const blk_config& cfg, PackRecord* out) {
 struct BlockWs {
   size_t q, o, h, a, r1, r2, part;
   size_t ctr_qkv, ctr_o, ctr_gu, ctr_d;
+  size_t big_part, big_ctr;     // large-chunk GEMM K splits
   size_t sm_att_o, sm_att_ml;   // small-chunk attention key-slice partials
   size_t xb0, xb1, flags, sync;
   size_t total;
@@ -209,6 +210,21 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
   off += align_up((size_t)ggu * 4);
   w.ctr_d = off;
   off += align_up((size_t)gd * 4);
+  {
+    size_t bp = 0, bc = 0;
+    if (!small && M > 0) {
+      const int m = (int)M;
+      for (const BigPlan& pl : {big_plan(m, gq, D), big_plan(m, go, Hq * d), big_plan(m, ggu, D),
+                                big_plan(m, gd, F)}) {
+        bp = std::max(bp, big_part_floats(pl));
+        bc = std::max(bc, (size_t)pl.tiles);
+      }
+    }
+    w.big_part = off;
+    off += align_up(bp * 4);
+    w.big_ctr = off;
+    off += align_up(bc * 4);
+  }
   w.sm_att_o = off;
   off += align_up(attn_sm_part_o_elems(B, T, P, Hq, Hkv, d) * 2);
   w.sm_att_ml = off;
@@ -529,6 +545,8 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
 
   GemmArgs base{};
   base.M = M;
+  base.part = at<float>(ws, w.big_part);
+  base.ctr = at<unsigned>(ws, w.big_ctr);
 
   // 1. RMS(x) -> fused QKV GEMM with row scale and RoPE epilogue (Q in the
   //    attention's operand order)

@@ -65,7 +65,7 @@ __device__ __forceinline__ void dma16(unsigned lds, const void* gp) {
 // that stage's k-tile-0 fragments while its k-tile-1 MFMAs run; the DMA of
 // the stage after next goes out right after that barrier.
 template <int BM, int BN, bool AFRAG, class Epi>
-__global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int n_tm) {
+__global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int n_tm, int splits) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t big_dsm[];
   constexpr int BK = 64;
   constexpr int MTB = BM / 16;            // 16-row tiles per block
@@ -82,16 +82,19 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   // a contiguous run of tiles, taken in bands of GM row tiles with the column
   // tiles outer, so the tiles an XCD runs at once share row and column blocks
   // in its L2.
+  // A unit is (tile, K split), the splits of a tile adjacent.
   const int nwg = gridDim.x, id = blockIdx.x;
   const int xcd = id & 7, jx = id >> 3, qx = nwg >> 3, rx = nwg & 7;
-  const int tile = xcd * qx + min(xcd, rx) + jx;
+  const int unit = xcd * qx + min(xcd, rx) + jx;
+  const int tile = unit / splits, split = unit - tile * splits;
   constexpr int GM = 4;
-  const int n_tn = nwg / n_tm;
+  const int n_tn = nwg / splits / n_tm;
   const int band = tile / (GM * n_tn), tib = tile - band * GM * n_tn;
   const int rows_b = min(GM, n_tm - band * GM);
   const int tm = band * GM + tib % rows_b, tn = tib / rows_b;
   const int m0 = tm * BM, g0 = tn * GB;
-  const int KT = ga.K >> 5, nk = ga.K / BK;
+  const int KT = ga.K >> 5;
+  const int nk = ga.K / BK / splits, sk0 = split * nk;   // this split's K steps
   const int MTa = mt_of(ga.M);
 
   // this wave's fragments of a stage: f = w + 4 i (A fragments first); rows
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   auto issue = [&](int s, int buf) {
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      dma16(lds0 + buf * STAGE + (w + 4 * i) * kFragBytes, gsrc[i] + (size_t)s * gstep[i]);
+      dma16(lds0 + buf * STAGE + (w + 4 * i) * kFragBytes, gsrc[i] + (size_t)(sk0 + s) * gstep[i]);
   };
   auto rd = [&](int buf, int kt, uint4 (&af)[MTW], uint4 (&bfv)[GW][2]) {
     const uint8_t* base = big_dsm + buf * STAGE;
@@ -177,6 +180,48 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   }
   __syncthreads();
 
+  // ---- K splits: every split publishes its accumulators in MFMA layout (16
+  //      coherent bytes per lane); the last to arrive at the tile's counter
+  //      sums all of them in split order and runs the epilogue
+  if (splits > 1) {
+    constexpr int NACC = MTW * GW * 2;                  // f32x4 per lane
+    constexpr int SPLIT_BYTES = 4 * NACC * 64 * 16;     // one split of a tile
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc(ga.part + (size_t)tile * splits * (SPLIT_BYTES / 4), (size_t)splits * SPLIT_BYTES);
+    auto slot = [&](int sp, int q) { return sp * SPLIT_BYTES + ((w * NACC + q) * 64 + l) * 16; };
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+      for (int gg = 0; gg < GW; ++gg)
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const f32x4 v = acc[mt][gg][ii];
+          buf_st16(rp, slot(split, (mt * GW + gg) * 2 + ii),
+                   make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                              __float_as_uint(v[3])));
+        }
+    if (!arrive_last(&ga.ctr[tile], (unsigned)splits, reinterpret_cast<int*>(big_dsm))) return;
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+      for (int gg = 0; gg < GW; ++gg)
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int q = (mt * GW + gg) * 2 + ii;
+          f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int sp = 0; sp < splits; ++sp) {
+            f32x4 v = acc[mt][gg][ii];
+            if (sp != split) {
+              const uint4 u = buf_ld_act(rp, slot(sp, q));
+              v = f32x4{__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
+            }
+            sum += v;
+          }
+          acc[mt][gg][ii] = sum;
+        }
+    __syncthreads();   // the arrival flag's LDS word is reused below
+  }
+
   // ---- epilogue, 32 rows of the wave's tile at a time: math() in the MFMA
   //      layout into this wave's LDS region, then 16-byte row stores
   constexpr int LROW = 32 * GW + 4;       // floats per staged row
@@ -219,7 +264,7 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
 }
 
 template <int BM, int BN, bool AFRAG, class Epi>
-static void launch_big(const GemmArgs& ga, const Epi& e, hipStream_t st) {
+static void launch_big(const GemmArgs& ga, const Epi& e, int splits, hipStream_t st) {
   constexpr int NFR = (BM / 16) * 2 + (BN / 32) * 4;
   const size_t smem = 2 * (size_t)NFR * kFragBytes;
   auto kern = big_gemm_kernel<BM, BN, AFRAG, Epi>;
@@ -230,19 +275,34 @@ static void launch_big(const GemmArgs& ga, const Epi& e, hipStream_t st) {
     attr_set = true;
   }
   const int n_tm = (ga.M + BM - 1) / BM, n_tn = (ga.n_groups + BN / 32 - 1) / (BN / 32);
-  hipLaunchKernelGGL(kern, dim3(n_tm * n_tn), dim3(256), smem, st, ga, e, n_tm);
+  hipLaunchKernelGGL(kern, dim3(n_tm * n_tn * splits), dim3(256), smem, st, ga, e, n_tm, splits);
 }
 
 // 256 x 256 tiles where they fill the chip (about one workgroup per compute
-// unit or more), else 128 x 128 where those do, else 128 x 64.
+// unit or more), else 128 x 128 where those do, else 128 x 64.  Two K splits
+// (long K only) where they trim a mostly idle last round of tiles: rounds of
+// half-length units against whole ones.
+BigPlan big_plan(int M, int n_groups, int K) {
+  const long cus = device_cus();
+  auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((n_groups + bn / 32 - 1) / (bn / 32)); };
+  BigPlan p{128, 64, 1, 0};
+  if (tiles(256, 256) >= cus * 15 / 16) p = BigPlan{256, 256, 1, 0};
+  else if (tiles(128, 128) >= cus * 15 / 16) p = BigPlan{128, 128, 1, 0};
+  p.tiles = (int)tiles(p.bm, p.bn);
+  const long r1 = (p.tiles + cus - 1) / cus, r2 = (2L * p.tiles + cus - 1) / cus;   // r2 half-length rounds
+  if (K >= 4096 && (K / 64) % 2 == 0 && 10 * r2 <= 18 * r1) p.splits = 2;
+  return p;
+}
+size_t big_part_floats(const BigPlan& p) {
+  return p.splits > 1 ? (size_t)p.tiles * p.splits * p.bm * p.bn : 0;
+}
+
 template <bool AFRAG, class Epi>
 static void launch_tiled(const GemmArgs& ga, const Epi& e, hipStream_t st) {
-  const long cus = device_cus();
-  const long t256 = (long)((ga.M + 255) / 256) * ((ga.n_groups + 7) / 8);
-  const long t128 = (long)((ga.M + 127) / 128) * ((ga.n_groups + 3) / 4);
-  if (t256 >= cus * 15 / 16) launch_big<256, 256, AFRAG>(ga, e, st);
-  else if (t128 >= cus * 15 / 16) launch_big<128, 128, AFRAG>(ga, e, st);
-  else launch_big<128, 64, AFRAG>(ga, e, st);
+  const BigPlan p = big_plan(ga.M, ga.n_groups, ga.K);
+  if (p.bm == 256) launch_big<256, 256, AFRAG>(ga, e, p.splits, st);
+  else if (p.bn == 128) launch_big<128, 128, AFRAG>(ga, e, p.splits, st);
+  else launch_big<128, 64, AFRAG>(ga, e, p.splits, st);
 }
 
 // ============================================================================ dispatch

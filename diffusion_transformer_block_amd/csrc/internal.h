@@ -117,7 +117,18 @@ struct GemmArgs {
   int n_groups;
   // row scale r (the RMS statistic; may be NULL = 1)
   const float* r;
+  // K splits (big_plan) and their scratch: fp32 partial tiles and one
+  // self-resetting arrival counter per output tile (zero on entry)
+  float* part;
+  unsigned* ctr;
 };
+
+// Tile shape and K splits of a large-chunk GEMM, and the scratch they need.
+struct BigPlan {
+  int bm, bn, splits, tiles;
+};
+BigPlan big_plan(int M, int n_groups, int K);
+size_t big_part_floats(const BigPlan& p);
 
 // The large-chunk (M > 64) GEMMs; A in operand order (fa_index).
 void launch_gemm_qkv(const GemmArgs& ga, const EpiQKV& e, hipStream_t st);
