@@ -43,17 +43,18 @@ void launch_flow_embed(const FlowEmbedArgs& a, hipStream_t st) {
 }
 
 // One block per action row i: r = RMS(X[i + 1]); v[c] = r sum_k X[i+1][k] W_out'[k][c]
-// + b_out[c]; a_out[i][c] = a_in[i][c] + dt v[c].  Thread t takes k = t, t + 256, ...
-// and up to 32 columns at a time in registers, so all of its loads are independent
-// (one memory round trip); the 256 partial rows are summed through LDS in a fixed
-// order.  X is in operand order (fa_index, N + 1 rows).
+// + b_out[c]; a_out[i][c] = a_in[i][c] + dt v[c].  Thread t takes k = t, t + 256,
+// ... and 32 columns at a time, its W_out' rows as 16-byte loads (all of them
+// independent: one memory round trip); a wave folds its 64 lanes' 32 column
+// sums in 5 exchange rounds (each lane keeps half of what it holds and sends
+// the other half), the 4 waves' sums meet in LDS in a fixed order.  X is in
+// operand order (fa_index, N + 1 rows).
 __global__ __launch_bounds__(256) void flow_velocity_kernel(FlowVelArgs a) {
   constexpr int CW = 32;              // columns per pass
-  __shared__ float red[256][CW + 1];
-  __shared__ float part[8][CW];
+  __shared__ float part[4][64];
   __shared__ float wsum[4];
   const int i = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int MT = mt_of(a.N + 1);
   const int nk = (a.D + 255) / 256;   // k values per thread (D <= 8192: <= 32)
   float xk[32];
@@ -66,10 +67,11 @@ __global__ __launch_bounds__(256) void flow_velocity_kernel(FlowVelArgs a) {
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  if (l == 0) wsum[w] = ss;
   __syncthreads();
   const float r = rsqrtf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) / (float)a.D + a.eps);
   const float dt = *a.dt;
+  const bool vec = (a.A & 3) == 0;
   for (int c0 = 0; c0 < a.A; c0 += CW) {
     const int nc = min(CW, a.A - c0);
     float acc[CW];
@@ -80,28 +82,47 @@ __global__ __launch_bounds__(256) void flow_velocity_kernel(FlowVelArgs a) {
       const int k = tid + 256 * j;
       if (j < nk && k < a.D) {
         const float* wr = a.w_out + (size_t)k * a.A + c0;
+        if (vec && nc == CW) {
 #pragma unroll
-        for (int c = 0; c < CW; ++c)
-          if (c < nc) acc[c] = fmaf(xk[j], wr[c], acc[c]);
+          for (int c4 = 0; c4 < CW / 4; ++c4) {
+            const float4 wv = *reinterpret_cast<const float4*>(wr + 4 * c4);
+            acc[4 * c4] = fmaf(xk[j], wv.x, acc[4 * c4]);
+            acc[4 * c4 + 1] = fmaf(xk[j], wv.y, acc[4 * c4 + 1]);
+            acc[4 * c4 + 2] = fmaf(xk[j], wv.z, acc[4 * c4 + 2]);
+            acc[4 * c4 + 3] = fmaf(xk[j], wv.w, acc[4 * c4 + 3]);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < CW; ++c)
+            if (c < nc) acc[c] = fmaf(xk[j], wr[c], acc[c]);
+        }
       }
     }
+    // fold the wave: after the round with offset o (16, 8, 4, 2, 1) a lane
+    // holds the sums of o columns over 32 / o lanes; lanes with bit o set keep
+    // the upper half.  Column of lane l at the end: the bits of l & 31.
 #pragma unroll
-    for (int c = 0; c < CW; ++c) red[tid][c] = acc[c];
-    __syncthreads();
-    {
-      const int c = tid & (CW - 1), g = tid >> 5;
-      float v = 0.f;
-      for (int q = 0; q < 32; ++q) v += red[32 * g + q][c];
-      part[g][c] = v;
+    for (int o = 16; o >= 1; o >>= 1) {
+      const bool up = (l & o) != 0;
+#pragma unroll
+      for (int c = 0; c < o; ++c) {
+        const float send = up ? acc[c] : acc[c + o];
+        const float got = __shfl_xor(send, o);
+        acc[c] = (up ? acc[c + o] : acc[c]) + got;
+      }
     }
+    // lane l now holds column col(l) summed over its half-wave; add the other half
+    const float v = acc[0] + __shfl_xor(acc[0], 32);
+    int col = 0;
+#pragma unroll
+    for (int o = 16, b = 0; o >= 1; o >>= 1, ++b) col |= (l & o) ? o : 0;
+    if (l < 32) part[w][col] = v;
     __syncthreads();
     if (tid < nc) {
-      float v = 0.f;
-#pragma unroll
-      for (int g = 0; g < 8; ++g) v += part[g][tid];
-      v = v * r + a.b_out[c0 + tid];
+      float vs = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+      vs = vs * r + a.b_out[c0 + tid];
       const size_t o = (size_t)i * a.A + c0 + tid;
-      a.a_out[o] = a.a_in[o] + dt * v;
+      a.a_out[o] = a.a_in[o] + dt * vs;
     }
     __syncthreads();
   }
