@@ -10,13 +10,15 @@
 //
 // The rows of one (stream b, kv head hk) are the G = Hq / Hkv query heads of
 // each of the T tokens, row ar = t G + gh; they all read that kv head's keys,
-// so one K/V tile serves 64 rows.  A task takes 64 rows and one slice of the
-// keys, in steps of 64 keys:
+// so one K/V tile serves a block of rows.  A task takes a row block and one
+// slice of the keys, in steps of 64 keys:
 //  * K / V tiles are loaded with row-contiguous 16-byte loads one step ahead
 //    and staged through double-buffered LDS;
-//  * wave w takes 32 query rows (w % 2) and one 32-key half (w / 2) of every
-//    step, with 32 x 32 x 16 MFMAs (twice the operand reuse of 16 x 16 tiles:
-//    the LDS reads, not the MFMAs, bound this loop);
+//  * 64-row blocks: wave w takes 32 query rows (w % 2) and one 32-key half
+//    (w / 2) of every step; 128-row blocks (LONG, long key runs): wave w takes
+//    32 rows and both halves, so a tile serves twice the rows and the halves
+//    need no merge; 32 x 32 x 16 MFMAs throughout (twice the operand reuse of
+//    16 x 16 tiles);
 //  * S^T = K Q^T: K rows as the A operand (LDS), Q^T as the B operand held in
 //    registers (the QKV epilogue stores Q in exactly that operand order,
 //    qa_index), so a lane holds 16 keys of one query row;
@@ -29,8 +31,9 @@
 //    lane i of each 16-lane group element i % 4 of the 8 bytes at lane
 //    4 k + i / 4 (k < 4): pointing lane i at key row 4 k' + i / 4, dims
 //    4 (i % 4) .. + 3 yields V[key k][dim i] in that key order;
-//  * the two key halves meet in LDS; one key slice then writes the normalised
-//    rows straight into the O projection's operand order; several slices
+//  * (64-row blocks) the two key halves meet in LDS; one key slice then
+//    writes the normalised rows straight into the O projection's operand
+//    order (both modes); several slices
 //    publish bf16 partials normalised by their own sum plus (max, sum), which
 //    a separate merge step (attn_combine_task, one thread per 16 output
 //    bytes, all slices' loads in flight together) combines in slice order.

@@ -210,7 +210,8 @@ int blk_version(void);
  *     denoise loop, its workgroups handing off through flags in the workspace
  *     ([TR]-style execution without launch gaps); BLK_EUNSUPPORTED where it
  *     does not cover the shape.
- * Results agree within rounding.  Large chunks always use per-operator kernels.
+ * Results agree within rounding.  Large chunks (B*T > 64) always use
+ * per-operator kernels.
  * Errors: BLK_EINVAL for another value.
  */
 int blk_set_execution_mode(int mode);
