@@ -63,11 +63,17 @@ TRAFFIC_SOURCES = ("common.h", "skinny.h", "attn_small.h", "small.hip")
 
 
 def sources_digest():
+    """SHA-256 of the small-path kernel sources, comments and blank space
+    stripped (a comment edit does not invalidate measured traffic)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, "diffusion_transformer_block_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "diffusion_transformer_block_amd", "csrc", f)) as fh:
+            for line in fh:
+                code = re.sub(r"//.*", "", line).strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
