@@ -51,11 +51,11 @@ OP_KERNELS = {
 # the SHA-256 of the kernel sources when the counters were taken: a changed
 # kernel reports null until it is profiled again.
 TRAFFIC = {
-    "qkv_rope": {"fetch": 6634845, "write": 622592, "bytes": 7257437, "sources": "66ff8585158c690d"},
-    "attention": {"fetch": 6363013, "write": 4087808, "bytes": 10450821, "sources": "66ff8585158c690d"},
-    "o_proj": {"fetch": 7705740, "write": 2364416, "bytes": 10070156, "sources": "66ff8585158c690d"},
-    "gate_up": {"fetch": 18015122, "write": 1048576, "bytes": 19063698, "sources": "66ff8585158c690d"},
-    "down": {"fetch": 13877588, "write": 2364416, "bytes": 16242004, "sources": "66ff8585158c690d"},
+    "qkv_rope": {"fetch": 6634861, "write": 622592, "bytes": 7257453, "sources": "a742c4108202babe"},
+    "attention": {"fetch": 6369157, "write": 4087808, "bytes": 10456965, "sources": "a742c4108202babe"},
+    "o_proj": {"fetch": 7705709, "write": 2364416, "bytes": 10070125, "sources": "a742c4108202babe"},
+    "gate_up": {"fetch": 18015145, "write": 1048576, "bytes": 19063721, "sources": "a742c4108202babe"},
+    "down": {"fetch": 13877648, "write": 2364416, "bytes": 16242064, "sources": "a742c4108202babe"},
 }
 TRAFFIC_FETCH_SCALE = 2.000   # FETCH_SIZE of a 256 MiB copy reads 128 MiB
 TRAFFIC_WRITE_SCALE = 1.000   # WRITE_SIZE of the same copy reads 256 MiB
