@@ -58,21 +58,47 @@ struct AttnSmArgs {
   int B, T, P, Hq, Hkv;
   int splits, kps;        // key slices and keys per slice (multiple of 32)
   float scale_log2;       // log2(e) / sqrt(d)
-  bf16_t* part_o;         // [splits][n_rbt][64][d] (normalised partials)
+  bf16_t* part_o;         // [splits][n_rbt][64 * d] (normalised partials, attn_part_slot order)
   float* part_ml;         // [splits][n_rbt][64][2] (max, sum)
   int long_rows;          // 1: 128-row blocks over a single key slice (attn_sm_task LONG)
 };
 
 constexpr int kAttnMaxSplits = 16;
 
+// A slice partial of a 64-row block holds 16-byte chunks (row r < 64, 8-dim
+// chunk c) in the O projection's operand order, restricted to the block:
+// 16 rows x 4 chunks per group of 64 slots.  The attention's lanes then store
+// 512-byte runs, and the merge step reads one slot per thread, coalesced.
+__host__ __device__ inline int attn_part_slot(int r, int c) {
+  return ((c >> 2) * 4 + (r >> 4)) * 64 + (r & 15) + 16 * (c & 3);
+}
+
 template <int HD>
 struct AttnSmSmem {
-  // K / V tiles; after the key loop both arrays hold the two key halves'
-  // unnormalised rows [2][64][HD + 4] (fp32, fits in k and v together)
-  bf16_t k[2][64 * (HD + 8)];
-  bf16_t v[2][64 * (HD + 16)];
+  // K / V tiles of 64 key rows, unpadded: the 16-byte chunks of a row are
+  // XOR-swizzled (attn_swz_k / attn_swz_v) so that the fragment reads hit
+  // distinct banks.  After the key loop the K tiles carry the key-half
+  // hand-off.
+  bf16_t k[2][64 * HD];
+  bf16_t v[2][64 * HD];
   float2 mlh[2][64];                 // per key half and row: (max, sum)
 };
+
+// Physical 16-byte chunk of logical chunk c of tile row r is c ^ swz(r).
+// K is read as MFMA A fragments: 16 lanes take 16 consecutive rows at one
+// chunk, so the swizzle must spread 16 rows over the 16 four-bank groups.
+// V is read with ds_read_b64_tr_b16: 16 lanes take 4 consecutive rows x 4
+// consecutive chunks (aligned to 4), so 4 rows must land in distinct groups
+// of 4 chunks.  At HD 64 a row is 8 chunks (half the banks), so row parity
+// contributes the other half.
+template <int HD>
+__device__ __forceinline__ int attn_swz_k(int r) {
+  return HD >= 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int HD>
+__device__ __forceinline__ int attn_swz_v(int r) {
+  return HD >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
 
 __device__ __forceinline__ uint2 lds_tr16(const bf16_t* p) {
   typedef short v4s __attribute__((ext_vector_type(4)));
@@ -94,20 +120,27 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // needed; its slice partials go out per 64-row half, as the merge step reads
 // them.
 template <int HD, bool LONG = false, class Wait>
-__device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSmSmem<HD>& sm,
+__device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_in, AttnSmSmem<HD>& sm,
                              Wait&& wait) {
-  constexpr int KROW = HD + 8, VROW = HD + 16;
+  // task coordinates are workgroup-uniform; saying so keeps every buffer
+  // descriptor built from them in scalar registers
+  const int bh = __builtin_amdgcn_readfirstlane(bh_in);
+  const int rb = __builtin_amdgcn_readfirstlane(rb_in);
+  const int ks = __builtin_amdgcn_readfirstlane(ks_in);
   constexpr int NDS = HD / 16;                 // 16-wide d steps of S^T (32x32x16)
   constexpr int NDT = HD / 32;                 // 32-row d tiles of O^T
   constexpr int CPR = HD / 8;                  // 16-byte chunks per key row
-  constexpr int NCH = 64 * CPR / 256;          // chunks per thread per 64-key tile (K or V)
+  constexpr int NCH = 64 * CPR / 256;          // DMA passes per 64-key tile (K or V)
+  constexpr unsigned TILE_BYTES = 64 * HD * 2;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int l = tid & 63;
   const int rp = LONG ? w : (w & 1);          // 32-row tile of the block
   const int kh_w = w >> 1;                     // the wave's 32-key half of a tile (not LONG)
-  const int b = bh / a.Hkv, hk = bh - b * a.Hkv;
-  const int G = a.Hq / a.Hkv;
+  // (integer division runs on the vector unit; readfirstlane keeps the
+  // quotients scalar)
+  const int b = __builtin_amdgcn_readfirstlane(bh / a.Hkv), hk = bh - b * a.Hkv;
+  const int G = __builtin_amdgcn_readfirstlane(a.Hq / a.Hkv);
   const int rows = G * a.T;
   const int n_rt = (rows + 31) >> 5;           // 32-row tiles of this (stream, kv head)
   const int L = a.P + a.T;
@@ -116,74 +149,65 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
   const int n_tiles = (key_end - key_begin + 63) >> 6;
   const int kvrow = a.Hkv * HD;
 
-  // K / V sources: prefix (caller's cache, read once) and the chunk's own rows
-  // (written by the QKV step, possibly earlier in the same launch: coherent)
-  const __amdgpu_buffer_rsrc_t rkp =
-      make_rsrc(a.kp ? a.kp + (size_t)b * a.prefix_stride + (size_t)hk * HD : a.kn, (size_t)a.P * kvrow * 2);
-  const __amdgpu_buffer_rsrc_t rvp =
-      make_rsrc(a.vp ? a.vp + (size_t)b * a.prefix_stride + (size_t)hk * HD : a.vn, (size_t)a.P * kvrow * 2);
-  const __amdgpu_buffer_rsrc_t rkn = make_rsrc(a.kn + (size_t)b * a.new_stride + (size_t)hk * HD, (size_t)a.T * kvrow * 2);
-  const __amdgpu_buffer_rsrc_t rvn = make_rsrc(a.vn + (size_t)b * a.new_stride + (size_t)hk * HD, (size_t)a.T * kvrow * 2);
-  uint4 reg[2][NCH];   // one tile in flight: [K, V][chunk]
-  // thread tid moves 16-byte chunk c0 of key rows kk0 + j RPJ, j < NCH
+  // K / V sources: prefix (caller's cache, read once: streaming) and the
+  // chunk's own rows (written by the QKV step, possibly earlier in the same
+  // launch: device-coherent loads)
+  const bf16_t* kpb = a.kp ? a.kp + (size_t)b * a.prefix_stride + (size_t)hk * HD : nullptr;
+  const bf16_t* vpb = a.vp ? a.vp + (size_t)b * a.prefix_stride + (size_t)hk * HD : nullptr;
+  const bf16_t* knb = a.kn + (size_t)b * a.new_stride + (size_t)hk * HD;
+  const bf16_t* vnb = a.vn + (size_t)b * a.new_stride + (size_t)hk * HD;
+  // Tiles move by LDS DMA, 1 KiB per wave and pass: thread tid fills 16-byte
+  // slot c0 of tile rows kk0 + j RPJ (j < NCH) with the row's logical chunk
+  // c0 ^ swz(row).  Rows past the slice repeat its last key (finite values;
+  // their scores are masked and their probabilities are exactly 0).
   constexpr int RPJ = 256 / CPR;               // key rows per pass of the workgroup
   const int kk0 = tid / CPR, c0 = tid - kk0 * CPR;
-  auto load_tile = [&](int tile) {
-    const int base = key_begin + 64 * tile + kk0;
-    if (base - kk0 + 64 <= a.P) {   // wholly in the prefix (uniform)
-      const int off0 = (base * kvrow + 8 * c0) * 2;
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        reg[0][j] = buf_ld_stream(rkp, off0 + j * RPJ * kvrow * 2);
-        reg[1][j] = buf_ld_stream(rvp, off0 + j * RPJ * kvrow * 2);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const int key = base + j * RPJ;
-        if (key >= key_end) {
-          reg[0][j] = make_uint4(0, 0, 0, 0);
-          reg[1][j] = make_uint4(0, 0, 0, 0);
-        } else if (key < a.P) {
-          const int off = (key * kvrow + 8 * c0) * 2;
-          reg[0][j] = buf_ld_stream(rkp, off);
-          reg[1][j] = buf_ld_stream(rvp, off);
-        } else {
-          const int off = ((key - a.P) * kvrow + 8 * c0) * 2;
-          reg[0][j] = buf_ld_act(rkn, off);
-          reg[1][j] = buf_ld_act(rvn, off);
-        }
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    bf16_t* kd = &sm.k[buf][kk0 * KROW + 8 * c0];
-    bf16_t* vd = &sm.v[buf][kk0 * VROW + 8 * c0];
+  const unsigned lds_k = lds_u32(&sm.k[0][0]), lds_v = lds_u32(&sm.v[0][0]);
+  auto load_tile = [&](int tile, int buf) {
+    const int row0 = key_begin + 64 * tile;
+    const bool prefix_only = row0 + 64 <= a.P;   // uniform
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      *reinterpret_cast<uint4*>(kd + j * RPJ * KROW) = reg[0][j];
-      *reinterpret_cast<uint4*>(vd + j * RPJ * VROW) = reg[1][j];
+      const int r = kk0 + j * RPJ;
+      const int key = min(row0 + r, key_end - 1);
+      const bool pre = key < a.P;
+      const size_t ro = (size_t)(pre ? key : key - a.P) * kvrow;
+      const bf16_t* kg = (pre ? kpb : knb) + ro + 8 * (c0 ^ attn_swz_k<HD>(r));
+      const bf16_t* vg = (pre ? vpb : vnb) + ro + 8 * (c0 ^ attn_swz_v<HD>(r));
+      const unsigned off = buf * TILE_BYTES + (j * 256 + w * 64) * 16;
+      if (prefix_only) {
+        dma16_nt(lds_k + off, kg);
+        dma16_nt(lds_v + off, vg);
+      } else {
+        dma16_sc1(lds_k + off, kg);
+        dma16_sc1(lds_v + off, vg);
+      }
     }
   };
 
+  __syncthreads();   // a previous task's readers of sm are done (the DMA writes it)
   // the first tile, if wholly in the prefix, does not depend on earlier work
   // and starts before the wait
   const bool pre0 = key_begin + 64 <= a.P;
-  if (n_tiles > 0 && pre0) load_tile(0);
-  if (!wait()) return false;
-  if (n_tiles > 0 && !pre0) load_tile(0);
+  if (n_tiles > 0 && pre0) load_tile(0, 0);
+  if (!wait()) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // no DMA may land after the workgroup ends
+    return false;
+  }
+  if (n_tiles > 0 && !pre0) load_tile(0, 0);
 
   // this wave's 32 query rows: Q^T fragments (B operand), one per d step
-  const int rt = min((LONG ? 4 : 2) * rb + rp, n_rt - 1);
+  const int rt = __builtin_amdgcn_readfirstlane(min((LONG ? 4 : 2) * rb + rp, n_rt - 1));
   const __amdgpu_buffer_rsrc_t rq =
       make_rsrc(a.q + (size_t)(bh * n_rt + rt) * NDS * 512, (size_t)NDS * kFragBytes);
   uint4 qf[NDS];
 #pragma unroll
   for (int s = 0; s < NDS; ++s) qf[s] = buf_ld_act(rq, s * kFragBytes + l * 16);
-  // Let Q land here, once: otherwise the compiler's wait for Q sits at the
-  // head of the key loop, where (counters being in order) it waits for each
-  // step's K/V prefetch as well.  (vmcnt(0); expcnt, lgkmcnt left free)
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // Q and tile 0 land here, before tile 1 is issued: the compiler counts
+  // only Q among the loads, and a DMA still in flight behind Q would make
+  // its waits for Q (at the head of the key loop) wait for that DMA too.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  if (n_tiles > 1) load_tile(1, 1);
 
   f32x16 o[NDT];
 #pragma unroll
@@ -192,29 +216,29 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
     for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
   // running reference max (may trail the true max by up to 2^8, see below) and sum
   float m_run = -INFINITY, l_run = 0.f;
-
-  __syncthreads();   // a previous task's readers of sm are done
-  if (n_tiles > 0) {
-    store_tile(0);
-    if (n_tiles > 1) load_tile(1);
-  }
   __syncthreads();
 
   // lane roles: query row l % 32 of this wave's 32 rows; S^T keys
   // 32 kh + 8 (v/4) + 4 (l/32) + v%4 of the 64-key tile, v < 16
   const int hl = l >> 5;
   const int p16 = l & 15;
+  // K fragment (A operand): row 32 kh + l % 32, logical chunk 2 s + hl, i.e.
+  // physical chunk 2 s ^ xk: byte (32 s) ^ kx of the row
+  const unsigned kx = 16 * (hl ^ attn_swz_k<HD>(l & 31));
   // V^T operand (transposed LDS reads): d = 32 dt + 16 ((l/16) % 2) + 4 (p16 % 4),
-  // key rows 32 kh + 16 u + 4 hl + p16 / 4 (+ 8 for the second read)
-  const int vt_off0 = (4 * hl + (p16 >> 2)) * VROW + 16 * ((l >> 4) & 1) + 4 * (p16 & 3);
+  // key rows 32 kh + 16 u + 4 hl + p16 / 4 (+ 8 for the second read): logical
+  // chunk 4 dt + cl, physical 4 (dt ^ (swz / 4)) + cl, byte (64 dt) ^ vx + 16 cl
+  const int vrow = 4 * hl + (p16 >> 2);
+  const unsigned vt_off0 = vrow * HD * 2 + 16 * (2 * ((l >> 4) & 1) + ((p16 & 3) >> 1)) + 8 * (p16 & 1);
+  const unsigned vx = 16 * attn_swz_v<HD>(vrow);
 
   // key halves this wave takes of every tile: both (LONG) or its own
   constexpr int NH = LONG ? 2 : 1;
   auto step = [&](int it, auto cur_c) {
     constexpr int cur = decltype(cur_c)::value;   // LDS buffer of tile it
     // ---- S^T (32 keys x 32 rows) of each half: K fragments read from LDS in
-    //      batches ahead of their MFMAs; the halves' chains (and at HD < 256
-    //      two per half) are independent
+    //      batches ahead of their MFMAs; each half runs two independent
+    //      chains (even and odd d steps)
     f32x16 sacc[NH], sacc2[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h)
@@ -223,28 +247,25 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
         sacc[h][v] = 0.f;
         sacc2[h][v] = 0.f;
       }
-    constexpr int KB = NDS < 8 ? NDS : (HD >= 256 ? 4 : 8);   // registers bound the batch at HD 256
+    constexpr int KB = NDS < 8 ? NDS : 8;   // K fragments read ahead of their MFMAs
 #pragma unroll
     for (int s0 = 0; s0 < NDS; s0 += KB) {
       uint4 kf[NH][KB];
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
         const int kh = LONG ? h : kh_w;
-        const bf16_t* kr = &sm.k[cur][(32 * kh + (l & 31)) * KROW + 8 * hl];
+        const uint8_t* kr = reinterpret_cast<const uint8_t*>(&sm.k[cur][(32 * kh + (l & 31)) * HD]);
 #pragma unroll
-        for (int s = 0; s < KB; ++s) kf[h][s] = *reinterpret_cast<const uint4*>(kr + 16 * (s0 + s));
+        for (int s = 0; s < KB; ++s)
+          kf[h][s] = *reinterpret_cast<const uint4*>(kr + ((32u * (s0 + s)) ^ kx));
       }
 #pragma unroll
       for (int s = 0; s < KB; s += 2)
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
           sacc[h] = mfma32(as_bf16x8(kf[h][s]), as_bf16x8(qf[s0 + s]), sacc[h]);
-          if (s + 1 < KB) {
-            if constexpr (HD >= 256)
-              sacc[h] = mfma32(as_bf16x8(kf[h][s + 1]), as_bf16x8(qf[s0 + s + 1]), sacc[h]);
-            else
-              sacc2[h] = mfma32(as_bf16x8(kf[h][s + 1]), as_bf16x8(qf[s0 + s + 1]), sacc2[h]);
-          }
+          if (s + 1 < KB)
+            sacc2[h] = mfma32(as_bf16x8(kf[h][s + 1]), as_bf16x8(qf[s0 + s + 1]), sacc2[h]);
         }
     }
     // ---- online softmax in base 2, one update for all of the wave's keys
@@ -291,20 +312,21 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
     //      values 8 u + e)
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      const int vt_off = vt_off0 + 32 * (LONG ? h : kh_w) * VROW;
+      const unsigned vt_off = vt_off0 + 32 * (LONG ? h : kh_w) * HD * 2;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const bf16x8 pb =
             as_bf16x8(make_uint4(pw[h][4 * u], pw[h][4 * u + 1], pw[h][4 * u + 2], pw[h][4 * u + 3]));
-        const bf16_t* vt = &sm.v[cur][vt_off + 16 * u * VROW];
+        const uint8_t* vt = reinterpret_cast<const uint8_t*>(&sm.v[cur][0]) + vt_off + 16 * u * HD * 2;
         constexpr int VB = NDT < 4 ? NDT : 4;   // transposed reads issued ahead of their MFMAs
 #pragma unroll
         for (int d0 = 0; d0 < NDT; d0 += VB) {
           uint2 vlo[VB], vhi[VB];
 #pragma unroll
           for (int dt = 0; dt < VB; ++dt) {
-            vlo[dt] = lds_tr16(vt + 32 * (d0 + dt));
-            vhi[dt] = lds_tr16(vt + 8 * VROW + 32 * (d0 + dt));
+            const unsigned dx = (64u * (d0 + dt)) ^ vx;
+            vlo[dt] = lds_tr16(reinterpret_cast<const bf16_t*>(vt + dx));
+            vhi[dt] = lds_tr16(reinterpret_cast<const bf16_t*>(vt + 8 * HD * 2 + dx));
           }
 #pragma unroll
           for (int dt = 0; dt < VB; ++dt)
@@ -313,183 +335,142 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh, int rb, int ks, AttnSm
         }
       }
     }
-    // ---- stage the next tile into the other buffer (last read one tile ago)
-    //      and start the loads of the tile after it
-    if (it + 1 < n_tiles) {
-      store_tile(cur ^ 1);
-      if (it + 2 < n_tiles) load_tile(it + 2);
-    }
+    // ---- tile it + 1 (the only loads in flight) has landed in the other
+    //      buffer once every wave has waited for its own DMA; then refill
+    //      this buffer, which no wave reads any more, with tile it + 2
+    if (it + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
+    if (it + 2 < n_tiles) load_tile(it + 2, cur);
   };
   for (int it = 0; it < n_tiles; it += 2) {
     step(it, std::integral_constant<int, 0>{});
     if (it + 1 < n_tiles) step(it + 1, std::integral_constant<int, 1>{});
   }
 
-  // ---- merge the two key halves: every wave parks its unnormalised O^T rows
-  //      (fp32) and (max, sum) in LDS -- the K / V tiles are no longer read --
-  //      then all 256 threads combine 16-byte output chunks and store them
-  //      (one key slice: the O projection's operand order; several: this
-  //      slice's normalised bf16 partial and its (max, sum))
+  // ---- epilogue.  Lane l holds O^T slots v of query row l % 32: dims
+  //      32 dt + 8 (v / 4) + 4 (l / 32) + v % 4.  Its four values of an 8-dim
+  //      output chunk pair up with the other four in lane l ^ 32 through
+  //      v_permlane32_swap, so every lane stores whole 16-byte chunks: the
+  //      normalised rows in the O projection's operand order (one key slice),
+  //      or this slice's normalised bf16 partial and its (max, sum) per row
+  //      (several).  Upper lanes give dims 4..7 of chunk 2 j and take dims
+  //      0..3 of chunk 2 j + 1, so lane l ends with dims 16 j + 8 (l / 32) + 0..7.
   const float l_tot = l_run + __shfl_xor(l_run, 32);   // the two lanes of a row share m_run
-  constexpr int PROW = HD + 4;
-  if constexpr (LONG) {
-    // ---- every wave holds its rows' whole result: park them (fp32, with
-    //      1 / sum) in LDS and store the 128 rows in the O projection's
-    //      operand order, 16 bytes per lane as in the merge below
-    float* park = reinterpret_cast<float*>(&sm.k[0][0]);   // [128 rows][PROW]
-    float* inv_row = &sm.mlh[0][0].x;                        // [128]
-    const int row32 = l & 31;
-    {
-      float* dst = park + (32 * rp + row32) * PROW + 4 * hl;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<float4*>(dst + 32 * dt + 8 * q) =
-              make_float4(o[dt][4 * q], o[dt][4 * q + 1], o[dt][4 * q + 2], o[dt][4 * q + 3]);
-      if (hl == 0) inv_row[32 * rp + row32] = 1.f / l_tot;
-      if (a.splits > 1 && hl == 0) {
-        // this slice's (max, sum) of the row, by 64-row block
-        const int row = 32 * rp + row32, ar = 128 * rb + row;
-        const int n_rb64 = (rows + 63) >> 6;
-        const int sub = __builtin_amdgcn_readfirstlane((128 * rb + 32 * rp) >> 6);   // wave-uniform
-        if (ar < rows) {
-          const size_t rb_id = (size_t)bh * n_rb64 + sub;
-          const __amdgpu_buffer_rsrc_t rpm = make_rsrc(
-              a.part_ml + ((size_t)ks * a.B * a.Hkv * n_rb64 + rb_id) * 128, 512);
-          buf_st8(rpm, (ar & 63) * 8, __float_as_uint(m_run), __float_as_uint(l_tot));
-        }
-      }
-    }
-    __syncthreads();
-    const int MTo = mt_of(a.B * a.T);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o, (size_t)MTo * 16 * a.Hq * HD * 2);
-    constexpr int LPR = HD / 8, RPP = 64 / LPR, PASSES = 128 / (4 * RPP);
-    const int c = l % LPR, odd = c & 1;
-    uint4 res[PASSES];
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int row = (w + 4 * p) * RPP + l / LPR;
-      const float inv = inv_row[row];
-      const float* p0 = park + row * PROW;
-      uint2 half[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float4 x = *reinterpret_cast<const float4*>(p0 + 4 * (LPR * e + c));
-        half[e] = make_uint2(pack2(x.x * inv, x.y * inv), pack2(x.z * inv, x.w * inv));
-      }
-      const uint2 give = odd ? half[0] : half[1];
-      const uint2 got = make_uint2(__shfl_xor(give.x, 1), __shfl_xor(give.y, 1));
-      res[p] = odd ? make_uint4(got.x, got.y, half[1].x, half[1].y)
-                   : make_uint4(half[0].x, half[0].y, got.x, got.y);
-    }
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int row = (w + 4 * p) * RPP + l / LPR;
-      const int ch = (c >> 1) + (odd ? LPR / 2 : 0);
-      const int ar = 128 * rb + row;
-      if (ar < rows) {
-        if (a.splits == 1) {
-          const int t = ar / G, h = hk * G + (ar - t * G);
-          buf_st16(ro, (int)(fa_index(b * a.T + t, h * HD + 8 * ch, MTo) * 2), res[p]);
-        } else {
-          // the slice's normalised partial row, in its 64-row block's slab
-          const int n_rb64 = (rows + 63) >> 6;
-          // a wave's rows of a pass lie in one 64-row block (wave-uniform)
-          const int sub = __builtin_amdgcn_readfirstlane((128 * rb + (w + 4 * p) * RPP) >> 6);
-          const size_t rb_id = (size_t)bh * n_rb64 + sub;
-          const size_t slab = (size_t)64 * HD;
-          const __amdgpu_buffer_rsrc_t rpo = make_rsrc(
-              a.part_o + ((size_t)ks * a.B * a.Hkv * n_rb64 + rb_id) * slab, slab * 2);
-          buf_st16(rpo, ((ar & 63) * HD + 8 * ch) * 2, res[p]);
-        }
-      }
-    }
-    return a.splits == 1;
-  }
-  const int kh = kh_w;
-  float* park = reinterpret_cast<float*>(&sm.k[0][0]);   // [2 key halves][64 rows][PROW]
+  auto chunk_of = [&](const float (&v)[8]) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(pack2(v[0], v[1]), pack2(v[4], v[5]), false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(pack2(v[2], v[3]), pack2(v[6], v[7]), false, false);
+    return make_uint4(s0[0], s1[0], s0[1], s1[1]);
+  };
   const int row32 = l & 31;
-  {
-    float* dst = park + (kh * 64 + rp * 32 + row32) * PROW + 4 * hl;
+  const int MTo = mt_of(a.B * a.T);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o, (size_t)MTo * 16 * a.Hq * HD * 2);
+  const size_t slab = (size_t)64 * HD;     // bf16 per (slice, 64-row block)
+  const int n_rb64 = (rows + 63) >> 6;
+  const int n_rbt64 = a.B * a.Hkv * n_rb64;
+  if constexpr (LONG) {
+    // ---- every wave holds its rows' whole result: normalise and store
+    const int arow = 128 * rb + 32 * rp + row32;
+    const bool live = arow < rows;
+    const float inv = 1.f / l_tot;
+    // the 64-row block of this wave's rows (uniform; past the last block
+    // only for a wave with no live rows, which stores nothing)
+    const int rb_id = __builtin_amdgcn_readfirstlane(bh * n_rb64 + ((128 * rb + 32 * rp) >> 6));
+    const __amdgpu_buffer_rsrc_t rpo =
+        make_rsrc(a.part_o + ((size_t)ks * n_rbt64 + rb_id) * slab, a.splits > 1 ? slab * 2 : 0);
+    const int t = arow / G, hq = hk * G + (arow - t * G);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * q) =
-            make_float4(o[dt][4 * q], o[dt][4 * q + 1], o[dt][4 * q + 2], o[dt][4 * q + 3]);
-    if (hl == 0) sm.mlh[kh][rp * 32 + row32] = make_float2(m_run, l_tot);
+      for (int j = 0; j < 2; ++j) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = o[dt][8 * j + e] * inv;
+        const uint4 chunk = chunk_of(v);
+        const int dd = 32 * dt + 16 * j + 8 * hl;
+        if (live) {
+          if (a.splits == 1)
+            buf_st16(ro, (int)(fa_index(b * a.T + t, hq * HD + dd, MTo) * 2), chunk);
+          else
+            buf_st16(rpo, attn_part_slot(arow & 63, dd >> 3) * 16, chunk);
+        }
+      }
+    if (a.splits > 1 && hl == 0 && live) {
+      const __amdgpu_buffer_rsrc_t rpm = make_rsrc(a.part_ml + ((size_t)ks * n_rbt64 + rb_id) * 128, 512);
+      buf_st8(rpm, (arow & 63) * 8, __float_as_uint(m_run), __float_as_uint(l_tot));
+    }
+    return a.splits == 1;
   }
+  // ---- merge the two key halves (64-row blocks).  The waves of a pair hold
+  //      the same 32 rows over different keys; each merges half of the d
+  //      tiles: it hands the partner's half of its unnormalised O^T registers
+  //      to LDS in register order (lane-contiguous 16-byte slots, no bank
+  //      conflicts), reads the partner's copy of its own half, and combines
+  //      and stores slot by slot as above.
+  constexpr int NH2 = NDT / 2;   // d tiles each wave of a pair merges
+  static_assert(sizeof(sm.k) >= sizeof(float4) * 4 * NH2 * 4 * 64, "hand-off slots fit in the K tiles");
+  float4* hand = reinterpret_cast<float4*>(&sm.k[0][0]);   // [row tile][dest half][NH2 * 4][64 lanes]
+  auto give = [&](auto off_c) {
+    constexpr int off = decltype(off_c)::value;   // first d tile the partner merges
+    float4* dst = hand + (rp * 2 + (kh_w ^ 1)) * (NH2 * 4 * 64) + l;
+#pragma unroll
+    for (int i = 0; i < NH2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        dst[(4 * i + q) * 64] = make_float4(o[off + i][4 * q], o[off + i][4 * q + 1],
+                                            o[off + i][4 * q + 2], o[off + i][4 * q + 3]);
+  };
+  if (kh_w == 0)
+    give(std::integral_constant<int, NH2>{});
+  else
+    give(std::integral_constant<int, 0>{});
+  if (hl == 0) sm.mlh[kh_w][rp * 32 + row32] = make_float2(m_run, l_tot);
   __syncthreads();
 
-  const int n_rb = (rows + 63) >> 6;
-  const int rb_id = bh * n_rb + rb;
-  const int n_rbt = a.B * a.Hkv * n_rb;
-  const size_t slab = (size_t)64 * HD;     // bf16 per (slice, row block)
-  const int MTo = mt_of(a.B * a.T);
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o, (size_t)MTo * 16 * a.Hq * HD * 2);
+  const float2 pm = sm.mlh[kh_w ^ 1][rp * 32 + row32];
+  const float mm = fmaxf(m_run, pm.x);
+  const float a_own = m_run == -INFINITY ? 0.f : exp2f(m_run - mm);
+  const float a_oth = pm.x == -INFINITY ? 0.f : exp2f(pm.x - mm);
+  const float lsum = l_tot * a_own + pm.y * a_oth;   // > 0: key half 0 of a slice has a key
+  const float s_own = a_own / lsum, s_oth = a_oth / lsum;
+  const int row64 = 32 * rp + row32, arow = 64 * rb + row64;
+  const bool live = arow < rows;
+  const int rb_id = __builtin_amdgcn_readfirstlane(bh * n_rb64 + rb);
   const __amdgpu_buffer_rsrc_t rpo =
-      make_rsrc(a.part_o + ((size_t)ks * n_rbt + rb_id) * slab, a.splits > 1 ? slab * 2 : 0);
-  // LPR = HD / 8 lanes share a row: lane c reads float4 c and LPR + c of
-  // both halves (adjacent lanes, adjacent 16 bytes: no LDS bank conflicts),
-  // combines each into four bf16 and swaps one 8-byte half with its
-  // neighbour, so even lane 2j ends with the row's 16-byte output chunk j and
-  // odd lane 2j + 1 with chunk LPR / 2 + j.  A wave covers 64 / LPR rows per
-  // pass, the workgroup's 4 waves the 64 rows in LPR / 4 passes.
-  constexpr int LPR = HD / 8, RPP = 64 / LPR, PASSES = LPR / 4;
-  const int c = l % LPR, odd = c & 1;
-  uint4 res[PASSES];
+      make_rsrc(a.part_o + ((size_t)ks * n_rbt64 + rb_id) * slab, a.splits > 1 ? slab * 2 : 0);
+  const int t = arow / G, hq = hk * G + (arow - t * G);
+  auto merge_store = [&](auto off_c) {
+    constexpr int off = decltype(off_c)::value;   // first d tile this wave merges
+    const float4* src = hand + (rp * 2 + kh_w) * (NH2 * 4 * 64) + l;
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int row = (w + 4 * p) * RPP + l / LPR;
-    const float2 h0 = sm.mlh[0][row], h1 = sm.mlh[1][row];
-    const float mm = fmaxf(h0.x, h1.x);
-    const float a0 = h0.x == -INFINITY ? 0.f : exp2f(h0.x - mm);
-    const float a1 = h1.x == -INFINITY ? 0.f : exp2f(h1.x - mm);
-    const float inv = 1.f / (h0.y * a0 + h1.y * a1);
-    const float s0 = a0 * inv, s1 = a1 * inv;
-    const float* p0 = park + row * PROW;
-    const float* p1 = p0 + 64 * PROW;
-    uint2 half[2];
+    for (int i = 0; i < NH2; ++i) {
+      float p[16];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int f4 = LPR * e + c;
-      const float4 x = *reinterpret_cast<const float4*>(p0 + 4 * f4);
-      const float4 y = *reinterpret_cast<const float4*>(p1 + 4 * f4);
-      half[e] = make_uint2(pack2(x.x * s0 + y.x * s1, x.y * s0 + y.y * s1),
-                           pack2(x.z * s0 + y.z * s1, x.w * s0 + y.w * s1));
-    }
-    const uint2 give = odd ? half[0] : half[1];
-    const uint2 got = make_uint2(__shfl_xor(give.x, 1), __shfl_xor(give.y, 1));
-    res[p] = odd ? make_uint4(got.x, got.y, half[1].x, half[1].y)
-                 : make_uint4(half[0].x, half[0].y, got.x, got.y);
-  }
-  // then all the stores (interleaved with the reads they would serialise them)
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<float4*>(&p[4 * q]) = src[(4 * i + q) * 64];
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int row = (w + 4 * p) * RPP + l / LPR;
-    const int ch = (c >> 1) + (odd ? LPR / 2 : 0);   // 16-byte chunk of the row
-    if (a.splits == 1) {
-      const int ar = 64 * rb + row;
-      if (ar < rows) {
-        const int t = ar / G, h = hk * G + (ar - t * G);
-        buf_st16(ro, (int)(fa_index(b * a.T + t, h * HD + 8 * ch, MTo) * 2), res[p]);
+      for (int j = 0; j < 2; ++j) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = o[off + i][8 * j + e] * s_own + p[8 * j + e] * s_oth;
+        const uint4 chunk = chunk_of(v);
+        const int dd = 32 * (off + i) + 16 * j + 8 * hl;
+        if (live) {
+          if (a.splits == 1)
+            buf_st16(ro, (int)(fa_index(b * a.T + t, hq * HD + dd, MTo) * 2), chunk);
+          else
+            buf_st16(rpo, attn_part_slot(row64, dd >> 3) * 16, chunk);
+        }
       }
-    } else {
-      buf_st16(rpo, (row * HD + 8 * ch) * 2, res[p]);
     }
+  };
+  if (kh_w == 0)
+    merge_store(std::integral_constant<int, 0>{});
+  else
+    merge_store(std::integral_constant<int, NH2>{});
+  if (a.splits > 1 && kh_w == 0 && hl == 0 && live) {
+    const __amdgpu_buffer_rsrc_t rpm = make_rsrc(a.part_ml + ((size_t)ks * n_rbt64 + rb_id) * 128, 512);
+    buf_st8(rpm, row64 * 8, __float_as_uint(mm), __float_as_uint(lsum));
   }
-  if (a.splits == 1) return true;
-  if (tid < 64) {
-    const float2 h0 = sm.mlh[0][tid], h1 = sm.mlh[1][tid];
-    const float mm = fmaxf(h0.x, h1.x);
-    const float a0 = h0.x == -INFINITY ? 0.f : exp2f(h0.x - mm);
-    const float a1 = h1.x == -INFINITY ? 0.f : exp2f(h1.x - mm);
-    const __amdgpu_buffer_rsrc_t rpm = make_rsrc(a.part_ml + ((size_t)ks * n_rbt + rb_id) * 128, 512);
-    buf_st8(rpm, tid * 8, __float_as_uint(mm), __float_as_uint(h0.y * a0 + h1.y * a1));
-  }
-  return false;
+  return a.splits == 1;
 }
 
 // Items of the key-slice merge: one per (row block, row, 16-byte chunk).
@@ -509,8 +490,9 @@ __device__ void attn_combine_task(const AttnSmArgs& a, int task) {
   const int n_rbt = a.B * a.Hkv * n_rb;
   const int i = task * 256 + (int)threadIdx.x;
   if (i >= n_rbt * 64 * CPR) return;
-  const int rb_id = i / (64 * CPR), rem = i - rb_id * 64 * CPR;
-  const int row = rem / CPR, c = rem - row * CPR;
+  const int rb_id = i / (64 * CPR), slot = i - rb_id * 64 * CPR;
+  const int gi = slot & 63, gg = slot >> 6;
+  const int row = 16 * (gg & 3) + (gi & 15), c = 4 * (gg >> 2) + (gi >> 4);   // inverse of attn_part_slot
   const int bh = rb_id / n_rb, rb = rb_id - bh * n_rb;
   const int b = bh / a.Hkv, hk = bh - b * a.Hkv;
   const int ar = 64 * rb + row;
@@ -525,7 +507,7 @@ __device__ void attn_combine_task(const AttnSmArgs& a, int task) {
     if (sp < a.splits) {
       const u32x2v u = __builtin_amdgcn_raw_buffer_load_b64(rpm, ((sp * n_rbt + rb_id) * 64 + row) * 8, 0, 16);
       ml[sp] = make_float2(__uint_as_float(u[0]), __uint_as_float(u[1]));
-      pv[sp] = buf_ld_act(rpo, (int)((((size_t)sp * n_rbt + rb_id) * 64 + row) * HD + 8 * c) * 2);
+      pv[sp] = buf_ld_act(rpo, (int)((((size_t)sp * n_rbt + rb_id) * slab + 8 * (size_t)slot) * 2));
     }
   float mx = -INFINITY;
 #pragma unroll

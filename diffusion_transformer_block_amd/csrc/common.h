@@ -19,17 +19,16 @@ constexpr int kWave = 64;
 // ---------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// float -> bf16, round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
-
+// float -> bf16, round to nearest, ties to even; NaN stays NaN: gfx950's
+// v_cvt_pk_bf16_f32, two per instruction (the first operand goes to the low
+// half).  Written as assembly: the compiler's own lowering of __bf16
+// conversions fails instruction selection in the persistent stage kernel.
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  uint32_t r;
+  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
 }
+__device__ __forceinline__ bf16_t f2bf(float f) { return (bf16_t)(pack2(f, 0.f) & 0xffffu); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -101,6 +100,40 @@ __device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected
   __syncthreads();
   return *flag != 0;
 }
+
+// ---------------------------------------------------------------- LDS DMA
+// s_waitcnt immediate that waits until at most n vector memory operations of
+// the wave are outstanding (expcnt and lgkmcnt left free).
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+  return 0x0F70 | (n & 15) | ((n >> 4) << 14);
+}
+// LDS byte address of a generic pointer into LDS: the shared aperture is
+// 4 GiB aligned, so it is the pointer's low 32 bits (no address-space cast:
+// the compiler's cast of a non-inlined generic pointer fails instruction
+// selection in the persistent stage kernel).
+__device__ __forceinline__ unsigned lds_u32(const void* p) { return (unsigned)(uintptr_t)p; }
+// LDS DMA of 1 KiB per wave: lane l's 16 bytes at gp land at LDS byte
+// address lds + 16 l (lds wave-uniform).  Written as assembly so that the
+// compiler adds no waits of its own for it (it would wait for the DMA before
+// every later LDS read); callers wait (vmcnt) before the barrier that hands
+// the data on.  M0 is declared clobbered; nothing else in these kernels
+// keeps a value in it.  Variants: default caching, streaming (nt: read once)
+// and device-coherent (sc1: written earlier in the same launch).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(unsigned lds, const void* gp) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(gp) : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_nt(unsigned lds, const void* gp) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+               :: "s"(lds), "v"(gp) : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_sc1(unsigned lds, const void* gp) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off sc1"
+               :: "s"(lds), "v"(gp) : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // ---------------------------------------------------------------- buffer resources
 // Raw buffer accesses through a descriptor whose record count bounds the

@@ -39,21 +39,6 @@ __device__ __forceinline__ void EpiQKV::store8(int m, int g, int qc, const float
 }
 
 // ============================================================================ large-chunk GEMM
-__device__ __forceinline__ unsigned lds_u32(const void* p) {
-  return (unsigned)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
-}
-// LDS DMA of one 1 KiB fragment: lane l's 16 bytes at gp land at LDS byte
-// address lds + 16 l.  Written as assembly so that the compiler adds no
-// waits of its own for it (it would wait for the DMA before every later LDS
-// read); the kernel waits (vmcnt) before a barrier hands the stage on.
-// (M0 is reserved to the compiler: no other code in these kernels uses it.)
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(unsigned lds, const void* gp) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds), "v"(gp) : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // BM x BN output tile per workgroup (4 waves in a 2 x 2 grid, each BM/2 x
 // BN/2 of 16 x 16 x 32 MFMAs), K steps of 64 in two LDS stages.  A stage holds

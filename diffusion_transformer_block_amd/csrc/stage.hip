@@ -57,8 +57,11 @@ __device__ __forceinline__ void st_u32c(unsigned* p, unsigned v) {
 }
 
 // Wave 0 polls flags[0 .. n) until all equal `want`; returns false on abort.
-__device__ bool wait_flags(const unsigned* flags, int n, unsigned want, unsigned* abort_word,
-                           int* ok_sh) {
+__device__ bool wait_flags(const unsigned* flags, int n, unsigned want, unsigned* abort_word) {
+  // (the verdict goes through an LDS word of this function's own, not a
+  // pointer to one: the compiler mishandles generic pointers to LDS
+  // variables captured in the task lambdas)
+  __shared__ int ok_sh;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     unsigned spins = 0;
@@ -78,10 +81,10 @@ __device__ bool wait_flags(const unsigned* flags, int n, unsigned want, unsigned
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    if (lane == 0) *ok_sh = ok;
+    if (lane == 0) ok_sh = ok;
   }
   __syncthreads();
-  return *ok_sh != 0;
+  return ok_sh != 0;
 }
 
 // All of this workgroup's task outputs are acknowledged, then publish.
@@ -231,13 +234,13 @@ __device__ __noinline__ void cmb_run(AttnSmArgs aa, int t, W& wait) {
 }
 
 template <class W>
-__device__ __noinline__ void emb_run(FlowTask f, int t, FlowSmem& fs, W& wait) {
-  if (wait()) emb_task(f, t, fs);
+__device__ __noinline__ void emb_run(FlowTask f, int t, uint8_t* smem, W& wait) {
+  if (wait()) emb_task(f, t, *reinterpret_cast<FlowSmem*>(smem));
 }
 
 template <class W>
-__device__ __noinline__ void vel_run(FlowTask f, int t, FlowSmem& fs, W& wait) {
-  if (wait()) vel_task(f, t, fs);
+__device__ __noinline__ void vel_run(FlowTask f, int t, uint8_t* smem, W& wait) {
+  if (wait()) vel_task(f, t, *reinterpret_cast<FlowSmem*>(smem));
 }
 
 // ---------------------------------------------------------------- the kernel
@@ -272,11 +275,10 @@ __global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
     const unsigned* pflags = flags + (prev < 0 ? 0 : prev) * kStageMaxFlags;
     const int pn = prev < 0 ? 0 : sa.ph[prev].n_flags;
     const unsigned want = e0 + phi - 1;
-    int* okp = &ok_sh;
-    auto wait = [&waited, &alive, pflags, pn, want, abort_word, okp]() -> bool {
+    auto wait = [&waited, &alive, pflags, pn, want, abort_word]() -> bool {
       if (!waited) {
         waited = true;
-        alive = wait_flags(pflags, pn, want, abort_word, okp);
+        alive = wait_flags(pflags, pn, want, abort_word);
       }
       return alive;
     };
@@ -417,7 +419,7 @@ __global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
       f.MTz = mt_of(sa.N + 1);
       f.eps = sa.eps;
       ok = phase(kPhEMB, [&](int t, auto& wait) {
-        emb_run(f, t, fsm, wait);
+        emb_run(f, t, smem, wait);
         return t;
       });
       if (ok)
@@ -438,7 +440,7 @@ __global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
         ok = run_layer(l, sa.xb[l & 1], true, sa.xb[(l + 1) & 1], true, sa.kp[l], sa.vp[l]);
       if (ok)
         ok = phase(kPhVEL, [&](int t, auto& wait) {
-          vel_run(f, t, fsm, wait);
+          vel_run(f, t, smem, wait);
           return t;
         });
     }
