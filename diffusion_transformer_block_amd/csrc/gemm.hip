@@ -214,6 +214,20 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   float* stg = reinterpret_cast<float*>(big_dsm) + w * 32 * LROW;
 #pragma unroll
   for (int pass = 0; pass < MTW / 2; ++pass) {
+    // the pass's row scales and epilogue operands, all loads issued before
+    // the first use (one memory round trip per pass, not one per slot)
+    float rr[2][4];
+    typename Epi::Aux ax[2][4][GW];
+#pragma unroll
+    for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = min(m0 + wm * (BM / 2) + 16 * (2 * pass + mh) + 4 * (l >> 4) + j, ga.M - 1);
+        rr[mh][j] = ga.r ? ga.r[row] : 1.f;
+#pragma unroll
+        for (int gg = 0; gg < GW; ++gg)
+          ax[mh][j][gg] = epi.aux(row, min(g0 + wn * GW + gg, ga.n_groups - 1), l & 15);
+      }
 #pragma unroll
     for (int mh = 0; mh < 2; ++mh) {
       const int mt = 2 * pass + mh;
@@ -221,11 +235,11 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
       for (int j = 0; j < 4; ++j) {
         const int rl = 16 * mh + 4 * (l >> 4) + j;
         const int row = min(m0 + wm * (BM / 2) + 16 * mt + 4 * (l >> 4) + j, ga.M - 1);
-        const float r = ga.r ? ga.r[row] : 1.f;
 #pragma unroll
         for (int gg = 0; gg < GW; ++gg) {
           const int g = min(g0 + wn * GW + gg, ga.n_groups - 1);
-          const float2 o = epi.math(row, g, l & 15, acc[mt][gg][0][j], acc[mt][gg][1][j], r);
+          const float2 o =
+              epi.math(row, g, l & 15, acc[mt][gg][0][j], acc[mt][gg][1][j], rr[mh][j], ax[mh][j][gg]);
           stg[rl * LROW + 32 * gg + (l & 15)] = o.x;
           stg[rl * LROW + 32 * gg + 16 + (l & 15)] = o.y;
         }

@@ -56,16 +56,22 @@ struct EpiQKV {
   const float* sin_t;
   int T, P, Hq, Hkv, d;
 
-  __device__ __forceinline__ float2 math(int m, int g, int c, float v0, float v1, float r) const {
+  // cos / sin of slot c of group g at row m's position: the index is valid
+  // for every group (V groups ignore it), so the loads carry no condition
+  // and the caller can issue a whole pass of them before the first use
+  struct Aux {
+    float cs, sn;
+  };
+  __device__ __forceinline__ Aux aux(int m, int g, int c) const {
+    const int gpr = d >> 5;
+    const size_t ti = (size_t)(P + m % T) * (d >> 1) + 16 * (g % gpr) + c;   // column j < d/2
+    return {cos_t[ti], sin_t[ti]};
+  }
+  __device__ __forceinline__ float2 math(int, int g, int, float v0, float v1, float r, const Aux& x) const {
     v0 *= r;
     v1 *= r;
-    const int gpr = d >> 5;
-    if (g >= (Hq + Hkv) * gpr) return make_float2(v0, v1);
-    const int t = m % T;
-    const int j = 16 * (g % gpr) + c;  // < d/2
-    const size_t ti = (size_t)(P + t) * (d >> 1) + j;
-    const float cs = cos_t[ti], sn = sin_t[ti];
-    return make_float2(v0 * cs - v1 * sn, v0 * sn + v1 * cs);
+    if (g >= (Hq + Hkv) * (d >> 5)) return make_float2(v0, v1);
+    return make_float2(v0 * x.cs - v1 * x.sn, v0 * x.sn + v1 * x.cs);
   }
   __device__ __forceinline__ void store8(int m, int g, int qc, const float* v) const;
 };
@@ -79,7 +85,9 @@ struct EpiResidual {
   bf16_t* out;
   int out_frag;
   int ld, MT;
-  __device__ __forceinline__ float2 math(int, int, int, float v0, float v1, float) const {
+  struct Aux {};
+  __device__ __forceinline__ Aux aux(int, int, int) const { return {}; }
+  __device__ __forceinline__ float2 math(int, int, int, float v0, float v1, float, const Aux&) const {
     return make_float2(v0, v1);
   }
   __device__ __forceinline__ void store8(int m, int g, int qc, const float* v) const {
@@ -100,7 +108,9 @@ struct EpiGateUp {
   static constexpr int SLOT_CHUNKS = 2;
   bf16_t* out;
   int MT;
-  __device__ __forceinline__ float2 math(int, int, int, float v0, float v1, float r) const {
+  struct Aux {};
+  __device__ __forceinline__ Aux aux(int, int, int) const { return {}; }
+  __device__ __forceinline__ float2 math(int, int, int, float v0, float v1, float r, const Aux&) const {
     return make_float2(silu(v0 * r) * (v1 * r), 0.f);
   }
   __device__ __forceinline__ void store8(int m, int g, int qc, const float* v) const {
