@@ -19,7 +19,7 @@
 
 namespace blk {
 
-__device__ __forceinline__ void EpiQKV::store8(int m, int g, int qc, const float* v) const {
+__device__ __forceinline__ void EpiQKV::store8(int m, int g, int qc, const float* v, const Pre8&) const {
   const int b = m / T, t = m - b * T;
   const int gpr = d >> 5, n_rot_groups = (Hq + Hkv) * gpr;
   bf16_t* dst;
@@ -246,8 +246,20 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
       }
     }
     __syncthreads();
+    constexpr int NIT = 32 * GW * SC / 64;
+    // the pass's store-side operands (residual chunks), all loaded before the
+    // first store (positions past the edges clamped: loaded, never stored)
+    typename Epi::Pre8 p8[NIT];
 #pragma unroll
-    for (int it = 0; it < 32 * GW * SC / 64; ++it) {
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = it * 64 + l;
+      const int rl = idx / (GW * SC), rem = idx - rl * (GW * SC);
+      const int gg = rem / SC, qc = rem - gg * SC;
+      p8[it] = epi.pre8(min(m0 + wm * (BM / 2) + 32 * pass + rl, ga.M - 1),
+                        min(g0 + wn * GW + gg, ga.n_groups - 1), qc);
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
       const int idx = it * 64 + l;
       const int rl = idx / (GW * SC), rem = idx - rl * (GW * SC);
       const int gg = rem / SC, qc = rem - gg * SC;
@@ -256,7 +268,7 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
       const float4 lo = *reinterpret_cast<const float4*>(&stg[rl * LROW + 32 * gg + 8 * qc]);
       const float4 hi = *reinterpret_cast<const float4*>(&stg[rl * LROW + 32 * gg + 8 * qc + 4]);
       const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      if (row < ga.M && g < ga.n_groups) epi.store8(row, g, qc, v);
+      if (row < ga.M && g < ga.n_groups) epi.store8(row, g, qc, v, p8[it]);
     }
     __syncthreads();
   }

@@ -73,7 +73,9 @@ struct EpiQKV {
     if (g >= (Hq + Hkv) * (d >> 5)) return make_float2(v0, v1);
     return make_float2(v0 * x.cs - v1 * x.sn, v0 * x.sn + v1 * x.cs);
   }
-  __device__ __forceinline__ void store8(int m, int g, int qc, const float* v) const;
+  struct Pre8 {};
+  __device__ __forceinline__ Pre8 pre8(int, int, int) const { return {}; }
+  __device__ __forceinline__ void store8(int m, int g, int qc, const float* v, const Pre8&) const;
 };
 
 // out = res + acc (residual add; O projection and down projection).  res and
@@ -90,12 +92,21 @@ struct EpiResidual {
   __device__ __forceinline__ float2 math(int, int, int, float v0, float v1, float, const Aux&) const {
     return make_float2(v0, v1);
   }
-  __device__ __forceinline__ void store8(int m, int g, int qc, const float* v) const {
+  // the residual chunk, loaded by the caller for a whole pass before any of
+  // its stores (out may alias res)
+  struct Pre8 {
+    uint4 r;
+  };
+  __device__ __forceinline__ Pre8 pre8(int m, int g, int qc) const {
     const int c = 32 * g + 8 * qc;
     const size_t ro = res_frag ? fa_index(m, c, MT) : (size_t)m * ld + c;
+    return {*reinterpret_cast<const uint4*>(res + ro)};
+  }
+  __device__ __forceinline__ void store8(int m, int g, int qc, const float* v, const Pre8& p) const {
+    const int c = 32 * g + 8 * qc;
     const size_t oo = out_frag ? fa_index(m, c, MT) : (size_t)m * ld + c;
     float x[8];
-    unpack8(*reinterpret_cast<const uint4*>(res + ro), x);
+    unpack8(p.r, x);
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] += v[e];
     *reinterpret_cast<uint4*>(out + oo) = pack8(x);
@@ -113,7 +124,9 @@ struct EpiGateUp {
   __device__ __forceinline__ float2 math(int, int, int, float v0, float v1, float r, const Aux&) const {
     return make_float2(silu(v0 * r) * (v1 * r), 0.f);
   }
-  __device__ __forceinline__ void store8(int m, int g, int qc, const float* v) const {
+  struct Pre8 {};
+  __device__ __forceinline__ Pre8 pre8(int, int, int) const { return {}; }
+  __device__ __forceinline__ void store8(int m, int g, int qc, const float* v, const Pre8&) const {
     *reinterpret_cast<uint4*>(out + fa_index(m, 16 * g + 8 * qc, MT)) = pack8(v);
   }
 };
