@@ -162,7 +162,8 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
   // their scores are masked and their probabilities are exactly 0).
   constexpr int RPJ = 256 / CPR;               // key rows per pass of the workgroup
   const int kk0 = tid / CPR, c0 = tid - kk0 * CPR;
-  const unsigned lds_k = lds_u32(&sm.k[0][0]), lds_v = lds_u32(&sm.v[0][0]);
+  const unsigned lds_k = __builtin_amdgcn_readfirstlane(lds_u32(&sm.k[0][0]));
+  const unsigned lds_v = __builtin_amdgcn_readfirstlane(lds_u32(&sm.v[0][0]));
   auto load_tile = [&](int tile, int buf) {
     const int row0 = key_begin + 64 * tile;
     const bool prefix_only = row0 + 64 <= a.P;   // uniform
@@ -209,11 +210,9 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   if (n_tiles > 1) load_tile(1, 1);
 
+  // O^T accumulators: the slice's first tile (every slice has one) writes
+  // them with zero C operands, so they need no zero fill
   f32x16 o[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
   // running reference max (may trail the true max by up to 2^8, see below) and sum
   float m_run = -INFINITY, l_run = 0.f;
   __syncthreads();
@@ -234,8 +233,9 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
 
   // key halves this wave takes of every tile: both (LONG) or its own
   constexpr int NH = LONG ? 2 : 1;
-  auto step = [&](int it, auto cur_c) {
-    constexpr int cur = decltype(cur_c)::value;   // LDS buffer of tile it
+  auto step = [&](int it, auto cur_c, auto first_c) {
+    constexpr int cur = decltype(cur_c)::value;          // LDS buffer of tile it
+    constexpr bool FIRST = decltype(first_c)::value;     // it == 0
     // ---- S^T (32 keys x 32 rows) of each half: K fragments read from LDS in
     //      batches ahead of their MFMAs; each half runs two independent
     //      chains (even and odd d steps)
@@ -269,8 +269,14 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
         }
     }
     // ---- online softmax in base 2, one update for all of the wave's keys
+    //      (in tiles without masked keys v_exp_f32 directly: its arguments
+    //      are finite and <= 8, and results below the normal range are
+    //      negligible next to the row's largest term, which is >= 1; the
+    //      last tile's -inf scores take exp2f, which maps them to 0)
     float x[NH][16];
     float mloc = -INFINITY;
+    // keys past the slice exist only in its last tile
+    const bool masked = key_begin + 64 * it + 64 > key_end;   // uniform
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       sacc[h] += sacc2[h];
@@ -278,35 +284,50 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = base + 8 * (v >> 2) + 4 * hl + (v & 3);
-        x[h][v] = key < key_end ? sacc[h][v] * a.scale_log2 : -INFINITY;
+        x[h][v] = sacc[h][v] * a.scale_log2;
+        if (masked && key >= key_end) x[h][v] = -INFINITY;
         mloc = fmaxf(mloc, x[h][v]);
       }
     }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
     // Rescale only when some row's max grew past the reference by more than
     // 2^8 (exp2 of scores against a stale reference stays <= 256: exact
-    // enough in bf16 and far from fp32 overflow); otherwise keep it.
+    // enough in bf16 and far from fp32 overflow); otherwise keep it.  Rows
+    // whose reference is still -inf hold zero sums: nothing to rescale (a
+    // slice's first tile skips the pass over O entirely).
     const bool grow = mloc > m_run + 8.f;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    if (FIRST) {
+      m_run = grow ? mloc : m_run;
+    } else if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float m_new = grow ? mloc : m_run;
-      const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+      if (__builtin_amdgcn_ballot_w64(grow && m_run != -INFINITY) != 0) {
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] = o[dt] * alpha;
-      l_run *= alpha;
+        for (int dt = 0; dt < NDT; ++dt) o[dt] = o[dt] * alpha;
+        l_run *= alpha;
+      }
       m_run = m_new;
     }
-    // masked keys (and rows that have seen no key yet) contribute exactly 0
+    // masked keys contribute exactly 0 (exp2f(-inf)); a row that has seen no
+    // key yet (reference -inf, every score -inf) takes reference 0
+    const float mref = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
     uint32_t pw[NH][8];
+    auto probs = [&](auto exp_fn) {
 #pragma unroll
-    for (int h = 0; h < NH; ++h)
+      for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        const float p0 = x[h][v] == -INFINITY ? 0.f : exp2f(x[h][v] - m_run);
-        const float p1 = x[h][v + 1] == -INFINITY ? 0.f : exp2f(x[h][v + 1] - m_run);
-        psum += p0 + p1;
-        pw[h][v / 2] = pack2(p0, p1);
-      }
+        for (int v = 0; v < 16; v += 2) {
+          const float p0 = exp_fn(x[h][v] - mref);
+          const float p1 = exp_fn(x[h][v + 1] - mref);
+          psum += p0 + p1;
+          pw[h][v / 2] = pack2(p0, p1);
+        }
+    };
+    if (masked)
+      probs([](float z) { return exp2f(z); });
+    else
+      probs([](float z) { return __builtin_amdgcn_exp2f(z); });
     l_run += psum;
     // ---- O^T += V^T P^T, two 16-key steps per half (P^T slots e <-> S^T
     //      values 8 u + e)
@@ -329,9 +350,13 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
             vhi[dt] = lds_tr16(reinterpret_cast<const bf16_t*>(vt + 8 * HD * 2 + dx));
           }
 #pragma unroll
-          for (int dt = 0; dt < VB; ++dt)
-            o[d0 + dt] =
-                mfma32(as_bf16x8(make_uint4(vlo[dt].x, vlo[dt].y, vhi[dt].x, vhi[dt].y)), pb, o[d0 + dt]);
+          for (int dt = 0; dt < VB; ++dt) {
+            const bf16x8 va = as_bf16x8(make_uint4(vlo[dt].x, vlo[dt].y, vhi[dt].x, vhi[dt].y));
+            if (FIRST && h == 0 && u == 0)
+              o[d0 + dt] = mfma32(va, pb, f32x16{});
+            else
+              o[d0 + dt] = mfma32(va, pb, o[d0 + dt]);
+          }
         }
       }
     }
@@ -342,9 +367,10 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
     __syncthreads();
     if (it + 2 < n_tiles) load_tile(it + 2, cur);
   };
-  for (int it = 0; it < n_tiles; it += 2) {
-    step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < n_tiles) step(it + 1, std::integral_constant<int, 1>{});
+  step(0, std::integral_constant<int, 0>{}, std::true_type{});
+  for (int it = 1; it < n_tiles; it += 2) {
+    step(it, std::integral_constant<int, 1>{}, std::false_type{});
+    if (it + 1 < n_tiles) step(it + 1, std::integral_constant<int, 0>{}, std::false_type{});
   }
 
   // ---- epilogue.  Lane l holds O^T slots v of query row l % 32: dims
@@ -428,8 +454,8 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
 
   const float2 pm = sm.mlh[kh_w ^ 1][rp * 32 + row32];
   const float mm = fmaxf(m_run, pm.x);
-  const float a_own = m_run == -INFINITY ? 0.f : exp2f(m_run - mm);
-  const float a_oth = pm.x == -INFINITY ? 0.f : exp2f(pm.x - mm);
+  const float a_own = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
+  const float a_oth = pm.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(pm.x - mm);
   const float lsum = l_tot * a_own + pm.y * a_oth;   // > 0: key half 0 of a slice has a key
   const float s_own = a_own / lsum, s_oth = a_oth / lsum;
   const int row64 = 32 * rp + row32, arow = 64 * rb + row64;

@@ -113,25 +113,26 @@ __host__ __device__ constexpr int vmcnt_imm(int n) {
 // selection in the persistent stage kernel).
 __device__ __forceinline__ unsigned lds_u32(const void* p) { return (unsigned)(uintptr_t)p; }
 // LDS DMA of 1 KiB per wave: lane l's 16 bytes at gp land at LDS byte
-// address lds + 16 l (lds wave-uniform).  Written as assembly so that the
-// compiler adds no waits of its own for it (it would wait for the DMA before
-// every later LDS read); callers wait (vmcnt) before the barrier that hands
-// the data on.  M0 is declared clobbered; nothing else in these kernels
-// keeps a value in it.  Variants: default caching, streaming (nt: read once)
-// and device-coherent (sc1: written earlier in the same launch).
+// address lds + 16 l (lds wave-uniform: read from the first lane).  Written
+// as assembly so that the compiler adds no waits of its own for it (it would
+// wait for the DMA before every later LDS read); callers wait (vmcnt) before
+// the barrier that hands the data on.  The LDS address goes in as an M0
+// operand (the compiler writes M0; the s_nop is the wait state before a DMA
+// reads it).  Variants: default caching, streaming (nt: read once) and
+// device-coherent (sc1: written earlier in the same launch).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(unsigned lds, const void* gp) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds), "v"(gp) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(gp) : "memory");
 }
 __device__ __forceinline__ void dma16_nt(unsigned lds, const void* gp) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
-               :: "s"(lds), "v"(gp) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+               :: "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(gp) : "memory");
 }
 __device__ __forceinline__ void dma16_sc1(unsigned lds, const void* gp) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off sc1"
-               :: "s"(lds), "v"(gp) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off sc1"
+               :: "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(gp) : "memory");
 }
 #pragma clang diagnostic pop
 

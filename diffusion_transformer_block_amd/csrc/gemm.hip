@@ -292,7 +292,9 @@ static void launch_big(const GemmArgs& ga, const Epi& e, int splits, hipStream_t
 // 256 x 256 tiles where they fill the chip (about one workgroup per compute
 // unit or more), else 128 x 128 where those do, else 128 x 64.  Two K splits
 // (long K only) where they trim a mostly idle last round of tiles: rounds of
-// half-length units against whole ones.
+// half-length units against whole ones, with a fifth in hand for the partial
+// tiles' round trip (measured: 3 whole rounds of 256 x 256 tiles beat 5 half
+// ones; 2 whole rounds of 128 x 64 tiles lose to 3 half ones).
 BigPlan big_plan(int M, int n_groups, int K) {
   const long cus = device_cus();
   auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((n_groups + bn / 32 - 1) / (bn / 32)); };
@@ -301,7 +303,7 @@ BigPlan big_plan(int M, int n_groups, int K) {
   else if (tiles(128, 128) >= cus * 15 / 16) p = BigPlan{128, 128, 1, 0};
   p.tiles = (int)tiles(p.bm, p.bn);
   const long r1 = (p.tiles + cus - 1) / cus, r2 = (2L * p.tiles + cus - 1) / cus;   // r2 half-length rounds
-  if (K >= 4096 && (K / 64) % 2 == 0 && 10 * r2 <= 18 * r1) p.splits = 2;
+  if (K >= 4096 && (K / 64) % 2 == 0 && 10 * r2 <= 16 * r1) p.splits = 2;
   return p;
 }
 size_t big_part_floats(const BigPlan& p) {
