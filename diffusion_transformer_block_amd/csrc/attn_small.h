@@ -504,8 +504,8 @@ __host__ __device__ inline int attn_combine_items(int B, int T, int Hq, int Hkv,
   return B * Hkv * ((Hq / Hkv * T + 63) / 64) * 64 * (HD / 8);
 }
 
-// Merges the key slices of attn_sm_task for the 256 items of workgroup-sized
-// task `task`: o = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m),
+// Merges the key slices of attn_sm_task for the blockDim.x items of task
+// `task`: o = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m),
 // in slice order, stored in the O projection's operand order.
 template <int HD>
 __device__ void attn_combine_task(const AttnSmArgs& a, int task) {
@@ -514,7 +514,7 @@ __device__ void attn_combine_task(const AttnSmArgs& a, int task) {
   const int rows = G * a.T;
   const int n_rb = (rows + 63) >> 6;
   const int n_rbt = a.B * a.Hkv * n_rb;
-  const int i = task * 256 + (int)threadIdx.x;
+  const int i = task * (int)blockDim.x + (int)threadIdx.x;
   if (i >= n_rbt * 64 * CPR) return;
   const int rb_id = i / (64 * CPR), slot = i - rb_id * 64 * CPR;
   const int gi = slot & 63, gg = slot >> 6;

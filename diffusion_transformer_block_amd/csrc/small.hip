@@ -205,8 +205,10 @@ __global__ __launch_bounds__(256, LONG ? 2 : 1) void attn_sm_kernel(AttnSmArgs a
   attn_sm_task<HD, LONG>(a, bh, rb, ks, *reinterpret_cast<AttnSmSmem<HD>*>(at_dsm), NoWait{});
 }
 
+// one wave per workgroup: the merge is a single memory round trip per item,
+// spread over as many compute units as there are items
 template <int HD>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnSmArgs a) {
+__global__ __launch_bounds__(64) void attn_combine_kernel(AttnSmArgs a) {
   attn_combine_task<HD>(a, blockIdx.x);
 }
 
@@ -238,7 +240,7 @@ static void attn_sm_go(const AttnSmArgs& a, hipStream_t st) {
   if (!launched) attn_sm_launch<HD, false>(a, st);
   if (a.splits > 1) {
     const int items = attn_combine_items(a.B, a.T, a.Hq, a.Hkv, HD);
-    hipLaunchKernelGGL(attn_combine_kernel<HD>, dim3((items + 255) / 256), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attn_combine_kernel<HD>, dim3((items + 63) / 64), dim3(64), 0, st, a);
   }
 }
 
