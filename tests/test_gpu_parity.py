@@ -109,6 +109,10 @@ def test_ae_block_peaked_softmax():
                       tokens=65, prefix=200, hidden=256, ffn=384),
     synth.small_shape("mqa_d256_1x64_longP", n_q_heads=2, n_kv_heads=1, head_dim=256, batch=1,
                       tokens=64, prefix=3001, hidden=256, ffn=512),
+    # the flow loop's layer: 96-key slices of two tiles whose second tile
+    # leaves one key half fully masked
+    synth.small_shape("mqa_d256_1x64_p768", n_q_heads=8, n_kv_heads=1, head_dim=256, batch=1,
+                      tokens=64, prefix=768, hidden=1024, ffn=4096),
     # 128-row attention blocks with key slices, GQA, ragged rows (1040 per kv head)
     synth.small_shape("gqa_d64_1x520_long", n_q_heads=8, n_kv_heads=4, head_dim=64, batch=1,
                       tokens=520, prefix=1500, hidden=512, ffn=1024),
