@@ -82,9 +82,9 @@ int sk_nb(int KW, int gpw, int MT) {
 }
 
 // Key slices per 64-row block: enough workgroups (about 96) that each takes
-// one or two 64-key steps -- one memory round trip for its K/V -- and the
-// merge kernel spreads the combine over every row; slices are multiples of
-// 32 keys (a wave's half of a step).
+// few 64-key steps -- one memory round trip for its K/V -- and the merge
+// kernel spreads the combine over every row; slices are whole 64-key tiles
+// (multiples of 32 keys, a wave's half of a step, for the shortest runs).
 void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps, int* long_rows) {
   const int G = Hq / Hkv;
   const int n_rbt = B * Hkv * ((G * T + 63) / 64);
@@ -107,7 +107,15 @@ void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps, i
   int s = std::max(1, std::min(kAttnMaxSplits, (96 + n_rbt - 1) / n_rbt));
   s = std::min(s, (L + 31) / 32);
   int k = (L + s - 1) / s;
-  k = (k + 31) / 32 * 32;
+  if (L > 128) {
+    // whole 64-key tiles: a slice of 64 + 32 keys costs a second step for a
+    // third more keys (measured at 832 keys: 13 slices of 64 beat 9 of 96)
+    int k64 = std::max(64, k / 64 * 64);
+    if ((L + k64 - 1) / k64 > kAttnMaxSplits) k64 = (k + 63) / 64 * 64;
+    k = k64;
+  } else {
+    k = (k + 31) / 32 * 32;
+  }
   *kps = k;
   *splits = (L + k - 1) / k;
 }
