@@ -49,6 +49,10 @@ void launch_flow_embed(const FlowEmbedArgs& a, hipStream_t st) {
 // sums in 5 exchange rounds (each lane keeps half of what it holds and sends
 // the other half), the 4 waves' sums meet in LDS in a fixed order.  X is in
 // operand order (fa_index, N + 1 rows).
+// NK = k values per thread (a power of two >= D / 256): every load has a
+// valid, clamped address and no condition, so a thread's loads are issued
+// together rather than one round trip each; k >= D contributes x = 0.
+template <int NK>
 __global__ __launch_bounds__(256) void flow_velocity_kernel(FlowVelArgs a) {
   constexpr int CW = 32;              // columns per pass
   __shared__ float part[4][64];
@@ -56,13 +60,13 @@ __global__ __launch_bounds__(256) void flow_velocity_kernel(FlowVelArgs a) {
   const int i = blockIdx.x;
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int MT = mt_of(a.N + 1);
-  const int nk = (a.D + 255) / 256;   // k values per thread (D <= 8192: <= 32)
-  float xk[32];
+  float xk[NK];
   float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
+  for (int j = 0; j < NK; ++j) {
     const int k = tid + 256 * j;
-    xk[j] = (j < nk && k < a.D) ? bf2f(a.X[fa_index(i + 1, k, MT)]) : 0.f;
+    const float v = bf2f(a.X[fa_index(i + 1, min(k, a.D - 1), MT)]);
+    xk[j] = k < a.D ? v : 0.f;
     ss = fmaf(xk[j], xk[j], ss);
   }
 #pragma unroll
@@ -77,25 +81,36 @@ __global__ __launch_bounds__(256) void flow_velocity_kernel(FlowVelArgs a) {
     float acc[CW];
 #pragma unroll
     for (int c = 0; c < CW; ++c) acc[c] = 0.f;
+    if (vec && nc == CW) {
+      // all of the thread's W_out' rows in flight at once (in batches of up
+      // to 4 rows = 128 registers), then the FMAs
+      constexpr int JB = NK < 4 ? NK : 4;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {   // unrolled: xk stays in registers
-      const int k = tid + 256 * j;
-      if (j < nk && k < a.D) {
-        const float* wr = a.w_out + (size_t)k * a.A + c0;
-        if (vec && nc == CW) {
+      for (int j0 = 0; j0 < NK; j0 += JB) {
+        float4 wv[JB][CW / 4];
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+          const float* wr = a.w_out + (size_t)min(tid + 256 * (j0 + jj), a.D - 1) * a.A + c0;
+#pragma unroll
+          for (int c4 = 0; c4 < CW / 4; ++c4) wv[jj][c4] = *reinterpret_cast<const float4*>(wr + 4 * c4);
+        }
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj)
 #pragma unroll
           for (int c4 = 0; c4 < CW / 4; ++c4) {
-            const float4 wv = *reinterpret_cast<const float4*>(wr + 4 * c4);
-            acc[4 * c4] = fmaf(xk[j], wv.x, acc[4 * c4]);
-            acc[4 * c4 + 1] = fmaf(xk[j], wv.y, acc[4 * c4 + 1]);
-            acc[4 * c4 + 2] = fmaf(xk[j], wv.z, acc[4 * c4 + 2]);
-            acc[4 * c4 + 3] = fmaf(xk[j], wv.w, acc[4 * c4 + 3]);
+            const float xv = xk[j0 + jj];
+            acc[4 * c4] = fmaf(xv, wv[jj][c4].x, acc[4 * c4]);
+            acc[4 * c4 + 1] = fmaf(xv, wv[jj][c4].y, acc[4 * c4 + 1]);
+            acc[4 * c4 + 2] = fmaf(xv, wv[jj][c4].z, acc[4 * c4 + 2]);
+            acc[4 * c4 + 3] = fmaf(xv, wv[jj][c4].w, acc[4 * c4 + 3]);
           }
-        } else {
+      }
+    } else {
 #pragma unroll
-          for (int c = 0; c < CW; ++c)
-            if (c < nc) acc[c] = fmaf(xk[j], wr[c], acc[c]);
-        }
+      for (int j = 0; j < NK; ++j) {
+        const float* wr = a.w_out + (size_t)min(tid + 256 * j, a.D - 1) * a.A + c0;
+#pragma unroll
+        for (int c = 0; c < CW; ++c) acc[c] = fmaf(xk[j], wr[min(c, nc - 1)], acc[c]);
       }
     }
     // fold the wave: after the round with offset o (16, 8, 4, 2, 1) a lane
@@ -129,7 +144,13 @@ __global__ __launch_bounds__(256) void flow_velocity_kernel(FlowVelArgs a) {
 }
 
 void launch_flow_velocity(const FlowVelArgs& a, hipStream_t st) {
-  flow_velocity_kernel<<<a.N, 256, 0, st>>>(a);
+  const int need = (a.D + 255) / 256;   // D <= 8192 (checked by the caller)
+  if (need <= 1) flow_velocity_kernel<1><<<a.N, 256, 0, st>>>(a);
+  else if (need <= 2) flow_velocity_kernel<2><<<a.N, 256, 0, st>>>(a);
+  else if (need <= 4) flow_velocity_kernel<4><<<a.N, 256, 0, st>>>(a);
+  else if (need <= 8) flow_velocity_kernel<8><<<a.N, 256, 0, st>>>(a);
+  else if (need <= 16) flow_velocity_kernel<16><<<a.N, 256, 0, st>>>(a);
+  else flow_velocity_kernel<32><<<a.N, 256, 0, st>>>(a);
 }
 
 }  // namespace blk
