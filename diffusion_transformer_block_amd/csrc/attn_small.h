@@ -12,8 +12,9 @@
 // each of the T tokens, row ar = t G + gh; they all read that kv head's keys,
 // so one K/V tile serves a block of rows.  A task takes a row block and one
 // slice of the keys, in steps of 64 keys:
-//  * K / V tiles are loaded with row-contiguous 16-byte loads one step ahead
-//    and staged through double-buffered LDS;
+//  * K / V tiles move one step ahead by LDS DMA into double-buffered,
+//    unpadded LDS tiles whose 16-byte chunks are XOR-swizzled per row (no
+//    bank conflicts for the K fragment reads or the transposed V reads);
 //  * 64-row blocks: wave w takes 32 query rows (w % 2) and one 32-key half
 //    (w / 2) of every step; 128-row blocks (LONG, long key runs): wave w takes
 //    32 rows and both halves, so a tile serves twice the rows and the halves
@@ -31,13 +32,15 @@
 //    lane i of each 16-lane group element i % 4 of the 8 bytes at lane
 //    4 k + i / 4 (k < 4): pointing lane i at key row 4 k' + i / 4, dims
 //    4 (i % 4) .. + 3 yields V[key k][dim i] in that key order;
-//  * (64-row blocks) the two key halves meet in LDS; one key slice then
-//    writes the normalised rows straight into the O projection's operand
-//    order (both modes); several slices
-//    publish bf16 partials normalised by their own sum plus (max, sum), which
-//    a separate merge step (attn_combine_task, one thread per 16 output
-//    bytes, all slices' loads in flight together) combines in slice order.
-//    Many small slices keep every workgroup to about one memory round trip.
+//  * (64-row blocks) the two key halves of a row pair merge through an LDS
+//    hand-off in register order, each wave finishing half the d tiles; lanes
+//    then store whole 16-byte chunks (lane pairs l, l ^ 32 swap halves).  One
+//    key slice writes the normalised rows straight into the O projection's
+//    operand order (both modes); several slices publish bf16 partials
+//    normalised by their own sum plus (max, sum), which a separate merge step
+//    (attn_combine_task, one thread per 16 output bytes, all slices' loads in
+//    flight together) combines in slice order.  Many small slices keep every
+//    workgroup to about one memory round trip.
 #pragma once
 #include "common.h"
 #include "skinny.h"
