@@ -51,11 +51,11 @@ OP_KERNELS = {
 # the SHA-256 of the kernel sources when the counters were taken: a changed
 # kernel reports null until it is profiled again.
 TRAFFIC = {
-    "qkv_rope": {"fetch": 6628753, "write": 622592, "bytes": 7251345, "sources": "34fa1a51b95fc547"},
-    "attention": {"fetch": 6145542, "write": 2924544, "bytes": 9070086, "sources": "34fa1a51b95fc547"},
-    "o_proj": {"fetch": 7700616, "write": 2364416, "bytes": 10065032, "sources": "34fa1a51b95fc547"},
-    "gate_up": {"fetch": 18006988, "write": 1048576, "bytes": 19055564, "sources": "34fa1a51b95fc547"},
-    "down": {"fetch": 13872510, "write": 2364416, "bytes": 16236926, "sources": "34fa1a51b95fc547"},
+    "qkv_rope": {"fetch": 6628770, "write": 622592, "bytes": 7251362, "sources": "247d674832c1b4dc"},
+    "attention": {"fetch": 6145516, "write": 2924544, "bytes": 9070060, "sources": "247d674832c1b4dc"},
+    "o_proj": {"fetch": 7700600, "write": 2364416, "bytes": 10065016, "sources": "247d674832c1b4dc"},
+    "gate_up": {"fetch": 18007022, "write": 1048576, "bytes": 19055598, "sources": "247d674832c1b4dc"},
+    "down": {"fetch": 13872520, "write": 2364416, "bytes": 16236936, "sources": "247d674832c1b4dc"},
 }
 TRAFFIC_FETCH_SCALE = 2.000   # FETCH_SIZE of a 256 MiB copy reads 128 MiB
 TRAFFIC_WRITE_SCALE = 1.000   # WRITE_SIZE of the same copy reads 256 MiB
