@@ -249,7 +249,6 @@ __global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ unsigned e0_sh;
   __shared__ int ok_sh;
-  FlowSmem& fsm = *reinterpret_cast<FlowSmem*>(smem);
 
   if (threadIdx.x == 0) {
     e0_sh = ld_u32c(sa.epoch);
