@@ -50,7 +50,8 @@ __device__ __forceinline__ void EpiQKV::store8(int m, int g, int qc, const float
 // that stage's k-tile-0 fragments while its k-tile-1 MFMAs run; the DMA of
 // the stage after next goes out right after that barrier.
 template <int BM, int BN, bool AFRAG, class Epi>
-__global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int n_tm, int splits) {
+__global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int n_tm, int n_tn,
+                                                       int n_full, int splits) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t big_dsm[];
   constexpr int BK = 64;
   constexpr int MTB = BM / 16;            // 16-row tiles per block
@@ -63,23 +64,36 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
   const int wm = w >> 1, wn = w & 1;
-  // The hardware deals workgroups round-robin over the 8 XCDs: give each XCD
-  // a contiguous run of tiles, taken in bands of GM row tiles with the column
-  // tiles outer, so the tiles an XCD runs at once share row and column blocks
-  // in its L2.
-  // A unit is (tile, K split), the splits of a tile adjacent.
+  // Units: the first n_full tiles whole, then each remaining tile as `splits`
+  // K slices (adjacent).  The hardware deals workgroups round-robin over the
+  // 8 XCDs (XCD x runs ids x, x + 8, ... in order): each XCD gets a
+  // contiguous run of whole tiles and then a contiguous run of slices, so the
+  // slices -- the last round -- spread over every XCD.  Tiles go in bands of
+  // GM row tiles with the column tiles outer, so the tiles an XCD runs at once
+  // share row and column blocks in its L2.
   const int nwg = gridDim.x, id = blockIdx.x;
-  const int xcd = id & 7, jx = id >> 3, qx = nwg >> 3, rx = nwg & 7;
-  const int unit = xcd * qx + min(xcd, rx) + jx;
-  const int tile = unit / splits, split = unit - tile * splits;
+  const int xcd = id & 7, jx = id >> 3;
+  auto share = [](int n, int x) { return n / 8 + (x < n % 8 ? 1 : 0); };
+  auto start = [](int n, int x) { return x * (n / 8) + min(x, n % 8); };
+  const int f_x = share(n_full, xcd);
+  int tile, split, nsplit;
+  if (jx < f_x) {
+    tile = start(n_full, xcd) + jx;
+    split = 0;
+    nsplit = 1;
+  } else {
+    const int u = start(nwg, xcd) - start(n_full, xcd) + (jx - f_x);
+    tile = n_full + u / splits;
+    split = u - (u / splits) * splits;
+    nsplit = splits;
+  }
   constexpr int GM = 4;
-  const int n_tn = nwg / splits / n_tm;
   const int band = tile / (GM * n_tn), tib = tile - band * GM * n_tn;
   const int rows_b = min(GM, n_tm - band * GM);
   const int tm = band * GM + tib % rows_b, tn = tib / rows_b;
   const int m0 = tm * BM, g0 = tn * GB;
   const int KT = ga.K >> 5;
-  const int nk = ga.K / BK / splits, sk0 = split * nk;   // this split's K steps
+  const int nk = ga.K / BK / nsplit, sk0 = split * nk;   // this unit's K steps
   const int MTa = mt_of(ga.M);
 
   // this wave's fragments of a stage: f = w + 4 i (A fragments first); rows
@@ -168,11 +182,11 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   // ---- K splits: every split publishes its accumulators in MFMA layout (16
   //      coherent bytes per lane); the last to arrive at the tile's counter
   //      sums all of them in split order and runs the epilogue
-  if (splits > 1) {
+  if (nsplit > 1) {
     constexpr int NACC = MTW * GW * 2;                  // f32x4 per lane
     constexpr int SPLIT_BYTES = 4 * NACC * 64 * 16;     // one split of a tile
-    const __amdgpu_buffer_rsrc_t rp =
-        make_rsrc(ga.part + (size_t)tile * splits * (SPLIT_BYTES / 4), (size_t)splits * SPLIT_BYTES);
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(
+        ga.part + (size_t)(tile - n_full) * nsplit * (SPLIT_BYTES / 4), (size_t)nsplit * SPLIT_BYTES);
     auto slot = [&](int sp, int q) { return sp * SPLIT_BYTES + ((w * NACC + q) * 64 + l) * 16; };
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
@@ -185,7 +199,7 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
                    make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
                               __float_as_uint(v[3])));
         }
-    if (!arrive_last(&ga.ctr[tile], (unsigned)splits, reinterpret_cast<int*>(big_dsm))) return;
+    if (!arrive_last(&ga.ctr[tile], (unsigned)nsplit, reinterpret_cast<int*>(big_dsm))) return;
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
@@ -194,7 +208,7 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
         for (int ii = 0; ii < 2; ++ii) {
           const int q = (mt * GW + gg) * 2 + ii;
           f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-          for (int sp = 0; sp < splits; ++sp) {
+          for (int sp = 0; sp < nsplit; ++sp) {
             f32x4 v = acc[mt][gg][ii];
             if (sp != split) {
               const uint4 u = buf_ld_act(rp, slot(sp, q));
@@ -275,7 +289,7 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
 }
 
 template <int BM, int BN, bool AFRAG, class Epi>
-static void launch_big(const GemmArgs& ga, const Epi& e, int splits, hipStream_t st) {
+static void launch_big(const GemmArgs& ga, const Epi& e, const BigPlan& p, hipStream_t st) {
   constexpr int NFR = (BM / 16) * 2 + (BN / 32) * 4;
   const size_t smem = 2 * (size_t)NFR * kFragBytes;
   auto kern = big_gemm_kernel<BM, BN, AFRAG, Epi>;
@@ -286,36 +300,58 @@ static void launch_big(const GemmArgs& ga, const Epi& e, int splits, hipStream_t
     attr_set = true;
   }
   const int n_tm = (ga.M + BM - 1) / BM, n_tn = (ga.n_groups + BN / 32 - 1) / (BN / 32);
-  hipLaunchKernelGGL(kern, dim3(n_tm * n_tn * splits), dim3(256), smem, st, ga, e, n_tm, splits);
+  const int units = p.n_full + (n_tm * n_tn - p.n_full) * p.splits;
+  hipLaunchKernelGGL(kern, dim3(units), dim3(256), smem, st, ga, e, n_tm, n_tn, p.n_full, p.splits);
 }
 
 // 256 x 256 tiles where they fill the chip (about one workgroup per compute
-// unit or more), else 128 x 128 where those do, else 128 x 64.  Two K splits
-// (long K only) where they trim a mostly idle last round of tiles: rounds of
-// half-length units against whole ones, with a fifth in hand for the partial
-// tiles' round trip (measured: 3 whole rounds of 256 x 256 tiles beat 5 half
-// ones; 2 whole rounds of 128 x 64 tiles lose to 3 half ones).
+// unit or more), else 128 x 128 where those do, else 128 x 64.  Costs in
+// rounds of whole-tile work per compute unit.  Two K splits of every tile
+// (long K only) where rounds of half-length units beat whole ones with a
+// fifth in hand (measured: 3 whole rounds of 256 x 256 tiles beat 5 half
+// ones; 2 whole rounds of 128 x 64 tiles lose to 3 half ones).  Or whole
+// tiles for the full rounds and only the last, partial round's tiles in s K
+// slices that fit in one round: its cost counted at 1/s + 0.3.
 BigPlan big_plan(int M, int n_groups, int K) {
   const long cus = device_cus();
   auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((n_groups + bn / 32 - 1) / (bn / 32)); };
-  BigPlan p{128, 64, 1, 0};
-  if (tiles(256, 256) >= cus * 15 / 16) p = BigPlan{256, 256, 1, 0};
-  else if (tiles(128, 128) >= cus * 15 / 16) p = BigPlan{128, 128, 1, 0};
+  BigPlan p{128, 64, 1, 0, 0};
+  if (tiles(256, 256) >= cus * 15 / 16) p = BigPlan{256, 256, 1, 0, 0};
+  else if (tiles(128, 128) >= cus * 15 / 16) p = BigPlan{128, 128, 1, 0, 0};
   p.tiles = (int)tiles(p.bm, p.bn);
+  p.n_full = p.tiles;
+  const long ks = K / 64;
   const long r1 = (p.tiles + cus - 1) / cus, r2 = (2L * p.tiles + cus - 1) / cus;   // r2 half-length rounds
-  if (K >= 4096 && (K / 64) % 2 == 0 && 10 * r2 <= 16 * r1) p.splits = 2;
+  double best = (double)r1;
+  if (K >= 4096 && ks % 2 == 0 && 10 * r2 <= 16 * r1) {
+    best = 0.5 * (double)r2;
+    p.n_full = 0;
+    p.splits = 2;
+  }
+  const long full = p.tiles / cus * cus, tail = p.tiles - full;
+  if (full > 0 && tail > 0) {
+    for (int s = 8; s >= 2; --s) {
+      if (ks % s != 0 || tail * s > cus || ks / s < 2) continue;
+      const double c = (double)(full / cus) + 1.0 / s + 0.3;
+      if (c < best) {
+        p.n_full = (int)full;
+        p.splits = s;
+      }
+      break;
+    }
+  }
   return p;
 }
 size_t big_part_floats(const BigPlan& p) {
-  return p.splits > 1 ? (size_t)p.tiles * p.splits * p.bm * p.bn : 0;
+  return p.splits > 1 ? (size_t)(p.tiles - p.n_full) * p.splits * p.bm * p.bn : 0;
 }
 
 template <bool AFRAG, class Epi>
 static void launch_tiled(const GemmArgs& ga, const Epi& e, hipStream_t st) {
   const BigPlan p = big_plan(ga.M, ga.n_groups, ga.K);
-  if (p.bm == 256) launch_big<256, 256, AFRAG>(ga, e, p.splits, st);
-  else if (p.bn == 128) launch_big<128, 128, AFRAG>(ga, e, p.splits, st);
-  else launch_big<128, 64, AFRAG>(ga, e, p.splits, st);
+  if (p.bm == 256) launch_big<256, 256, AFRAG>(ga, e, p, st);
+  else if (p.bn == 128) launch_big<128, 128, AFRAG>(ga, e, p, st);
+  else launch_big<128, 64, AFRAG>(ga, e, p, st);
 }
 
 // ============================================================================ dispatch

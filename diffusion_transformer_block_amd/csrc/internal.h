@@ -149,6 +149,7 @@ struct GemmArgs {
 // Tile shape and K splits of a large-chunk GEMM, and the scratch they need.
 struct BigPlan {
   int bm, bn, splits, tiles;
+  int n_full;   // tiles run whole (the first n_full); the rest in `splits` K slices each
 };
 BigPlan big_plan(int M, int n_groups, int K);
 size_t big_part_floats(const BigPlan& p);
