@@ -41,23 +41,25 @@ __device__ __forceinline__ void EpiQKV::store8(int m, int g, int qc, const float
 // ============================================================================ large-chunk GEMM
 
 // BM x BN output tile per workgroup (4 waves in a 2 x 2 grid, each BM/2 x
-// BN/2 of 16 x 16 x 32 MFMAs), K steps of 64 in two LDS stages.  A stage holds
-// the tile's operands as 1 KiB MFMA fragments: B (packed weights) and, for
-// AFRAG, A (an operand-order activation, fa_index) one contiguous fragment
-// each; a row-major A is gathered as 16 rows x 64 bytes per fragment.  The
-// loop is software-pipelined: a wave reads its k-tile-1 fragments while its
-// k-tile-0 MFMAs run, and, after the barrier that publishes the next stage,
-// that stage's k-tile-0 fragments while its k-tile-1 MFMAs run; the DMA of
-// the stage after next goes out right after that barrier.
+// BN/2 of 16 x 16 x 32 MFMAs), one 32-wide k-tile per LDS stage, four stages
+// (three in flight ahead of the one in use; measured 3 % faster on the large
+// chunks than two stages of 64).  A stage holds the tile's operands as 1 KiB
+// MFMA fragments: B (packed weights) and, for AFRAG, A (an operand-order
+// activation, fa_index) one contiguous fragment each; a row-major A is
+// gathered as 16 rows x 64 bytes per fragment.  The loop is
+// software-pipelined: after the barrier that publishes stage s + 1 a wave
+// issues the DMA of stage s + 3 and reads stage s + 1's fragments while
+// stage s's MFMAs run.
 template <int BM, int BN, bool AFRAG, class Epi>
 __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int n_tm, int n_tn,
                                                        int n_full, int splits) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t big_dsm[];
-  constexpr int BK = 64;
+  constexpr int BK = 32;                  // one k-tile per LDS stage
+  constexpr int NST = 4;                  // LDS stages (three in flight ahead of the one in use)
   constexpr int MTB = BM / 16;            // 16-row tiles per block
   constexpr int GB = BN / 32;             // 32-column groups per block
   constexpr int MTW = MTB / 2, GW = GB / 2;
-  constexpr int AFR = MTB * 2, BFR = GB * 4, NFR = AFR + BFR;
+  constexpr int AFR = MTB, BFR = GB * 2, NFR = AFR + BFR;
   constexpr int STAGE = NFR * kFragBytes;
   constexpr int PER = NFR / 4;            // fragments each wave moves per stage
   const int tid = threadIdx.x;
@@ -104,20 +106,20 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   for (int i = 0; i < PER; ++i) {
     const int f = w + 4 * i;
     if (f < AFR) {
-      const int kt = f / MTB, mt = f - kt * MTB;
+      const int mt = f;
       if (AFRAG) {
         const int rt = min(m0 / 16 + mt, MTa - 1);
-        gsrc[i] = reinterpret_cast<const uint8_t*>(ga.A) + ((size_t)kt * MTa + rt) * kFragBytes + 16 * l;
-        gstep[i] = 2 * MTa * kFragBytes;
+        gsrc[i] = reinterpret_cast<const uint8_t*>(ga.A) + (size_t)rt * kFragBytes + 16 * l;
+        gstep[i] = MTa * kFragBytes;
       } else {
         const int row = min(m0 + 16 * mt + (l & 15), ga.M - 1);
-        gsrc[i] = reinterpret_cast<const uint8_t*>(ga.A) + ((size_t)row * ga.lda + 32 * kt + 8 * (l >> 4)) * 2;
+        gsrc[i] = reinterpret_cast<const uint8_t*>(ga.A) + ((size_t)row * ga.lda + 8 * (l >> 4)) * 2;
         gstep[i] = BK * 2;
       }
     } else {
-      const int fb = f - AFR, gg = fb >> 2, kt = (fb >> 1) & 1, ii = fb & 1;
-      gsrc[i] = ga.Bp + frag_offset(min(g0 + gg, ga.n_groups - 1), kt, ii, KT) + 16 * l;
-      gstep[i] = 2 * 2 * kFragBytes;
+      const int fb = f - AFR, gg = fb >> 1, ii = fb & 1;
+      gsrc[i] = ga.Bp + frag_offset(min(g0 + gg, ga.n_groups - 1), 0, ii, KT) + 16 * l;
+      gstep[i] = 2 * kFragBytes;
     }
   }
   const unsigned lds0 = lds_u32(big_dsm);
@@ -126,17 +128,17 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
     for (int i = 0; i < PER; ++i)
       dma16(lds0 + buf * STAGE + (w + 4 * i) * kFragBytes, gsrc[i] + (size_t)(sk0 + s) * gstep[i]);
   };
-  auto rd = [&](int buf, int kt, uint4 (&af)[MTW], uint4 (&bfv)[GW][2]) {
+  auto rd = [&](int buf, uint4 (&af)[MTW], uint4 (&bfv)[GW][2]) {
     const uint8_t* base = big_dsm + buf * STAGE;
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
-      af[mt] = *reinterpret_cast<const uint4*>(base + (kt * MTB + wm * MTW + mt) * kFragBytes + 16 * l);
+      af[mt] = *reinterpret_cast<const uint4*>(base + (wm * MTW + mt) * kFragBytes + 16 * l);
 #pragma unroll
     for (int gg = 0; gg < GW; ++gg)
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii)
         bfv[gg][ii] = *reinterpret_cast<const uint4*>(
-            base + (AFR + (wn * GW + gg) * 4 + kt * 2 + ii) * kFragBytes + 16 * l);
+            base + (AFR + (wn * GW + gg) * 2 + ii) * kFragBytes + 16 * l);
   };
   f32x4 acc[MTW][GW][2];
 #pragma unroll
@@ -156,26 +158,30 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
           acc[mt][gg][ii] = mfma16(as_bf16x8(af[mt]), as_bf16x8(bfv[gg][ii]), acc[mt][gg][ii]);
   };
 
-  // prologue: stages 0 and 1 in flight, stage 0 landed, its k-tile-0 fragments read
+  // prologue: stages 0..2 in flight, stage 0 landed and its fragments read
   issue(0, 0);
-  if (nk > 1) {
-    issue(1, 1);
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER) : "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
+  if (nk > 1) issue(1, 1);
+  if (nk > 2) issue(2, 2);
+  if (nk > 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * PER) : "memory");
+  else if (nk > 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   uint4 a0[MTW], b0[GW][2], a1[MTW], b1[GW][2];
-  rd(0, 0, a0, b0);
-  for (int s = 0; s < nk; ++s) {
-    const int b = s & 1;
-    rd(b, 1, a1, b1);
-    mm(a0, b0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // stage s + 1 landed
-    __syncthreads();                                    // and every wave has read stage s
-    if (s + 2 < nk) issue(s + 2, b);
-    if (s + 1 < nk) rd(b ^ 1, 0, a0, b0);
-    mm(a1, b1);
+  rd(0, a0, b0);
+  // stage s: its fragments are in registers; stage s + 1 lands (stages s + 2
+  // and, after the barrier, s + 3 stay in flight) and is read while stage
+  // s's MFMAs run
+  auto step = [&](int s, uint4 (&ca)[MTW], uint4 (&cb)[GW][2], uint4 (&na)[MTW], uint4 (&nb)[GW][2]) {
+    if (s + 2 < nk) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();   // stage s + 1 visible; every wave is done with stage s - 1's buffer
+    if (s + 3 < nk) issue(s + 3, (s + 3) & (NST - 1));
+    if (s + 1 < nk) rd((s + 1) & (NST - 1), na, nb);
+    mm(ca, cb);
+  };
+  for (int s = 0; s < nk; s += 2) {
+    step(s, a0, b0, a1, b1);
+    if (s + 1 < nk) step(s + 1, a1, b1, a0, b0);
   }
   __syncthreads();
 
@@ -290,8 +296,8 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
 
 template <int BM, int BN, bool AFRAG, class Epi>
 static void launch_big(const GemmArgs& ga, const Epi& e, const BigPlan& p, hipStream_t st) {
-  constexpr int NFR = (BM / 16) * 2 + (BN / 32) * 4;
-  const size_t smem = 2 * (size_t)NFR * kFragBytes;
+  constexpr int NFR = (BM / 16) + (BN / 32) * 2;
+  const size_t smem = 4 * (size_t)NFR * kFragBytes;
   auto kern = big_gemm_kernel<BM, BN, AFRAG, Epi>;
   static bool attr_set = false;
   if (!attr_set) {
