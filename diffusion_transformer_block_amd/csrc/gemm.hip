@@ -10,7 +10,8 @@
 // a GEMM is bound by reading its bf16 weights.
 //
 // The large-chunk GEMM (M > 64 rows; chunks of <= 64 rows run the skinny
-// GEMM of skinny.h): 256 x 256 (or 128 x 128) output tiles, both operands
+// GEMM of skinny.h): 256 x 256 (224 x 256 where that pads fewer rows; or
+// 128 x 128, 128 x 64 on narrow shapes) output tiles, both operands
 // moved into LDS by the load DMA as MFMA fragments, 2 x 2 waves of
 // 16 x 16 x 32 MFMAs, XCD-aware tile order (big_gemm_kernel below).
 #include "common.h"
@@ -61,11 +62,20 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   constexpr int MTW = MTB / 2, GW = GB / 2;
   constexpr int AFR = MTB, BFR = GB * 2, NFR = AFR + BFR;
   constexpr int STAGE = NFR * kFragBytes;
-  constexpr int PER = NFR / 4;            // fragments each wave moves per stage
+  // fragments each wave moves per stage: f = w + 4 i < NFR (waves w < PER_X
+  // move one more when NFR is not a multiple of 4, e.g. 224-row tiles)
+  constexpr int PER_X = NFR % 4, PER = NFR / 4 + (PER_X ? 1 : 0);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
   const int wm = w >> 1, wn = w & 1;
+  const bool full_per = PER_X == 0 || w < PER_X;   // this wave moves PER fragments, else PER - 1
+  // vmcnt allowing this wave's DMAs of the last `st` stages to be in flight
+  auto wait_stages = [&](auto st) {
+    constexpr int S = decltype(st)::value;
+    if (full_per) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(S * PER) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(S * (PER - 1)) : "memory");
+  };
   // Units: the first n_full tiles whole, then each remaining tile as `splits`
   // K slices (adjacent).  The hardware deals workgroups round-robin over the
   // 8 XCDs (XCD x runs ids x, x + 8, ... in order): each XCD gets a
@@ -104,7 +114,7 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   int gstep[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int f = w + 4 * i;
+    const int f = min(w + 4 * i, NFR - 1);   // past NFR: never issued
     if (f < AFR) {
       const int mt = f;
       if (AFRAG) {
@@ -126,7 +136,8 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   auto issue = [&](int s, int buf) {
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      dma16(lds0 + buf * STAGE + (w + 4 * i) * kFragBytes, gsrc[i] + (size_t)(sk0 + s) * gstep[i]);
+      if (i < PER - 1 || full_per)
+        dma16(lds0 + buf * STAGE + (w + 4 * i) * kFragBytes, gsrc[i] + (size_t)(sk0 + s) * gstep[i]);
   };
   auto rd = [&](int buf, uint4 (&af)[MTW], uint4 (&bfv)[GW][2]) {
     const uint8_t* base = big_dsm + buf * STAGE;
@@ -162,8 +173,8 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   issue(0, 0);
   if (nk > 1) issue(1, 1);
   if (nk > 2) issue(2, 2);
-  if (nk > 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * PER) : "memory");
-  else if (nk > 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER) : "memory");
+  if (nk > 2) wait_stages(std::integral_constant<int, 2>{});
+  else if (nk > 1) wait_stages(std::integral_constant<int, 1>{});
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   uint4 a0[MTW], b0[GW][2], a1[MTW], b1[GW][2];
@@ -172,7 +183,7 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   // and, after the barrier, s + 3 stay in flight) and is read while stage
   // s's MFMAs run
   auto step = [&](int s, uint4 (&ca)[MTW], uint4 (&cb)[GW][2], uint4 (&na)[MTW], uint4 (&nb)[GW][2]) {
-    if (s + 2 < nk) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER) : "memory");
+    if (s + 2 < nk) wait_stages(std::integral_constant<int, 1>{});
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();   // stage s + 1 visible; every wave is done with stage s - 1's buffer
     if (s + 3 < nk) issue(s + 3, (s + 3) & (NST - 1));
@@ -233,7 +244,8 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   constexpr int SC = Epi::SLOT_CHUNKS;
   float* stg = reinterpret_cast<float*>(big_dsm) + w * 32 * LROW;
 #pragma unroll
-  for (int pass = 0; pass < MTW / 2; ++pass) {
+  for (int pass = 0; pass < (MTW + 1) / 2; ++pass) {
+    const int pass_rows = min(32, 16 * (MTW - 2 * pass));   // 16 in the half pass of an odd MTW
     // the pass's row scales and epilogue operands, all loads issued before
     // the first use (one memory round trip per pass, not one per slot)
     float rr[2][4];
@@ -250,7 +262,8 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
       }
 #pragma unroll
     for (int mh = 0; mh < 2; ++mh) {
-      const int mt = 2 * pass + mh;
+      const int mt = min(2 * pass + mh, MTW - 1);
+      if (2 * pass + mh >= MTW) break;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rl = 16 * mh + 4 * (l >> 4) + j;
@@ -288,7 +301,7 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
       const float4 lo = *reinterpret_cast<const float4*>(&stg[rl * LROW + 32 * gg + 8 * qc]);
       const float4 hi = *reinterpret_cast<const float4*>(&stg[rl * LROW + 32 * gg + 8 * qc + 4]);
       const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      if (row < ga.M && g < ga.n_groups) epi.store8(row, g, qc, v, p8[it]);
+      if (rl < pass_rows && row < ga.M && g < ga.n_groups) epi.store8(row, g, qc, v, p8[it]);
     }
     __syncthreads();
   }
@@ -322,7 +335,13 @@ BigPlan big_plan(int M, int n_groups, int K) {
   const long cus = device_cus();
   auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((n_groups + bn / 32 - 1) / (bn / 32)); };
   BigPlan p{128, 64, 1, 0, 0};
-  if (tiles(256, 256) >= cus * 15 / 16) p = BigPlan{256, 256, 1, 0, 0};
+  if (tiles(256, 256) >= cus * 15 / 16) {
+    p = BigPlan{256, 256, 1, 0, 0};
+    // 224-row tiles where they leave less padding per round of the chip
+    // (1560 rows: 7 x 224 = 1568 against 7 x 256 = 1792)
+    auto round_rows = [&](int bm) { return (tiles(bm, 256) + cus - 1) / cus * bm; };
+    if (round_rows(224) < round_rows(256)) p.bm = 224;
+  }
   else if (tiles(128, 128) >= cus * 15 / 16) p = BigPlan{128, 128, 1, 0, 0};
   p.tiles = (int)tiles(p.bm, p.bn);
   p.n_full = p.tiles;
@@ -356,6 +375,7 @@ template <bool AFRAG, class Epi>
 static void launch_tiled(const GemmArgs& ga, const Epi& e, hipStream_t st) {
   const BigPlan p = big_plan(ga.M, ga.n_groups, ga.K);
   if (p.bm == 256) launch_big<256, 256, AFRAG>(ga, e, p, st);
+  else if (p.bm == 224) launch_big<224, 256, AFRAG>(ga, e, p, st);
   else if (p.bn == 128) launch_big<128, 128, AFRAG>(ga, e, p, st);
   else launch_big<128, 64, AFRAG>(ga, e, p, st);
 }

@@ -293,8 +293,10 @@ def test_two_layers_of_one_packed_stack():
 def test_video_dit_block_full_size():
     shape = synth.VIDEO_DIT
     rng = np.random.default_rng(0)
-    rows = sorted(set([0, 1, 63, 64, 127, 128, 1535, 1536, shape.tokens - 1]
-                      + list(rng.choice(shape.tokens, 23, replace=False))))
+    # edges of 256- and 224-row tiles, their wave halves and 16-row epilogue passes
+    edges = [0, 1, 63, 64, 95, 96, 111, 112, 127, 128, 207, 208, 223, 224, 1343, 1344, 1455,
+             1456, 1535, 1536, shape.tokens - 1]
+    rows = sorted(set(edges + list(rng.choice(shape.tokens, 23, replace=False))))
     check_block(shape, synth.block_case(shape), rows=rows)
 
 
