@@ -51,11 +51,11 @@ OP_KERNELS = {
 # the SHA-256 of the kernel sources when the counters were taken: a changed
 # kernel reports null until it is profiled again.
 TRAFFIC = {
-    "qkv_rope": {"fetch": 6628770, "write": 622592, "bytes": 7251362, "sources": "247d674832c1b4dc"},
-    "attention": {"fetch": 6145516, "write": 2924544, "bytes": 9070060, "sources": "247d674832c1b4dc"},
-    "o_proj": {"fetch": 7700600, "write": 2364416, "bytes": 10065016, "sources": "247d674832c1b4dc"},
-    "gate_up": {"fetch": 18007022, "write": 1048576, "bytes": 19055598, "sources": "247d674832c1b4dc"},
-    "down": {"fetch": 13872520, "write": 2364416, "bytes": 16236936, "sources": "247d674832c1b4dc"},
+    "qkv_rope": {"fetch": 6642041, "write": 622592, "bytes": 7264633, "sources": "4339cecb9d27ff24"},
+    "attention": {"fetch": 6158820, "write": 2924544, "bytes": 9083364, "sources": "4339cecb9d27ff24"},
+    "o_proj": {"fetch": 7700623, "write": 2364416, "bytes": 10065039, "sources": "4339cecb9d27ff24"},
+    "gate_up": {"fetch": 18002921, "write": 1048576, "bytes": 19051497, "sources": "4339cecb9d27ff24"},
+    "down": {"fetch": 13872541, "write": 2364416, "bytes": 16236957, "sources": "4339cecb9d27ff24"},
 }
 TRAFFIC_FETCH_SCALE = 2.000   # FETCH_SIZE of a 256 MiB copy reads 128 MiB
 TRAFFIC_WRITE_SCALE = 1.000   # WRITE_SIZE of the same copy reads 256 MiB
@@ -93,7 +93,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=320, help="timed block stages (multiple of 16)")
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--only", choices=["all", "block", "loop", "large", "video", "batched"],
+    ap.add_argument("--only", choices=["all", "block", "tiny", "loop", "large", "video", "batched"],
                     default="all", help="restrict the run (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rotate", type=int, default=16, help="weight copies in rotation")
@@ -443,6 +443,19 @@ def main():
             f"{r['us_warm']:.2f} us warm, {gbs:.0f} GB/s")
         for o in operators:
             log(f"    {o['operator']:9s} {o['us']:7.2f} us  {o['achieved_GBs']:7.1f} GB/s")
+    if args.only in ("all", "tiny"):
+        tiny = synth.TINY
+        log(f"block {tiny.name}: {steps} timed stages, {rotate} weight copies")
+        r = time_block(tiny, steps, args.warmup, rotate)
+        wb, ob = block_bytes(tiny, tiny.prefix)
+        gbs = (wb + ob) / (r["us"] * 1e-6) / 1e9
+        line["tiny_block"] = {
+            "workload": tiny.name, "us": round(r["us"], 3), "us_eager": round(r["us_eager"], 3),
+            "us_p10_p50_p90": [round(v, 3) for v in r["us_p10_p50_p90"]],
+            "algorithmic_bytes": wb + ob, "achieved_GBs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "timed_steps": r["timed_steps"],
+            "operators_us": {k: round(v[0], 3) for k, v in r["ops"].items()}}
+        log(f"  {line['tiny_block']}")
     if args.only in ("all", "loop"):
         log("loop flow_18x10")
         line["loop"] = time_loop(args.warmup)
