@@ -106,6 +106,9 @@ void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps, i
   }
   int s = std::max(1, std::min(kAttnMaxSplits, (96 + n_rbt - 1) / n_rbt));
   s = std::min(s, (L + 31) / 32);
+  // up to two 64-key tiles: one workgroup runs both (one more step) rather
+  // than slices and the merge kernel's launch
+  if (L <= 128) s = 1;
   int k = (L + s - 1) / s;
   if (L > 128) {
     // whole 64-key tiles: a slice of 64 + 32 keys costs a second step for a
