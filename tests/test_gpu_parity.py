@@ -104,6 +104,9 @@ def test_ae_block_peaked_softmax():
 @pytest.mark.parametrize("shape", [
     synth.small_shape("gqa_2x37_tiled"),                             # M = 74: tiled GEMMs
     synth.small_shape("gqa_1x37_skinny", batch=1),                  # ragged M = 37
+    # ragged M = 37 with K = 1024: the row-major block input is read two
+    # k-tiles per pair of loads, rows past M clamped
+    synth.small_shape("gqa_1x37_pairs", batch=1, hidden=1024, ffn=2048),
     synth.small_shape("mqa_1x1", n_kv_heads=1, n_q_heads=4, batch=1, tokens=1, prefix=3),
     synth.small_shape("mha_d128_3x65", n_q_heads=2, n_kv_heads=2, head_dim=128, batch=3,
                       tokens=65, prefix=200, hidden=256, ffn=384),
