@@ -143,7 +143,72 @@ __global__ __launch_bounds__(256) void flow_velocity_kernel(FlowVelArgs a) {
   }
 }
 
+// The same velocity and Euler step for A a multiple of 32 (actions padded to
+// 32 dims), with W_out' read coalesced: thread t takes the 4 columns 4 (t % 8)
+// of a 32-column block over the rows t / 8 + 32 m, so a wave's load covers 8
+// consecutive rows x 128 bytes (8 cache lines) instead of 64 rows x 16 bytes;
+// the X row is staged once in LDS; the 32 threads of a column chunk (8 per
+// wave) fold by shuffles and the 4 waves meet in LDS in a fixed order.
+__global__ __launch_bounds__(256) void flow_velocity32_kernel(FlowVelArgs a) {
+  __shared__ float xs[8192];          // D <= 8192 (checked by the caller)
+  __shared__ float4 part[4][8];
+  __shared__ float wsum[4];
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  const int MT = mt_of(a.N + 1);
+  float ss = 0.f;
+  for (int k = tid; k < a.D; k += 256) {
+    const float v = bf2f(a.X[fa_index(i + 1, k, MT)]);
+    xs[k] = v;
+    ss = fmaf(v, v, ss);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  if (l == 0) wsum[w] = ss;
+  __syncthreads();
+  const float r = rsqrtf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) / (float)a.D + a.eps);
+  const float dt = *a.dt;
+  const int cc = tid & 7, r0 = tid >> 3;
+  for (int c0 = 0; c0 < a.A; c0 += 32) {
+    const float* wb = a.w_out + c0 + 4 * cc;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 16
+    for (int row = r0; row < a.D; row += 32) {
+      const float4 wv = *reinterpret_cast<const float4*>(wb + (size_t)row * a.A);
+      const float xv = xs[row];
+      acc.x = fmaf(xv, wv.x, acc.x);
+      acc.y = fmaf(xv, wv.y, acc.y);
+      acc.z = fmaf(xv, wv.z, acc.z);
+      acc.w = fmaf(xv, wv.w, acc.w);
+    }
+#pragma unroll
+    for (int o = 8; o <= 32; o <<= 1) {
+      acc.x += __shfl_xor(acc.x, o);
+      acc.y += __shfl_xor(acc.y, o);
+      acc.z += __shfl_xor(acc.z, o);
+      acc.w += __shfl_xor(acc.w, o);
+    }
+    if (l < 8) part[w][l] = acc;
+    __syncthreads();
+    if (tid < 32) {
+      const float* p0 = reinterpret_cast<const float*>(&part[0][0]);
+      const float* p1 = reinterpret_cast<const float*>(&part[1][0]);
+      const float* p2 = reinterpret_cast<const float*>(&part[2][0]);
+      const float* p3 = reinterpret_cast<const float*>(&part[3][0]);
+      float vs = ((p0[tid] + p1[tid]) + p2[tid]) + p3[tid];
+      vs = vs * r + a.b_out[c0 + tid];
+      const size_t o = (size_t)i * a.A + c0 + tid;
+      a.a_out[o] = a.a_in[o] + dt * vs;
+    }
+    __syncthreads();
+  }
+}
+
 void launch_flow_velocity(const FlowVelArgs& a, hipStream_t st) {
+  if (a.A % 32 == 0 && a.D <= 8192) {
+    flow_velocity32_kernel<<<a.N, 256, 0, st>>>(a);
+    return;
+  }
   const int need = (a.D + 255) / 256;   // D <= 8192 (checked by the caller)
   if (need <= 1) flow_velocity_kernel<1><<<a.N, 256, 0, st>>>(a);
   else if (need <= 2) flow_velocity_kernel<2><<<a.N, 256, 0, st>>>(a);

@@ -360,6 +360,26 @@ def test_flow_denoise(n_layers):
     assert err <= LOOP_TOL
 
 
+@pytest.mark.parametrize("action_dim", [7, 64])
+def test_flow_other_action_widths(action_dim):
+    """Action widths other than 32 (the head allows 1..64): 7 takes the
+    general velocity kernel (a partial column block), 64 the coalesced one
+    over two 32-column blocks."""
+    import diffusion_transformer_block_amd as blk
+    layer = synth.BlockShape(f"flow_a{action_dim}_layer", 256, 512, 4, 1, 64, 1, 21, 40,
+                             1100 + action_dim)
+    flow = synth.FlowShape(f"flow_a{action_dim}", layer, n_layers=2, n_steps=3, n_actions=20,
+                           action_dim=action_dim, seed=1100 + action_dim)
+    case, cfg, packed, kp, vp, head = flow_inputs(flow)
+    acts = blk.flow_denoise(cfg, packed, flow.n_steps, kp, vp, head["noise"], head["state"])
+    torch.cuda.synchronize()
+    assert acts.shape == (flow.n_actions, action_dim)
+    ref = oracle_flow(flow, case, flow.n_layers)
+    err = max_err_ratio(acts.cpu().numpy(), ref)
+    say(f"  a{action_dim}: err {err:.2e}")
+    assert err <= LOOP_TOL
+
+
 def test_flow_graph_replay_and_recapture():
     import diffusion_transformer_block_amd as blk
     flow = synth.FLOW
