@@ -388,31 +388,49 @@ void launch_gemm_residual(const GemmArgs& ga, const EpiResidual& e, hipStream_t 
 void launch_gemm_gateup(const GemmArgs& ga, const EpiGateUp& e, hipStream_t st) { launch_tiled<true>(ga, e, st); }
 
 // ============================================================================ RMS rows
-// r[m] = (sum_k x[m][k]^2 / K + eps)^-1/2, one wave per row; x row-major or,
-// with frag, in operand order (fa_index over mt_of(M) row tiles)
-// xf (may be NULL): a copy of a row-major x in operand order.
+// r[m] = (sum_k x[m][k]^2 / K + eps)^-1/2.  One workgroup per 16-row tile:
+// wave w takes the k-tiles kt = w, w + 4, ...; with frag (x in operand order,
+// fa_index over mt_of(M) row tiles) each load is one whole 1 KiB fragment,
+// row-major x is read 16 rows x 64 bytes at a time and, when xf is given,
+// stored as that same whole fragment of the operand-order copy.  Lane l holds
+// row l % 16; lanes of a row fold by shuffles, the waves meet in LDS.  Rows
+// past M (clamped loads) fill the last tile's padding; their r is not written.
 __global__ __launch_bounds__(256) void rms_rows_kernel(const bf16_t* __restrict__ x, int M, int K,
                                                        int frag, float eps, float* __restrict__ r,
                                                        bf16_t* __restrict__ xf) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int l = threadIdx.x & 63;
-  if (row >= M) return;
-  const int MT = mt_of(M);
+  __shared__ float part[4][16];
+  const int mt = blockIdx.x, MT = mt_of(M);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int row = min(16 * mt + (l & 15), M - 1);
+  const int nkt = K >> 5;
   float s = 0.f;
-  for (int k = 8 * l; k < K; k += 512) {
-    const bf16_t* p = frag ? x + fa_index(row, k, MT) : x + (size_t)row * K + k;
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    if (xf) *reinterpret_cast<uint4*>(xf + fa_index(row, k, MT)) = v;
+#pragma unroll 8
+  for (int kt = w; kt < nkt; kt += 4) {
+    const size_t fo = ((size_t)(kt * MT + mt) * 64 + l) * 8;   // this lane's slot of fragment (kt, mt)
+    uint4 v;
+    if (frag) {
+      v = *reinterpret_cast<const uint4*>(x + fo);
+    } else {
+      v = *reinterpret_cast<const uint4*>(x + (size_t)row * K + kt * 32 + 8 * (l >> 4));
+      if (xf) *reinterpret_cast<uint4*>(xf + fo) = v;
+    }
     s += sumsq8(v);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-  if (l == 0) r[row] = rsqrtf(s / (float)K + eps);
+  s += __shfl_xor(s, 16);
+  s += __shfl_xor(s, 32);
+  if (l < 16) part[w][l] = s;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const int m = 16 * mt + threadIdx.x;
+    const float t = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) +
+                    part[3][threadIdx.x];
+    if (m < M) r[m] = rsqrtf(t / (float)K + eps);
+  }
 }
 
 void launch_rms_rows(const bf16_t* x, int M, int K, bool frag, float eps, float* r, bf16_t* xf,
                      hipStream_t st) {
-  rms_rows_kernel<<<(M + 3) / 4, 256, 0, st>>>(x, M, K, frag ? 1 : 0, eps, r, xf);
+  rms_rows_kernel<<<mt_of(M), 256, 0, st>>>(x, M, K, frag ? 1 : 0, eps, r, xf);
 }
 
 }  // namespace blk
