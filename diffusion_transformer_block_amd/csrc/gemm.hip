@@ -217,24 +217,39 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
                               __float_as_uint(v[3])));
         }
     if (!arrive_last(&ga.ctr[tile], (unsigned)nsplit, reinterpret_cast<int*>(big_dsm))) return;
+    // every split (this one too) has published: re-read all of them in split
+    // order, two 16-row fragments' worth of loads in flight per round trip
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-      for (int gg = 0; gg < GW; ++gg)
+      for (int gg = 0; gg < GW; ++gg) {
+        acc[mt][gg][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[mt][gg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    for (int sp = 0; sp < nsplit; ++sp) {
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-          const int q = (mt * GW + gg) * 2 + ii;
-          f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-          for (int sp = 0; sp < nsplit; ++sp) {
-            f32x4 v = acc[mt][gg][ii];
-            if (sp != split) {
-              const uint4 u = buf_ld_act(rp, slot(sp, q));
-              v = f32x4{__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
-            }
-            sum += v;
-          }
-          acc[mt][gg][ii] = sum;
-        }
+      for (int mt0 = 0; mt0 < MTW; mt0 += 2) {
+        uint4 u[2][GW][2];
+#pragma unroll
+        for (int dm = 0; dm < 2; ++dm)
+#pragma unroll
+          for (int gg = 0; gg < GW; ++gg)
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+              if (mt0 + dm < MTW) u[dm][gg][ii] = buf_ld_act(rp, slot(sp, ((mt0 + dm) * GW + gg) * 2 + ii));
+#pragma unroll
+        for (int dm = 0; dm < 2; ++dm)
+#pragma unroll
+          for (int gg = 0; gg < GW; ++gg)
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+              if (mt0 + dm < MTW) {
+                const uint4 v = u[dm][gg][ii];
+                acc[mt0 + dm][gg][ii] += f32x4{__uint_as_float(v.x), __uint_as_float(v.y),
+                                               __uint_as_float(v.z), __uint_as_float(v.w)};
+              }
+      }
+    }
     __syncthreads();   // the arrival flag's LDS word is reused below
   }
 
