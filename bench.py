@@ -51,11 +51,11 @@ OP_KERNELS = {
 # the SHA-256 of the kernel sources when the counters were taken: a changed
 # kernel reports null until it is profiled again.
 TRAFFIC = {
-    "qkv_rope": {"fetch": 6642038, "write": 622592, "bytes": 7264630, "sources": "4a54c6f7c9899a92"},
-    "attention": {"fetch": 6158844, "write": 2924544, "bytes": 9083388, "sources": "4a54c6f7c9899a92"},
-    "o_proj": {"fetch": 7700601, "write": 2364416, "bytes": 10065017, "sources": "4a54c6f7c9899a92"},
-    "gate_up": {"fetch": 18002904, "write": 1048576, "bytes": 19051480, "sources": "4a54c6f7c9899a92"},
-    "down": {"fetch": 13872533, "write": 2364416, "bytes": 16236949, "sources": "4a54c6f7c9899a92"},
+    "qkv_rope": {"fetch": 6642023, "write": 622592, "bytes": 7264615, "sources": "4a54c6f7c9899a92"},
+    "attention": {"fetch": 6158797, "write": 2924544, "bytes": 9083341, "sources": "4a54c6f7c9899a92"},
+    "o_proj": {"fetch": 7700559, "write": 2364416, "bytes": 10064975, "sources": "4a54c6f7c9899a92"},
+    "gate_up": {"fetch": 18002882, "write": 1048576, "bytes": 19051458, "sources": "4a54c6f7c9899a92"},
+    "down": {"fetch": 13872481, "write": 2364416, "bytes": 16236897, "sources": "4a54c6f7c9899a92"},
 }
 TRAFFIC_FETCH_SCALE = 2.000   # FETCH_SIZE of a 256 MiB copy reads 128 MiB
 TRAFFIC_WRITE_SCALE = 1.000   # WRITE_SIZE of the same copy reads 256 MiB
