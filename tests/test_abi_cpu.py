@@ -171,3 +171,15 @@ def test_operator_timing_arguments(lib):
     finally:
         blk.blk_set_operator_timing(False)
     assert len(_lib.OPERATORS) == 6
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The bench line is one GPU's throughput: --gpus N > 1 exits with a
+    message (status 2) before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "4"],
+                       capture_output=True, text=True, timeout=300, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
