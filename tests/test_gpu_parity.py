@@ -303,6 +303,27 @@ def test_video_dit_block_full_size():
     check_block(shape, synth.block_case(shape), rows=rows)
 
 
+@pytest.mark.timeout(300)
+def test_video_dit_block_is_deterministic():
+    """The large path's K-split reductions (tail slices of the O and down
+    GEMMs, key slices of the attention) sum in slice order, not arrival
+    order: two runs give the same bits."""
+    import diffusion_transformer_block_amd as blk
+    shape = synth.VIDEO_DIT
+    case = synth.block_case(shape)
+    cfg = config_of(shape)
+    packed = blk.blk_prepare_weights(cfg, [synth.tree_to_device(case["weights"])])
+    x = stack_streams(case, "x")
+    kp, vp = stack_streams(case, "k_prefix"), stack_streams(case, "v_prefix")
+    first = [t.clone() for t in blk.blk_forward(cfg, packed, 0, x, kp, vp)]
+    for _ in range(3):
+        junk = torch.randn(1 << 20, device="cuda").sum()   # other work between the runs
+        again = blk.blk_forward(cfg, packed, 0, x, kp, vp)
+        torch.cuda.synchronize()
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)
+
+
 @pytest.mark.timeout(600)
 def test_video_dit_attention_dominated_full_size():
     """The video chunk's attention (128-row blocks, 3 key slices) carrying y,
