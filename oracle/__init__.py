@@ -23,18 +23,22 @@ arrive already widened exactly to float32.
 Pins (tests/test_oracle_pins.py) tie each function to something outside
 itself: fold identities, brute force, closed forms, torch CPU library
 routines, RoPE invariants and the pages' parameter counts.  The whole-block
-and whole-loop compositions are pinned through their parts plus a torch
-re-composition built from library primitives (rms_norm,
-scaled_dot_product_attention, silu); beyond that composition their values are
-parity unpinned, because the pages print no worked numeric example.
+and whole-loop compositions are pinned through their parts plus float64 torch
+re-compositions built from library primitives (rms_norm,
+scaled_dot_product_attention, linear, silu): the block on its own, and the
+loop over two layers and three Euler steps with distinct per-layer weights and
+cached prefixes.  Several streams on one block's weights are independent
+applications of block_forward, one per stream with its own cache.  Beyond
+these compositions the values are parity unpinned, because the pages print no
+worked numeric example.
 """
 from .block import (rms_norm, rope_tables, apply_rope, attention, gated_ffn,
-                    block_forward, block_forward_streams)
+                    block_forward)
 from .flow import (silu, time_embedding, suffix_embed, velocity_head, euler_integrate,
                    flow_denoise)
 
 __all__ = [
     "rms_norm", "rope_tables", "apply_rope", "attention", "gated_ffn", "block_forward",
-    "block_forward_streams", "silu", "time_embedding", "suffix_embed", "velocity_head",
-    "euler_integrate", "flow_denoise",
+    "silu", "time_embedding", "suffix_embed", "velocity_head", "euler_integrate",
+    "flow_denoise",
 ]

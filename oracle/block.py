@@ -133,15 +133,3 @@ def block_forward(x, w, k_prefix, v_prefix, *, n_q_heads, n_kv_heads, head_dim,
     b = rms_norm(h, w["g_ffn"], eps, dtype)
     y = h + gated_ffn(b, w["w_gate"], w["w_up"], w["w_down"], dtype)
     return y, k, v
-
-
-def block_forward_streams(xs, w, k_prefixes, v_prefixes, *, rows=None, dtype=np.float32,
-                          **shape):
-    """Several independent streams on one set of block weights ([PS]: tasks of
-    different chunks on the same block are batched; each keeps its own KV).
-    Returns lists (y_b, k_new_b, v_new_b) per stream."""
-    out = []
-    for b, x in enumerate(xs):
-        out.append(block_forward(x, w, k_prefixes[b], v_prefixes[b], rows=rows,
-                                 dtype=dtype, **shape))
-    return out

@@ -393,6 +393,121 @@ def test_flow_fp32_agrees_with_fp64_twin_two_layers():
     assert rel(a32, a64) < 1e-4
 
 
+# ---------------------------------------------------------------- loop composition (RT §2, §4.2)
+# A small action-expert stack: distinct weights and cached prefixes per layer,
+# a state token plus 7 action tokens of width 8, three Euler evaluations.
+LOOP_SMALL = synth.FlowShape(
+    "flow_small_pin",
+    synth.BlockShape("flow_small_layer", 128, 256, 4, 1, 32, 1, 8, 20, 4242),
+    n_layers=2, n_steps=3, n_actions=7, action_dim=8, seed=4242)
+
+
+def torch_loop(case, flow):
+    """The denoise loop re-composed in float64 from torch CPU primitives: the
+    embedding with F.linear / F.silu and the state token in row 0, each layer
+    through torch_block with its own weights and its own cached prefix, the
+    velocity as F.rms_norm + F.linear on the action rows X[1:], and explicit
+    Euler with dt = t_{s+1} - t_s (t_n = 0)."""
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    h = f32_tree(case["head"])
+    layers = [f32_tree(l) for l in case["layers"]]
+    b = flow.block
+    D = b.hidden
+    sched = [float(v) for v in case["schedule"]] + [0.0]
+    a = t(h["noise"])
+    for s in range(flow.n_steps):
+        u = F.linear(a, t(h["w1"]).T, t(h["b1"]))
+        tau = t(oracle.time_embedding(sched[s], D)).expand(flow.n_actions, D)
+        z = F.silu(F.linear(torch.cat([u, tau], 1), t(h["w2"]).T, t(h["b2"])))
+        e_act = F.linear(z, t(h["w3"]).T, t(h["b3"]))
+        e_state = F.linear(t(h["state"])[None], t(h["ws"]).T, t(h["bs"]))
+        X = torch.cat([e_state, e_act], 0).numpy()
+        for lw in layers:
+            X, _, _ = torch_block(X, lw, lw["k_prefix"], lw["v_prefix"], b.n_q_heads,
+                                  b.n_kv_heads, b.head_dim, b.rope_base, b.rms_eps)
+        v = F.linear(F.rms_norm(t(X[1:]), (D,), t(h["g_f"]), b.rms_eps), t(h["w_out"]).T,
+                     t(h["b_out"]))
+        a = a + (sched[s + 1] - sched[s]) * v
+    return a.numpy()
+
+
+def oracle_loop(case, flow, layers=None):
+    h = f32_tree(case["head"])
+    ls = [f32_tree(l) for l in case["layers"]] if layers is None else layers
+    a, _ = oracle.flow_denoise(h["noise"], h["state"], case["schedule"], ls, h, dtype=F64,
+                               **shape_kwargs(flow.block))
+    return a
+
+
+def test_flow_loop_matches_torch_recomposition():
+    case = synth.flow_case(LOOP_SMALL)
+    assert rel(oracle_loop(case, LOOP_SMALL), torch_loop(case, LOOP_SMALL)) < 1e-12
+
+
+@pytest.mark.slow
+def test_flow_loop_matches_torch_recomposition_action_expert_shape():
+    """Two layers of the action-expert stack (hidden 1024, 768 cached keys per
+    layer) over the first three times of the ten-step schedule."""
+    flow = synth.FlowShape("flow_2x3", synth.FLOW.block, n_layers=2, n_steps=3,
+                           n_actions=63, action_dim=32, seed=synth.FLOW.seed)
+    case = dict(synth.flow_case(flow))
+    assert rel(oracle_loop(case, flow), torch_loop(case, flow)) < 1e-12
+
+
+def test_loop_pin_catches_planted_mistakes(monkeypatch):
+    """Plausible composition mistakes, planted in the oracle's loop on the CPU,
+    that the torch re-composition must reject."""
+    flow = LOOP_SMALL
+    case = synth.flow_case(flow)
+    ref = torch_loop(case, flow)
+    layers = [f32_tree(l) for l in case["layers"]]
+    assert rel(oracle_loop(case, flow, layers), ref) < 1e-12
+
+    # every layer reads layer 0's cached prefix
+    shared = [dict(l, k_prefix=layers[0]["k_prefix"], v_prefix=layers[0]["v_prefix"])
+              for l in layers]
+    assert rel(oracle_loop(case, flow, shared), ref) > 1e-3
+    # the layers run in the wrong order
+    assert rel(oracle_loop(case, flow, layers[::-1]), ref) > 1e-3
+
+    import oracle.flow as of
+
+    # the velocity taken on X[:-1] (state row kept, last action row dropped)
+    def vel_wrong_rows(X, head, eps, dtype=np.float32):
+        Xa = np.asarray(X, dtype)[:-1]
+        return of.rms_norm(Xa, head["g_f"], eps, dtype) @ np.asarray(head["w_out"], dtype) \
+            + np.asarray(head["b_out"], dtype)
+
+    with monkeypatch.context() as m:
+        m.setattr(of, "velocity_head", vel_wrong_rows)
+        assert rel(oracle_loop(case, flow, layers), ref) > 1e-3
+
+    # Euler with the step's sign flipped (+|dt|)
+    def euler_plus(a0, schedule, velocity, dtype=np.float32):
+        a = np.asarray(a0, dtype)
+        n = len(schedule)
+        for s in range(n):
+            t = float(schedule[s])
+            t_next = float(schedule[s + 1]) if s + 1 < n else 0.0
+            a = a + dtype(t - t_next) * np.asarray(velocity(a, s, t), dtype)
+        return a, []
+
+    with monkeypatch.context() as m:
+        m.setattr(of, "euler_integrate", euler_plus)
+        assert rel(oracle_loop(case, flow, layers), ref) > 1e-3
+
+    # the state token appended last instead of first
+    good_embed = of.suffix_embed
+
+    def embed_state_last(actions, state, t, head, dtype=np.float32):
+        X = good_embed(actions, state, t, head, dtype)
+        return np.concatenate([X[1:], X[:1]], axis=0)
+
+    with monkeypatch.context() as m:
+        m.setattr(of, "suffix_embed", embed_state_last)
+        assert rel(oracle_loop(case, flow, layers), ref) > 1e-3
+
+
 # ---------------------------------------------------------------- planted mistakes are caught
 def test_pins_catch_planted_mistakes(monkeypatch):
     """Plant plausible mistakes in copies of oracle steps (on the CPU) and check
