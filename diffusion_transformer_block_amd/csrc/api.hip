@@ -45,6 +45,9 @@ int fail(int code, const char* fmt, ...) {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+constexpr size_t kSkCtrWords = 4096;    // split-K counters per skinny GEMM: one per group block
+constexpr size_t kBigCtrWords = kBigMaxSplitTiles;
+
 // ---------------------------------------------------------------- validation
 int check_config(const blk_config* c) {
   if (!c) return fail(BLK_EINVAL, "cfg is NULL");
@@ -68,6 +71,8 @@ int check_config(const blk_config* c) {
   if ((c->n_q_heads * d) % 128 != 0 || ((c->n_q_heads + 2 * c->n_kv_heads) * d) % 128 != 0)
     return fail(BLK_EUNSUPPORTED, "Hq*d and (Hq+2Hkv)*d must be multiples of 128");
   if (c->max_pos > (1 << 20)) return fail(BLK_EUNSUPPORTED, "max_pos > 2^20");
+  if ((size_t)(c->n_q_heads + 2 * c->n_kv_heads) * d / 32 > kSkCtrWords)
+    return fail(BLK_EUNSUPPORTED, "(Hq + 2 Hkv) * head_dim above %zu", kSkCtrWords * 32);
   return BLK_OK;
 }
 
@@ -158,6 +163,40 @@ int lookup(const void* packed, const blk_config& cfg, PackRecord* out) {
 }
 
 // ---------------------------------------------------------------- workspace layout
+// Every workspace starts with the same synchronization region, whatever the
+// config and whichever entry point uses it: the skinny GEMMs' split-K arrival
+// counters, the large GEMMs' tail-split counters, the persistent kernel's
+// phase flags and its epoch / done / abort words.  Counters are zero at rest
+// (each call leaves them zero); flags and the epoch only grow.  Activations
+// and partials follow the region, so a workspace can be reused across shapes
+// and entry points without a counter ever landing on stale activation bytes.
+struct SyncRegion {
+  size_t ctr_qkv, ctr_o, ctr_gu, ctr_d, big_ctr, flags, sync, total;
+};
+constexpr SyncRegion make_sync_region() {
+  SyncRegion r{};
+  size_t off = 0;
+  r.ctr_qkv = off;
+  off += kSkCtrWords * 4;
+  r.ctr_o = off;
+  off += kSkCtrWords * 4;
+  r.ctr_gu = off;
+  off += kSkCtrWords * 4;
+  r.ctr_d = off;
+  off += kSkCtrWords * 4;
+  r.big_ctr = off;
+  off += kBigCtrWords * 4;
+  r.flags = off;
+  off += (size_t)kPhCount * kStageMaxFlags * 4;
+  r.sync = off;
+  off += 256;
+  r.total = off;
+  return r;
+}
+constexpr SyncRegion kSync = make_sync_region();
+static_assert(kSync.total % 256 == 0, "the sync region keeps the activations 256-byte aligned");
+static_assert(kSync.total == BLK_WS_SYNC_BYTES, "blk.h states the sync region's size");
+
 struct BlockWs {
   size_t q, o, h, a, r1, r2, part;
   size_t ctr_qkv, ctr_o, ctr_gu, ctr_d;
@@ -167,18 +206,27 @@ struct BlockWs {
   size_t total;
 };
 
+// Activations and partials of one block stage from offset `base` (at least
+// the end of the sync region) on.
 BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
                         size_t extra_part = 0) {
   BlockWs w;
   const size_t M = (size_t)B * T;
   const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const int gq = (Hq + 2 * Hkv) * d / 32, go = D / 32, ggu = F / 16, gd = D / 32;
+  w.ctr_qkv = kSync.ctr_qkv;
+  w.ctr_o = kSync.ctr_o;
+  w.ctr_gu = kSync.ctr_gu;
+  w.ctr_d = kSync.ctr_d;
+  w.big_ctr = kSync.big_ctr;
+  w.flags = kSync.flags;
+  w.sync = kSync.sync;
   // activations between operators are in operand order, padded to 16-row
   // tiles; Q is in the attention's operand order (32-row tiles per kv head)
   const bool small = M > 0 && (int)M <= kSkinnyMaxM;
   const size_t Mp = (size_t)16 * mt_of((int)M);
   const size_t q_rows = std::max(Mp * Hq, (size_t)B * Hkv * 32 * (((Hq / Hkv) * (size_t)T + 31) / 32));
-  size_t off = base;
+  size_t off = std::max(base, kSync.total);
   w.q = off;
   off += align_up(q_rows * d * 2);
   w.o = off;
@@ -202,28 +250,16 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
   }
   w.part = off;
   off += align_up(part * 4);
-  w.ctr_qkv = off;
-  off += align_up((size_t)gq * 4);
-  w.ctr_o = off;
-  off += align_up((size_t)go * 4);
-  w.ctr_gu = off;
-  off += align_up((size_t)ggu * 4);
-  w.ctr_d = off;
-  off += align_up((size_t)gd * 4);
   {
-    size_t bp = 0, bc = 0;
+    size_t bp = 0;
     if (!small && M > 0) {
       const int m = (int)M;
       for (const BigPlan& pl : {big_plan(m, gq, D), big_plan(m, go, Hq * d), big_plan(m, ggu, D),
-                                big_plan(m, gd, F)}) {
+                                big_plan(m, gd, F)})
         bp = std::max(bp, big_part_floats(pl));
-        bc = std::max(bc, (size_t)pl.tiles);
-      }
     }
     w.big_part = off;
     off += align_up(bp * 4);
-    w.big_ctr = off;
-    off += align_up(bc * 4);
   }
   w.sm_att_o = off;
   off += align_up(attn_sm_part_o_elems(B, T, P, Hq, Hkv, d) * 2);
@@ -233,10 +269,6 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
   off += align_up(Mp * D * 2);
   w.xb1 = off;
   off += align_up(Mp * D * 2);
-  w.flags = off;
-  off += align_up((size_t)kPhCount * kStageMaxFlags * 4);
-  w.sync = off;
-  off += align_up(4 * 4);
   w.total = off;
   return w;
 }
@@ -636,7 +668,7 @@ FlowWs flow_ws_layout(const blk_config& c, int N, int P) {
   FlowWs f;
   const int T = N + 1;
   const size_t D = c.hidden;
-  size_t off = 0;
+  size_t off = kSync.total;
   // X and z rows in operand order, padded to 16-row tiles
   f.x0 = off;
   off += align_up((size_t)16 * mt_of(T) * D * 2);
@@ -742,6 +774,113 @@ void destroy_entry(GraphEntry& e) {
   if (e.graph) (void)hipGraphDestroy(e.graph);
   e.exec = nullptr;
   e.graph = nullptr;
+}
+
+// ---------------------------------------------------------------- block entry helpers
+// Shape checks that precede the workspace layout.
+int forward_shape_checks(const blk_config* cfg, int batch, int tokens, int prefix) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (batch < 0 || tokens < 0 || prefix < 0) return fail(BLK_EINVAL, "negative batch/tokens/prefix");
+  if ((long)prefix + tokens > cfg->max_pos)
+    return fail(BLK_EUNSUPPORTED, "prefix + tokens = %ld exceeds max_pos %d",
+                (long)prefix + tokens, cfg->max_pos);
+  if ((long)batch * tokens > (1L << 24)) return fail(BLK_EUNSUPPORTED, "batch * tokens too large");
+  // the large-chunk kernels address an activation matrix with 32-bit byte offsets
+  const long widest = std::max({(long)cfg->hidden, (long)cfg->ffn, (long)cfg->n_q_heads * cfg->head_dim});
+  if ((long)batch * tokens * widest > (1L << 30))
+    return fail(BLK_EUNSUPPORTED, "batch * tokens * max(hidden, ffn, Hq d) exceeds 2^30");
+  return BLK_OK;
+}
+
+// The remaining argument checks; *nothing = true for an empty chunk.
+int forward_arg_checks(const blk_config* cfg, const void* packed, int layer, int batch, int tokens,
+                       int prefix, const uint16_t* x, const uint16_t* k_prefix,
+                       const uint16_t* v_prefix, int64_t prefix_stride, uint16_t* y,
+                       uint16_t* k_new, uint16_t* v_new, int64_t new_stride, PackRecord* rec,
+                       bool* nothing) {
+  *nothing = false;
+  if (!packed) return fail(BLK_EINVAL, "packed is NULL");
+  int rc = lookup(packed, *cfg, rec);
+  if (rc) return rc;
+  if (layer < 0 || layer >= rec->lay.n_layers)
+    return fail(BLK_EINVAL, "layer %d out of range [0, %d)", layer, rec->lay.n_layers);
+  if (batch == 0 || tokens == 0) {
+    *nothing = true;
+    return BLK_OK;
+  }
+  if (!x || !y || !k_new || !v_new) return fail(BLK_EINVAL, "x, y, k_new and v_new must be non-NULL");
+  if (prefix > 0 && (!k_prefix || !v_prefix)) return fail(BLK_EINVAL, "prefix K/V is NULL with prefix > 0");
+  for (const void* p : {(const void*)x, (const void*)y, (const void*)k_new, (const void*)v_new,
+                        (const void*)k_prefix, (const void*)v_prefix})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+      return fail(BLK_EINVAL, "x, y, k_new, v_new, k_prefix and v_prefix must be 16-byte aligned");
+  if (prefix_stride % 8 != 0 || new_stride % 8 != 0)
+    return fail(BLK_EINVAL, "prefix_stride and new_stride must be multiples of 8 elements");
+  const int64_t kvrow = (int64_t)cfg->n_kv_heads * cfg->head_dim;
+  if (batch > 1) {
+    if (prefix > 0 && prefix_stride < (int64_t)prefix * kvrow)
+      return fail(BLK_EINVAL, "prefix_stride smaller than one stream's prefix");
+    if (new_stride < (int64_t)tokens * kvrow)
+      return fail(BLK_EINVAL, "new_stride smaller than one stream's tokens");
+  }
+  if (batch * tokens <= kSkinnyMaxM && !small_plan_ok(*cfg, batch * tokens, true))
+    return fail(BLK_EUNSUPPORTED, "hidden %d too wide for a %d-row chunk", cfg->hidden, batch * tokens);
+  return BLK_OK;
+}
+
+// Enqueues one validated block stage on `st` with workspace ws (layout w).
+// `timing`: whether operator timing (when on) may record events.
+int forward_enqueue(const blk_config& c, const PackRecord& rec, const void* packed, int layer,
+                    int batch, int tokens, int prefix, const uint16_t* x, const uint16_t* k_prefix,
+                    const uint16_t* v_prefix, int64_t prefix_stride, uint16_t* y, uint16_t* k_new,
+                    uint16_t* v_new, int64_t new_stride, void* ws, const BlockWs& w,
+                    hipStream_t st, bool timing) {
+  std::unique_lock<std::mutex> tlk(g_timer_mu, std::defer_lock);
+  if (timing && g_timer.on) {
+    tlk.lock();
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing(st, &cs));
+    if (cs != hipStreamCaptureStatusNone)
+      return fail(BLK_ESTATE, "operator timing is on while the stream is being captured");
+    if (g_timer.used + BLK_N_OPS + 1 > kTimerMaxEvents)
+      return fail(BLK_ESIZE, "operator timing holds %zu events; read them with blk_operator_times",
+                  kTimerMaxEvents);
+    HIP_TRY(timer_event(st, &g_mark_prev));
+    g_mark_stream = st;
+    g_marking = true;
+  }
+  struct MarkReset {
+    ~MarkReset() { g_marking = false; }
+  } mark_reset;
+  (void)hipGetLastError();
+  if (want_persistent()) {
+    StageArgs sa{};
+    const int nwg = stage_grid(c.head_dim, batch * tokens);
+    if (stage_plan(c, batch, tokens, prefix, 0, nwg, sa)) {
+      stage_fill_common(sa, rec.lay, packed, ws, w);
+      sa.flow = 0;
+      sa.n_layers = 1;
+      sa.layer_first = layer;
+      sa.n_steps = 1;
+      sa.x = x;
+      sa.y = y;
+      sa.kn = k_new;
+      sa.vn = v_new;
+      sa.new_stride = new_stride;
+      sa.kp[0] = k_prefix;
+      sa.vp[0] = v_prefix;
+      sa.prefix_stride = prefix_stride;
+      HIP_TRY(launch_stage(sa, nwg, st));
+      op_done(BLK_OP_STAGE);
+      return BLK_OK;
+    }
+    if (g_exec_mode == 2) return fail(BLK_EUNSUPPORTED, "the persistent stage kernel does not cover this shape");
+  }
+  BlockIO io{x, k_prefix, v_prefix, prefix_stride, y, k_new, v_new, new_stride};
+  enqueue_block(c, rec.lay, packed, layer, batch, tokens, prefix, io, ws, w, st);
+  HIP_TRY(hipGetLastError());
+  return BLK_OK;
 }
 
 }  // namespace
@@ -908,96 +1047,23 @@ int blk_forward(const blk_config* cfg, const void* packed, int layer, int batch,
                 const uint16_t* v_prefix, int64_t prefix_stride, uint16_t* y, uint16_t* k_new,
                 uint16_t* v_new, int64_t new_stride, void* ws, size_t* ws_bytes, void* stream) {
   g_err.clear();
-  int rc = check_config(cfg);
+  int rc = forward_shape_checks(cfg, batch, tokens, prefix);
   if (rc) return rc;
   if (!ws_bytes) return fail(BLK_EINVAL, "ws_bytes is NULL");
-  if (batch < 0 || tokens < 0 || prefix < 0) return fail(BLK_EINVAL, "negative batch/tokens/prefix");
-  if ((long)prefix + tokens > cfg->max_pos)
-    return fail(BLK_EUNSUPPORTED, "prefix + tokens = %ld exceeds max_pos %d",
-                (long)prefix + tokens, cfg->max_pos);
-  if ((long)batch * tokens > (1L << 24)) return fail(BLK_EUNSUPPORTED, "batch * tokens too large");
-  {
-    // the large-chunk kernels address an activation matrix with 32-bit byte offsets
-    const long widest = std::max({(long)cfg->hidden, (long)cfg->ffn, (long)cfg->n_q_heads * cfg->head_dim});
-    if ((long)batch * tokens * widest > (1L << 30))
-      return fail(BLK_EUNSUPPORTED, "batch * tokens * max(hidden, ffn, Hq d) exceeds 2^30");
-  }
   const BlockWs w = block_ws_layout(*cfg, batch, tokens, prefix, 0);
   if (!ws) {
     *ws_bytes = w.total;
     return BLK_OK;
   }
   if (*ws_bytes < w.total) return fail(BLK_ESIZE, "ws has %zu bytes, %zu needed", *ws_bytes, w.total);
-  if (!packed) return fail(BLK_EINVAL, "packed is NULL");
   PackRecord rec;
-  rc = lookup(packed, *cfg, &rec);
-  if (rc) return rc;
-  if (layer < 0 || layer >= rec.lay.n_layers)
-    return fail(BLK_EINVAL, "layer %d out of range [0, %d)", layer, rec.lay.n_layers);
-  if (batch == 0 || tokens == 0) return BLK_OK;
-  if (!x || !y || !k_new || !v_new) return fail(BLK_EINVAL, "x, y, k_new and v_new must be non-NULL");
-  if (prefix > 0 && (!k_prefix || !v_prefix)) return fail(BLK_EINVAL, "prefix K/V is NULL with prefix > 0");
-  for (const void* p : {(const void*)x, (const void*)y, (const void*)k_new, (const void*)v_new,
-                        (const void*)k_prefix, (const void*)v_prefix})
-    if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
-      return fail(BLK_EINVAL, "x, y, k_new, v_new, k_prefix and v_prefix must be 16-byte aligned");
-  if (prefix_stride % 8 != 0 || new_stride % 8 != 0)
-    return fail(BLK_EINVAL, "prefix_stride and new_stride must be multiples of 8 elements");
-  const int64_t kvrow = (int64_t)cfg->n_kv_heads * cfg->head_dim;
-  if (batch > 1) {
-    if (prefix > 0 && prefix_stride < (int64_t)prefix * kvrow)
-      return fail(BLK_EINVAL, "prefix_stride smaller than one stream's prefix");
-    if (new_stride < (int64_t)tokens * kvrow)
-      return fail(BLK_EINVAL, "new_stride smaller than one stream's tokens");
-  }
-  if (batch * tokens <= kSkinnyMaxM && !small_plan_ok(*cfg, batch * tokens, true))
-    return fail(BLK_EUNSUPPORTED, "hidden %d too wide for a %d-row chunk", cfg->hidden, batch * tokens);
-  hipStream_t st = (hipStream_t)stream;
-  std::unique_lock<std::mutex> tlk(g_timer_mu, std::defer_lock);
-  if (g_timer.on) {
-    tlk.lock();
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    HIP_TRY(hipStreamIsCapturing(st, &cs));
-    if (cs != hipStreamCaptureStatusNone)
-      return fail(BLK_ESTATE, "operator timing is on while the stream is being captured");
-    if (g_timer.used + BLK_N_OPS + 1 > kTimerMaxEvents)
-      return fail(BLK_ESIZE, "operator timing holds %zu events; read them with blk_operator_times",
-                  kTimerMaxEvents);
-    HIP_TRY(timer_event(st, &g_mark_prev));
-    g_mark_stream = st;
-    g_marking = true;
-  }
-  struct MarkReset {
-    ~MarkReset() { g_marking = false; }
-  } mark_reset;
-  (void)hipGetLastError();
-  if (want_persistent()) {
-    StageArgs sa{};
-    const int nwg = stage_grid(cfg->head_dim, batch * tokens);
-    if (stage_plan(*cfg, batch, tokens, prefix, 0, nwg, sa)) {
-      stage_fill_common(sa, rec.lay, packed, ws, w);
-      sa.flow = 0;
-      sa.n_layers = 1;
-      sa.layer_first = layer;
-      sa.n_steps = 1;
-      sa.x = x;
-      sa.y = y;
-      sa.kn = k_new;
-      sa.vn = v_new;
-      sa.new_stride = new_stride;
-      sa.kp[0] = k_prefix;
-      sa.vp[0] = v_prefix;
-      sa.prefix_stride = prefix_stride;
-      HIP_TRY(launch_stage(sa, nwg, st));
-      op_done(BLK_OP_STAGE);
-      return BLK_OK;
-    }
-    if (g_exec_mode == 2) return fail(BLK_EUNSUPPORTED, "the persistent stage kernel does not cover this shape");
-  }
-  BlockIO io{x, k_prefix, v_prefix, prefix_stride, y, k_new, v_new, new_stride};
-  enqueue_block(*cfg, rec.lay, packed, layer, batch, tokens, prefix, io, ws, w, st);
-  HIP_TRY(hipGetLastError());
-  return BLK_OK;
+  bool nothing = false;
+  rc = forward_arg_checks(cfg, packed, layer, batch, tokens, prefix, x, k_prefix, v_prefix,
+                          prefix_stride, y, k_new, v_new, new_stride, &rec, &nothing);
+  if (rc || nothing) return rc;
+  return forward_enqueue(*cfg, rec, packed, layer, batch, tokens, prefix, x, k_prefix, v_prefix,
+                         prefix_stride, y, k_new, v_new, new_stride, ws, w, (hipStream_t)stream,
+                         true);
 }
 
 int flow_denoise(const blk_config* cfg, const void* packed, int n_layers, int n_steps, int prefix,

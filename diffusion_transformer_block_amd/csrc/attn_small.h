@@ -2,9 +2,11 @@
 // as a device task shared by the standalone kernel and the persistent stage
 // kernel.
 //
-// [PS] = "PhysisServe" (arXiv:2605.11143): a stage runs one block for a chunk
-// of query tokens against the cached KV of earlier chunks plus its own;
-// [RT] = "Running VLAs at Real-time Speed" (arXiv:2510.26742v1) §2: the action
+// [PS] = AREX Feed article on PhysisServe, section on splitting the pipeline
+// per denoise step and block: a stage runs one block for a chunk of query
+// tokens against the cached KV of earlier chunks plus its own;
+// [RT] = reading note on "Running VLAs at Real-time Speed" (Ma et al.,
+// arXiv:2510.26742v1) §2: the action
 // expert's 64 query tokens attend to the cached prefix and to each other with
 // no causal mask inside the chunk.
 //

@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
                    make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
                               __float_as_uint(v[3])));
         }
-    if (!arrive_last(&ga.ctr[tile], (unsigned)nsplit, reinterpret_cast<int*>(big_dsm))) return;
+    if (!arrive_last(&ga.ctr[tile - n_full], (unsigned)nsplit, reinterpret_cast<int*>(big_dsm))) return;
     // every split (this one too) has published: re-read all of them in split
     // order, two 16-row fragments' worth of loads in flight per round trip
 #pragma unroll
@@ -379,6 +379,10 @@ BigPlan big_plan(int M, int n_groups, int K) {
       }
       break;
     }
+  }
+  if (p.splits > 1 && p.tiles - p.n_full > kBigMaxSplitTiles) {   // more split tiles than counters
+    p.splits = 1;
+    p.n_full = p.tiles;
   }
   return p;
 }

@@ -147,6 +147,9 @@ struct GemmArgs {
 };
 
 // Tile shape and K splits of a large-chunk GEMM, and the scratch they need.
+// At most kBigMaxSplitTiles tiles run in K slices (their arrival counters are
+// indexed by tile - n_full).
+constexpr int kBigMaxSplitTiles = 2048;
 struct BigPlan {
   int bm, bn, splits, tiles;
   int n_full;   // tiles run whole (the first n_full); the rest in `splits` K slices each

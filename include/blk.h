@@ -41,8 +41,12 @@
  *   - Size-query protocol: a call whose output buffer pointer is NULL only
  *     writes the required byte count to *bytes / *ws_bytes and returns 0.
  *   - Calls sharing a workspace must not overlap in time (same stream is
- *     fine).  A workspace must be zero-filled before its first use; every
- *     call leaves its synchronization counters at zero again.
+ *     fine).  A workspace must be zero-filled before its first use.  Its
+ *     first BLK_WS_SYNC_BYTES bytes are a synchronization region laid out the
+ *     same way for every config and entry point (arrival counters, which
+ *     every call leaves at zero, and monotonic phase flags); activations and
+ *     partials follow it.  So one workspace, large enough for each call, may
+ *     serve blk_forward and flow_denoise calls of different shapes in turn.
  */
 #ifndef BLK_H_
 #define BLK_H_
@@ -60,6 +64,9 @@ extern "C" {
 #define BLK_ESIZE (-3)        /* a buffer is smaller than its size query              */
 #define BLK_ESTATE (-4)       /* packed buffer unknown, or config/steps do not match */
 #define BLK_EHIP (-5)         /* a HIP runtime call failed (message has the reason)  */
+
+/* Size of the synchronization region at the start of every workspace. */
+#define BLK_WS_SYNC_BYTES 110848
 
 /* Shape of one block.  Supported: head_dim in {64, 128, 256}; hidden % 128 == 0;
  * ffn % 128 == 0; n_q_heads % n_kv_heads == 0; 1 <= max_pos <= 1<<20. */

@@ -183,3 +183,4 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=300, cwd=root)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+

@@ -339,7 +339,8 @@ def test_batched_block_full_size():
     shape = synth.BATCHED
     rng = np.random.default_rng(1)
     rows = sorted(set([0, 127, 128, shape.tokens - 1] + list(rng.choice(shape.tokens, 12, replace=False))))
-    check_block(shape, synth.block_case(shape), rows=rows, streams=[0, 3, 7])
+    # every stream: K_new / V_new in full (each stream's own cache stride), y on the sampled rows
+    check_block(shape, synth.block_case(shape), rows=rows)
 
 
 # ---------------------------------------------------------------- flow loop
@@ -364,6 +365,50 @@ def oracle_flow(flow, case, n_layers):
     a, _ = oracle.flow_denoise(head["noise"], head["state"], case["schedule"], layers, head,
                                n_layers=n_layers, **shape_kwargs(flow.block))
     return a
+
+
+@pytest.mark.parametrize("mode", [1, 2], ids=["per_operator", "persistent"])
+def test_workspace_reused_across_shapes_and_entry_points(mode):
+    """One zero-filled workspace serves, in turn, the 16-token block, the
+    64-token block, a denoise loop and the 16-token block again: the sync
+    words sit in the same region for every shape, so no counter starts on
+    stale activation bytes.  Each result is checked against the oracle."""
+    import diffusion_transformer_block_amd as blk
+    blk.blk_set_execution_mode(mode)
+    try:
+        tiny, ae, flow = synth.TINY, synth.AE_BLOCK, synth.FLOW
+        case_t, case_a = synth.block_case(tiny), synth.block_case(ae)
+        cfg_t, cfg_a = config_of(tiny), config_of(ae)
+        fcase, fcfg, fpacked, kp, vp, head = flow_inputs(flow, 1)
+        need = max(blk.forward_workspace_bytes(cfg_t, 1, tiny.tokens, tiny.prefix),
+                   blk.forward_workspace_bytes(cfg_a, 1, ae.tokens, ae.prefix),
+                   blk.flow_workspace_bytes(fcfg, fpacked, 1, flow.n_steps, flow.block.prefix))
+        ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+
+        def block(shape, case, cfg):
+            packed = blk.blk_prepare_weights(cfg, [synth.tree_to_device(case["weights"])])
+            y, kn, vn = blk.blk_forward(cfg, packed, 0, stack_streams(case, "x"),
+                                        stack_streams(case, "k_prefix"),
+                                        stack_streams(case, "v_prefix"), ws=ws)
+            torch.cuda.synchronize()
+            ry, rk, rv = oracle_block(shape, case, 0)
+            errs = [max_err_ratio(y[0].float().cpu().numpy(), ry),
+                    max_err_ratio(kn[0].float().cpu().numpy(), rk),
+                    max_err_ratio(vn[0].float().cpu().numpy(), rv)]
+            say(f"  {shape.name} on the shared workspace: {max(errs):.2e}")
+            assert max(errs) <= BLOCK_TOL
+
+        block(tiny, case_t, cfg_t)
+        block(ae, case_a, cfg_a)
+        acts = blk.flow_denoise(fcfg, fpacked, flow.n_steps, kp, vp, head["noise"], head["state"],
+                                ws=ws)
+        torch.cuda.synchronize()
+        err = max_err_ratio(acts.cpu().numpy(), oracle_flow(flow, fcase, 1))
+        say(f"  flow (1 layer) on the shared workspace: {err:.2e}")
+        assert err <= LOOP_TOL
+        block(tiny, case_t, cfg_t)
+    finally:
+        blk.blk_set_execution_mode(blk.EXEC_AUTO)
 
 
 @pytest.mark.parametrize("n_layers", [1, 18])
