@@ -21,6 +21,7 @@ from ._lib import (BLK_EHIP, BLK_EINVAL, BLK_ESIZE, BLK_ESTATE, BLK_EUNSUPPORTED
                    FlowHeadSrc, LayerSrc, check, load)
 
 __all__ = ["BlkConfig", "BlkError", "make_config", "blk_prepare_weights", "blk_forward",
+           "blk_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
            "flow_denoise", "blk_last_error", "blk_release", "blk_version", "EXPORTS",
            "blk_set_execution_mode", "EXEC_AUTO", "EXEC_PER_OPERATOR", "EXEC_PERSISTENT",
            "forward_workspace_bytes", "flow_workspace_bytes", "packed_bytes",
@@ -136,6 +137,39 @@ def blk_forward(cfg: BlkConfig, packed, layer: int, x, k_prefix=None, v_prefix=N
         c_void_p(_ptr(k_prefix)), c_void_p(_ptr(v_prefix)), prefix_stride, c_void_p(y.data_ptr()),
         c_void_p(k_new.data_ptr()), c_void_p(v_new.data_ptr()), new_stride,
         c_void_p(ws.data_ptr()), byref(cap), c_void_p(_stream(stream))))
+    return y, k_new, v_new
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def blk_forward_noalloc(cfg: BlkConfig, packed, layer: int, x, k_prefix=None, v_prefix=None, *,
+                        y=None, k_new=None, v_new=None, prefix_stride=None, new_stride=None,
+                        stream=None):
+    """blk_forward on the library's static per-GPU scratch (no workspace
+    argument, nothing allocated by the library).  Outputs not passed are
+    allocated here by torch, before the call; pass y, k_new and v_new to
+    allocate nothing at all."""
+    torch = _torch()
+    lib = load()
+    B, T, D = x.shape
+    P = 0 if k_prefix is None else k_prefix.shape[-3]
+    kvrow = cfg.n_kv_heads * cfg.head_dim
+    if y is None:
+        y = torch.empty_like(x)
+    if k_new is None:
+        k_new = torch.empty(B, T, cfg.n_kv_heads, cfg.head_dim, dtype=x.dtype, device=x.device)
+    if v_new is None:
+        v_new = torch.empty_like(k_new)
+    if prefix_stride is None:
+        prefix_stride = P * kvrow
+    if new_stride is None:
+        new_stride = T * kvrow
+    check("blk_forward_noalloc", lib.blk_forward_noalloc(
+        byref(cfg), c_void_p(packed.data_ptr()), layer, B, T, P, c_void_p(x.data_ptr()),
+        c_void_p(_ptr(k_prefix)), c_void_p(_ptr(v_prefix)), prefix_stride, c_void_p(y.data_ptr()),
+        c_void_p(k_new.data_ptr()), c_void_p(v_new.data_ptr()), new_stride,
+        c_void_p(_stream(stream))))
     return y, k_new, v_new
 
 

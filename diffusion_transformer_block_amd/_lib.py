@@ -17,7 +17,7 @@ ERROR_NAMES = {BLK_EINVAL: "BLK_EINVAL", BLK_EUNSUPPORTED: "BLK_EUNSUPPORTED",
                BLK_ESIZE: "BLK_ESIZE", BLK_ESTATE: "BLK_ESTATE", BLK_EHIP: "BLK_EHIP"}
 
 # every function include/blk.h declares
-EXPORTS = ("blk_prepare_weights", "blk_forward", "flow_denoise", "blk_last_error",
+EXPORTS = ("blk_prepare_weights", "blk_forward", "blk_forward_noalloc", "flow_denoise", "blk_last_error",
            "blk_release", "blk_version", "blk_set_execution_mode", "blk_set_operator_timing",
            "blk_operator_times")
 
@@ -63,6 +63,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                 c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
                                 c_void_p, c_int64, c_void_p, POINTER(c_size_t), c_void_p]
     lib.blk_forward.restype = c_int
+    lib.blk_forward_noalloc.argtypes = [POINTER(BlkConfig), c_void_p, c_int, c_int, c_int, c_int,
+                                        c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
+                                        c_void_p, c_int64, c_void_p]
+    lib.blk_forward_noalloc.restype = c_int
     lib.flow_denoise.argtypes = [POINTER(BlkConfig), c_void_p, c_int, c_int, c_int,
                                  POINTER(c_void_p), POINTER(c_void_p), c_void_p, c_void_p,
                                  c_void_p, c_void_p, POINTER(c_size_t), c_void_p]

@@ -883,6 +883,46 @@ int forward_enqueue(const blk_config& c, const PackRecord& rec, const void* pack
   return BLK_OK;
 }
 
+// ---------------------------------------------------------------- static scratch
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): blk_forward_noalloc's workspace is this file-scope array, one copy
+// per GPU, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel (on the host it is a stand-in symbol, not a device
+// address): the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+static_assert(kScratchBytes == BLK_NOALLOC_SCRATCH_BYTES, "blk.h states the scratch size");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+__global__ void zero_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// Device address of the current device's scratch; its first use on a device
+// also enqueues (on st) a fill kernel that zeroes the sync region.
+int scratch_for_current_device(hipStream_t st, void** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(BLK_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) return fail(BLK_EHIP, "hipGetSymbolAddress returned NULL for the scratch array");
+    (void)hipGetLastError();
+    zero_words_kernel<<<(unsigned)((kSync.total / 4 + 255) / 256), 256, 0, st>>>(
+        reinterpret_cast<uint32_t*>(ptr), kSync.total / 4);
+    HIP_TRY(hipGetLastError());
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return BLK_OK;
+}
+
 }  // namespace
 
 // ============================================================================ exports
@@ -1064,6 +1104,30 @@ int blk_forward(const blk_config* cfg, const void* packed, int layer, int batch,
   return forward_enqueue(*cfg, rec, packed, layer, batch, tokens, prefix, x, k_prefix, v_prefix,
                          prefix_stride, y, k_new, v_new, new_stride, ws, w, (hipStream_t)stream,
                          true);
+}
+
+int blk_forward_noalloc(const blk_config* cfg, const void* packed, int layer, int batch,
+                        int tokens, int prefix, const uint16_t* x, const uint16_t* k_prefix,
+                        const uint16_t* v_prefix, int64_t prefix_stride, uint16_t* y,
+                        uint16_t* k_new, uint16_t* v_new, int64_t new_stride, void* stream) {
+  g_err.clear();
+  int rc = forward_shape_checks(cfg, batch, tokens, prefix);
+  if (rc) return rc;
+  const BlockWs w = block_ws_layout(*cfg, batch, tokens, prefix, 0);
+  if (w.total > kScratchBytes)
+    return fail(BLK_ESIZE, "the stage needs %zu bytes of scratch; the library's static scratch holds %zu",
+                w.total, kScratchBytes);
+  PackRecord rec;
+  bool nothing = false;
+  rc = forward_arg_checks(cfg, packed, layer, batch, tokens, prefix, x, k_prefix, v_prefix,
+                          prefix_stride, y, k_new, v_new, new_stride, &rec, &nothing);
+  if (rc || nothing) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = nullptr;
+  rc = scratch_for_current_device(st, &ws);
+  if (rc) return rc;
+  return forward_enqueue(*cfg, rec, packed, layer, batch, tokens, prefix, x, k_prefix, v_prefix,
+                         prefix_stride, y, k_new, v_new, new_stride, ws, w, st, false);
 }
 
 int flow_denoise(const blk_config* cfg, const void* packed, int n_layers, int n_steps, int prefix,

@@ -173,6 +173,28 @@ int blk_forward(const blk_config* cfg, const void* packed, int layer, int batch,
                 uint16_t* v_new, int64_t new_stride, void* ws, size_t* ws_bytes, void* stream);
 
 /*
+ * blk_forward_noalloc -- blk_forward without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, layouts, results and errors as blk_forward, minus ws and
+ * ws_bytes.  The workspace is a static array inside the library, one copy per
+ * GPU, 16 MiB (BLK_NOALLOC_SCRATCH_BYTES), held until the process ends; a
+ * stage that needs more (its blk_forward size query) fails with BLK_ESIZE.
+ * The first call on a device also enqueues a small kernel that zeroes the
+ * array's synchronization region.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine) and records no operator timing.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (two streams, two threads) race and must be serialized by the
+ * caller; one stream is fine.
+ */
+#define BLK_NOALLOC_SCRATCH_BYTES (16u << 20)
+int blk_forward_noalloc(const blk_config* cfg, const void* packed, int layer, int batch,
+                        int tokens, int prefix, const uint16_t* x, const uint16_t* k_prefix,
+                        const uint16_t* v_prefix, int64_t prefix_stride, uint16_t* y,
+                        uint16_t* k_new, uint16_t* v_new, int64_t new_stride, void* stream);
+
+/*
  * flow_denoise -- the action expert's Euler flow-matching loop ([RT] §2-§4).
  *
  * For s = 0..n_steps-1: X = [state Ws + bs ; SiLU(a W1W2a + table[s]) W3 + b3]

@@ -184,3 +184,13 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
 
+
+def test_noalloc_rejects_a_stage_beyond_its_scratch(lib):
+    """The video chunk needs far more than the static scratch: refused with
+    BLK_ESIZE before any device work (no packed buffer is even looked up)."""
+    c = cfg(hidden=1536, ffn=8960, n_q_heads=12, n_kv_heads=12, head_dim=128, max_pos=6240)
+    assert blk.forward_workspace_bytes(c, 1, 1560, 4680) > blk.NOALLOC_SCRATCH_BYTES
+    rc = lib.blk_forward_noalloc(byref(c), None, 0, 1, 1560, 4680, None, None, None, 0, None,
+                                 None, None, 0, None)
+    assert rc == _lib.BLK_ESIZE
+    assert "scratch" in lib.blk_last_error().decode()
