@@ -432,7 +432,6 @@ void stage_fill_common(StageArgs& sa, const Layout& lay, const void* packed, voi
   sa.ctr_gu = at<unsigned>(ws, w.ctr_gu);
   sa.ctr_d = at<unsigned>(ws, w.ctr_d);
   sa.flags = at<unsigned>(ws, w.flags);
-  sa.epoch = at<unsigned>(ws, w.sync);
   sa.done_ctr = at<unsigned>(ws, w.sync) + 1;
   sa.abort_word = at<unsigned>(ws, w.sync) + 2;
 }

@@ -8,7 +8,12 @@ namespace blk {
 
 enum StagePhase : int { kPhQKV = 0, kPhATT, kPhCMB, kPhO, kPhGU, kPhD, kPhEMB, kPhW3, kPhVEL, kPhCount };
 constexpr int kStageMaxLayers = 64;
-constexpr int kStageMaxFlags = 1024;   // tasks (flags) per phase
+constexpr int kStageMaxFlags = 1024;   // tasks (flag indices) per phase
+// arrival counters: kShards per phase type, kShardWords apart (128 bytes)
+constexpr int kShards = 32;
+constexpr int kShardWords = 32;
+static_assert(kPhCount * kShards * kShardWords <= kPhCount * kStageMaxFlags,
+              "the counters fit the workspace's flag region");
 
 // Task t of a phase runs on workgroup (w0 + t mod nw); n_flags tasks publish a flag.
 struct PhaseMap {
@@ -72,8 +77,7 @@ struct StageArgs {
   float* actions;
   bf16_t* z;
   // synchronisation words (workspace, zero-filled before first use)
-  unsigned* flags;          // [kPhCount][kStageMaxFlags]
-  unsigned* epoch;
+  unsigned* flags;          // arrival counters [kPhCount][kShards] (kShardWords apart)
   unsigned* done_ctr;
   unsigned* abort_word;
   PhaseMap ph[kPhCount];
