@@ -91,7 +91,7 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=320, help="timed block stages (multiple of 16)")
+    ap.add_argument("--steps", type=int, default=320, help="timed block stages (exactly)")
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--only", choices=["all", "block", "tiny", "loop", "large", "video", "batched"],
                     default="all", help="restrict the run (for profiling)")
@@ -177,7 +177,9 @@ def time_block(shape, steps, warmup, rotate):
     def run(i):
         blk.blk_forward(cfg, packs[i], 0, x, kps[i], vps[i], y=y, k_new=kn, v_new=vn, ws=ws)
 
-    # eager reference output, then the graph of one rotation
+    # eager reference output, then the graph of one rotation (stages on
+    # copies 0 .. rotate-1) and, when `steps` is not a multiple of `rotate`,
+    # a graph of the remaining steps % rotate stages
     run(0)
     torch.cuda.synchronize()
     y_eager = y.clone()
@@ -188,28 +190,47 @@ def time_block(shape, steps, warmup, rotate):
             run(i)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(rotate):
-            run(i)
+
+    def capture(n):
+        g_ = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_):
+            for i in range(n):
+                run(i)
+        return g_
+
+    g = capture(rotate)
     g.replay()
     torch.cuda.synchronize()
     assert torch.equal(y, y_eager), "graph replay differs from the eager block"
+    rem = steps % rotate
+    g_rem = capture(rem) if rem else None
 
-    n_rep = max(1, steps // rotate)
-    for _ in range(max(1, warmup // rotate)):
-        g.replay()
+    # warm-up: exactly `warmup` stages (eager calls, cycling the copies)
+    for i in range(warmup):
+        run(i % rotate)
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep + 1)]
+    # timed region: exactly `steps` stages
+    n_full = steps // rotate
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(n_full):
+        g.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    us_graph = e0.elapsed_time(e1) * 1e3 / steps
+    # spread: at least 5 replays of the rotation graph, each timed
+    n_pct = max(5, n_full)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_pct + 1)]
     ev[0].record(st)
-    for r in range(n_rep):
+    for r in range(n_pct):
         g.replay()
         ev[r + 1].record(st)
     torch.cuda.synchronize()
-    us_graph = ev[0].elapsed_time(ev[-1]) * 1e3 / (n_rep * rotate)
-    per_rep = [ev[r].elapsed_time(ev[r + 1]) * 1e3 / rotate for r in range(n_rep)]
-    e0, e1 = ev[0], ev[-1]
+    per_rep = [ev[r].elapsed_time(ev[r + 1]) * 1e3 / rotate for r in range(n_pct)]
+    n_rep = max(1, n_full)
 
     # eager (one C call per block, five launches each)
     for i in range(rotate):
@@ -249,10 +270,11 @@ def time_block(shape, steps, warmup, rotate):
     finally:
         blk.blk_set_operator_timing(False)
     torch.cuda.synchronize()
-    del g, gw, packs, kps, vps
+    del g, g_rem, gw, packs, kps, vps
     torch.cuda.empty_cache()
     return {"us": us_graph, "us_eager": us_eager, "us_warm": us_warm,
-            "us_p10_p50_p90": percentiles(per_rep), "timed_steps": n_rep * rotate, "ops": ops}
+            "us_p10_p50_p90": percentiles(per_rep), "pct_replays": n_pct, "timed_steps": steps,
+            "ops": ops}
 
 
 def time_loop(warmup, reps=20):
@@ -342,8 +364,21 @@ def time_large(shape, reps):
             "timed_blocks": reps}
 
 
-def cpu_baseline(budget_s=12.0):
-    """The oracle, as it stands, timed on the host on the headline workload."""
+def cpu_model():
+    """The host CPU's model name (what lscpu prints as 'Model name')."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(budget_s=4.0, runs=3):
+    """The oracle, as it stands, timed on the host on the headline workload:
+    `runs` runs of about `budget_s` seconds each, median per-stage time."""
     import numpy as np
     import oracle
     import synth
@@ -355,20 +390,45 @@ def cpu_baseline(budget_s=12.0):
               rope_base=shape.rope_base, eps=shape.rms_eps)
     x, kp, vp = st["x"].f32, st["k_prefix"].f32, st["v_prefix"].f32
     oracle.block_forward(x, w, kp, vp, **kw)    # warm
-    n = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        oracle.block_forward(x, w, kp, vp, **kw)
-        n += 1
-    dt = time.perf_counter() - t0
+    per_run, counts = [], []
+    for _ in range(runs):
+        n = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            oracle.block_forward(x, w, kp, vp, **kw)
+            n += 1
+        per_run.append((time.perf_counter() - t0) / n * 1e6)
+        counts.append(n)
     threads = None
     try:
         from threadpoolctl import threadpool_info
         threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    return {"value": round(dt / n * 1e6, 1), "unit": "us", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} block stages of the 64-token AE block (NumPy float32, {dt:.1f} s)"}
+    med = sorted(per_run)[len(per_run) // 2]
+    return {"value": round(med, 1), "unit": "us", "cores": int(threads), "kind": "oracle",
+            "sample": f"{runs} runs of about {budget_s:.0f} s each ({', '.join(map(str, counts))} "
+                      f"block stages of the 64-token AE block, NumPy float32); median per stage",
+            "runs_us": [round(v, 1) for v in per_run], "statistic": f"median of {runs}",
+            "cpu_model": cpu_model(), "host_cpus_visible": len(os.sched_getaffinity(0))}
+
+
+def measured_peaks():
+    """The chip's sustained HBM read bandwidth, dense bf16 MFMA throughput and
+    shader clock under that load, from the library's probes."""
+    import torch
+    import diffusion_transformer_block_amd as blk
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")   # 2 GiB: 8x the last-level cache
+    hbm = blk.probe_hbm_read(buf, reps=5)
+    del buf
+    torch.cuda.empty_cache()
+    tf, ghz = blk.probe_mfma_bf16(20000)
+    return {"hbm_read_GBs": {"nominal": HBM_PEAK_GBS, "measured": round(hbm, 1),
+                             "probe": "blk_probe_hbm_read: 5 passes of 16-byte non-temporal loads over 2 GiB"},
+            "bf16_mfma_TFLOPs": {"nominal": BF16_PEAK_TFLOPS, "measured": round(tf, 1),
+                                 "probe": "blk_probe_mfma_bf16: 4 chains of 32x32x16 MFMAs per wave, 2 waves per SIMD"},
+            "shader_clock_GHz_under_mfma": round(ghz, 3),
+            "nominal_clock_GHz": 2.4}
 
 
 def main():
@@ -398,9 +458,13 @@ def main():
         log(f"calibration copy: {args.calib_copy} MiB read + {args.calib_copy} MiB written, 4 times")
         del src, dst
     rotate = max(1, args.rotate)
-    steps = max(rotate, (args.steps // rotate) * rotate)
+    steps = max(1, args.steps)
     shape = synth.AE_BLOCK
     line = {"metric": METRIC}
+    if args.only in ("all", "block"):
+        log("measured peaks (probes)")
+        line["peaks"] = measured_peaks()
+        log(f"  {line['peaks']}")
     if args.only in ("all", "block"):
         log(f"block {shape.name}: {steps} timed stages, {rotate} weight copies")
         r = time_block(shape, steps, args.warmup, rotate)
@@ -415,6 +479,8 @@ def main():
                               "achieved_GBs": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4),
                               "traffic": traffic_of(name)})
         dom = max(operators, key=lambda o: o["us"])
+        op_traffic = [o["traffic"] for o in operators]
+        stage_traffic = sum(op_traffic) if op_traffic and all(t is not None for t in op_traffic) else None
         line.update({
             "value": round(r["us"], 3), "unit": "us", "n_gpus": 1, "steps": r["timed_steps"],
             "warmup": args.warmup, "ms_per_step": round(r["us"] / 1e3, 6),
@@ -428,11 +494,17 @@ def main():
             "eager_us": round(r["us_eager"], 3),
             "warm_us": round(r["us_warm"], 3),
             "us_p10_p50_p90": [round(v, 3) for v in r["us_p10_p50_p90"]],
-            "roofline": {"bound": "hbm", "kernel": f"{dom['operator']}: {dom['kernels']}",
-                         "achieved": dom["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": dom["frac"], "algorithmic_bytes": dom["algorithmic_bytes"],
-                         "us_per_launch": dom["us"], "timing": "HIP events on the launch stream",
-                         "traffic": traffic_of(dom["operator"])},
+            "pct_replays": r["pct_replays"],
+            "roofline": {"bound": "hbm",
+                         "kernel": "the 64-token block stage: " + " -> ".join(
+                             o["kernels"] for o in operators),
+                         "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": wb + ob,
+                         "us_per_launch": round(r["us"], 3),
+                         "timing": "HIP events on the launch stream around graph replays of whole stages",
+                         "traffic": stage_traffic,
+                         "dominant_operator": {"operator": dom["operator"], "us": dom["us"],
+                                               "frac": dom["frac"]}},
             "stage_roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                                "algorithmic_bytes": wb + ob,

@@ -16,16 +16,18 @@ from __future__ import annotations
 import ctypes
 from ctypes import byref, c_double, c_size_t, c_void_p
 
-from ._lib import (BLK_EHIP, BLK_EINVAL, BLK_ESIZE, BLK_ESTATE, BLK_EUNSUPPORTED, BLK_OK,
-                   EXPORTS, HEAD_FIELDS, LAYER_FIELDS, OPERATORS, BlkConfig, BlkError,
-                   FlowHeadSrc, LayerSrc, check, load)
+from ._lib import (BLK_EABORTED, BLK_EHIP, BLK_EINVAL, BLK_ESIZE, BLK_ESTATE, BLK_EUNSUPPORTED,
+                   BLK_OK, EXPORTS, HEAD_FIELDS, LAYER_FIELDS, OPERATORS, WS_ABORT_OFFSET,
+                   BlkConfig, BlkError, FlowHeadSrc, LayerSrc, check, load)
 
 __all__ = ["BlkConfig", "BlkError", "make_config", "blk_prepare_weights", "blk_forward",
            "blk_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
            "flow_denoise", "blk_last_error", "blk_release", "blk_version", "EXPORTS",
            "blk_set_execution_mode", "EXEC_AUTO", "EXEC_PER_OPERATOR", "EXEC_PERSISTENT",
            "forward_workspace_bytes", "flow_workspace_bytes", "packed_bytes",
-           "blk_set_operator_timing", "blk_operator_times", "OPERATORS"]
+           "blk_set_operator_timing", "blk_operator_times", "OPERATORS", "probe_hbm_read",
+           "blk_workspace_status", "WS_ABORT_OFFSET",
+           "probe_mfma_bf16"]
 
 
 def _torch():
@@ -228,6 +230,13 @@ def blk_set_execution_mode(mode: int) -> None:
     check("blk_set_execution_mode", load().blk_set_execution_mode(mode))
 
 
+def blk_workspace_status(ws, stream=None) -> None:
+    """Wait for the stream and raise BlkError (BLK_EABORTED) if a persistent
+    launch on workspace ``ws`` timed out."""
+    check("blk_workspace_status", load().blk_workspace_status(c_void_p(ws.data_ptr()),
+                                                              c_void_p(_stream(stream))))
+
+
 def blk_set_operator_timing(enable: bool) -> None:
     """Bracket every operator of each blk_forward call with HIP events on its
     stream (or stop); either call discards what was accumulated."""
@@ -242,3 +251,26 @@ def blk_operator_times() -> dict:
     calls = (ctypes.c_int * n)()
     check("blk_operator_times", load().blk_operator_times(avg, calls, n))
     return {OPERATORS[i]: (avg[i], calls[i]) for i in range(n) if calls[i] > 0}
+
+
+def _probe_check(fn: str, rc: int) -> None:
+    if rc != BLK_OK:
+        raise BlkError(fn, rc, load().blk_probe_last_error().decode())
+
+
+def probe_hbm_read(buf, reps: int = 10, stream=None) -> float:
+    """Sustained HBM read GB/s over the device tensor ``buf`` (make it larger
+    than the 256 MB last-level cache)."""
+    gbs = c_double(0.0)
+    _probe_check("blk_probe_hbm_read", load().blk_probe_hbm_read(
+        c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(), reps, byref(gbs),
+        c_void_p(_stream(stream))))
+    return gbs.value
+
+
+def probe_mfma_bf16(iters: int = 20000, stream=None):
+    """(dense bf16 MFMA TFLOP/s, shader clock GHz under that load)."""
+    tf, ghz = c_double(0.0), c_double(0.0)
+    _probe_check("blk_probe_mfma_bf16", load().blk_probe_mfma_bf16(
+        iters, byref(tf), byref(ghz), c_void_p(_stream(stream))))
+    return tf.value, ghz.value

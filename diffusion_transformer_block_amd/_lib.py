@@ -13,13 +13,16 @@ BLK_EUNSUPPORTED = -2
 BLK_ESIZE = -3
 BLK_ESTATE = -4
 BLK_EHIP = -5
+BLK_EABORTED = -6
 ERROR_NAMES = {BLK_EINVAL: "BLK_EINVAL", BLK_EUNSUPPORTED: "BLK_EUNSUPPORTED",
-               BLK_ESIZE: "BLK_ESIZE", BLK_ESTATE: "BLK_ESTATE", BLK_EHIP: "BLK_EHIP"}
+               BLK_ESIZE: "BLK_ESIZE", BLK_ESTATE: "BLK_ESTATE", BLK_EHIP: "BLK_EHIP",
+               BLK_EABORTED: "BLK_EABORTED"}
+WS_ABORT_OFFSET = 110600   # BLK_WS_ABORT_OFFSET
 
 # every function include/blk.h declares
 EXPORTS = ("blk_prepare_weights", "blk_forward", "blk_forward_noalloc", "flow_denoise", "blk_last_error",
            "blk_release", "blk_version", "blk_set_execution_mode", "blk_set_operator_timing",
-           "blk_operator_times")
+           "blk_operator_times", "blk_workspace_status", "blk_probe_hbm_read", "blk_probe_mfma_bf16", "blk_probe_last_error")
 
 # operator indices of blk_operator_times (BLK_OP_* in include/blk.h)
 OPERATORS = ("qkv_rope", "attention", "o_proj", "gate_up", "down", "stage")
@@ -83,6 +86,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.blk_set_operator_timing.restype = c_int
     lib.blk_operator_times.argtypes = [POINTER(c_double), POINTER(c_int), c_int]
     lib.blk_operator_times.restype = c_int
+    lib.blk_workspace_status.argtypes = [c_void_p, c_void_p]
+    lib.blk_workspace_status.restype = c_int
+    lib.blk_probe_hbm_read.argtypes = [c_void_p, c_size_t, c_int, POINTER(c_double), c_void_p]
+    lib.blk_probe_hbm_read.restype = c_int
+    lib.blk_probe_mfma_bf16.argtypes = [c_int, POINTER(c_double), POINTER(c_double), c_void_p]
+    lib.blk_probe_mfma_bf16.restype = c_int
+    lib.blk_probe_last_error.argtypes = []
+    lib.blk_probe_last_error.restype = ctypes.c_char_p
     _lib = lib
     return lib
 

@@ -196,6 +196,8 @@ constexpr SyncRegion make_sync_region() {
 constexpr SyncRegion kSync = make_sync_region();
 static_assert(kSync.total % 256 == 0, "the sync region keeps the activations 256-byte aligned");
 static_assert(kSync.total == BLK_WS_SYNC_BYTES, "blk.h states the sync region's size");
+// the persistent kernel's words in the sync slot: [1] done counter, [2] abort
+static_assert(kSync.sync + 2 * sizeof(unsigned) == BLK_WS_ABORT_OFFSET, "blk.h states the abort word's offset");
 
 struct BlockWs {
   size_t q, o, h, a, r1, r2, part;
@@ -935,6 +937,19 @@ int blk_set_execution_mode(int mode) {
   g_err.clear();
   if (mode < 0 || mode > 2) return fail(BLK_EINVAL, "execution mode %d not in {0, 1, 2}", mode);
   g_exec_mode = mode;
+  return BLK_OK;
+}
+
+int blk_workspace_status(const void* ws, void* stream) {
+  g_err.clear();
+  if (!ws) return fail(BLK_EINVAL, "ws is NULL");
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
+  unsigned word = 0;
+  HIP_TRY(hipMemcpy(&word, at<unsigned>(ws, BLK_WS_ABORT_OFFSET), sizeof word, hipMemcpyDeviceToHost));
+  if (word != 0u)
+    return fail(BLK_EABORTED,
+                "a persistent launch on this workspace timed out waiting for other workgroups "
+                "(its outputs hold NaN); zero-fill the workspace to use it again");
   return BLK_OK;
 }
 

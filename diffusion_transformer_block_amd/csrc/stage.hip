@@ -104,6 +104,26 @@ __device__ __forceinline__ void signal_count(unsigned* ctr) {
   if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// An aborted launch writes NaN over its outputs (y, K_new and V_new of a block,
+// or the actions of the loop), so that no caller reads stale values as a
+// result; every workgroup that sees the abort covers all of them.
+__device__ void poison_outputs(const StageArgs& sa) {
+  const uint32_t nan2 = 0x7FC07FC0u;   // two bf16 quiet NaNs
+  if (sa.flow) {
+    const int n = sa.N * sa.A;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) sa.actions[i] = __uint_as_float(0x7FC00000u);
+    return;
+  }
+  const size_t ny = (size_t)sa.M * sa.D / 2;
+  for (size_t i = threadIdx.x; i < ny; i += blockDim.x) reinterpret_cast<uint32_t*>(sa.y)[i] = nan2;
+  const size_t nkv = (size_t)sa.T * sa.Hkv * sa.d / 2;
+  for (int b = 0; b < sa.B; ++b)
+    for (size_t i = threadIdx.x; i < nkv; i += blockDim.x) {
+      reinterpret_cast<uint32_t*>(sa.kn + (size_t)b * sa.new_stride)[i] = nan2;
+      reinterpret_cast<uint32_t*>(sa.vn + (size_t)b * sa.new_stride)[i] = nan2;
+    }
+}
+
 // ---------------------------------------------------------------- flow head tasks
 struct FlowSmem {
   float xs[8192];
@@ -261,7 +281,10 @@ __global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
 
   if (threadIdx.x == 0) ok_sh = ld_u32c(sa.abort_word) == 0u;
   __syncthreads();
-  if (!ok_sh) return;
+  if (!ok_sh) {   // an earlier launch on this workspace aborted
+    poison_outputs(sa);
+    return;
+  }
   const int nwg = gridDim.x;
   unsigned* const ctrs = sa.flags;
   unsigned* const abort_word = sa.abort_word;
@@ -453,7 +476,10 @@ __global__ __launch_bounds__(256) void stage_kernel(StageArgs sa) {
         });
     }
   }
-  if (!ok) return;
+  if (!ok) {
+    poison_outputs(sa);
+    return;
+  }
   // the last workgroup to finish (every wait of every workgroup is over)
   // clears the arrival counters for the next launch
   __shared__ int last_sh;

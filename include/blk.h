@@ -64,9 +64,12 @@ extern "C" {
 #define BLK_ESIZE (-3)        /* a buffer is smaller than its size query              */
 #define BLK_ESTATE (-4)       /* packed buffer unknown, or config/steps do not match */
 #define BLK_EHIP (-5)         /* a HIP runtime call failed (message has the reason)  */
+#define BLK_EABORTED (-6)     /* a persistent launch on this workspace timed out     */
 
-/* Size of the synchronization region at the start of every workspace. */
+/* Size of the synchronization region at the start of every workspace, and the
+ * byte offset of its abort word (see blk_set_execution_mode). */
 #define BLK_WS_SYNC_BYTES 110848
+#define BLK_WS_ABORT_OFFSET 110600
 
 /* Shape of one block.  Supported: head_dim in {64, 128, 256}; hidden % 128 == 0;
  * ffn % 128 == 0; n_q_heads % n_kv_heads == 0; 1 <= max_pos <= 1<<20. */
@@ -246,6 +249,25 @@ int blk_version(void);
 int blk_set_execution_mode(int mode);
 
 /*
+ * The persistent mode's workgroups wait for each other through memory: it
+ * launches one workgroup per compute unit and assumes they are all resident at
+ * once (nothing else may hold the GPU's compute units so that some of them
+ * cannot start).  Every wait is bounded (about seconds): a wait that times out
+ * sets the workspace's abort word (the 32-bit word at BLK_WS_ABORT_OFFSET),
+ * every other wait then gives up, and the launch writes NaN over its outputs
+ * (y, K_new and V_new, or the actions); later persistent launches on that
+ * workspace do the same at once until the workspace is zero-filled again.
+ * Since calls are asynchronous, such a call itself returns BLK_OK; the abort
+ * is reported by:
+ *
+ * blk_workspace_status -- waits for `stream` (hipStreamSynchronize), then
+ *   reads the abort word of device workspace `ws`: BLK_OK if clear,
+ *   BLK_EABORTED if set (zero-fill the workspace to use it again).
+ *   Errors: BLK_EINVAL (ws NULL), BLK_EHIP.
+ */
+int blk_workspace_status(const void* ws, void* stream);
+
+/*
  * Operator timing.  The operators of one block stage, in order:
  */
 #define BLK_OP_QKV 0        /* RMS(x), fused QKV GEMM, RoPE epilogue              */
@@ -278,6 +300,28 @@ int blk_set_operator_timing(int enable);
  * never ran).  Errors: BLK_EINVAL (NULL arrays with n > 0, n < 0), BLK_EHIP.
  */
 int blk_operator_times(double* avg_us, int* calls, int n);
+
+/*
+ * Measurement probes (not part of the block stage).  Benchmarks report their
+ * results beside the chip's nominal peaks.  Both synchronize `stream` (they
+ * time work on it with HIP events) and allocate no device memory.
+ *
+ * blk_probe_hbm_read -- sustained read bandwidth: `reps` passes of 16-byte
+ *   non-temporal loads over the caller's device buffer `buf` (16-byte aligned,
+ *   bytes >= 1 MiB and a multiple of 16; make it several times the 256 MB
+ *   last-level cache so the passes come from HBM); *gb_per_s = bytes x reps /
+ *   elapsed (1 GB = 1e9 bytes).
+ * blk_probe_mfma_bf16 -- dense bf16 MFMA throughput: two waves per SIMD each
+ *   run four independent chains of `iters` v_mfma_f32_32x32x16_bf16 on
+ *   register operands; *tflops = 2 x 32 x 32 x 16 x MFMAs / elapsed, and
+ *   *clock_ghz is the shader clock over one wave's loop (s_memtime cycles over
+ *   the 100 MHz s_memrealtime counter).
+ * Errors: BLK_EINVAL (NULL outputs, sizes out of range), BLK_EHIP; the message
+ * is in blk_probe_last_error() (per calling thread).
+ */
+int blk_probe_hbm_read(const void* buf, size_t bytes, int reps, double* gb_per_s, void* stream);
+int blk_probe_mfma_bf16(int iters, double* tflops, double* clock_ghz, void* stream);
+const char* blk_probe_last_error(void);
 
 #ifdef __cplusplus
 }

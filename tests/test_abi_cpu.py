@@ -18,7 +18,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_]+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -194,3 +194,16 @@ def test_noalloc_rejects_a_stage_beyond_its_scratch(lib):
                                  None, None, 0, None)
     assert rc == _lib.BLK_ESIZE
     assert "scratch" in lib.blk_last_error().decode()
+
+
+def test_status_and_probe_arguments(lib):
+    """The workspace status query and the measurement probes reject bad
+    arguments before touching the device."""
+    assert lib.blk_workspace_status(None, None) == _lib.BLK_EINVAL
+    g = c_double(0.0)
+    assert lib.blk_probe_hbm_read(None, 1 << 30, 1, byref(g), None) == _lib.BLK_EINVAL
+    assert lib.blk_probe_mfma_bf16(0, byref(g), byref(g), None) == _lib.BLK_EINVAL
+    assert lib.blk_probe_mfma_bf16(10, None, byref(g), None) == _lib.BLK_EINVAL
+    assert lib.blk_probe_last_error()
+    hdr = open(HEADER).read()
+    assert f"#define BLK_WS_ABORT_OFFSET {_lib.WS_ABORT_OFFSET}" in hdr

@@ -511,6 +511,67 @@ def test_paths_agree_on_ae_block(exec_mode):
         assert max_err_ratio(a, b) <= 1e-2
 
 
+def test_persistent_abort_is_reported(exec_mode):
+    """A workspace whose abort word is set (pre-set here from the host; no
+    kernel is made to time out): the persistent launch returns at once and
+    writes NaN over y, K_new and V_new, blk_workspace_status reports
+    BLK_EABORTED, and after a zero-fill the same call gives the oracle's
+    result again.  The same for the denoise loop and its actions."""
+    import diffusion_transformer_block_amd as blk
+    exec_mode(2)
+    shape = synth.AE_BLOCK
+    case = synth.block_case(shape)
+    cfg = config_of(shape)
+    packed = blk.blk_prepare_weights(cfg, [synth.tree_to_device(case["weights"])])
+    x = stack_streams(case, "x")
+    kp, vp = stack_streams(case, "k_prefix"), stack_streams(case, "v_prefix")
+    ws = torch.zeros(blk.forward_workspace_bytes(cfg, 1, shape.tokens, shape.prefix),
+                     dtype=torch.uint8, device="cuda")
+    ws[blk.WS_ABORT_OFFSET:blk.WS_ABORT_OFFSET + 4].view(torch.int32).fill_(1)
+    y, kn, vn = blk.blk_forward(cfg, packed, 0, x, kp, vp, ws=ws)
+    with pytest.raises(blk.BlkError) as ei:
+        blk.blk_workspace_status(ws)
+    assert ei.value.code == blk.BLK_EABORTED
+    for t in (y, kn, vn):
+        assert torch.isnan(t.float()).all()
+    ws.zero_()
+    y, kn, vn = blk.blk_forward(cfg, packed, 0, x, kp, vp, ws=ws)
+    blk.blk_workspace_status(ws)
+    ry, _, _ = oracle_block(shape, case, 0)
+    assert max_err_ratio(y[0].float().cpu().numpy(), ry) <= BLOCK_TOL
+
+    flow = synth.FLOW
+    fcase, fcfg, fpacked, fkp, fvp, head = flow_inputs(flow, 1)
+    fws = torch.zeros(blk.flow_workspace_bytes(fcfg, fpacked, 1, flow.n_steps, flow.block.prefix),
+                      dtype=torch.uint8, device="cuda")
+    fws[blk.WS_ABORT_OFFSET:blk.WS_ABORT_OFFSET + 4].view(torch.int32).fill_(1)
+    acts = blk.flow_denoise(fcfg, fpacked, flow.n_steps, fkp, fvp, head["noise"], head["state"], ws=fws)
+    with pytest.raises(blk.BlkError) as ei:
+        blk.blk_workspace_status(fws)
+    assert ei.value.code == blk.BLK_EABORTED
+    assert torch.isnan(acts).all()
+    fws.zero_()
+    acts = blk.flow_denoise(fcfg, fpacked, flow.n_steps, fkp, fvp, head["noise"], head["state"], ws=fws)
+    blk.blk_workspace_status(fws)
+    assert max_err_ratio(acts.cpu().numpy(), oracle_flow(flow, fcase, 1)) <= LOOP_TOL
+
+
+@pytest.mark.parametrize("n_layers", [18])
+@pytest.mark.timeout(900)
+def test_flow_persistent_full_stack(exec_mode, n_layers):
+    """The persistent kernel over the whole 18-layer x 10-step loop."""
+    import diffusion_transformer_block_amd as blk
+    flow = synth.FLOW
+    exec_mode(2)
+    case, cfg, packed, kp, vp, head = flow_inputs(flow, n_layers)
+    acts = blk.flow_denoise(cfg, packed, flow.n_steps, kp, vp, head["noise"], head["state"])
+    torch.cuda.synchronize()
+    ref = oracle_flow(flow, case, n_layers)
+    err = max_err_ratio(acts.cpu().numpy(), ref)
+    say(f"  persistent flow {n_layers} layers: err {err:.2e}")
+    assert err <= LOOP_TOL
+
+
 @pytest.mark.parametrize("mode", [1, 2], ids=["per_operator", "persistent"])
 def test_flow_each_execution_path(exec_mode, mode):
     import diffusion_transformer_block_amd as blk
