@@ -93,7 +93,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=320, help="timed block stages (exactly)")
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--only", choices=["all", "block", "tiny", "loop", "large", "video", "batched"],
+    ap.add_argument("--only", choices=["all", "block", "tiny", "loop", "frame", "large", "video",
+                                       "batched"],
                     default="all", help="restrict the run (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rotate", type=int, default=16, help="weight copies in rotation")
@@ -326,6 +327,97 @@ def time_loop(warmup, reps=20):
             "timed_loops": reps}
 
 
+def time_frame(reps=10):
+    """The prefix stage (18 layers over the 768 prefix tokens, last layer K/V
+    only) beside the denoise loop on a second stream: the prefix stage writes
+    one set of per-layer caches while the loop reads the other (the pages'
+    two-stream schedule).  Times each alone, one after the other on one stream,
+    and both at once; then the loop with 16 Euler steps (16 action-expert
+    calls per prefix frame) beside the prefix stage."""
+    import torch
+    import diffusion_transformer_block_amd as blk
+    import synth
+    flow = synth.FLOW
+    fb = flow.block
+    T, L = fb.prefix, flow.n_layers
+    cfg = config_of(blk, fb, fb.prefix + flow.n_actions + 1)
+    case = synth.flow_case(flow)
+    head = synth.tree_to_device(case["head"])
+    head["n_actions"] = flow.n_actions
+    loop_layers = [synth.tree_to_device(l) for l in case["layers"]]
+    packed10 = blk.blk_prepare_weights(cfg, loop_layers, head, list(case["schedule"]))
+    sched16 = [(16 - s_) / 16 for s_ in range(16)]
+    packed16 = blk.blk_prepare_weights(cfg, loop_layers, head, sched16)
+    del loop_layers
+    pre_layers = [synth.tree_to_device(synth.layer_weights(fb, 7700 + l)) for l in range(L)]
+    packed_pre = blk.blk_prepare_weights(cfg, pre_layers, None, None)
+    del pre_layers
+    x = synth.to_device(synth.stream_activations(fb, 7700, tokens=T, prefix=0)["x"])
+    kv = lambda: [torch.empty(T, fb.n_kv_heads, fb.head_dim, dtype=torch.bfloat16, device="cuda")
+                  for _ in range(L)]
+    kc_a, vc_a, kc_b, vc_b = kv(), kv(), kv(), kv()
+    pws = torch.zeros(blk.prefill_workspace_bytes(cfg, packed_pre, L, T), dtype=torch.uint8, device="cuda")
+    lws10 = torch.zeros(blk.flow_workspace_bytes(cfg, packed10, L, 10, T), dtype=torch.uint8, device="cuda")
+    lws16 = torch.zeros(blk.flow_workspace_bytes(cfg, packed16, L, 16, T), dtype=torch.uint8, device="cuda")
+    out10, out16 = torch.empty_like(head["noise"]), torch.empty_like(head["noise"])
+    s_pre = torch.cuda.Stream()
+    # the caches the loop reads: one prefix pass
+    blk.prefix_prefill(cfg, packed_pre, x, kc_a, vc_a, ws=pws)
+    torch.cuda.synchronize()
+    # the prefix stage as a graph (the loop captures its own on first use)
+    g_pre = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s_pre):
+        blk.prefix_prefill(cfg, packed_pre, x, kc_b, vc_b, ws=pws, stream=s_pre)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g_pre, stream=s_pre):
+            blk.prefix_prefill(cfg, packed_pre, x, kc_b, vc_b, ws=pws, stream=s_pre)
+    loop10 = lambda st: blk.flow_denoise(cfg, packed10, 10, kc_a, vc_a, head["noise"], head["state"],
+                                         actions=out10, ws=lws10, stream=st)
+    loop16 = lambda st: blk.flow_denoise(cfg, packed16, 16, kc_a, vc_a, head["noise"], head["state"],
+                                         actions=out16, ws=lws16, stream=st)
+    for _ in range(2):
+        loop10(None)
+        loop16(None)
+        g_pre.replay()
+    torch.cuda.synchronize()
+
+    main = torch.cuda.current_stream()
+
+    def timed(body):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main)
+        for _ in range(reps):
+            body()
+        e1.record(main)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def concurrent(loop):
+        # the loop on the launch stream, the prefix stage on a second stream
+        # that starts with it and that the launch stream waits for
+        def body():
+            s_pre.wait_stream(main)
+            with torch.cuda.stream(s_pre):
+                g_pre.replay()
+            loop(main)
+            main.wait_stream(s_pre)
+        return body
+
+    r = {"prefill_ms": timed(lambda: g_pre.replay()), "loop10_ms": timed(lambda: loop10(main)),
+         "loop16_ms": timed(lambda: loop16(main)),
+         "sequential_ms": timed(lambda: (g_pre.replay(), loop10(main))),
+         "concurrent_ms": timed(concurrent(loop10)), "concurrent16_ms": timed(concurrent(loop16))}
+    out = {"workload": "prefix 18 layers x 768 tokens (last layer K/V only) beside flow_18x10",
+           "reps": reps}
+    out.update({k: round(v, 4) for k, v in r.items()})
+    out["overlap_saved_ms"] = round(r["sequential_ms"] - r["concurrent_ms"], 4)
+    out["ae_calls_per_s_16_per_frame"] = round(16 / (r["concurrent16_ms"] * 1e-3), 1)
+    out["frames_per_s_16"] = round(1 / (r["concurrent16_ms"] * 1e-3), 1)
+    del packed10, packed16, packed_pre, pws, lws10, lws16
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_large(shape, reps):
     import torch
     import diffusion_transformer_block_amd as blk
@@ -532,6 +624,10 @@ def main():
         log("loop flow_18x10")
         line["loop"] = time_loop(args.warmup)
         log(f"  {line['loop']}")
+    if args.only in ("all", "frame"):
+        log("prefix stage beside the loop (two streams)")
+        line["frame"] = time_frame()
+        log(f"  {line['frame']}")
     if args.only in ("all", "large", "video", "batched"):
         large = []
         if args.only in ("all", "large", "video"):

@@ -21,7 +21,8 @@ from ._lib import (BLK_EABORTED, BLK_EHIP, BLK_EINVAL, BLK_ESIZE, BLK_ESTATE, BL
                    BlkConfig, BlkError, FlowHeadSrc, LayerSrc, check, load)
 
 __all__ = ["BlkConfig", "BlkError", "make_config", "blk_prepare_weights", "blk_forward",
-           "blk_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
+           "blk_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "prefix_prefill",
+           "prefill_workspace_bytes",
            "flow_denoise", "blk_last_error", "blk_release", "blk_version", "EXPORTS",
            "blk_set_execution_mode", "EXEC_AUTO", "EXEC_PER_OPERATOR", "EXEC_PERSISTENT",
            "forward_workspace_bytes", "flow_workspace_bytes", "packed_bytes",
@@ -173,6 +174,34 @@ def blk_forward_noalloc(cfg: BlkConfig, packed, layer: int, x, k_prefix=None, v_
         c_void_p(k_new.data_ptr()), c_void_p(v_new.data_ptr()), new_stride,
         c_void_p(_stream(stream))))
     return y, k_new, v_new
+
+
+def prefill_workspace_bytes(cfg: BlkConfig, packed, n_layers: int, tokens: int) -> int:
+    lib = load()
+    nbytes = c_size_t(0)
+    check("prefix_prefill", lib.prefix_prefill(byref(cfg), c_void_p(packed.data_ptr()), n_layers,
+                                               tokens, None, None, None, None, byref(nbytes), None))
+    return nbytes.value
+
+
+def prefix_prefill(cfg: BlkConfig, packed, x, k_cache: list, v_cache: list, *, ws=None,
+                   stream=None) -> None:
+    """The prefix stage: len(k_cache) layers on the prefix tokens x (bf16
+    [T, D]); layer l writes its keys and values into k_cache[l], v_cache[l]
+    (bf16 [T, Hkv, d] each); the last layer computes only its keys and values."""
+    torch = _torch()
+    lib = load()
+    L = len(k_cache)
+    T = x.shape[0]
+    if ws is None:
+        ws = torch.zeros(prefill_workspace_bytes(cfg, packed, L, T), dtype=torch.uint8,
+                         device=x.device)
+    kp = (c_void_p * L)(*[t.data_ptr() for t in k_cache])
+    vp = (c_void_p * L)(*[t.data_ptr() for t in v_cache])
+    cap = c_size_t(ws.numel())
+    check("prefix_prefill", lib.prefix_prefill(
+        byref(cfg), c_void_p(packed.data_ptr()), L, T, c_void_p(x.data_ptr()), kp, vp,
+        c_void_p(ws.data_ptr()), byref(cap), c_void_p(_stream(stream))))
 
 
 def flow_workspace_bytes(cfg: BlkConfig, packed, n_layers: int, n_steps: int, prefix: int) -> int:

@@ -659,6 +659,71 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
   }
 }
 
+// K and V of a chunk only (no attention, O projection or FFN): RMS(x), then the
+// fused QKV GEMM over its K and V column groups with the RoPE epilogue.  The
+// last layer of a prefix stack runs this way, since only its K/V is read.
+void enqueue_kv_only(const blk_config& c, const Layout& lay, const void* packed, int layer, int T,
+                     int P, const bf16_t* x, bf16_t* kn, bf16_t* vn, void* ws, const BlockWs& w,
+                     hipStream_t st) {
+  const int M = T;
+  const int D = c.hidden, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const uint8_t* lw = at<uint8_t>(packed, lay.layer0 + (size_t)layer * lay.layer_bytes);
+  const int g_kv = Hq * d / 32, n_kv = 2 * Hkv * d / 32;
+  const uint8_t* bp = lw + lay.wqkv + frag_offset(g_kv, 0, 0, D / 32);
+  if (M <= kSkinnyMaxM) {
+    SkArgs ga{};
+    ga.A = x;
+    ga.lda = D;
+    ga.M = M;
+    ga.K = D;
+    ga.Bp = bp;
+    ga.n_groups = n_kv;
+    ga.eps = c.rms_eps;
+    ga.part = at<float>(ws, w.part);
+    const SkPlan p = sk_plan(M, D, n_kv, true);
+    ga.splits = p.splits;
+    ga.counters = at<unsigned>(ws, w.ctr_qkv);
+    EpiQkvS e{nullptr, kn, vn, 0, at<float>(packed, lay.rope_cos), at<float>(packed, lay.rope_sin),
+              T, P, Hq, Hkv, d, g_kv};
+    launch_sk_qkv(ga, p.gpw, true, e, st);
+    return;
+  }
+  bf16_t* a = at<bf16_t>(ws, w.a);
+  float* r1 = at<float>(ws, w.r1);
+  launch_rms_rows(x, M, D, false, c.rms_eps, r1, a, st);
+  GemmArgs ga{};
+  ga.A = a;
+  ga.lda = D;
+  ga.M = M;
+  ga.K = D;
+  ga.Bp = bp;
+  ga.n_groups = n_kv;
+  ga.r = r1;
+  ga.part = at<float>(ws, w.big_part);
+  ga.ctr = at<unsigned>(ws, w.big_ctr);
+  EpiQKV e{nullptr, kn, vn, 0, at<float>(packed, lay.rope_cos), at<float>(packed, lay.rope_sin),
+           T, P, Hq, Hkv, d, g_kv};
+  launch_gemm_qkv(ga, e, st);
+}
+
+// ---------------------------------------------------------------- prefix stage
+struct PrefillWs {
+  BlockWs blk;
+  size_t h0, h1, total;
+};
+
+PrefillWs prefill_ws_layout(const blk_config& c, int T) {
+  PrefillWs f;
+  size_t off = kSync.total;
+  f.h0 = off;   // hidden states between layers, row-major [T][D]
+  off += align_up((size_t)T * c.hidden * 2);
+  f.h1 = off;
+  off += align_up((size_t)T * c.hidden * 2);
+  f.blk = block_ws_layout(c, 1, T, 0, off);
+  f.total = f.blk.total;
+  return f;
+}
+
 // ---------------------------------------------------------------- flow workspace + driver
 struct FlowWs {
   BlockWs blk;
@@ -1142,6 +1207,50 @@ int blk_forward_noalloc(const blk_config* cfg, const void* packed, int layer, in
   if (rc) return rc;
   return forward_enqueue(*cfg, rec, packed, layer, batch, tokens, prefix, x, k_prefix, v_prefix,
                          prefix_stride, y, k_new, v_new, new_stride, ws, w, st, false);
+}
+
+int prefix_prefill(const blk_config* cfg, const void* packed, int n_layers, int tokens,
+                   const uint16_t* x, uint16_t* const* k_cache, uint16_t* const* v_cache, void* ws,
+                   size_t* ws_bytes, void* stream) {
+  g_err.clear();
+  int rc = forward_shape_checks(cfg, 1, tokens, 0);
+  if (rc) return rc;
+  if (!ws_bytes) return fail(BLK_EINVAL, "ws_bytes is NULL");
+  if (n_layers <= 0 || tokens <= 0) return fail(BLK_EINVAL, "n_layers and tokens must be > 0");
+  const PrefillWs pw = prefill_ws_layout(*cfg, tokens);
+  if (!ws) {
+    *ws_bytes = pw.total;
+    return BLK_OK;
+  }
+  if (*ws_bytes < pw.total) return fail(BLK_ESIZE, "ws has %zu bytes, %zu needed", *ws_bytes, pw.total);
+  if (!packed) return fail(BLK_EINVAL, "packed is NULL");
+  PackRecord rec;
+  rc = lookup(packed, *cfg, &rec);
+  if (rc) return rc;
+  if (n_layers > rec.lay.n_layers)
+    return fail(BLK_EINVAL, "n_layers %d exceeds the %d prepared layers", n_layers, rec.lay.n_layers);
+  if (!x || !k_cache || !v_cache) return fail(BLK_EINVAL, "x, k_cache and v_cache must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(x) % 16) return fail(BLK_EINVAL, "x must be 16-byte aligned");
+  for (int l = 0; l < n_layers; ++l) {
+    if (!k_cache[l] || !v_cache[l]) return fail(BLK_EINVAL, "cache pointer of layer %d is NULL", l);
+    if (reinterpret_cast<uintptr_t>(k_cache[l]) % 16 || reinterpret_cast<uintptr_t>(v_cache[l]) % 16)
+      return fail(BLK_EINVAL, "cache buffers must be 16-byte aligned");
+  }
+  if (tokens <= kSkinnyMaxM && !small_plan_ok(*cfg, tokens, true))
+    return fail(BLK_EUNSUPPORTED, "hidden %d too wide for a %d-row chunk", cfg->hidden, tokens);
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  bf16_t* h[2] = {at<bf16_t>(ws, pw.h0), at<bf16_t>(ws, pw.h1)};
+  const bf16_t* in = reinterpret_cast<const bf16_t*>(x);
+  for (int l = 0; l + 1 < n_layers; ++l) {
+    BlockIO io{in, nullptr, nullptr, 0, h[l & 1], k_cache[l], v_cache[l], 0};
+    enqueue_block(*cfg, rec.lay, packed, l, 1, tokens, 0, io, ws, pw.blk, st);
+    in = h[l & 1];
+  }
+  enqueue_kv_only(*cfg, rec.lay, packed, n_layers - 1, tokens, 0, in, k_cache[n_layers - 1],
+                  v_cache[n_layers - 1], ws, pw.blk, st);
+  HIP_TRY(hipGetLastError());
+  return BLK_OK;
 }
 
 int flow_denoise(const blk_config* cfg, const void* packed, int n_layers, int n_steps, int prefix,

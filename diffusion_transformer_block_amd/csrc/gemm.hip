@@ -21,6 +21,7 @@
 namespace blk {
 
 __device__ __forceinline__ void EpiQKV::store8(int m, int g, int qc, const float* v, const Pre8&) const {
+  g += g_base;
   const int b = m / T, t = m - b * T;
   const int gpr = d >> 5, n_rot_groups = (Hq + Hkv) * gpr;
   bf16_t* dst;

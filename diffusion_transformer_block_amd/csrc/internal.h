@@ -55,6 +55,7 @@ struct EpiQKV {
   const float* cos_t;   // [max_pos][d/2]
   const float* sin_t;
   int T, P, Hq, Hkv, d;
+  int g_base;           // packed group of the GEMM's group 0 (> 0: a K/V-only run)
 
   // cos / sin of slot c of group g at row m's position: the index is valid
   // for every group (V groups ignore it), so the loads carry no condition
@@ -63,6 +64,7 @@ struct EpiQKV {
     float cs, sn;
   };
   __device__ __forceinline__ Aux aux(int m, int g, int c) const {
+    g += g_base;
     const int gpr = d >> 5;
     const size_t ti = (size_t)(P + m % T) * (d >> 1) + 16 * (g % gpr) + c;   // column j < d/2
     return {cos_t[ti], sin_t[ti]};
@@ -70,7 +72,7 @@ struct EpiQKV {
   __device__ __forceinline__ float2 math(int, int g, int, float v0, float v1, float r, const Aux& x) const {
     v0 *= r;
     v1 *= r;
-    if (g >= (Hq + Hkv) * (d >> 5)) return make_float2(v0, v1);
+    if (g + g_base >= (Hq + Hkv) * (d >> 5)) return make_float2(v0, v1);
     return make_float2(v0 * x.cs - v1 * x.sn, v0 * x.sn + v1 * x.cs);
   }
   struct Pre8 {};

@@ -340,11 +340,13 @@ struct EpiQkvS {
   const float* cos_t;   // [max_pos][d/2]
   const float* sin_t;
   int T, P, Hq, Hkv, d;
+  int g_base;           // packed group of the GEMM's group 0 (> 0: a K/V-only run)
   // this thread's cos / sin quadruple, loaded while the GEMM runs
   struct Pre {
     float4 cs, sn;
   };
   __device__ Pre prefetch(int g, int M) const {
+    g += g_base;
     const int t = threadIdx.x, r = t >> 2;
     const int gpr = d >> 5;
     Pre p{make_float4(1.f, 1.f, 1.f, 1.f), make_float4(0.f, 0.f, 0.f, 0.f)};
@@ -357,6 +359,7 @@ struct EpiQkvS {
     return p;
   }
   __device__ void run(const float* tile, int ts, const float* rrow, bool rms, int g, int M, const Pre& pf) const {
+    g += g_base;
     const int t = threadIdx.x;
     const int r = t >> 2;
     if (r >= M) return;

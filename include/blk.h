@@ -198,6 +198,27 @@ int blk_forward_noalloc(const blk_config* cfg, const void* packed, int layer, in
                         uint16_t* k_new, uint16_t* v_new, int64_t new_stride, void* stream);
 
 /*
+ * prefix_prefill -- the prefix stage that builds the per-layer K/V caches a
+ * denoise loop reads ([RT] §2: vision and language produce the KV cache once
+ * per inference and the action expert reuses it over its denoise steps; §4.3:
+ * when only the last layer's K/V is consumed, its attention and FFN are dead
+ * work; §7.1: this stage runs on its own stream beside the loop).
+ *
+ * Runs layers 0..n_layers-1 of `packed` on the T = tokens prefix tokens x
+ * (device bf16 [T][D], positions 0..T-1, no cached keys before them, no mask).
+ * Layer l < n_layers - 1 is a full block stage whose output feeds layer l + 1;
+ * every layer l writes its keys (after RoPE) and values to k_cache[l] and
+ * v_cache[l] (host arrays of n_layers device pointers, each bf16 [T][Hkv][d],
+ * 16-byte aligned); the last layer computes only its keys and values.
+ * ws: device workspace (query with ws == NULL), zero-filled before first use.
+ * Asynchronous on `stream`.  Errors: BLK_EINVAL, BLK_EUNSUPPORTED, BLK_ESIZE,
+ * BLK_ESTATE, BLK_EHIP.
+ */
+int prefix_prefill(const blk_config* cfg, const void* packed, int n_layers, int tokens,
+                   const uint16_t* x, uint16_t* const* k_cache, uint16_t* const* v_cache,
+                   void* ws, size_t* ws_bytes, void* stream);
+
+/*
  * flow_denoise -- the action expert's Euler flow-matching loop ([RT] §2-§4).
  *
  * For s = 0..n_steps-1: X = [state Ws + bs ; SiLU(a W1W2a + table[s]) W3 + b3]

@@ -584,3 +584,84 @@ def test_flow_each_execution_path(exec_mode, mode):
     err = max_err_ratio(acts.cpu().numpy(), ref)
     say(f"  flow 3 layers, mode {mode}: err {err:.2e}")
     assert err <= LOOP_TOL
+
+
+# ---------------------------------------------------------------- prefix stage
+def _prefill_case(shape, n_layers, tokens, seed):
+    """Prefix-stage inputs: `n_layers` layers of `shape` (their own seeds) and
+    `tokens` prefix tokens x ~ N(0, 1)."""
+    layers = [synth.layer_weights(shape, seed * 100 + l) for l in range(n_layers)]
+    x = synth.stream_activations(shape, seed, tokens=tokens, prefix=0)["x"]
+    return layers, x
+
+
+def _oracle_prefill(shape, layers, x):
+    """Per-layer (K, V) of the prefix: layer l runs on layer l-1's output, no
+    cached keys before the prefix (P = 0)."""
+    P0 = np.zeros((0, shape.n_kv_heads, shape.head_dim), np.float32)
+    h = x.f32
+    out = []
+    for w in layers:
+        y, k, v = oracle.block_forward(h, f32_tree(w), P0, P0, **shape_kwargs(shape))
+        out.append((k, v))
+        h = y
+    return out
+
+
+def _gpu_prefill(shape, layers, x, max_pos):
+    import diffusion_transformer_block_amd as blk
+    cfg = config_of(shape, max_pos)
+    packed = blk.blk_prepare_weights(cfg, [synth.tree_to_device(w) for w in layers])
+    T = x.shape[0]
+    kc = [torch.empty(T, shape.n_kv_heads, shape.head_dim, dtype=torch.bfloat16, device="cuda")
+          for _ in layers]
+    vc = [torch.empty_like(k) for k in kc]
+    blk.prefix_prefill(cfg, packed, synth.to_device(x), kc, vc)
+    torch.cuda.synchronize()
+    return kc, vc
+
+
+@pytest.mark.parametrize("shape,tokens", [
+    (synth.AE_BLOCK, 768),                                                   # large-chunk path
+    (synth.small_shape("prefill_small", batch=1, n_kv_heads=1), 37),         # small path, ragged
+], ids=["ae_768", "small_37"])
+@pytest.mark.timeout(600)
+def test_prefix_prefill_caches(shape, tokens):
+    """Three prefix layers: each layer's K (after RoPE) and V against the
+    oracle's chain of blocks; the last layer runs K/V only."""
+    say(f"prefix prefill {shape.name}: 3 layers x {tokens} tokens")
+    layers, x = _prefill_case(shape, 3, tokens, 3301)
+    kc, vc = _gpu_prefill(shape, layers, x, tokens + 64)
+    ref = _oracle_prefill(shape, layers, x)
+    for l, ((rk, rv), k, v) in enumerate(zip(ref, kc, vc)):
+        ek = max_err_ratio(k.float().cpu().numpy(), rk)
+        ev = max_err_ratio(v.float().cpu().numpy(), rv)
+        say(f"  layer {l}: k {ek:.2e}  v {ev:.2e}")
+        assert ek <= BLOCK_TOL and ev <= BLOCK_TOL
+
+
+@pytest.mark.timeout(900)
+def test_prefill_then_denoise_loop():
+    """The prefix stage's caches (2 layers over 768 prefix tokens) feed a
+    2-layer, 10-step denoise loop: the actions against the oracle running the
+    same chain (prefix blocks, then the loop over their K/V)."""
+    import diffusion_transformer_block_amd as blk
+    flow = synth.FLOW
+    shape = flow.block
+    layers, x = _prefill_case(shape, 2, shape.prefix, 3302)
+    kc, vc = _gpu_prefill(shape, layers, x, shape.prefix + flow.n_actions + 1)
+    case, cfg, packed, _, _, head = flow_inputs(flow, 2)
+    acts = blk.flow_denoise(cfg, packed, flow.n_steps, kc, vc, head["noise"], head["state"])
+    torch.cuda.synchronize()
+    ref_kv = _oracle_prefill(shape, layers, x)
+    hf = f32_tree(case["head"])
+    lf = []
+    for l in range(2):
+        d = dict(f32_tree(case["layers"][l]))
+        d["k_prefix"], d["v_prefix"] = ref_kv[l]
+        lf.append(d)
+    ref, _ = oracle.flow_denoise(hf["noise"], hf["state"], case["schedule"], lf, hf, n_layers=2,
+                                 **shape_kwargs(shape))
+    err = max_err_ratio(acts.cpu().numpy(), ref)
+    say(f"  prefill -> loop actions: err {err:.2e}")
+    assert err <= LOOP_TOL
