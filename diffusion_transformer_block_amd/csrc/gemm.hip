@@ -18,6 +18,8 @@
 #include "internal.h"
 #include "skinny.h"
 
+#include <utility>
+
 namespace blk {
 
 __device__ __forceinline__ void EpiQKV::store8(int m, int g, int qc, const float* v, const Pre8&) const {
@@ -41,6 +43,18 @@ __device__ __forceinline__ void EpiQKV::store8(int m, int g, int qc, const float
 }
 
 // ============================================================================ large-chunk GEMM
+
+// Instruction order of one K step: the R fragment reads of the next stage
+// (LDS) alternate with the F MFMAs of this one, one read ahead of each run of
+// F / R MFMAs.  Issued together in front of the MFMAs, the reads of four
+// waves fill the LDS command queue at once and hold every wave's MFMAs back
+// until they drain.
+template <int F, int R, int... I>
+__device__ __forceinline__ void sched_reads_between_mfmas(std::integer_sequence<int, I...>) {
+  ((__builtin_amdgcn_sched_group_barrier(0x100, 1, 0),
+    __builtin_amdgcn_sched_group_barrier(0x008, (I + 1) * F / R - I * F / R, 0)),
+   ...);
+}
 
 // BM x BN output tile per workgroup (4 waves in a 2 x 2 grid, each BM/2 x
 // BN/2 of 16 x 16 x 32 MFMAs), one 32-wide k-tile per LDS stage, four stages
@@ -183,13 +197,17 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   // stage s: its fragments are in registers; stage s + 1 lands (stages s + 2
   // and, after the barrier, s + 3 stay in flight) and is read while stage
   // s's MFMAs run
+  // (the reads of stage s + 1 run unconditionally, so that they share one
+  // basic block with the MFMAs: past the last stage they read a stale buffer
+  // whose values are never used)
   auto step = [&](int s, uint4 (&ca)[MTW], uint4 (&cb)[GW][2], uint4 (&na)[MTW], uint4 (&nb)[GW][2]) {
     if (s + 2 < nk) wait_stages(std::integral_constant<int, 1>{});
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();   // stage s + 1 visible; every wave is done with stage s - 1's buffer
     if (s + 3 < nk) issue(s + 3, (s + 3) & (NST - 1));
-    if (s + 1 < nk) rd((s + 1) & (NST - 1), na, nb);
+    rd((s + 1) & (NST - 1), na, nb);
     mm(ca, cb);
+    sched_reads_between_mfmas<2 * MTW * GW, MTW + 2 * GW>(std::make_integer_sequence<int, MTW + 2 * GW>{});
   };
   for (int s = 0; s < nk; s += 2) {
     step(s, a0, b0, a1, b1);
