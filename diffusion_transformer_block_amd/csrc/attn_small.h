@@ -112,6 +112,14 @@ __device__ __forceinline__ uint2 lds_tr16(const bf16_t* p) {
 }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// max of three floats in one instruction (v_maximum3_f32).  fmaxf would
+// first quiet every MFMA result as a possible signalling NaN; the IEEE
+// maximum needs no such pass, and as a builtin (not inline assembly) it lets
+// the compiler insert the wait states between an MFMA and its reader.
+__device__ __forceinline__ float max3_f32(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -238,20 +246,23 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
 
   // key halves this wave takes of every tile: both (LONG) or its own
   constexpr int NH = LONG ? 2 : 1;
+  // S^T accumulation chains per half: two (even / odd d steps) for a single
+  // half, one per half when two halves already interleave
+  constexpr int NC = NH == 1 ? 2 : 1;
+  constexpr int VB = NDT < 4 ? NDT : 4;   // transposed V reads issued ahead of their MFMAs
+  const float sc = a.scale_log2;
   auto step = [&](int it, auto cur_c, auto first_c) {
     constexpr int cur = decltype(cur_c)::value;          // LDS buffer of tile it
     constexpr bool FIRST = decltype(first_c)::value;     // it == 0
     // ---- S^T (32 keys x 32 rows) of each half: K fragments read from LDS in
-    //      batches ahead of their MFMAs; each half runs two independent
-    //      chains (even and odd d steps)
-    f32x16 sacc[NH], sacc2[NH];
+    //      batches ahead of their MFMAs
+    f32x16 sacc[NH][NC];
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        sacc[h][v] = 0.f;
-        sacc2[h][v] = 0.f;
-      }
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[h][c][v] = 0.f;
     constexpr int KB = NDS < 8 ? NDS : 8;   // K fragments read ahead of their MFMAs
 #pragma unroll
     for (int s0 = 0; s0 < NDS; s0 += KB) {
@@ -265,94 +276,99 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
           kf[h][s] = *reinterpret_cast<const uint4*>(kr + ((32u * (s0 + s)) ^ kx));
       }
 #pragma unroll
-      for (int s = 0; s < KB; s += 2)
+      for (int s = 0; s < KB; ++s)
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          sacc[h] = mfma32(as_bf16x8(kf[h][s]), as_bf16x8(qf[s0 + s]), sacc[h]);
-          if (s + 1 < KB)
-            sacc2[h] = mfma32(as_bf16x8(kf[h][s + 1]), as_bf16x8(qf[s0 + s + 1]), sacc2[h]);
-        }
+        for (int h = 0; h < NH; ++h)
+          sacc[h][s % NC] = mfma32(as_bf16x8(kf[h][s]), as_bf16x8(qf[s0 + s]), sacc[h][s % NC]);
     }
-    // ---- online softmax in base 2, one update for all of the wave's keys
-    //      (in tiles without masked keys v_exp_f32 directly: its arguments
-    //      are finite and <= 8, and results below the normal range are
-    //      negligible next to the row's largest term, which is >= 1; the
-    //      last tile's -inf scores take exp2f, which maps them to 0)
-    float x[NH][16];
-    float mloc = -INFINITY;
-    // keys past the slice exist only in its last tile
-    const bool masked = key_begin + 64 * it + 64 > key_end;   // uniform
+    f32x16 sv[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      sacc[h] += sacc2[h];
-      const int base = key_begin + 64 * it + 32 * (LONG ? h : kh_w);
+      sv[h] = sacc[h][0];
+      if constexpr (NC == 2) sv[h] += sacc[h][1];
+    }
+    // keys past the slice exist only in its last tile: their scores become
+    // -inf (a uniform branch), and v_exp_f32 maps them to exactly 0
+    if (key_begin + 64 * it + 64 > key_end) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = base + 8 * (v >> 2) + 4 * hl + (v & 3);
-        x[h][v] = sacc[h][v] * a.scale_log2;
-        if (masked && key >= key_end) x[h][v] = -INFINITY;
-        mloc = fmaxf(mloc, x[h][v]);
+      for (int h = 0; h < NH; ++h) {
+        const int base = key_begin + 64 * it + 32 * (LONG ? h : kh_w);
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (base + 8 * (v >> 2) + 4 * hl + (v & 3) >= key_end) sv[h][v] = -INFINITY;
       }
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    // Rescale only when some row's max grew past the reference by more than
-    // 2^8 (exp2 of scores against a stale reference stays <= 256: exact
-    // enough in bf16 and far from fp32 overflow); otherwise keep it.  Rows
-    // whose reference is still -inf hold zero sums: nothing to rescale (a
-    // slice's first tile skips the pass over O entirely).
-    const bool grow = mloc > m_run + 8.f;
-    if (FIRST) {
-      m_run = grow ? mloc : m_run;
-    } else if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = grow ? mloc : m_run;
-      if (__builtin_amdgcn_ballot_w64(grow && m_run != -INFINITY) != 0) {
-        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] = o[dt] * alpha;
-        l_run *= alpha;
-      }
-      m_run = m_new;
-    }
-    // masked keys contribute exactly 0 (exp2f(-inf)); a row that has seen no
-    // key yet (reference -inf, every score -inf) takes reference 0
-    const float mref = m_run == -INFINITY ? 0.f : m_run;
-    float psum = 0.f;
-    uint32_t pw[NH][8];
-    auto probs = [&](auto exp_fn) {
-#pragma unroll
-      for (int h = 0; h < NH; ++h)
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          const float p0 = exp_fn(x[h][v] - mref);
-          const float p1 = exp_fn(x[h][v + 1] - mref);
-          psum += p0 + p1;
-          pw[h][v / 2] = pack2(p0, p1);
-        }
-    };
-    if (masked)
-      probs([](float z) { return exp2f(z); });
-    else
-      probs([](float z) { return __builtin_amdgcn_exp2f(z); });
-    l_run += psum;
-    // ---- O^T += V^T P^T, two 16-key steps per half (P^T slots e <-> S^T
-    //      values 8 u + e)
+    // ---- per half: online softmax in base 2, then O^T += V^T P^T (two
+    //      16-key steps; P^T slots e <-> S^T values 8 u + e).  The half's first
+    //      transposed V reads are issued ahead of its softmax.
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      const unsigned vt_off = vt_off0 + 32 * (LONG ? h : kh_w) * HD * 2;
+      const uint8_t* vt0 = reinterpret_cast<const uint8_t*>(&sm.v[cur][0]) + vt_off0 + 32 * (LONG ? h : kh_w) * HD * 2;
+      auto read_v = [&](int u, int d0, uint2 (&vlo)[VB], uint2 (&vhi)[VB]) {
+        const uint8_t* vt = vt0 + 16 * u * HD * 2;
+#pragma unroll
+        for (int dt = 0; dt < VB; ++dt) {
+          const unsigned dx = (64u * (d0 + dt)) ^ vx;
+          vlo[dt] = lds_tr16(reinterpret_cast<const bf16_t*>(vt + dx));
+          vhi[dt] = lds_tr16(reinterpret_cast<const bf16_t*>(vt + 8 * HD * 2 + dx));
+        }
+      };
+      uint2 vlo0[VB], vhi0[VB];
+      read_v(0, 0, vlo0, vhi0);
+      // the row max over this half's keys: raw scores (the scale is
+      // positive), then the row's other 16 keys in lane l ^ 32
+      float mx = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) mx = max3_f32(mx, sv[h][v], sv[h][v + 1]);
+      const float ms = mx * sc;
+      const auto mw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ms), __float_as_uint(ms), false, false);
+      const float mloc = fmaxf(__uint_as_float(mw[0]), __uint_as_float(mw[1]));
+      // Rescale only when some row's max grew past the reference by more than
+      // 2^8 (2^(s - reference) stays <= 256: exact enough in bf16 and far from
+      // fp32 overflow); otherwise keep it.  Rows whose reference is still
+      // -inf hold zero sums: nothing to rescale (a slice's first half-tile
+      // writes O with zero C operands and skips the pass entirely).
+      const bool grow = mloc > m_run + 8.f;
+      if (FIRST && h == 0) {
+        m_run = grow ? mloc : m_run;
+      } else if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? mloc : m_run;
+        if (__builtin_amdgcn_ballot_w64(grow && m_run != -INFINITY) != 0) {
+          const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) o[dt] = o[dt] * alpha;
+          l_run *= alpha;
+        }
+        m_run = m_new;
+      }
+      // a row that has seen no key yet (reference -inf, every score -inf)
+      // takes reference 0; its probabilities are exactly 0
+      const float nref = m_run == -INFINITY ? 0.f : -m_run;
+      // p = 2^(s scale - reference) (arguments <= 8 or -inf)
+      uint32_t pw[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[h][v], sc, nref));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[h][v + 1], sc, nref));
+        pw[v / 2] = pack2(p0, p1);
+        psum += p0 + p1;
+      }
+      l_run += psum;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const bf16x8 pb =
-            as_bf16x8(make_uint4(pw[h][4 * u], pw[h][4 * u + 1], pw[h][4 * u + 2], pw[h][4 * u + 3]));
-        const uint8_t* vt = reinterpret_cast<const uint8_t*>(&sm.v[cur][0]) + vt_off + 16 * u * HD * 2;
-        constexpr int VB = NDT < 4 ? NDT : 4;   // transposed reads issued ahead of their MFMAs
+        const bf16x8 pb = as_bf16x8(make_uint4(pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]));
 #pragma unroll
         for (int d0 = 0; d0 < NDT; d0 += VB) {
           uint2 vlo[VB], vhi[VB];
+          if (u == 0 && d0 == 0) {
 #pragma unroll
-          for (int dt = 0; dt < VB; ++dt) {
-            const unsigned dx = (64u * (d0 + dt)) ^ vx;
-            vlo[dt] = lds_tr16(reinterpret_cast<const bf16_t*>(vt + dx));
-            vhi[dt] = lds_tr16(reinterpret_cast<const bf16_t*>(vt + 8 * HD * 2 + dx));
+            for (int dt = 0; dt < VB; ++dt) {
+              vlo[dt] = vlo0[dt];
+              vhi[dt] = vhi0[dt];
+            }
+          } else {
+            read_v(u, d0, vlo, vhi);
           }
 #pragma unroll
           for (int dt = 0; dt < VB; ++dt) {

@@ -21,12 +21,13 @@ __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint3
 
 // float -> bf16, round to nearest, ties to even; NaN stays NaN: gfx950's
 // v_cvt_pk_bf16_f32, two per instruction (the first operand goes to the low
-// half).  Written as assembly: the compiler's own lowering of __bf16
-// conversions fails instruction selection in the persistent stage kernel.
+// half).  A two-lane vector conversion, not inline assembly: the compiler
+// then inserts the wait states an MFMA result needs before this instruction
+// reads it, which it cannot do for an assembly statement's inputs.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  uint32_t r;
-  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
-  return r;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
 }
 __device__ __forceinline__ bf16_t f2bf(float f) { return (bf16_t)(pack2(f, 0.f) & 0xffffu); }
 
