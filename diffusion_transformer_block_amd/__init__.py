@@ -14,13 +14,14 @@ Tensors:
 from __future__ import annotations
 
 import ctypes
-from ctypes import byref, c_double, c_size_t, c_void_p
+from ctypes import byref, c_double, c_int32, c_size_t, c_void_p
 
 from ._lib import (BLK_EABORTED, BLK_EHIP, BLK_EINVAL, BLK_ESIZE, BLK_ESTATE, BLK_EUNSUPPORTED,
                    BLK_OK, EXPORTS, HEAD_FIELDS, LAYER_FIELDS, OPERATORS, WS_ABORT_OFFSET,
                    BlkConfig, BlkError, FlowHeadSrc, LayerSrc, check, load)
 
 __all__ = ["BlkConfig", "BlkError", "make_config", "blk_prepare_weights", "blk_forward",
+           "blk_forward_chunks",
            "blk_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "prefix_prefill",
            "prefill_workspace_bytes",
            "flow_denoise", "blk_last_error", "blk_release", "blk_version", "EXPORTS",
@@ -137,6 +138,41 @@ def blk_forward(cfg: BlkConfig, packed, layer: int, x, k_prefix=None, v_prefix=N
     cap = c_size_t(ws.numel())
     check("blk_forward", lib.blk_forward(
         byref(cfg), c_void_p(packed.data_ptr()), layer, B, T, P, c_void_p(x.data_ptr()),
+        c_void_p(_ptr(k_prefix)), c_void_p(_ptr(v_prefix)), prefix_stride, c_void_p(y.data_ptr()),
+        c_void_p(k_new.data_ptr()), c_void_p(v_new.data_ptr()), new_stride,
+        c_void_p(ws.data_ptr()), byref(cap), c_void_p(_stream(stream))))
+    return y, k_new, v_new
+
+
+def blk_forward_chunks(cfg: BlkConfig, packed, layer: int, x, prefix_lens, k_prefix=None,
+                       v_prefix=None, *, y=None, k_new=None, v_new=None, prefix_stride=None,
+                       new_stride=None, ws=None, stream=None):
+    """blk_forward for chunks whose histories differ in length: stream b
+    attends to the first prefix_lens[b] rows of its prefix (P = k_prefix's
+    row count is the capacity) and to its own T keys; its token t is at
+    position prefix_lens[b] + t.  prefix_stride=0 shares one prefix among all
+    streams.  Returns (y, k_new, v_new)."""
+    torch = _torch()
+    lib = load()
+    B, T, D = x.shape
+    P = 0 if k_prefix is None else k_prefix.shape[-3]
+    kvrow = cfg.n_kv_heads * cfg.head_dim
+    lens = (c_int32 * max(B, 1))(*[int(v) for v in prefix_lens])
+    if y is None:
+        y = torch.empty_like(x)
+    if k_new is None:
+        k_new = torch.empty(B, T, cfg.n_kv_heads, cfg.head_dim, dtype=x.dtype, device=x.device)
+    if v_new is None:
+        v_new = torch.empty_like(k_new)
+    if prefix_stride is None:
+        prefix_stride = P * kvrow
+    if new_stride is None:
+        new_stride = T * kvrow
+    if ws is None:
+        ws = torch.zeros(forward_workspace_bytes(cfg, B, T, P), dtype=torch.uint8, device=x.device)
+    cap = c_size_t(ws.numel())
+    check("blk_forward_chunks", lib.blk_forward_chunks(
+        byref(cfg), c_void_p(packed.data_ptr()), layer, B, T, P, lens, c_void_p(x.data_ptr()),
         c_void_p(_ptr(k_prefix)), c_void_p(_ptr(v_prefix)), prefix_stride, c_void_p(y.data_ptr()),
         c_void_p(k_new.data_ptr()), c_void_p(v_new.data_ptr()), new_stride,
         c_void_p(ws.data_ptr()), byref(cap), c_void_p(_stream(stream))))

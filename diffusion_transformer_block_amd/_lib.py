@@ -20,7 +20,8 @@ ERROR_NAMES = {BLK_EINVAL: "BLK_EINVAL", BLK_EUNSUPPORTED: "BLK_EUNSUPPORTED",
 WS_ABORT_OFFSET = 110600   # BLK_WS_ABORT_OFFSET
 
 # every function include/blk.h declares
-EXPORTS = ("blk_prepare_weights", "blk_forward", "blk_forward_noalloc", "prefix_prefill",
+EXPORTS = ("blk_prepare_weights", "blk_forward", "blk_forward_chunks", "blk_forward_noalloc",
+           "prefix_prefill",
            "flow_denoise", "blk_last_error",
            "blk_release", "blk_version", "blk_set_execution_mode", "blk_set_operator_timing",
            "blk_operator_times", "blk_workspace_status", "blk_probe_hbm_read", "blk_probe_mfma_bf16", "blk_probe_last_error")
@@ -67,6 +68,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                 c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
                                 c_void_p, c_int64, c_void_p, POINTER(c_size_t), c_void_p]
     lib.blk_forward.restype = c_int
+    lib.blk_forward_chunks.argtypes = [POINTER(BlkConfig), c_void_p, c_int, c_int, c_int, c_int,
+                                       POINTER(c_int32), c_void_p, c_void_p, c_void_p, c_int64,
+                                       c_void_p, c_void_p, c_void_p, c_int64, c_void_p,
+                                       POINTER(c_size_t), c_void_p]
+    lib.blk_forward_chunks.restype = c_int
     lib.blk_forward_noalloc.argtypes = [POINTER(BlkConfig), c_void_p, c_int, c_int, c_int, c_int,
                                         c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
                                         c_void_p, c_int64, c_void_p]

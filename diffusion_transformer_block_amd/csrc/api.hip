@@ -448,7 +448,18 @@ struct BlockIO {
   bf16_t* kn;
   bf16_t* vn;
   int64_t new_stride;
+  const int32_t* plen;    // host: stream b's prefix length (NULL: every stream has P)
 };
+
+// The per-stream prefix lengths as kernel arguments.
+StreamPrefix stream_prefix_of(const BlockIO& io, int B) {
+  StreamPrefix sp{};
+  if (io.plen) {
+    sp.var = 1;
+    for (int b = 0; b < B; ++b) sp.len[b] = io.plen[b];
+  }
+  return sp;
+}
 
 // Whether every skinny GEMM of a small chunk has a valid split.
 bool small_plan_ok(const blk_config& c, int M, bool x_rowmajor) {
@@ -490,6 +501,7 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     ga.counters = at<unsigned>(ws, w.ctr_qkv);
     EpiQkvS e{q, io.kn, io.vn, io.new_stride, at<float>(packed, lay.rope_cos),
               at<float>(packed, lay.rope_sin), T, P, Hq, Hkv, d};
+    e.sp = stream_prefix_of(io, B);
     launch_sk_qkv(ga, p.gpw, !x_frag, e, st);
     op_done(BLK_OP_QKV);
   }
@@ -510,6 +522,7 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     aa.Hq = Hq;
     aa.Hkv = Hkv;
     attn_sm_plan(B, T, P, Hq, Hkv, &aa.splits, &aa.kps, &aa.long_rows);
+    aa.sp = stream_prefix_of(io, B);
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     aa.part_o = at<bf16_t>(ws, w.sm_att_o);
     aa.part_ml = at<float>(ws, w.sm_att_ml);
@@ -594,6 +607,7 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     ga.r = r1;
     EpiQKV e{q, io.kn, io.vn, io.new_stride, at<float>(packed, lay.rope_cos),
              at<float>(packed, lay.rope_sin), T, P, Hq, Hkv, d};
+    e.sp = stream_prefix_of(io, B);
     launch_gemm_qkv(ga, e, st);
     op_done(BLK_OP_QKV);
   }
@@ -616,6 +630,7 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     aa.Hq = Hq;
     aa.Hkv = Hkv;
     attn_sm_plan(B, T, P, Hq, Hkv, &aa.splits, &aa.kps, &aa.long_rows);
+    aa.sp = stream_prefix_of(io, B);
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     aa.part_o = at<bf16_t>(ws, w.sm_att_o);
     aa.part_ml = at<float>(ws, w.sm_att_ml);
@@ -885,8 +900,9 @@ int forward_arg_checks(const blk_config* cfg, const void* packed, int layer, int
     return fail(BLK_EINVAL, "prefix_stride and new_stride must be multiples of 8 elements");
   const int64_t kvrow = (int64_t)cfg->n_kv_heads * cfg->head_dim;
   if (batch > 1) {
-    if (prefix > 0 && prefix_stride < (int64_t)prefix * kvrow)
-      return fail(BLK_EINVAL, "prefix_stride smaller than one stream's prefix");
+    // prefix_stride 0: every stream reads one shared prefix (read only)
+    if (prefix > 0 && prefix_stride != 0 && prefix_stride < (int64_t)prefix * kvrow)
+      return fail(BLK_EINVAL, "prefix_stride is neither 0 (shared) nor at least one stream's prefix");
     if (new_stride < (int64_t)tokens * kvrow)
       return fail(BLK_EINVAL, "new_stride smaller than one stream's tokens");
   }
@@ -901,7 +917,7 @@ int forward_enqueue(const blk_config& c, const PackRecord& rec, const void* pack
                     int batch, int tokens, int prefix, const uint16_t* x, const uint16_t* k_prefix,
                     const uint16_t* v_prefix, int64_t prefix_stride, uint16_t* y, uint16_t* k_new,
                     uint16_t* v_new, int64_t new_stride, void* ws, const BlockWs& w,
-                    hipStream_t st, bool timing) {
+                    hipStream_t st, bool timing, const int32_t* prefix_lens = nullptr) {
   std::unique_lock<std::mutex> tlk(g_timer_mu, std::defer_lock);
   if (timing && g_timer.on) {
     tlk.lock();
@@ -920,7 +936,9 @@ int forward_enqueue(const blk_config& c, const PackRecord& rec, const void* pack
     ~MarkReset() { g_marking = false; }
   } mark_reset;
   (void)hipGetLastError();
-  if (want_persistent()) {
+  if (prefix_lens && g_exec_mode == 2)
+    return fail(BLK_EUNSUPPORTED, "per-stream prefix lengths run on the per-operator kernels only");
+  if (!prefix_lens && want_persistent()) {
     StageArgs sa{};
     const int nwg = stage_grid(c.head_dim, batch * tokens);
     if (stage_plan(c, batch, tokens, prefix, 0, nwg, sa)) {
@@ -943,7 +961,7 @@ int forward_enqueue(const blk_config& c, const PackRecord& rec, const void* pack
     }
     if (g_exec_mode == 2) return fail(BLK_EUNSUPPORTED, "the persistent stage kernel does not cover this shape");
   }
-  BlockIO io{x, k_prefix, v_prefix, prefix_stride, y, k_new, v_new, new_stride};
+  BlockIO io{x, k_prefix, v_prefix, prefix_stride, y, k_new, v_new, new_stride, prefix_lens};
   enqueue_block(c, rec.lay, packed, layer, batch, tokens, prefix, io, ws, w, st);
   HIP_TRY(hipGetLastError());
   return BLK_OK;
@@ -1183,6 +1201,38 @@ int blk_forward(const blk_config* cfg, const void* packed, int layer, int batch,
   return forward_enqueue(*cfg, rec, packed, layer, batch, tokens, prefix, x, k_prefix, v_prefix,
                          prefix_stride, y, k_new, v_new, new_stride, ws, w, (hipStream_t)stream,
                          true);
+}
+
+int blk_forward_chunks(const blk_config* cfg, const void* packed, int layer, int batch,
+                       int tokens, int prefix, const int32_t* prefix_lens, const uint16_t* x,
+                       const uint16_t* k_prefix, const uint16_t* v_prefix, int64_t prefix_stride,
+                       uint16_t* y, uint16_t* k_new, uint16_t* v_new, int64_t new_stride, void* ws,
+                       size_t* ws_bytes, void* stream) {
+  g_err.clear();
+  int rc = forward_shape_checks(cfg, batch, tokens, prefix);
+  if (rc) return rc;
+  if (!ws_bytes) return fail(BLK_EINVAL, "ws_bytes is NULL");
+  if (batch > kMaxVarStreams)
+    return fail(BLK_EUNSUPPORTED, "batch %d exceeds %d streams with their own prefix lengths", batch,
+                kMaxVarStreams);
+  const BlockWs w = block_ws_layout(*cfg, batch, tokens, prefix, 0);
+  if (!ws) {
+    *ws_bytes = w.total;
+    return BLK_OK;
+  }
+  if (*ws_bytes < w.total) return fail(BLK_ESIZE, "ws has %zu bytes, %zu needed", *ws_bytes, w.total);
+  if (batch > 0 && !prefix_lens) return fail(BLK_EINVAL, "prefix_lens is NULL");
+  for (int b = 0; b < batch; ++b)
+    if (prefix_lens[b] < 0 || prefix_lens[b] > prefix)
+      return fail(BLK_EINVAL, "prefix_lens[%d] = %d outside [0, %d]", b, prefix_lens[b], prefix);
+  PackRecord rec;
+  bool nothing = false;
+  rc = forward_arg_checks(cfg, packed, layer, batch, tokens, prefix, x, k_prefix, v_prefix,
+                          prefix_stride, y, k_new, v_new, new_stride, &rec, &nothing);
+  if (rc || nothing) return rc;
+  return forward_enqueue(*cfg, rec, packed, layer, batch, tokens, prefix, x, k_prefix, v_prefix,
+                         prefix_stride, y, k_new, v_new, new_stride, ws, w, (hipStream_t)stream,
+                         true, prefix_lens);
 }
 
 int blk_forward_noalloc(const blk_config* cfg, const void* packed, int layer, int batch,

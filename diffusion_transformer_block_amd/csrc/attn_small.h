@@ -66,6 +66,7 @@ struct AttnSmArgs {
   bf16_t* part_o;         // [splits][n_rbt][64 * d] (normalised partials, attn_part_slot order)
   float* part_ml;         // [splits][n_rbt][64][2] (max, sum)
   int long_rows;          // 1: 128-row blocks over a single key slice (attn_sm_task LONG)
+  StreamPrefix sp;        // per-stream prefix lengths (<= P; P sizes the key slices)
 };
 
 constexpr int kAttnMaxSplits = 16;
@@ -156,7 +157,10 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
   const int G = __builtin_amdgcn_readfirstlane(a.Hq / a.Hkv);
   const int rows = G * a.T;
   const int n_rt = (rows + 31) >> 5;           // 32-row tiles of this (stream, kv head)
-  const int L = a.P + a.T;
+  // this stream's prefix length (streams of one call may differ; the key
+  // slices are sized for the longest) and its keys
+  const int Pb = __builtin_amdgcn_readfirstlane(stream_prefix(a.sp, a.P, b));
+  const int L = Pb + a.T;
   const int key_begin = ks * a.kps;
   const int key_end = min(L, key_begin + a.kps);
   const int n_tiles = (key_end - key_begin + 63) >> 6;
@@ -179,13 +183,13 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
   const unsigned lds_v = __builtin_amdgcn_readfirstlane(lds_u32(&sm.v[0][0]));
   auto load_tile = [&](int tile, int buf) {
     const int row0 = key_begin + 64 * tile;
-    const bool prefix_only = row0 + 64 <= a.P;   // uniform
+    const bool prefix_only = row0 + 64 <= Pb;   // uniform
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int r = kk0 + j * RPJ;
       const int key = min(row0 + r, key_end - 1);
-      const bool pre = key < a.P;
-      const size_t ro = (size_t)(pre ? key : key - a.P) * kvrow;
+      const bool pre = key < Pb;
+      const size_t ro = (size_t)(pre ? key : key - Pb) * kvrow;
       const bf16_t* kg = (pre ? kpb : knb) + ro + 8 * (c0 ^ attn_swz_k<HD>(r));
       const bf16_t* vg = (pre ? vpb : vnb) + ro + 8 * (c0 ^ attn_swz_v<HD>(r));
       const unsigned off = buf * TILE_BYTES + (j * 256 + w * 64) * 16;
@@ -202,13 +206,28 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
   __syncthreads();   // a previous task's readers of sm are done (the DMA writes it)
   // the first tile, if wholly in the prefix, does not depend on earlier work
   // and starts before the wait
-  const bool pre0 = key_begin + 64 <= a.P;
+  const bool pre0 = key_begin + 64 <= Pb;
   if (n_tiles > 0 && pre0) load_tile(0, 0);
   if (!wait()) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // no DMA may land after the workgroup ends
     return false;
   }
-  if (n_tiles > 0 && !pre0) load_tile(0, 0);
+  if (n_tiles <= 0) {
+    // a key slice past this stream's keys (a stream with a shorter prefix
+    // than the call's longest): its rows' (max, sum) are (-inf, 0), which the
+    // merge weights by zero (several slices exist whenever one can be empty)
+    constexpr int BR = LONG ? 128 : 64;
+    const int n_rb64 = (rows + 63) >> 6;
+    const int n_rbt64 = a.B * a.Hkv * n_rb64;
+    const int arow = BR * rb + tid;
+    if (tid < BR && arow < rows) {
+      const __amdgpu_buffer_rsrc_t rpm =
+          make_rsrc(a.part_ml + ((size_t)ks * n_rbt64 + bh * n_rb64 + (arow >> 6)) * 128, 512);
+      buf_st8(rpm, (arow & 63) * 8, __float_as_uint(-INFINITY), __float_as_uint(0.f));
+    }
+    return false;
+  }
+  if (!pre0) load_tile(0, 0);
 
   // this wave's 32 query rows: Q^T fragments (B operand), one per d step
   const int rt = __builtin_amdgcn_readfirstlane(min((LONG ? 4 : 2) * rb + rp, n_rt - 1));
@@ -565,12 +584,16 @@ __device__ void attn_combine_task(const AttnSmArgs& a, int task) {
 #pragma unroll
   for (int sp = 0; sp < kAttnMaxSplits; ++sp)
     if (sp < a.splits) {
-      const float wgt = ml[sp].x == -INFINITY ? 0.f : ml[sp].y * exp2f(ml[sp].x - mx);
-      den += wgt;
-      float x[8];
-      unpack8(pv[sp], x);
+      // an empty slice ((max, sum) = (-inf, 0)) wrote no partial rows: skip
+      // them rather than multiply whatever they hold by zero
+      if (ml[sp].x != -INFINITY) {
+        const float wgt = ml[sp].y * exp2f(ml[sp].x - mx);
+        den += wgt;
+        float x[8];
+        unpack8(pv[sp], x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = fmaf(wgt, x[e], f[e]);
+        for (int e = 0; e < 8; ++e) f[e] = fmaf(wgt, x[e], f[e]);
+      }
     }
   const float inv = 1.f / den;
 #pragma unroll

@@ -151,7 +151,8 @@ int blk_prepare_weights(const blk_config* cfg, const blk_layer_src* layers, int 
  *   x       device bf16 [batch][T][D]           chunk hidden states (input)
  *   k_prefix, v_prefix  device bf16, stream b at element offset
  *           b * prefix_stride, each [P][Hkv][d]  cached keys (already rotated)
- *           and values; read only; may be NULL when P == 0
+ *           and values; read only; may be NULL when P == 0; prefix_stride 0
+ *           makes every stream read the same prefix
  *   y       device bf16 [batch][T][D]           block output
  *   k_new, v_new  device bf16, stream b at b * new_stride, each [T][Hkv][d]:
  *           the chunk's own keys (after RoPE) and values.  They may alias
@@ -174,6 +175,33 @@ int blk_forward(const blk_config* cfg, const void* packed, int layer, int batch,
                 int prefix, const uint16_t* x, const uint16_t* k_prefix,
                 const uint16_t* v_prefix, int64_t prefix_stride, uint16_t* y, uint16_t* k_new,
                 uint16_t* v_new, int64_t new_stride, void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * blk_forward_chunks -- blk_forward for a batch of chunks whose histories
+ * differ in length: the same-block batch of chunks at different points of a
+ * chunk-autoregressive schedule, each reading the cached (noisy) K/V written
+ * before it and producing its own ([PS], sections on the pipeline per denoise
+ * step and block and on same-block batching across chunks).
+ *
+ * Same arguments, layouts, results and errors as blk_forward, plus
+ *   prefix_lens  host int32 [batch]: stream b attends to the first
+ *                prefix_lens[b] rows of its prefix (0 <= prefix_lens[b] <= P,
+ *                P = prefix sizes the buffers and the workspace) and to its
+ *                own T keys, and its token t is at position prefix_lens[b] + t.
+ * With prefix_stride 0 every stream reads the first rows of one shared cache
+ * (a stream's K_new / V_new may then be appended to it for the next call; a
+ * call never reads what it writes).  Streams with prefix_lens[b] == P give
+ * exactly blk_forward's result.  The array is read during the call only.
+ * Runs on the per-operator kernels (BLK_EUNSUPPORTED when execution mode 2
+ * forces the persistent kernel).  Errors as blk_forward, plus BLK_EINVAL
+ * (prefix_lens NULL with batch > 0, or a length outside [0, P]) and
+ * BLK_EUNSUPPORTED (batch above 16).
+ */
+int blk_forward_chunks(const blk_config* cfg, const void* packed, int layer, int batch,
+                       int tokens, int prefix, const int32_t* prefix_lens, const uint16_t* x,
+                       const uint16_t* k_prefix, const uint16_t* v_prefix, int64_t prefix_stride,
+                       uint16_t* y, uint16_t* k_new, uint16_t* v_new, int64_t new_stride, void* ws,
+                       size_t* ws_bytes, void* stream);
 
 /*
  * blk_forward_noalloc -- blk_forward without a workspace argument, for callers

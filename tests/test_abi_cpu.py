@@ -207,3 +207,32 @@ def test_status_and_probe_arguments(lib):
     assert lib.blk_probe_last_error()
     hdr = open(HEADER).read()
     assert f"#define BLK_WS_ABORT_OFFSET {_lib.WS_ABORT_OFFSET}" in hdr
+
+
+def test_chunks_validation_before_any_device_work(lib):
+    """blk_forward_chunks checks its per-stream prefix lengths before any
+    device work: NULL lengths, a length outside [0, P], and more streams than
+    its kernel arguments carry are refused with the documented codes; valid
+    lengths reach the packed-buffer lookup (unknown here: BLK_ESTATE)."""
+    c = cfg()
+    B, T, P = 4, 16, 100
+    need = blk.forward_workspace_bytes(c, B, T, P)
+    fake = c_void_p(0x1000)
+    ok = c_size_t(need)
+    Lens = ctypes.c_int32 * 17
+
+    def call(batch, lens, ws=fake):
+        return lib.blk_forward_chunks(byref(c), fake, 0, batch, T, P, lens, fake, fake, fake, 0,
+                                      fake, fake, fake, T * 256, ws, byref(ok), None)
+
+    assert call(B, None) == _lib.BLK_EINVAL
+    assert "prefix_lens" in lib.blk_last_error().decode()
+    assert call(B, Lens(0, 37, 101, 64)) == _lib.BLK_EINVAL
+    assert call(B, Lens(0, 37, -1, 64)) == _lib.BLK_EINVAL
+    assert call(17, Lens(*([5] * 17))) == _lib.BLK_EUNSUPPORTED
+    assert call(B, Lens(0, 37, 100, 64)) == _lib.BLK_ESTATE
+    # size query with no lengths at all
+    n = c_size_t(0)
+    assert lib.blk_forward_chunks(byref(c), None, 0, B, T, P, None, None, None, None, 0, None, None,
+                                  None, 0, None, byref(n), None) == _lib.BLK_OK
+    assert n.value == need
