@@ -93,8 +93,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=320, help="timed block stages (exactly)")
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--only", choices=["all", "block", "tiny", "loop", "frame", "large", "video",
-                                       "batched"],
+    ap.add_argument("--only", choices=["all", "block", "tiny", "loop", "frame", "chunks", "large",
+                                       "video", "batched"],
                     default="all", help="restrict the run (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rotate", type=int, default=16, help="weight copies in rotation")
@@ -418,6 +418,67 @@ def time_frame(reps=10):
     return out
 
 
+def time_chunks(reps=20):
+    """A same-block batch of chunks at different points of one history
+    (blk_forward_chunks: one shared cache, a prefix length per chunk) against
+    the same chunks as separate blk_forward calls, each variant replayed from
+    a captured graph with the weights resident: the batch reads the weights
+    once and launches each operator once for all its chunks."""
+    import dataclasses
+    import torch
+    import diffusion_transformer_block_amd as blk
+    import synth
+    cases = [("ae_4x16tok_chunks", dataclasses.replace(synth.AE_BLOCK, tokens=16), [520, 536, 552, 568]),
+             ("video_2x1560tok_chunks", synth.VIDEO_DIT, [4680, 6240])]
+    out = []
+    for name, shape, lens in cases:
+        B, T, P = len(lens), shape.tokens, max(lens)
+        cfg = config_of(blk, shape, P + T)
+        packed = blk.blk_prepare_weights(cfg, [synth.tree_to_device(synth.layer_weights(shape, 8800))])
+        cache = synth.stream_activations(shape, 8800, tokens=T, prefix=P)
+        kc, vc = synth.to_device(cache["k_prefix"]), synth.to_device(cache["v_prefix"])
+        x = torch.stack([synth.to_device(synth.stream_activations(shape, 8801 + b, tokens=T, prefix=0)["x"])
+                         for b in range(B)])
+        y = torch.empty_like(x)
+        kn = torch.empty(B, T, shape.n_kv_heads, shape.head_dim, dtype=torch.bfloat16, device="cuda")
+        vn = torch.empty_like(kn)
+        ws = torch.zeros(blk.forward_workspace_bytes(cfg, B, T, P), dtype=torch.uint8, device="cuda")
+
+        def batched():
+            blk.blk_forward_chunks(cfg, packed, 0, x, lens, kc, vc, prefix_stride=0, y=y, k_new=kn,
+                                   v_new=vn, ws=ws)
+
+        def separate():
+            for b, L in enumerate(lens):
+                blk.blk_forward(cfg, packed, 0, x[b:b + 1], kc[:L], vc[:L], y=y[b:b + 1],
+                                k_new=kn[b:b + 1], v_new=vn[b:b + 1], ws=ws)
+
+        res = {"workload": name, "chunks": B, "tokens": T, "prefix_lens": lens}
+        for key, body in (("batched_us", batched), ("separate_us", separate)):
+            body()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                body()
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            st = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(reps):
+                g.replay()
+            e1.record(st)
+            torch.cuda.synchronize()
+            res[key] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+            del g
+        res["saved_frac"] = round(1 - res["batched_us"] / res["separate_us"], 4)
+        out.append(res)
+        del packed, kc, vc, x, y, kn, vn, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def time_large(shape, reps):
     import torch
     import diffusion_transformer_block_amd as blk
@@ -628,6 +689,10 @@ def main():
         log("prefix stage beside the loop (two streams)")
         line["frame"] = time_frame()
         log(f"  {line['frame']}")
+    if args.only in ("all", "chunks"):
+        log("same-block batch of chunks with their own history lengths")
+        line["chunks"] = time_chunks()
+        log(f"  {line['chunks']}")
     if args.only in ("all", "large", "video", "batched"):
         large = []
         if args.only in ("all", "large", "video"):

@@ -89,18 +89,33 @@ void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps, i
   const int G = Hq / Hkv;
   const int n_rbt = B * Hkv * ((G * T + 63) / 64);
   const int L = P + T;
-  // many 128-row blocks (long chunks): 128 rows per K/V tile, and key slices
-  // only as far as needed for about two workgroups per compute unit, each
-  // slice at least 4 tiles (long_rows == NULL: the caller runs 64-row blocks)
+  // many 128-row blocks (long chunks): 128 rows per K/V tile, and the number
+  // of key slices (each at least 4 tiles) that minimises rounds of the chip's
+  // workgroup slots (two per compute unit) x 64-key steps per slice, plus the
+  // merge: about a hundredth of a step per block and slice (the batched
+  // 8 x 880-token attention took ~100 us longer with 2 slices than with one
+  // for 27 fewer steps per slot).  long_rows == NULL: the caller runs 64-row
+  // blocks.
   const int n_rbt_long = B * Hkv * ((G * T + 127) / 128);
   if (long_rows) *long_rows = 0;
   if (long_rows && n_rbt_long >= 32) {
-    int s = std::max(1, std::min(kAttnMaxSplits, (2 * device_cus() + n_rbt_long / 2) / n_rbt_long));
-    s = std::max(1, std::min(s, L / 256));
-    int k = (L + s - 1) / s;
-    k = (k + 63) / 64 * 64;
-    *kps = k;
-    *splits = (L + k - 1) / k;
+    const long slots = 2L * device_cus();
+    const int tiles = (L + 63) / 64;
+    const int s_max = std::max(1, std::min(kAttnMaxSplits, L / 256));
+    int best_kt = tiles;
+    double best = 1e30;
+    for (int s = 1; s <= s_max; ++s) {
+      const int kt = (tiles + s - 1) / s;    // tiles per slice
+      const int ns = (tiles + kt - 1) / kt;  // slices this makes
+      const long wgs = (long)n_rbt_long * ns;
+      const double cost = (double)((wgs + slots - 1) / slots) * kt + (ns > 1 ? 0.01 * (double)wgs : 0.0);
+      if (cost < best - 1e-9) {
+        best = cost;
+        best_kt = kt;
+      }
+    }
+    *kps = best_kt * 64;
+    *splits = (L + *kps - 1) / *kps;
     *long_rows = 1;
     return;
   }
