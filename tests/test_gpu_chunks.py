@@ -106,6 +106,24 @@ def test_chunks_ragged_prefixes(shape, lens):
     check_streams(shape, case, lens, f(y), f(kn), f(vn), kp32)
 
 
+def test_chunks_at_the_stream_limit():
+    """16 chunks (the most one call takes) of 4 tokens, 64 rows in all, with
+    history lengths from 0 to the full 200."""
+    import diffusion_transformer_block_amd as blk
+    shape = synth.small_shape("chunks_16x4", hidden=256, ffn=512, n_q_heads=4, n_kv_heads=1,
+                              head_dim=64, batch=16, tokens=4, prefix=200)
+    lens = [0, 200, 13, 64, 65, 127, 128, 1, 199, 32, 100, 150, 7, 77, 180, 50]
+    case = synth.block_case(shape)
+    cfg, packed = prepared(shape, case, shape.prefix + shape.tokens)
+    x, kp, vp = stack(case, "x"), stack(case, "k_prefix"), stack(case, "v_prefix")
+    say(f"{shape.name}: B=16 T=4 P=200 lens={lens}")
+    y, kn, vn = blk.blk_forward_chunks(cfg, packed, 0, x, lens, kp, vp)
+    torch.cuda.synchronize()
+    kp32 = lambda b, L: (f32_tree(case["streams"][b])["k_prefix"][:L],
+                         f32_tree(case["streams"][b])["v_prefix"][:L])
+    check_streams(shape, case, lens, f(y), f(kn), f(vn), kp32)
+
+
 def test_chunks_with_full_prefixes_equal_blk_forward():
     """Every stream at the full prefix length: the same bits as blk_forward."""
     import diffusion_transformer_block_amd as blk

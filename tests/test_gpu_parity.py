@@ -127,6 +127,16 @@ def test_small_shapes(shape):
     check_block(shape, synth.block_case(shape))
 
 
+@pytest.mark.parametrize("tokens", [64, 65], ids=["small_path_max_64", "large_path_min_65"])
+def test_path_switch_at_64_rows(tokens):
+    """The last chunk size of the small path (64 rows: skinny split-K GEMMs,
+    64-row attention blocks) and the first of the large path (65 rows: tiled
+    GEMMs fed by LDS DMA), at the action-expert layer shape."""
+    shape = synth.small_shape(f"switch_{tokens}", hidden=1024, ffn=4096, n_q_heads=8, n_kv_heads=1,
+                              head_dim=256, batch=1, tokens=tokens, prefix=200)
+    check_block(shape, synth.block_case(shape))
+
+
 def test_no_prefix():
     shape = shrink(synth.TINY, name="tiny_no_prefix", prefix=0)
     check_block(shape, synth.block_case(shape), prefix=False)
