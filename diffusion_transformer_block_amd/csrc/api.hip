@@ -205,6 +205,7 @@ struct BlockWs {
   size_t big_part, big_ctr;     // large-chunk GEMM K splits
   size_t sm_att_o, sm_att_ml;   // small-chunk attention key-slice partials
   size_t xb0, xb1, flags, sync;
+  size_t plen;                  // per-stream prefix lengths (blk_forward_chunks)
   size_t total;
 };
 
@@ -271,6 +272,8 @@ BlockWs block_ws_layout(const blk_config& c, int B, int T, int P, size_t base,
   off += align_up(Mp * D * 2);
   w.xb1 = off;
   off += align_up(Mp * D * 2);
+  w.plen = off;
+  off += align_up(kMaxVarStreams * 4);
   w.total = off;
   return w;
 }
@@ -451,14 +454,24 @@ struct BlockIO {
   const int32_t* plen;    // host: stream b's prefix length (NULL: every stream has P)
 };
 
-// The per-stream prefix lengths as kernel arguments.
-StreamPrefix stream_prefix_of(const BlockIO& io, int B) {
-  StreamPrefix sp{};
-  if (io.plen) {
-    sp.var = 1;
-    for (int b = 0; b < B; ++b) sp.len[b] = io.plen[b];
-  }
-  return sp;
+// The per-stream prefix lengths travel to one small kernel by value and from
+// there, through the workspace, to the block's kernels.
+struct StreamLens {
+  int n;
+  int len[kMaxVarStreams];
+};
+__global__ void write_lens_kernel(int* dst, StreamLens v) {
+  if ((int)threadIdx.x < v.n) dst[threadIdx.x] = v.len[threadIdx.x];
+}
+// Enqueues the lengths' copy into the workspace; NULL when every stream has P.
+const int* stream_prefix_of(const BlockIO& io, int B, void* ws, const BlockWs& w, hipStream_t st) {
+  if (!io.plen) return nullptr;
+  StreamLens v{};
+  v.n = B;
+  for (int b = 0; b < B; ++b) v.len[b] = io.plen[b];
+  int* dst = at<int>(ws, w.plen);
+  write_lens_kernel<<<1, kMaxVarStreams, 0, st>>>(dst, v);
+  return dst;
 }
 
 // Whether every skinny GEMM of a small chunk has a valid split.
@@ -479,6 +492,7 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
   const int M = B * T, MT = mt_of(M);
   const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const uint8_t* lw = at<uint8_t>(packed, lay.layer0 + (size_t)layer * lay.layer_bytes);
+  const int* plen = stream_prefix_of(io, B, ws, w, st);
   bf16_t* q = at<bf16_t>(ws, w.q);
   bf16_t* o = at<bf16_t>(ws, w.o);
   bf16_t* h = at<bf16_t>(ws, w.h);
@@ -501,7 +515,7 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     ga.counters = at<unsigned>(ws, w.ctr_qkv);
     EpiQkvS e{q, io.kn, io.vn, io.new_stride, at<float>(packed, lay.rope_cos),
               at<float>(packed, lay.rope_sin), T, P, Hq, Hkv, d};
-    e.sp = stream_prefix_of(io, B);
+    e.plen = plen;
     launch_sk_qkv(ga, p.gpw, !x_frag, e, st);
     op_done(BLK_OP_QKV);
   }
@@ -522,7 +536,7 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     aa.Hq = Hq;
     aa.Hkv = Hkv;
     attn_sm_plan(B, T, P, Hq, Hkv, &aa.splits, &aa.kps, &aa.long_rows);
-    aa.sp = stream_prefix_of(io, B);
+    aa.plen = plen;
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     aa.part_o = at<bf16_t>(ws, w.sm_att_o);
     aa.part_ml = at<float>(ws, w.sm_att_ml);
@@ -582,6 +596,7 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
   const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const int MT = mt_of(M);
   const uint8_t* lw = at<uint8_t>(packed, lay.layer0 + (size_t)layer * lay.layer_bytes);
+  const int* plen = stream_prefix_of(io, B, ws, w, st);
   bf16_t* q = at<bf16_t>(ws, w.q);
   bf16_t* o = at<bf16_t>(ws, w.o);
   bf16_t* h = at<bf16_t>(ws, w.h);
@@ -607,7 +622,7 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     ga.r = r1;
     EpiQKV e{q, io.kn, io.vn, io.new_stride, at<float>(packed, lay.rope_cos),
              at<float>(packed, lay.rope_sin), T, P, Hq, Hkv, d};
-    e.sp = stream_prefix_of(io, B);
+    e.plen = plen;
     launch_gemm_qkv(ga, e, st);
     op_done(BLK_OP_QKV);
   }
@@ -630,7 +645,7 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     aa.Hq = Hq;
     aa.Hkv = Hkv;
     attn_sm_plan(B, T, P, Hq, Hkv, &aa.splits, &aa.kps, &aa.long_rows);
-    aa.sp = stream_prefix_of(io, B);
+    aa.plen = plen;
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     aa.part_o = at<bf16_t>(ws, w.sm_att_o);
     aa.part_ml = at<float>(ws, w.sm_att_ml);

@@ -66,7 +66,7 @@ struct AttnSmArgs {
   bf16_t* part_o;         // [splits][n_rbt][64 * d] (normalised partials, attn_part_slot order)
   float* part_ml;         // [splits][n_rbt][64][2] (max, sum)
   int long_rows;          // 1: 128-row blocks over a single key slice (attn_sm_task LONG)
-  StreamPrefix sp;        // per-stream prefix lengths (<= P; P sizes the key slices)
+  const int* plen;        // device: per-stream prefix lengths (<= P; P sizes the key slices) or NULL
 };
 
 constexpr int kAttnMaxSplits = 16;
@@ -159,7 +159,7 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
   const int n_rt = (rows + 31) >> 5;           // 32-row tiles of this (stream, kv head)
   // this stream's prefix length (streams of one call may differ; the key
   // slices are sized for the longest) and its keys
-  const int Pb = __builtin_amdgcn_readfirstlane(stream_prefix(a.sp, a.P, b));
+  const int Pb = __builtin_amdgcn_readfirstlane(stream_prefix(a.plen, a.P, b));
   const int L = Pb + a.T;
   const int key_begin = ks * a.kps;
   const int key_end = min(L, key_begin + a.kps);

@@ -18,20 +18,12 @@ constexpr int kWave = 64;
 
 // Streams of one call that may each have their own prefix length (a batch of
 // chunks at different points of a history: [PS], section on same-block
-// batching across chunks).  The lengths travel in the kernel arguments;
-// stream_prefix picks stream b's without an indexed (private-memory) access.
+// batching across chunks).  Kernels get a device pointer to the lengths
+// (written into the workspace ahead of the block), or NULL when every stream
+// has the call's P: a by-value table in the kernel arguments made the
+// compiler serialize the argument loads of the kernels' prologues.
 constexpr int kMaxVarStreams = 16;
-struct StreamPrefix {
-  int var;                     // 0: every stream has the call's prefix length P
-  int len[kMaxVarStreams];     // var: stream b's prefix length (<= P)
-};
-__host__ __device__ __forceinline__ int stream_prefix(const StreamPrefix& sp, int P, int b) {
-  if (!sp.var) return P;
-  int p = sp.len[0];
-#pragma unroll
-  for (int i = 1; i < kMaxVarStreams; ++i) p = b == i ? sp.len[i] : p;
-  return p;
-}
+__device__ __forceinline__ int stream_prefix(const int* plen, int P, int b) { return plen ? plen[b] : P; }
 
 // ---------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }

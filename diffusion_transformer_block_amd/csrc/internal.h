@@ -56,7 +56,7 @@ struct EpiQKV {
   const float* sin_t;
   int T, P, Hq, Hkv, d;
   int g_base;           // packed group of the GEMM's group 0 (> 0: a K/V-only run)
-  StreamPrefix sp;      // per-stream prefix lengths (token t of stream b at position P_b + t)
+  const int* plen;      // device: stream b's prefix length (NULL: all P); token t at P_b + t
 
   // cos / sin of slot c of group g at row m's position: the index is valid
   // for every group (V groups ignore it), so the loads carry no condition
@@ -68,7 +68,7 @@ struct EpiQKV {
     g += g_base;
     const int gpr = d >> 5;
     const int b = m / T;
-    const size_t ti = (size_t)(stream_prefix(sp, P, b) + m - b * T) * (d >> 1) + 16 * (g % gpr) + c;   // column j < d/2
+    const size_t ti = (size_t)(stream_prefix(plen, P, b) + m - b * T) * (d >> 1) + 16 * (g % gpr) + c;   // column j < d/2
     return {cos_t[ti], sin_t[ti]};
   }
   __device__ __forceinline__ float2 math(int, int g, int, float v0, float v1, float r, const Aux& x) const {

@@ -341,7 +341,7 @@ struct EpiQkvS {
   const float* sin_t;
   int T, P, Hq, Hkv, d;
   int g_base;           // packed group of the GEMM's group 0 (> 0: a K/V-only run)
-  StreamPrefix sp;      // per-stream prefix lengths (token t of stream b at position P_b + t)
+  const int* plen;      // device: stream b's prefix length (NULL: all P); token t at P_b + t
   // this thread's cos / sin quadruple, loaded while the GEMM runs
   struct Pre {
     float4 cs, sn;
@@ -353,7 +353,7 @@ struct EpiQkvS {
     Pre p{make_float4(1.f, 1.f, 1.f, 1.f), make_float4(0.f, 0.f, 0.f, 0.f)};
     if (r < M && g < (Hq + Hkv) * gpr) {
       const int b = r / T, tt = r - b * T, head = g / gpr;
-      const size_t ti = (size_t)(stream_prefix(sp, P, b) + tt) * (d >> 1) + 16 * (g - head * gpr) + (t & 3) * 4;
+      const size_t ti = (size_t)(stream_prefix(plen, P, b) + tt) * (d >> 1) + 16 * (g - head * gpr) + (t & 3) * 4;
       p.cs = *reinterpret_cast<const float4*>(cos_t + ti);
       p.sn = *reinterpret_cast<const float4*>(sin_t + ti);
     }
