@@ -30,7 +30,9 @@
 //    publish fp32 tiles and the last split to arrive (device counter, reset by
 //    it) sums all of them in split order, so results do not depend on timing.
 //  * With RMS the waves also sum x^2 of the rows they load (the statistic
-//    costs no extra pass) and the epilogue gets r = (mean x^2 + eps)^-1/2.
+//    costs no extra pass: one MFMA of each activation fragment with itself,
+//    whose diagonal is the rows' sums of squares) and the epilogue gets
+//    r = (mean x^2 + eps)^-1/2.
 //  * The epilogue reads the summed 64 x 32 tile from LDS in the order it
 //    stores (row-contiguous 16-byte stores).
 #pragma once
@@ -182,8 +184,11 @@ __device__ bool sk_task(const SkArgs& ga, const Epi& epi, int gb, int s, SkSmem<
   };
   auto get_a = [&](int b, int, int mt) -> uint4 { return av[b][mt]; };
 
+  // With RMS, ss[mt] = A_mt A_mt^T accumulated on the matrix unit: the same
+  // fragment as both operands puts each row's sum of squares on the diagonal
+  // (one MFMA per fragment instead of 16 vector instructions).
   f32x4 acc[MT][GPW][2];
-  float ss[MT];
+  f32x4 ss[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -191,7 +196,7 @@ __device__ bool sk_task(const SkArgs& ga, const Epi& epi, int gb, int s, SkSmem<
       acc[mt][j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
       acc[mt][j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    ss[mt] = 0.f;
+    ss[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int b = 0; b < NB; ++b) issue_a(b, b);
@@ -203,7 +208,7 @@ __device__ bool sk_task(const SkArgs& ga, const Epi& epi, int gb, int s, SkSmem<
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const uint4 a = get_a(b, u, mt);
-        if (RMS) ss[mt] += sumsq8(a);
+        if (RMS) ss[mt] = mfma16(as_bf16x8(a), as_bf16x8(a), ss[mt]);
 #pragma unroll
         for (int j = 0; j < GPW; ++j) {
           acc[mt][j][0] = mfma16(as_bf16x8(a), as_bf16x8(bw[b][j][0]), acc[mt][j][0]);
@@ -226,12 +231,15 @@ __device__ bool sk_task(const SkArgs& ga, const Epi& epi, int gb, int s, SkSmem<
 #pragma unroll
       for (int i = 0; i < 2; ++i) sm.red[w][((mt * GPW + j) * 2 + i) * 64 + l] = acc[mt][j][i];
   if (RMS) {
+    // C layout: lane l holds rows 4 (l >> 4) + i of column l & 15, so row r's
+    // diagonal entry sits in lane 16 (r >> 2) + r, element r & 3
+    const int di = l & 3;
+    if (((l & 15) >> 2) == (l >> 4)) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      float v = ss[mt];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      if (l < 16) sm.ss[w][16 * mt + lr] = v;
+      for (int mt = 0; mt < MT; ++mt) {
+        const f32x4 v = ss[mt];
+        sm.ss[w][16 * mt + lr] = di == 0 ? v[0] : di == 1 ? v[1] : di == 2 ? v[2] : v[3];
+      }
     }
   }
   __syncthreads();
