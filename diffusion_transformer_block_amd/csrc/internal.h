@@ -191,7 +191,7 @@ struct SkPlan {
 };
 SkPlan sk_plan(int M, int K, int n_groups, bool a_rowmajor);
 size_t sk_part_floats(int M, int K, int n_groups, bool a_rowmajor);
-int sk_nb(int KW, int gpw, int MT);
+int sk_nb(int KW, int gpw, int MT, int max_nb);
 void launch_sk_qkv(const SkArgs& ga, int gpw, bool a_rowmajor, const EpiQkvS& e, hipStream_t st);
 void launch_sk_resid(const SkArgs& ga, int gpw, const EpiResidS& e, hipStream_t st);
 void launch_sk_gateup(const SkArgs& ga, int gpw, const EpiGateUpS& e, hipStream_t st);

@@ -73,10 +73,15 @@ size_t sk_part_floats(int M, int K, int n_groups, bool a_rowmajor) {
   return (size_t)p.splits * n_groups * (64 * 32 + 64);
 }
 
-// k-tiles in flight per wave: a divisor of the wave's k-tiles whose loads
-// (2 GPW weight + MT activation fragments per k-tile) fit in 192 registers
-int sk_nb(int KW, int gpw, int MT) {
-  for (int nb = 8; nb > 1; nb >>= 1)
+// k-tiles in flight per wave: a divisor of the wave's k-tiles, at most
+// max_nb, whose loads (2 GPW weight + MT activation fragments per k-tile) fit
+// in 192 registers.  A wave issues its whole ring before its first MFMA, so
+// a shorter ring starts the k loop's matrix work while later loads are still
+// arriving: with the RMS statistic's extra MFMAs a ring of 4 measured faster
+// than 8 (64-token QKV 8.94 -> 8.73 us, gate/up 8.85 -> 8.45 us), without it
+// 8 (the down projection 9.02 against 9.26 us at 4).
+int sk_nb(int KW, int gpw, int MT, int max_nb) {
+  for (int nb = max_nb; nb > 1; nb >>= 1)
     if (KW % nb == 0 && nb * (2 * gpw + MT) <= 48) return nb;
   return 1;
 }
@@ -176,7 +181,7 @@ static void sk_go(const SkArgs& ga, const Epi& e, hipStream_t st) {
 
 template <int MT, int GPW, bool RMS, bool AROW, class Epi>
 static void sk_go_nb(const SkArgs& ga, const Epi& e, hipStream_t st) {
-  switch (sk_nb(ga.K / 32 / ga.splits / 4, GPW, MT)) {
+  switch (sk_nb(ga.K / 32 / ga.splits / 4, GPW, MT, RMS ? 4 : 8)) {
     case 8: sk_go<MT, 8, GPW, RMS, AROW>(ga, e, st); break;
     case 4: sk_go<MT, 4, GPW, RMS, AROW>(ga, e, st); break;
     case 2: sk_go<MT, 2, GPW, RMS, AROW>(ga, e, st); break;
