@@ -22,24 +22,44 @@
 
 namespace blk {
 
-__device__ __forceinline__ void EpiQKV::store8(int m, int g, int qc, const float* v, const Pre8&) const {
+__device__ __forceinline__ void EpiQKV::store(int m, int g, int qc, const float* srow, const Pre& p) const {
   g += g_base;
   const int b = m / T, t = m - b * T;
   const int gpr = d >> 5, n_rot_groups = (Hq + Hkv) * gpr;
-  bf16_t* dst;
+  float x1[8], x2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x1[e] = srow[8 * qc + e];
+    x2[e] = srow[16 + 8 * qc + e];
+  }
   if (g < n_rot_groups) {
+    const float cs[8] = {p.c0.x, p.c0.y, p.c0.z, p.c0.w, p.c1.x, p.c1.y, p.c1.z, p.c1.w};
+    const float sn[8] = {p.s0.x, p.s0.y, p.s0.z, p.s0.w, p.s1.x, p.s1.y, p.s1.z, p.s1.w};
+    float y1[8], y2[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      y1[e] = x1[e] * cs[e] - x2[e] * sn[e];
+      y2[e] = x1[e] * sn[e] + x2[e] * cs[e];
+    }
     const int head = g / gpr;
-    const int col = 16 * (g - head * gpr) + (qc & 1) * 8 + (qc >> 1) * (d >> 1);
+    const int col = 16 * (g - head * gpr) + 8 * qc;   // column j of the pair; j + d/2 holds its partner
+    bf16_t *d1, *d2;
     if (head < Hq) {
       const int G = Hq / Hkv, hk = head / G, gh = head - hk * G;
-      dst = q + qa_index(b * Hkv + hk, (G * T + 31) >> 5, d >> 4, t * G + gh, col);
+      const int n_rt = (G * T + 31) >> 5, NDS = d >> 4;
+      d1 = q + qa_index(b * Hkv + hk, n_rt, NDS, t * G + gh, col);
+      d2 = q + qa_index(b * Hkv + hk, n_rt, NDS, t * G + gh, col + (d >> 1));
     } else {
-      dst = kn + (size_t)b * new_stride + ((size_t)t * Hkv + (head - Hq)) * d + col;
+      d1 = kn + (size_t)b * new_stride + ((size_t)t * Hkv + (head - Hq)) * d + col;
+      d2 = d1 + (d >> 1);
     }
+    *reinterpret_cast<uint4*>(d1) = pack8(y1);
+    *reinterpret_cast<uint4*>(d2) = pack8(y2);
   } else {
-    dst = vn + (size_t)b * new_stride + (size_t)t * Hkv * d + 32 * (g - n_rot_groups) + 8 * qc;
+    bf16_t* d1 = vn + (size_t)b * new_stride + (size_t)t * Hkv * d + 32 * (g - n_rot_groups) + 8 * qc;
+    *reinterpret_cast<uint4*>(d1) = pack8(x1);
+    *reinterpret_cast<uint4*>(d1 + 16) = pack8(x2);
   }
-  *reinterpret_cast<uint4*>(dst) = pack8(v);
 }
 
 // ============================================================================ large-chunk GEMM
@@ -273,27 +293,42 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
   }
 
   // ---- epilogue, 32 rows of the wave's tile at a time: math() in the MFMA
-  //      layout into this wave's LDS region, then 16-byte row stores
+  //      layout into this wave's LDS region, then 16-byte row stores.  The
+  //      row scales of every pass are loaded at once, and each pass's
+  //      store-side operands one pass ahead, so the passes share one memory
+  //      round trip instead of paying one each.  The staging region is the
+  //      wave's own and LDS runs a wave's accesses in order: no barriers.
   constexpr int LROW = 32 * GW + 4;       // floats per staged row
   constexpr int SC = Epi::SLOT_CHUNKS;
+  constexpr int NP = (MTW + 1) / 2;       // passes of 32 rows (16 in the last of an odd MTW)
+  constexpr int GS = GW * SC;             // store items per staged row (divides 64)
+  constexpr int RPI = 64 / GS;            // staged rows per store round
+  constexpr int NIT = 32 / RPI;           // store rounds per pass
   float* stg = reinterpret_cast<float*>(big_dsm) + w * 32 * LROW;
+  const int mw = m0 + wm * (BM / 2);      // first row of the wave's tile
+  const int gg_s = (l % GS) / SC, qc_s = l % SC;   // this lane's store column: group, chunk
+  const int g_s = g0 + wn * GW + gg_s;
+  float rr[NP][2][4];
 #pragma unroll
-  for (int pass = 0; pass < (MTW + 1) / 2; ++pass) {
-    const int pass_rows = min(32, 16 * (MTW - 2 * pass));   // 16 in the half pass of an odd MTW
-    // the pass's row scales and epilogue operands, all loads issued before
-    // the first use (one memory round trip per pass, not one per slot)
-    float rr[2][4];
-    typename Epi::Aux ax[2][4][GW];
+  for (int pass = 0; pass < NP; ++pass)
 #pragma unroll
     for (int mh = 0; mh < 2; ++mh)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int row = min(m0 + wm * (BM / 2) + 16 * (2 * pass + mh) + 4 * (l >> 4) + j, ga.M - 1);
-        rr[mh][j] = ga.r ? ga.r[row] : 1.f;
-#pragma unroll
-        for (int gg = 0; gg < GW; ++gg)
-          ax[mh][j][gg] = epi.aux(row, min(g0 + wn * GW + gg, ga.n_groups - 1), l & 15);
+        const int row = min(mw + 16 * (2 * pass + mh) + 4 * (l >> 4) + j, ga.M - 1);
+        rr[pass][mh][j] = ga.r ? ga.r[row] : 1.f;
       }
+  typename Epi::Pre pre[2][NIT];
+  auto load_pre = [&](int pass, typename Epi::Pre (&pp)[NIT]) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+      pp[it] = epi.pre(min(mw + 32 * pass + it * RPI + l / GS, ga.M - 1), min(g_s, ga.n_groups - 1), qc_s);
+  };
+  load_pre(0, pre[0]);
+#pragma unroll
+  for (int pass = 0; pass < NP; ++pass) {
+    const int pass_rows = min(32, 16 * (MTW - 2 * pass));
+    if (pass + 1 < NP) load_pre(pass + 1, pre[(pass + 1) & 1]);
 #pragma unroll
     for (int mh = 0; mh < 2; ++mh) {
       const int mt = min(2 * pass + mh, MTW - 1);
@@ -301,43 +336,23 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(GemmArgs ga, Epi epi, int
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rl = 16 * mh + 4 * (l >> 4) + j;
-        const int row = min(m0 + wm * (BM / 2) + 16 * mt + 4 * (l >> 4) + j, ga.M - 1);
 #pragma unroll
         for (int gg = 0; gg < GW; ++gg) {
-          const int g = min(g0 + wn * GW + gg, ga.n_groups - 1);
-          const float2 o =
-              epi.math(row, g, l & 15, acc[mt][gg][0][j], acc[mt][gg][1][j], rr[mh][j], ax[mh][j][gg]);
+          const float2 o = epi.math(acc[mt][gg][0][j], acc[mt][gg][1][j], rr[pass][mh][j]);
           stg[rl * LROW + 32 * gg + (l & 15)] = o.x;
           stg[rl * LROW + 32 * gg + 16 + (l & 15)] = o.y;
         }
       }
     }
-    __syncthreads();
-    constexpr int NIT = 32 * GW * SC / 64;
-    // the pass's store-side operands (residual chunks), all loaded before the
-    // first store (positions past the edges clamped: loaded, never stored)
-    typename Epi::Pre8 p8[NIT];
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int idx = it * 64 + l;
-      const int rl = idx / (GW * SC), rem = idx - rl * (GW * SC);
-      const int gg = rem / SC, qc = rem - gg * SC;
-      p8[it] = epi.pre8(min(m0 + wm * (BM / 2) + 32 * pass + rl, ga.M - 1),
-                        min(g0 + wn * GW + gg, ga.n_groups - 1), qc);
+      const int rl = it * RPI + l / GS;
+      const int row = mw + 32 * pass + rl;
+      if (rl < pass_rows && row < ga.M && g_s < ga.n_groups)
+        epi.store(row, g_s, qc_s, &stg[rl * LROW + 32 * gg_s], pre[pass & 1][it]);
     }
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int idx = it * 64 + l;
-      const int rl = idx / (GW * SC), rem = idx - rl * (GW * SC);
-      const int gg = rem / SC, qc = rem - gg * SC;
-      const int row = m0 + wm * (BM / 2) + 32 * pass + rl;
-      const int g = g0 + wn * GW + gg;
-      const float4 lo = *reinterpret_cast<const float4*>(&stg[rl * LROW + 32 * gg + 8 * qc]);
-      const float4 hi = *reinterpret_cast<const float4*>(&stg[rl * LROW + 32 * gg + 8 * qc + 4]);
-      const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      if (rl < pass_rows && row < ga.M && g < ga.n_groups) epi.store8(row, g, qc, v, p8[it]);
-    }
-    __syncthreads();
+    asm volatile("" ::: "memory");
   }
 }
 

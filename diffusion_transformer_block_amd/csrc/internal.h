@@ -36,18 +36,22 @@ void launch_copy_f32(const float* in, size_t n, float* out, hipStream_t st);
 
 // ---------------------------------------------------------------- GEMM epilogues
 // The large-chunk GEMM finishes a tile in two phases.  math() sees one output
-// pair in the MFMA layout -- row m, group g, column c < 16 inside the group's
-// two tiles, their fp32 sums v0 (tile 0) and v1 (tile 1), the row scale r (the
-// RMS statistic, or 1) -- and returns the group's output slots c and 16 + c
-// (fp32).  The slots go through LDS, and store8() then writes 8 consecutive
-// slots (8 q .. 8 q + 7, q < 4 of the group's 32; q < SLOT_CHUNKS) of row m
-// with one 16-byte store.  The stores are plain: the next kernel reads them.
+// pair in the MFMA layout -- the fp32 sums v0 (tile 0) and v1 (tile 1) of
+// column c < 16 of a group's two tiles and the row scale r (the RMS
+// statistic, or 1) -- and returns the group's staged slots c and 16 + c.  The
+// slots go through LDS; store() then gets one row's 32 staged slots of group
+// g and writes chunk q < SLOT_CHUNKS of them (16-byte stores), with the
+// operands pre() loaded for it one pass of rows ahead.  The stores are plain:
+// the next kernel reads them.
 
-// Fused QKV: scale by r, rotate (Q, K) pairs (slot c = column j, slot 16 + c
-// = column j + d/2 of the rotated head), Q into the chunk attention's operand
-// order (qa_index in skinny.h), K_new / V_new row-major.
+// Fused QKV: scale by r; in the store phase, rotate (Q, K) pairs (slot c =
+// column j, slot 16 + c = column j + d/2 of the rotated head), with the
+// cos / sin of 8 consecutive j loaded as two 16-byte vectors each; Q into the
+// chunk attention's operand order (qa_index in skinny.h), K_new / V_new
+// row-major.  Chunk q < 2 of a group covers slots 8 q .. 8 q + 7 and
+// 16 + 8 q .. 16 + 8 q + 7 (both halves of a rotated pair).
 struct EpiQKV {
-  static constexpr int SLOT_CHUNKS = 4;
+  static constexpr int SLOT_CHUNKS = 2;
   bf16_t* q;
   bf16_t* kn;           // stream b at b * new_stride, [T][Hkv][d]
   bf16_t* vn;
@@ -58,28 +62,25 @@ struct EpiQKV {
   int g_base;           // packed group of the GEMM's group 0 (> 0: a K/V-only run)
   const int* plen;      // device: stream b's prefix length (NULL: all P); token t at P_b + t
 
-  // cos / sin of slot c of group g at row m's position: the index is valid
-  // for every group (V groups ignore it), so the loads carry no condition
-  // and the caller can issue a whole pass of them before the first use
-  struct Aux {
-    float cs, sn;
+  __device__ __forceinline__ float2 math(float v0, float v1, float r) const {
+    return make_float2(v0 * r, v1 * r);
+  }
+  // cos / sin of columns j .. j + 7 at row m's position: the index is valid
+  // for every group (V groups ignore it), so the loads carry no condition and
+  // a whole pass of them is issued before the first use
+  struct Pre {
+    float4 c0, c1, s0, s1;
   };
-  __device__ __forceinline__ Aux aux(int m, int g, int c) const {
+  __device__ __forceinline__ Pre pre(int m, int g, int qc) const {
     g += g_base;
     const int gpr = d >> 5;
     const int b = m / T;
-    const size_t ti = (size_t)(stream_prefix(plen, P, b) + m - b * T) * (d >> 1) + 16 * (g % gpr) + c;   // column j < d/2
-    return {cos_t[ti], sin_t[ti]};
+    const size_t ti = (size_t)(stream_prefix(plen, P, b) + m - b * T) * (d >> 1) + 16 * (g % gpr) + 8 * qc;
+    const float4* cp = reinterpret_cast<const float4*>(cos_t + ti);
+    const float4* sp = reinterpret_cast<const float4*>(sin_t + ti);
+    return {cp[0], cp[1], sp[0], sp[1]};
   }
-  __device__ __forceinline__ float2 math(int, int g, int, float v0, float v1, float r, const Aux& x) const {
-    v0 *= r;
-    v1 *= r;
-    if (g + g_base >= (Hq + Hkv) * (d >> 5)) return make_float2(v0, v1);
-    return make_float2(v0 * x.cs - v1 * x.sn, v0 * x.sn + v1 * x.cs);
-  }
-  struct Pre8 {};
-  __device__ __forceinline__ Pre8 pre8(int, int, int) const { return {}; }
-  __device__ __forceinline__ void store8(int m, int g, int qc, const float* v, const Pre8&) const;
+  __device__ __forceinline__ void store(int m, int g, int qc, const float* srow, const Pre& p) const;
 };
 
 // out = res + acc (residual add; O projection and down projection).  res and
@@ -91,28 +92,26 @@ struct EpiResidual {
   bf16_t* out;
   int out_frag;
   int ld, MT;
-  struct Aux {};
-  __device__ __forceinline__ Aux aux(int, int, int) const { return {}; }
-  __device__ __forceinline__ float2 math(int, int, int, float v0, float v1, float, const Aux&) const {
+  __device__ __forceinline__ float2 math(float v0, float v1, float) const {
     return make_float2(v0, v1);
   }
-  // the residual chunk, loaded by the caller for a whole pass before any of
-  // its stores (out may alias res)
-  struct Pre8 {
+  // the residual chunk, loaded a pass ahead of the stores (out may alias res:
+  // a pass's loads and stores cover the same rows, later passes other rows)
+  struct Pre {
     uint4 r;
   };
-  __device__ __forceinline__ Pre8 pre8(int m, int g, int qc) const {
+  __device__ __forceinline__ Pre pre(int m, int g, int qc) const {
     const int c = 32 * g + 8 * qc;
     const size_t ro = res_frag ? fa_index(m, c, MT) : (size_t)m * ld + c;
     return {*reinterpret_cast<const uint4*>(res + ro)};
   }
-  __device__ __forceinline__ void store8(int m, int g, int qc, const float* v, const Pre8& p) const {
+  __device__ __forceinline__ void store(int m, int g, int qc, const float* srow, const Pre& p) const {
     const int c = 32 * g + 8 * qc;
     const size_t oo = out_frag ? fa_index(m, c, MT) : (size_t)m * ld + c;
     float x[8];
     unpack8(p.r, x);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] += v[e];
+    for (int e = 0; e < 8; ++e) x[e] += srow[8 * qc + e];
     *reinterpret_cast<uint4*>(out + oo) = pack8(x);
   }
 };
@@ -123,14 +122,15 @@ struct EpiGateUp {
   static constexpr int SLOT_CHUNKS = 2;
   bf16_t* out;
   int MT;
-  struct Aux {};
-  __device__ __forceinline__ Aux aux(int, int, int) const { return {}; }
-  __device__ __forceinline__ float2 math(int, int, int, float v0, float v1, float r, const Aux&) const {
+  __device__ __forceinline__ float2 math(float v0, float v1, float r) const {
     return make_float2(silu(v0 * r) * (v1 * r), 0.f);
   }
-  struct Pre8 {};
-  __device__ __forceinline__ Pre8 pre8(int, int, int) const { return {}; }
-  __device__ __forceinline__ void store8(int m, int g, int qc, const float* v, const Pre8&) const {
+  struct Pre {};
+  __device__ __forceinline__ Pre pre(int, int, int) const { return {}; }
+  __device__ __forceinline__ void store(int m, int g, int qc, const float* srow, const Pre&) const {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = srow[8 * qc + e];
     *reinterpret_cast<uint4*>(out + fa_index(m, 16 * g + 8 * qc, MT)) = pack8(v);
   }
 };
