@@ -20,8 +20,11 @@
 //  * 64-row blocks: wave w takes 32 query rows (w % 2) and one 32-key half
 //    (w / 2) of every step; 128-row blocks (LONG, long key runs): wave w takes
 //    32 rows and both halves, so a tile serves twice the rows and the halves
-//    need no merge; 32 x 32 x 16 MFMAs throughout (twice the operand reuse of
-//    16 x 16 tiles);
+//    need no merge; 64-row blocks split by output dims (DSPLIT): wave w takes
+//    32 rows (w % 2), both key halves for the scores (each pair of waves
+//    computes them twice) and half of the head dims (w / 2) for O, so the
+//    halves need no merge either; 32 x 32 x 16 MFMAs throughout (twice the
+//    operand reuse of 16 x 16 tiles);
 //  * S^T = K Q^T: K rows as the A operand (LDS), Q^T as the B operand held in
 //    registers (the QKV epilogue stores Q in exactly that operand order,
 //    qa_index), so a lane holds 16 keys of one query row;
@@ -132,8 +135,10 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // runs) makes them 128 rows: wave w takes 32 rows and both key halves of
 // every tile in turn, so a K/V tile serves twice the rows and no merge is
 // needed; its slice partials go out per 64-row half, as the merge step reads
-// them.
-template <int HD, bool LONG = false, class Wait>
+// them.  DSPLIT keeps 64-row blocks without the merge: the two waves of a
+// row tile both take every key (the same scores and probabilities, computed
+// twice) and each accumulates O for half of the head dims.
+template <int HD, bool LONG = false, bool DSPLIT = false, class Wait>
 __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_in, AttnSmSmem<HD>& sm,
                              Wait&& wait) {
   // task coordinates are workgroup-uniform; saying so keeps every buffer
@@ -150,7 +155,8 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int l = tid & 63;
   const int rp = LONG ? w : (w & 1);          // 32-row tile of the block
-  const int kh_w = w >> 1;                     // the wave's 32-key half of a tile (not LONG)
+  const int kh_w = w >> 1;                     // the wave's 32-key half of a tile (not LONG / DSPLIT)
+  static_assert(!(LONG && DSPLIT), "one block mode");
   // (integer division runs on the vector unit; readfirstlane keeps the
   // quotients scalar)
   const int b = __builtin_amdgcn_readfirstlane(bh / a.Hkv), hk = bh - b * a.Hkv;
@@ -242,9 +248,12 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   if (n_tiles > 1) load_tile(1, 1);
 
+  // O^T d tiles this wave accumulates: all, or (DSPLIT) half, from d tile dbase
+  constexpr int NDO = DSPLIT ? NDT / 2 : NDT;
+  const int dbase = DSPLIT ? (w >> 1) * NDO : 0;
   // O^T accumulators: the slice's first tile (every slice has one) writes
   // them with zero C operands, so they need no zero fill
-  f32x16 o[NDT];
+  f32x16 o[NDO];
   // running reference max (may trail the true max by up to 2^8, see below) and sum
   float m_run = -INFINITY, l_run = 0.f;
   __syncthreads();
@@ -263,12 +272,12 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
   const unsigned vt_off0 = vrow * HD * 2 + 16 * (2 * ((l >> 4) & 1) + ((p16 & 3) >> 1)) + 8 * (p16 & 1);
   const unsigned vx = 16 * attn_swz_v<HD>(vrow);
 
-  // key halves this wave takes of every tile: both (LONG) or its own
-  constexpr int NH = LONG ? 2 : 1;
+  // key halves this wave takes of every tile: both (LONG, DSPLIT) or its own
+  constexpr int NH = (LONG || DSPLIT) ? 2 : 1;
   // S^T accumulation chains per half: two (even / odd d steps) for a single
   // half, one per half when two halves already interleave
   constexpr int NC = NH == 1 ? 2 : 1;
-  constexpr int VB = NDT < 4 ? NDT : 4;   // transposed V reads issued ahead of their MFMAs
+  constexpr int VB = NDO < 4 ? NDO : 4;   // transposed V reads issued ahead of their MFMAs
   const float sc = a.scale_log2;
   auto step = [&](int it, auto cur_c, auto first_c) {
     constexpr int cur = decltype(cur_c)::value;          // LDS buffer of tile it
@@ -288,7 +297,7 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
       uint4 kf[NH][KB];
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
-        const int kh = LONG ? h : kh_w;
+        const int kh = NH == 2 ? h : kh_w;
         const uint8_t* kr = reinterpret_cast<const uint8_t*>(&sm.k[cur][(32 * kh + (l & 31)) * HD]);
 #pragma unroll
         for (int s = 0; s < KB; ++s)
@@ -311,7 +320,7 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
     if (key_begin + 64 * it + 64 > key_end) {
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
-        const int base = key_begin + 64 * it + 32 * (LONG ? h : kh_w);
+        const int base = key_begin + 64 * it + 32 * (NH == 2 ? h : kh_w);
 #pragma unroll
         for (int v = 0; v < 16; ++v)
           if (base + 8 * (v >> 2) + 4 * hl + (v & 3) >= key_end) sv[h][v] = -INFINITY;
@@ -322,12 +331,12 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
     //      transposed V reads are issued ahead of its softmax.
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      const uint8_t* vt0 = reinterpret_cast<const uint8_t*>(&sm.v[cur][0]) + vt_off0 + 32 * (LONG ? h : kh_w) * HD * 2;
+      const uint8_t* vt0 = reinterpret_cast<const uint8_t*>(&sm.v[cur][0]) + vt_off0 + 32 * (NH == 2 ? h : kh_w) * HD * 2;
       auto read_v = [&](int u, int d0, uint2 (&vlo)[VB], uint2 (&vhi)[VB]) {
         const uint8_t* vt = vt0 + 16 * u * HD * 2;
 #pragma unroll
         for (int dt = 0; dt < VB; ++dt) {
-          const unsigned dx = (64u * (d0 + dt)) ^ vx;
+          const unsigned dx = (64u * (dbase + d0 + dt)) ^ vx;
           vlo[dt] = lds_tr16(reinterpret_cast<const bf16_t*>(vt + dx));
           vhi[dt] = lds_tr16(reinterpret_cast<const bf16_t*>(vt + 8 * HD * 2 + dx));
         }
@@ -355,7 +364,7 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
         if (__builtin_amdgcn_ballot_w64(grow && m_run != -INFINITY) != 0) {
           const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) o[dt] = o[dt] * alpha;
+          for (int dt = 0; dt < NDO; ++dt) o[dt] = o[dt] * alpha;
           l_run *= alpha;
         }
         m_run = m_new;
@@ -378,7 +387,7 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
       for (int u = 0; u < 2; ++u) {
         const bf16x8 pb = as_bf16x8(make_uint4(pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]));
 #pragma unroll
-        for (int d0 = 0; d0 < NDT; d0 += VB) {
+        for (int d0 = 0; d0 < NDO; d0 += VB) {
           uint2 vlo[VB], vhi[VB];
           if (u == 0 && d0 == 0) {
 #pragma unroll
@@ -433,26 +442,28 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
   const size_t slab = (size_t)64 * HD;     // bf16 per (slice, 64-row block)
   const int n_rb64 = (rows + 63) >> 6;
   const int n_rbt64 = a.B * a.Hkv * n_rb64;
-  if constexpr (LONG) {
-    // ---- every wave holds its rows' whole result: normalise and store
-    const int arow = 128 * rb + 32 * rp + row32;
+  if constexpr (LONG || DSPLIT) {
+    // ---- every wave holds its rows' whole result (DSPLIT: for its half of
+    //      the dims): normalise and store
+    constexpr int BR = LONG ? 128 : 64;
+    const int arow = BR * rb + 32 * rp + row32;
     const bool live = arow < rows;
     const float inv = 1.f / l_tot;
     // the 64-row block of this wave's rows (uniform; past the last block
     // only for a wave with no live rows, which stores nothing)
-    const int rb_id = __builtin_amdgcn_readfirstlane(bh * n_rb64 + ((128 * rb + 32 * rp) >> 6));
+    const int rb_id = __builtin_amdgcn_readfirstlane(bh * n_rb64 + ((BR * rb + 32 * rp) >> 6));
     const __amdgpu_buffer_rsrc_t rpo =
         make_rsrc(a.part_o + ((size_t)ks * n_rbt64 + rb_id) * slab, a.splits > 1 ? slab * 2 : 0);
     const int t = arow / G, hq = hk * G + (arow - t * G);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int dt = 0; dt < NDO; ++dt)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = o[dt][8 * j + e] * inv;
         const uint4 chunk = chunk_of(v);
-        const int dd = 32 * dt + 16 * j + 8 * hl;
+        const int dd = 32 * (dbase + dt) + 16 * j + 8 * hl;
         if (live) {
           if (a.splits == 1)
             buf_st16(ro, (int)(fa_index(b * a.T + t, hq * HD + dd, MTo) * 2), chunk);
@@ -460,83 +471,85 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
             buf_st16(rpo, attn_part_slot(arow & 63, dd >> 3) * 16, chunk);
         }
       }
-    if (a.splits > 1 && hl == 0 && live) {
+    // (both waves of a DSPLIT row tile hold the same (max, sum); one stores it)
+    if (a.splits > 1 && hl == 0 && live && (!DSPLIT || dbase == 0)) {
       const __amdgpu_buffer_rsrc_t rpm = make_rsrc(a.part_ml + ((size_t)ks * n_rbt64 + rb_id) * 128, 512);
       buf_st8(rpm, (arow & 63) * 8, __float_as_uint(m_run), __float_as_uint(l_tot));
     }
     return a.splits == 1;
-  }
-  // ---- merge the two key halves (64-row blocks).  The waves of a pair hold
-  //      the same 32 rows over different keys; each merges half of the d
-  //      tiles: it hands the partner's half of its unnormalised O^T registers
-  //      to LDS in register order (lane-contiguous 16-byte slots, no bank
-  //      conflicts), reads the partner's copy of its own half, and combines
-  //      and stores slot by slot as above.
-  constexpr int NH2 = NDT / 2;   // d tiles each wave of a pair merges
-  static_assert(sizeof(sm.k) >= sizeof(float4) * 4 * NH2 * 4 * 64, "hand-off slots fit in the K tiles");
-  float4* hand = reinterpret_cast<float4*>(&sm.k[0][0]);   // [row tile][dest half][NH2 * 4][64 lanes]
-  auto give = [&](auto off_c) {
-    constexpr int off = decltype(off_c)::value;   // first d tile the partner merges
-    float4* dst = hand + (rp * 2 + (kh_w ^ 1)) * (NH2 * 4 * 64) + l;
+  } else {
+    // ---- merge the two key halves (64-row blocks).  The waves of a pair hold
+    //      the same 32 rows over different keys; each merges half of the d
+    //      tiles: it hands the partner's half of its unnormalised O^T registers
+    //      to LDS in register order (lane-contiguous 16-byte slots, no bank
+    //      conflicts), reads the partner's copy of its own half, and combines
+    //      and stores slot by slot as above.
+    constexpr int NH2 = NDT / 2;   // d tiles each wave of a pair merges
+    static_assert(sizeof(sm.k) >= sizeof(float4) * 4 * NH2 * 4 * 64, "hand-off slots fit in the K tiles");
+    float4* hand = reinterpret_cast<float4*>(&sm.k[0][0]);   // [row tile][dest half][NH2 * 4][64 lanes]
+    auto give = [&](auto off_c) {
+      constexpr int off = decltype(off_c)::value;   // first d tile the partner merges
+      float4* dst = hand + (rp * 2 + (kh_w ^ 1)) * (NH2 * 4 * 64) + l;
 #pragma unroll
-    for (int i = 0; i < NH2; ++i)
+      for (int i = 0; i < NH2; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        dst[(4 * i + q) * 64] = make_float4(o[off + i][4 * q], o[off + i][4 * q + 1],
-                                            o[off + i][4 * q + 2], o[off + i][4 * q + 3]);
-  };
-  if (kh_w == 0)
-    give(std::integral_constant<int, NH2>{});
-  else
-    give(std::integral_constant<int, 0>{});
-  if (hl == 0) sm.mlh[kh_w][rp * 32 + row32] = make_float2(m_run, l_tot);
-  __syncthreads();
+        for (int q = 0; q < 4; ++q)
+          dst[(4 * i + q) * 64] = make_float4(o[off + i][4 * q], o[off + i][4 * q + 1],
+                                              o[off + i][4 * q + 2], o[off + i][4 * q + 3]);
+    };
+    if (kh_w == 0)
+      give(std::integral_constant<int, NH2>{});
+    else
+      give(std::integral_constant<int, 0>{});
+    if (hl == 0) sm.mlh[kh_w][rp * 32 + row32] = make_float2(m_run, l_tot);
+    __syncthreads();
 
-  const float2 pm = sm.mlh[kh_w ^ 1][rp * 32 + row32];
-  const float mm = fmaxf(m_run, pm.x);
-  const float a_own = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
-  const float a_oth = pm.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(pm.x - mm);
-  const float lsum = l_tot * a_own + pm.y * a_oth;   // > 0: key half 0 of a slice has a key
-  const float s_own = a_own / lsum, s_oth = a_oth / lsum;
-  const int row64 = 32 * rp + row32, arow = 64 * rb + row64;
-  const bool live = arow < rows;
-  const int rb_id = __builtin_amdgcn_readfirstlane(bh * n_rb64 + rb);
-  const __amdgpu_buffer_rsrc_t rpo =
-      make_rsrc(a.part_o + ((size_t)ks * n_rbt64 + rb_id) * slab, a.splits > 1 ? slab * 2 : 0);
-  const int t = arow / G, hq = hk * G + (arow - t * G);
-  auto merge_store = [&](auto off_c) {
-    constexpr int off = decltype(off_c)::value;   // first d tile this wave merges
-    const float4* src = hand + (rp * 2 + kh_w) * (NH2 * 4 * 64) + l;
+    const float2 pm = sm.mlh[kh_w ^ 1][rp * 32 + row32];
+    const float mm = fmaxf(m_run, pm.x);
+    const float a_own = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
+    const float a_oth = pm.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(pm.x - mm);
+    const float lsum = l_tot * a_own + pm.y * a_oth;   // > 0: key half 0 of a slice has a key
+    const float s_own = a_own / lsum, s_oth = a_oth / lsum;
+    const int row64 = 32 * rp + row32, arow = 64 * rb + row64;
+    const bool live = arow < rows;
+    const int rb_id = __builtin_amdgcn_readfirstlane(bh * n_rb64 + rb);
+    const __amdgpu_buffer_rsrc_t rpo =
+        make_rsrc(a.part_o + ((size_t)ks * n_rbt64 + rb_id) * slab, a.splits > 1 ? slab * 2 : 0);
+    const int t = arow / G, hq = hk * G + (arow - t * G);
+    auto merge_store = [&](auto off_c) {
+      constexpr int off = decltype(off_c)::value;   // first d tile this wave merges
+      const float4* src = hand + (rp * 2 + kh_w) * (NH2 * 4 * 64) + l;
 #pragma unroll
-    for (int i = 0; i < NH2; ++i) {
-      float p[16];
+      for (int i = 0; i < NH2; ++i) {
+        float p[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) *reinterpret_cast<float4*>(&p[4 * q]) = src[(4 * i + q) * 64];
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<float4*>(&p[4 * q]) = src[(4 * i + q) * 64];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float v[8];
+        for (int j = 0; j < 2; ++j) {
+          float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = o[off + i][8 * j + e] * s_own + p[8 * j + e] * s_oth;
-        const uint4 chunk = chunk_of(v);
-        const int dd = 32 * (off + i) + 16 * j + 8 * hl;
-        if (live) {
-          if (a.splits == 1)
-            buf_st16(ro, (int)(fa_index(b * a.T + t, hq * HD + dd, MTo) * 2), chunk);
-          else
-            buf_st16(rpo, attn_part_slot(row64, dd >> 3) * 16, chunk);
+          for (int e = 0; e < 8; ++e) v[e] = o[off + i][8 * j + e] * s_own + p[8 * j + e] * s_oth;
+          const uint4 chunk = chunk_of(v);
+          const int dd = 32 * (off + i) + 16 * j + 8 * hl;
+          if (live) {
+            if (a.splits == 1)
+              buf_st16(ro, (int)(fa_index(b * a.T + t, hq * HD + dd, MTo) * 2), chunk);
+            else
+              buf_st16(rpo, attn_part_slot(row64, dd >> 3) * 16, chunk);
+          }
         }
       }
+    };
+    if (kh_w == 0)
+      merge_store(std::integral_constant<int, 0>{});
+    else
+      merge_store(std::integral_constant<int, NH2>{});
+    if (a.splits > 1 && kh_w == 0 && hl == 0 && live) {
+      const __amdgpu_buffer_rsrc_t rpm = make_rsrc(a.part_ml + ((size_t)ks * n_rbt64 + rb_id) * 128, 512);
+      buf_st8(rpm, row64 * 8, __float_as_uint(mm), __float_as_uint(lsum));
     }
-  };
-  if (kh_w == 0)
-    merge_store(std::integral_constant<int, 0>{});
-  else
-    merge_store(std::integral_constant<int, NH2>{});
-  if (a.splits > 1 && kh_w == 0 && hl == 0 && live) {
-    const __amdgpu_buffer_rsrc_t rpm = make_rsrc(a.part_ml + ((size_t)ks * n_rbt64 + rb_id) * 128, 512);
-    buf_st8(rpm, row64 * 8, __float_as_uint(mm), __float_as_uint(lsum));
+    return a.splits == 1;
   }
-  return a.splits == 1;
 }
 
 // Items of the key-slice merge: one per (row block, row, 16-byte chunk).

@@ -221,7 +221,7 @@ void launch_sk_gateup(const SkArgs& ga, int gpw, const EpiGateUpS& e, hipStream_
 
 // ============================================================================ attention
 // (128-row mode: registers capped for two workgroups per compute unit)
-template <int HD, bool LONG>
+template <int HD, bool LONG, bool DSPLIT = false>
 __global__ __launch_bounds__(256, LONG ? 2 : 1) void attn_sm_kernel(AttnSmArgs a, int n_rb) {
   extern __shared__ __attribute__((aligned(16))) char at_dsm[];
   // Tasks in the order (stream x kv head, key slice, row block), row block
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256, LONG ? 2 : 1) void attn_sm_kernel(AttnSmArgs a
   const int task = xcd * qx + min(xcd, rx) + jx;
   const int rb = task % n_rb, rest = task / n_rb;
   const int ks = rest % a.splits, bh = rest / a.splits;
-  attn_sm_task<HD, LONG>(a, bh, rb, ks, *reinterpret_cast<AttnSmSmem<HD>*>(at_dsm), NoWait{});
+  attn_sm_task<HD, LONG, DSPLIT>(a, bh, rb, ks, *reinterpret_cast<AttnSmSmem<HD>*>(at_dsm), NoWait{});
 }
 
 // one wave per workgroup: the merge is a single memory round trip per item,
@@ -243,9 +243,9 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnSmArgs a) {
   attn_combine_task<HD>(a, blockIdx.x);
 }
 
-template <int HD, bool LONG>
+template <int HD, bool LONG, bool DSPLIT = false>
 static void attn_sm_launch(const AttnSmArgs& a, hipStream_t st) {
-  auto kern = attn_sm_kernel<HD, LONG>;
+  auto kern = attn_sm_kernel<HD, LONG, DSPLIT>;
   const size_t smem = sizeof(AttnSmSmem<HD>);
   static bool attr_set = false;
   if (!attr_set) {
@@ -268,7 +268,16 @@ static void attn_sm_go(const AttnSmArgs& a, hipStream_t st) {
       launched = true;
     }
   }
-  if (!launched) attn_sm_launch<HD, false>(a, st);
+  // 64-row blocks: at d = 256 the waves of a row tile split the output dims
+  // (each computes every score; no merge of key halves: the 64-token
+  // attention 12.07 -> 11.53 us); at d = 64 duplicating the scores costs more
+  // than the merge saves (the 16-token block 17.25 -> 17.42 us)
+  if (!launched) {
+    if constexpr (HD == 256)
+      attn_sm_launch<HD, false, true>(a, st);
+    else
+      attn_sm_launch<HD, false>(a, st);
+  }
   if (a.splits > 1) {
     const int items = attn_combine_items(a.B, a.T, a.Hq, a.Hkv, HD);
     hipLaunchKernelGGL(attn_combine_kernel<HD>, dim3((items + 63) / 64), dim3(64), 0, st, a);
