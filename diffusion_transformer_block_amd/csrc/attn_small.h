@@ -600,7 +600,7 @@ __device__ void attn_combine_task(const AttnSmArgs& a, int task) {
       // an empty slice ((max, sum) = (-inf, 0)) wrote no partial rows: skip
       // them rather than multiply whatever they hold by zero
       if (ml[sp].x != -INFINITY) {
-        const float wgt = ml[sp].y * exp2f(ml[sp].x - mx);
+        const float wgt = ml[sp].y * __builtin_amdgcn_exp2f(ml[sp].x - mx);   // argument <= 0
         den += wgt;
         float x[8];
         unpack8(pv[sp], x);
@@ -608,7 +608,7 @@ __device__ void attn_combine_task(const AttnSmArgs& a, int task) {
         for (int e = 0; e < 8; ++e) f[e] = fmaf(wgt, x[e], f[e]);
       }
     }
-  const float inv = 1.f / den;
+  const float inv = __builtin_amdgcn_rcpf(den);
 #pragma unroll
   for (int e = 0; e < 8; ++e) f[e] *= inv;
   const int t = ar / G, h = hk * G + (ar - t * G);
