@@ -51,11 +51,11 @@ OP_KERNELS = {
 # the SHA-256 of the kernel sources when the counters were taken: a changed
 # kernel reports null until it is profiled again.
 TRAFFIC = {
-    "qkv_rope": {"fetch": 6554903, "write": 622592, "bytes": 7177495, "sources": "0af0854c318b9229"},
-    "attention": {"fetch": 6171011, "write": 2924544, "bytes": 9095555, "sources": "0af0854c318b9229"},
-    "o_proj": {"fetch": 7698506, "write": 2364416, "bytes": 10062922, "sources": "0af0854c318b9229"},
-    "gate_up": {"fetch": 17936547, "write": 1048576, "bytes": 18985123, "sources": "0af0854c318b9229"},
-    "down": {"fetch": 13874206, "write": 2364416, "bytes": 16238622, "sources": "0af0854c318b9229"},
+    "qkv_rope": {"fetch": 6554904, "write": 622592, "bytes": 7177496, "sources": "ab9f151542033f81"},
+    "attention": {"fetch": 6126809, "write": 2924544, "bytes": 9051353, "sources": "ab9f151542033f81"},
+    "o_proj": {"fetch": 7698502, "write": 2364416, "bytes": 10062918, "sources": "ab9f151542033f81"},
+    "gate_up": {"fetch": 17928360, "write": 1048576, "bytes": 18976936, "sources": "ab9f151542033f81"},
+    "down": {"fetch": 13874211, "write": 2364416, "bytes": 16238627, "sources": "ab9f151542033f81"},
 }
 TRAFFIC_FETCH_SCALE = 2.000   # FETCH_SIZE of a 256 MiB copy reads 128 MiB
 TRAFFIC_WRITE_SCALE = 1.000   # WRITE_SIZE of the same copy reads 256 MiB
