@@ -116,6 +116,13 @@ def test_ae_block_peaked_softmax():
     # leaves one key half fully masked
     synth.small_shape("mqa_d256_1x64_p768", n_q_heads=8, n_kv_heads=1, head_dim=256, batch=1,
                       tokens=64, prefix=768, hidden=1024, ffn=4096),
+    # d = 256 (waves split the output dims): all 56 keys in one slice, the
+    # rows stored as final output; and two kv heads of 80 rows each, whose
+    # second 64-row block has 16 live rows, over several key slices
+    synth.small_shape("mqa_d256_2x16_one_slice", n_q_heads=4, n_kv_heads=1, head_dim=256, batch=2,
+                      tokens=16, prefix=40, hidden=256, ffn=512),
+    synth.small_shape("gqa_d256_1x40_ragged_rows", n_q_heads=4, n_kv_heads=2, head_dim=256, batch=1,
+                      tokens=40, prefix=300, hidden=256, ffn=512),
     # 128-row attention blocks with key slices, GQA, ragged rows (1040 per kv head)
     synth.small_shape("gqa_d64_1x520_long", n_q_heads=8, n_kv_heads=4, head_dim=64, batch=1,
                       tokens=520, prefix=1500, hidden=512, ffn=1024),
