@@ -43,7 +43,7 @@
 //    key slice writes the normalised rows straight into the O projection's
 //    operand order (both modes); several slices publish bf16 partials
 //    normalised by their own sum plus (max, sum), which a separate merge step
-//    (attn_combine_task, one thread per 16 output bytes, all slices' loads in
+//    (attn_combine_task, one thread per 8 output bytes, all slices' loads in
 //    flight together) combines in slice order.  Many small slices keep every
 //    workgroup to about one memory round trip.
 #pragma once
@@ -552,9 +552,12 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
   }
 }
 
-// Items of the key-slice merge: one per (row block, row, 16-byte chunk).
+// Items of the key-slice merge: one per (row block, row, 8-byte half of a
+// 16-byte chunk).  Half chunks halve each thread's serial arithmetic (the
+// merge is one memory round trip and then vector work on one wave per
+// compute unit) at twice the threads.
 __host__ __device__ inline int attn_combine_items(int B, int T, int Hq, int Hkv, int HD) {
-  return B * Hkv * ((Hq / Hkv * T + 63) / 64) * 64 * (HD / 8);
+  return B * Hkv * ((Hq / Hkv * T + 63) / 64) * 64 * (HD / 4);
 }
 
 // Merges the key slices of attn_sm_task for the blockDim.x items of task
@@ -568,8 +571,9 @@ __device__ void attn_combine_task(const AttnSmArgs& a, int task) {
   const int n_rb = (rows + 63) >> 6;
   const int n_rbt = a.B * a.Hkv * n_rb;
   const int i = task * (int)blockDim.x + (int)threadIdx.x;
-  if (i >= n_rbt * 64 * CPR) return;
-  const int rb_id = i / (64 * CPR), slot = i - rb_id * 64 * CPR;
+  if (i >= n_rbt * 128 * CPR) return;
+  const int rb_id = i / (128 * CPR), rem = i - rb_id * 128 * CPR;
+  const int slot = rem >> 1, half = rem & 1;   // 16-byte slot, its 8-byte half
   const int gi = slot & 63, gg = slot >> 6;
   const int row = 16 * (gg & 3) + (gi & 15), c = 4 * (gg >> 2) + (gi >> 4);   // inverse of attn_part_slot
   const int bh = rb_id / n_rb, rb = rb_id - bh * n_rb;
@@ -580,20 +584,21 @@ __device__ void attn_combine_task(const AttnSmArgs& a, int task) {
   const __amdgpu_buffer_rsrc_t rpo = make_rsrc(a.part_o, (size_t)a.splits * n_rbt * slab * 2);
   const __amdgpu_buffer_rsrc_t rpm = make_rsrc(a.part_ml, (size_t)a.splits * n_rbt * 512);
   float2 ml[kAttnMaxSplits];
-  uint4 pv[kAttnMaxSplits];
+  u32x2v pv[kAttnMaxSplits];
 #pragma unroll
   for (int sp = 0; sp < kAttnMaxSplits; ++sp)
     if (sp < a.splits) {
       const u32x2v u = __builtin_amdgcn_raw_buffer_load_b64(rpm, ((sp * n_rbt + rb_id) * 64 + row) * 8, 0, 16);
       ml[sp] = make_float2(__uint_as_float(u[0]), __uint_as_float(u[1]));
-      pv[sp] = buf_ld_act(rpo, (int)((((size_t)sp * n_rbt + rb_id) * slab + 8 * (size_t)slot) * 2));
+      pv[sp] = __builtin_amdgcn_raw_buffer_load_b64(
+          rpo, (int)((((size_t)sp * n_rbt + rb_id) * slab + 8 * (size_t)slot) * 2) + 8 * half, 0, 16);
     }
   float mx = -INFINITY;
 #pragma unroll
   for (int sp = 0; sp < kAttnMaxSplits; ++sp)
     if (sp < a.splits) mx = fmaxf(mx, ml[sp].x);
   float den = 0.f;
-  float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float f[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int sp = 0; sp < kAttnMaxSplits; ++sp)
     if (sp < a.splits) {
@@ -602,19 +607,18 @@ __device__ void attn_combine_task(const AttnSmArgs& a, int task) {
       if (ml[sp].x != -INFINITY) {
         const float wgt = ml[sp].y * __builtin_amdgcn_exp2f(ml[sp].x - mx);   // argument <= 0
         den += wgt;
-        float x[8];
-        unpack8(pv[sp], x);
+        const float x[4] = {__uint_as_float(pv[sp][0] << 16), __uint_as_float(pv[sp][0] & 0xffff0000u),
+                            __uint_as_float(pv[sp][1] << 16), __uint_as_float(pv[sp][1] & 0xffff0000u)};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = fmaf(wgt, x[e], f[e]);
+        for (int e = 0; e < 4; ++e) f[e] = fmaf(wgt, x[e], f[e]);
       }
     }
   const float inv = __builtin_amdgcn_rcpf(den);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] *= inv;
   const int t = ar / G, h = hk * G + (ar - t * G);
   const int MTo = mt_of(a.B * a.T);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o, (size_t)MTo * 16 * a.Hq * HD * 2);
-  buf_st16(ro, (int)(fa_index(b * a.T + t, h * HD + 8 * c, MTo) * 2), pack8(f));
+  buf_st8(ro, (int)(fa_index(b * a.T + t, h * HD + 8 * c, MTo) * 2) + 8 * half, pack2(f[0] * inv, f[1] * inv),
+          pack2(f[2] * inv, f[3] * inv));
 }
 
 }  // namespace blk
