@@ -443,10 +443,14 @@ void launch_gemm_gateup(const GemmArgs& ga, const EpiGateUp& e, hipStream_t st) 
 // ============================================================================ RMS rows
 // r[m] = (sum_k x[m][k]^2 / K + eps)^-1/2.  One workgroup per 16-row tile:
 // wave w takes the k-tiles kt = w, w + 4, ...; with frag (x in operand order,
-// fa_index over mt_of(M) row tiles) each load is one whole 1 KiB fragment,
-// row-major x is read 16 rows x 64 bytes at a time and, when xf is given,
-// stored as that same whole fragment of the operand-order copy.  Lane l holds
-// row l % 16; lanes of a row fold by shuffles, the waves meet in LDS.  Rows
+// fa_index over mt_of(M) row tiles) each load is one whole 1 KiB fragment.
+// Row-major x is read two k-tiles at a time, each load 8 rows x one whole
+// 128-byte line (the rows of one parity; lane l: row 2 ((l >> 1) & 7) + h,
+// k-tile l & 1, 16-byte chunk l >> 4), and one swap of adjacent lanes turns
+// the pair of loads into the two k-tiles' fragments, which are stored whole
+// into the operand-order copy when xf is given (16 rows x 64 bytes per load
+// instead touched twice the cache lines).  Lane l holds row l % 16 of each
+// fragment; lanes of a row fold by shuffles, the waves meet in LDS.  Rows
 // past M (clamped loads) fill the last tile's padding; their r is not written.
 __global__ __launch_bounds__(256) void rms_rows_kernel(const bf16_t* __restrict__ x, int M, int K,
                                                        int frag, float eps, float* __restrict__ r,
@@ -454,20 +458,66 @@ __global__ __launch_bounds__(256) void rms_rows_kernel(const bf16_t* __restrict_
   __shared__ float part[4][16];
   const int mt = blockIdx.x, MT = mt_of(M);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int row = min(16 * mt + (l & 15), M - 1);
   const int nkt = K >> 5;
+  auto slot = [&](int kt) { return ((size_t)(kt * MT + mt) * 64 + l) * 8; };   // lane's slot of fragment (kt, mt)
   float s = 0.f;
-#pragma unroll 8
-  for (int kt = w; kt < nkt; kt += 4) {
-    const size_t fo = ((size_t)(kt * MT + mt) * 64 + l) * 8;   // this lane's slot of fragment (kt, mt)
-    uint4 v;
-    if (frag) {
-      v = *reinterpret_cast<const uint4*>(x + fo);
-    } else {
-      v = *reinterpret_cast<const uint4*>(x + (size_t)row * K + kt * 32 + 8 * (l >> 4));
-      if (xf) *reinterpret_cast<uint4*>(xf + fo) = v;
+  // loads go out in batches (indices past the end clamped: loaded, not used)
+  // ahead of their first use
+  if (frag) {
+    for (int kt0 = w; kt0 < nkt; kt0 += 32) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = *reinterpret_cast<const uint4*>(x + slot(min(kt0 + 4 * u, nkt - 1)));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (kt0 + 4 * u < nkt) s += sumsq8(v[u]);
     }
-    s += sumsq8(v);
+  } else if ((nkt & 1) == 0) {
+    const bool odd = (l & 1) != 0;
+    const int npr = nkt >> 1;
+    const bf16_t* xr[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      xr[h] = x + (size_t)min(16 * mt + 2 * ((l >> 1) & 7) + h, M - 1) * K + 32 * (l & 1) + 8 * (l >> 4);
+    for (int kp0 = w; kp0 < npr; kp0 += 16) {
+      uint4 ld[4][2];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)   // h = 0: even rows, 1: odd rows
+          ld[u][h] = *reinterpret_cast<const uint4*>(xr[h] + 64 * min(kp0 + 4 * u, npr - 1));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kp = kp0 + 4 * u;
+        if (kp >= npr) break;
+        const uint4 a = ld[u][0], b = ld[u][1];
+        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+        uint32_t f0[4], f1[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // quad_perm [1, 0, 3, 2]: each lane reads its neighbour l ^ 1
+          const uint32_t as = (uint32_t)__builtin_amdgcn_mov_dpp((int)av[e], 0xB1, 0xF, 0xF, true);
+          const uint32_t bs = (uint32_t)__builtin_amdgcn_mov_dpp((int)bv[e], 0xB1, 0xF, 0xF, true);
+          f0[e] = odd ? bs : av[e];
+          f1[e] = odd ? bv[e] : as;
+        }
+        const uint4 v0{f0[0], f0[1], f0[2], f0[3]}, v1{f1[0], f1[1], f1[2], f1[3]};
+        if (xf) {
+          *reinterpret_cast<uint4*>(xf + slot(2 * kp)) = v0;
+          *reinterpret_cast<uint4*>(xf + slot(2 * kp + 1)) = v1;
+        }
+        s += sumsq8(v0) + sumsq8(v1);
+      }
+    }
+  } else {
+    const int row = min(16 * mt + (l & 15), M - 1);
+#pragma unroll 8
+    for (int kt = w; kt < nkt; kt += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)row * K + kt * 32 + 8 * (l >> 4));
+      if (xf) *reinterpret_cast<uint4*>(xf + slot(kt)) = v;
+      s += sumsq8(v);
+    }
   }
   s += __shfl_xor(s, 16);
   s += __shfl_xor(s, 32);
