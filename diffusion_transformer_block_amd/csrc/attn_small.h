@@ -37,11 +37,11 @@
 //    lane i of each 16-lane group element i % 4 of the 8 bytes at lane
 //    4 k + i / 4 (k < 4): pointing lane i at key row 4 k' + i / 4, dims
 //    4 (i % 4) .. + 3 yields V[key k][dim i] in that key order;
-//  * (64-row blocks) the two key halves of a row pair merge through an LDS
-//    hand-off in register order, each wave finishing half the d tiles; lanes
-//    then store whole 16-byte chunks (lane pairs l, l ^ 32 swap halves).  One
-//    key slice writes the normalised rows straight into the O projection's
-//    operand order (both modes); several slices publish bf16 partials
+//  * (64-row blocks over key halves) the two key halves of a row pair merge
+//    through an LDS hand-off in register order, each wave finishing half the
+//    d tiles; lanes then store whole 16-byte chunks (lane pairs l, l ^ 32
+//    swap halves).  One key slice writes the normalised rows straight into
+//    the O projection's operand order (every mode); several slices publish bf16 partials
 //    normalised by their own sum plus (max, sum), which a separate merge step
 //    (attn_combine_task, one thread per 8 output bytes, all slices' loads in
 //    flight together) combines in slice order.  Many small slices keep every
