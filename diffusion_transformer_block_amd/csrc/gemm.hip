@@ -392,6 +392,15 @@ BigPlan big_plan(int M, int n_groups, int K) {
     if (round_rows(224) < round_rows(256)) p.bm = 224;
   }
   else if (tiles(128, 128) >= cus * 15 / 16) p = BigPlan{128, 128, 1, 0, 0};
+  else if (K >= 4096 && (K / 64) % 2 == 0 && 2 * tiles(128, 128) >= cus && tiles(128, 128) <= cus) {
+    // a long K over too few 128 x 128 tiles for the chip: those tiles in two
+    // K slices (two workgroups fit a compute unit; a 64 x 64 wave tile reads
+    // half the LDS bytes per MFMA of 128 x 64's 64 x 32): the video down
+    // projection 74.7 -> 69.0 us against 128 x 64 tiles in two slices (with
+    // K = 1536 the O projection went 18 -> 28 us, so short K keeps 128 x 64)
+    const int t = (int)tiles(128, 128);
+    return BigPlan{128, 128, 2, t, 0};
+  }
   p.tiles = (int)tiles(p.bm, p.bn);
   p.n_full = p.tiles;
   const long ks = K / 64;
