@@ -535,7 +535,9 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     aa.P = P;
     aa.Hq = Hq;
     aa.Hkv = Hkv;
-    attn_sm_plan(B, T, P, Hq, Hkv, &aa.splits, &aa.kps, &aa.long_rows);
+    // (128-row blocks exist for d <= 128; at d = 256 the 64-row blocks take
+    // their own plan)
+    attn_sm_plan(B, T, P, Hq, Hkv, &aa.splits, &aa.kps, d <= 128 ? &aa.long_rows : nullptr);
     aa.plen = plen;
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     aa.part_o = at<bf16_t>(ws, w.sm_att_o);
@@ -644,7 +646,9 @@ void enqueue_block(const blk_config& c, const Layout& lay, const void* packed, i
     aa.P = P;
     aa.Hq = Hq;
     aa.Hkv = Hkv;
-    attn_sm_plan(B, T, P, Hq, Hkv, &aa.splits, &aa.kps, &aa.long_rows);
+    // (128-row blocks exist for d <= 128; at d = 256 the 64-row blocks take
+    // their own plan)
+    attn_sm_plan(B, T, P, Hq, Hkv, &aa.splits, &aa.kps, d <= 128 ? &aa.long_rows : nullptr);
     aa.plen = plen;
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     aa.part_o = at<bf16_t>(ws, w.sm_att_o);

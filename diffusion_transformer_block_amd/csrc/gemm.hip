@@ -403,6 +403,25 @@ BigPlan big_plan(int M, int n_groups, int K) {
   }
   p.tiles = (int)tiles(p.bm, p.bn);
   p.n_full = p.tiles;
+  // too few tiles to give half the compute units one (a 768-row chunk's O and
+  // down projections: 96 tiles): every tile in K slices, the most (of 2, 4,
+  // 8; at least 8 k-steps each) that keep to one workgroup per compute unit.
+  // Filling every unit instead made the 768-token prefix stage faster alone
+  // (1.76 against 1.86 ms) but slower beside the denoise loop on a second
+  // stream, whose small kernels then wait for free units (14.49 against
+  // 14.36 ms for the prefix stage and a 16-step loop).
+  if (2 * p.tiles <= cus) {
+    int best = 1;
+    for (int s = 2; s <= 8; s *= 2) {
+      if ((K / 64) % s != 0 || K / 32 / s < 8 || (long)p.tiles * s > cus) break;
+      best = s;
+    }
+    if (best > 1 && p.tiles <= kBigMaxSplitTiles) {
+      p.splits = best;
+      p.n_full = 0;
+    }
+    return p;
+  }
   const long ks = K / 64;
   const long r1 = (p.tiles + cus - 1) / cus, r2 = (2L * p.tiles + cus - 1) / cus;   // r2 half-length rounds
   double best = (double)r1;

@@ -124,6 +124,31 @@ void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps, i
     *long_rows = 1;
     return;
   }
+  // many 64-row blocks (one workgroup per compute unit at d = 256): the same
+  // cost model over one slot per compute unit, plus about three steps for
+  // the merge kernel when there are slices (the 768-token prefix attention:
+  // 96 blocks in 2 slices of 6 tiles, where the 128-row plan's 3 slices made
+  // 288 workgroups, a second round for 32 of them)
+  if (n_rbt >= 32) {
+    const long slots = device_cus();
+    const int tiles = (L + 63) / 64;
+    const int s_max = std::max(1, std::min(kAttnMaxSplits, L / 256));
+    int best_kt = tiles;
+    double best = 1e30;
+    for (int s = 1; s <= s_max; ++s) {
+      const int kt = (tiles + s - 1) / s;
+      const int ns = (tiles + kt - 1) / kt;
+      const long wgs = (long)n_rbt * ns;
+      const double cost = (double)((wgs + slots - 1) / slots) * kt + (ns > 1 ? 3.0 + 0.01 * (double)wgs : 0.0);
+      if (cost < best - 1e-9) {
+        best = cost;
+        best_kt = kt;
+      }
+    }
+    *kps = best_kt * 64;
+    *splits = (L + *kps - 1) / *kps;
+    return;
+  }
   int s = std::max(1, std::min(kAttnMaxSplits, (96 + n_rbt - 1) / n_rbt));
   s = std::min(s, (L + 31) / 32);
   // up to two 64-key tiles: one workgroup runs both (one more step) rather
