@@ -51,11 +51,11 @@ OP_KERNELS = {
 # the SHA-256 of the kernel sources when the counters were taken: a changed
 # kernel reports null until it is profiled again.
 TRAFFIC = {
-    "qkv_rope": {"fetch": 6554897, "write": 622592, "bytes": 7177489, "sources": "6016d1ea3c243eda"},
-    "attention": {"fetch": 6105302, "write": 2924544, "bytes": 9029846, "sources": "6016d1ea3c243eda"},
-    "o_proj": {"fetch": 7698506, "write": 2364416, "bytes": 10062922, "sources": "6016d1ea3c243eda"},
-    "gate_up": {"fetch": 17928387, "write": 1048576, "bytes": 18976963, "sources": "6016d1ea3c243eda"},
-    "down": {"fetch": 13874179, "write": 2364416, "bytes": 16238595, "sources": "6016d1ea3c243eda"},
+    "qkv_rope": {"fetch": 6554833, "write": 622592, "bytes": 7177425, "sources": "c73d352f374bfef6"},
+    "attention": {"fetch": 6105303, "write": 2924544, "bytes": 9029847, "sources": "c73d352f374bfef6"},
+    "o_proj": {"fetch": 7698487, "write": 2364416, "bytes": 10062903, "sources": "c73d352f374bfef6"},
+    "gate_up": {"fetch": 17928320, "write": 1048576, "bytes": 18976896, "sources": "c73d352f374bfef6"},
+    "down": {"fetch": 13874209, "write": 2364416, "bytes": 16238625, "sources": "c73d352f374bfef6"},
 }
 TRAFFIC_FETCH_SCALE = 2.000   # FETCH_SIZE of a 256 MiB copy reads 128 MiB
 TRAFFIC_WRITE_SCALE = 1.000   # WRITE_SIZE of the same copy reads 256 MiB
