@@ -51,6 +51,7 @@
 #include "skinny.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace blk {
 
@@ -123,6 +124,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // the compiler insert the wait states between an MFMA and its reader.
 __device__ __forceinline__ float max3_f32(float a, float b, float c) {
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+// Instruction order of the S^T MFMAs and their K fragment reads (LDS): R
+// reads first, then one read after each MFMA, so R reads stay in flight.
+template <int R, int... I>
+__device__ __forceinline__ void attn_sched_reads_ahead(std::integer_sequence<int, I...>) {
+  __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  ((__builtin_amdgcn_sched_group_barrier(0x008, 1, 0), __builtin_amdgcn_sched_group_barrier(0x100, 1, 0 * I)), ...);
+  __builtin_amdgcn_sched_group_barrier(0x008, R, 0);
 }
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -295,20 +304,24 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
 #pragma unroll
     for (int s0 = 0; s0 < NDS; s0 += KB) {
       uint4 kf[NH][KB];
+      // (read in the MFMAs' order)
 #pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        const int kh = NH == 2 ? h : kh_w;
-        const uint8_t* kr = reinterpret_cast<const uint8_t*>(&sm.k[cur][(32 * kh + (l & 31)) * HD]);
+      for (int s = 0; s < KB; ++s)
 #pragma unroll
-        for (int s = 0; s < KB; ++s)
+        for (int h = 0; h < NH; ++h) {
+          const int kh = NH == 2 ? h : kh_w;
+          const uint8_t* kr = reinterpret_cast<const uint8_t*>(&sm.k[cur][(32 * kh + (l & 31)) * HD]);
           kf[h][s] = *reinterpret_cast<const uint4*>(kr + ((32u * (s0 + s)) ^ kx));
-      }
+        }
 #pragma unroll
       for (int s = 0; s < KB; ++s)
 #pragma unroll
         for (int h = 0; h < NH; ++h)
           sacc[h][s % NC] = mfma32(as_bf16x8(kf[h][s]), as_bf16x8(qf[s0 + s]), sacc[h][s % NC]);
     }
+    // K fragment reads kept four ahead of their MFMAs: left to itself the
+    // compiler reads each just before its MFMA and waits on it
+    if constexpr (NH == 2) attn_sched_reads_ahead<4>(std::make_integer_sequence<int, NH * NDS - 4>{});
     f32x16 sv[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -326,14 +339,15 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
           if (base + 8 * (v >> 2) + 4 * hl + (v & 3) >= key_end) sv[h][v] = -INFINITY;
       }
     }
-    // ---- per half: online softmax in base 2, then O^T += V^T P^T (two
-    //      16-key steps; P^T slots e <-> S^T values 8 u + e).  The half's first
-    //      transposed V reads are issued ahead of its softmax.
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const uint8_t* vt0 = reinterpret_cast<const uint8_t*>(&sm.v[cur][0]) + vt_off0 + 32 * (NH == 2 ? h : kh_w) * HD * 2;
-      auto read_v = [&](int u, int d0, uint2 (&vlo)[VB], uint2 (&vhi)[VB]) {
-        const uint8_t* vt = vt0 + 16 * u * HD * 2;
+    if constexpr (NH == 2) {
+      // ---- both key halves: one reference max per tile (one rescale
+      //      decision), then each half's probabilities and O^T += V^T P^T
+      //      (two 16-key steps; P^T slots e <-> S^T values 8 u + e).  Half 1's
+      //      probabilities depend on nothing half 0's MFMAs write, so they
+      //      can issue among them.
+      auto read_v = [&](int h, int u, int d0, uint2 (&vlo)[VB], uint2 (&vhi)[VB]) {
+        const uint8_t* vt = reinterpret_cast<const uint8_t*>(&sm.v[cur][0]) + vt_off0 + 32 * h * HD * 2 +
+                            16 * u * HD * 2;
 #pragma unroll
         for (int dt = 0; dt < VB; ++dt) {
           const unsigned dx = (64u * (dbase + d0 + dt)) ^ vx;
@@ -342,22 +356,24 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
         }
       };
       uint2 vlo0[VB], vhi0[VB];
-      read_v(0, 0, vlo0, vhi0);
-      // the row max over this half's keys: raw scores (the scale is
-      // positive), then the row's other 16 keys in lane l ^ 32
+      read_v(0, 0, 0, vlo0, vhi0);
+      // the row max over the tile's keys: raw scores (the scale is positive),
+      // then the row's other keys in lane l ^ 32
       float mx = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) mx = max3_f32(mx, sv[h][v], sv[h][v + 1]);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) mx = max3_f32(mx, sv[h][v], sv[h][v + 1]);
       const float ms = mx * sc;
       const auto mw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ms), __float_as_uint(ms), false, false);
       const float mloc = fmaxf(__uint_as_float(mw[0]), __uint_as_float(mw[1]));
       // Rescale only when some row's max grew past the reference by more than
       // 2^8 (2^(s - reference) stays <= 256: exact enough in bf16 and far from
       // fp32 overflow); otherwise keep it.  Rows whose reference is still
-      // -inf hold zero sums: nothing to rescale (a slice's first half-tile
-      // writes O with zero C operands and skips the pass entirely).
+      // -inf hold zero sums: nothing to rescale (a slice's first tile writes O
+      // with zero C operands and skips the pass entirely).
       const bool grow = mloc > m_run + 8.f;
-      if (FIRST && h == 0) {
+      if (FIRST) {
         m_run = grow ? mloc : m_run;
       } else if (__builtin_amdgcn_ballot_w64(grow) != 0) {
         const float m_new = grow ? mloc : m_run;
@@ -369,42 +385,127 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
         }
         m_run = m_new;
       }
-      // a row that has seen no key yet (reference -inf, every score -inf)
-      // takes reference 0; its probabilities are exactly 0
       const float nref = m_run == -INFINITY ? 0.f : -m_run;
-      // p = 2^(s scale - reference) (arguments <= 8 or -inf)
-      uint32_t pw[8];
+      uint32_t pw[2][8];
       float psum = 0.f;
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[h][v], sc, nref));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[h][v + 1], sc, nref));
-        pw[v / 2] = pack2(p0, p1);
-        psum += p0 + p1;
-      }
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[h][v], sc, nref));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[h][v + 1], sc, nref));
+          pw[h][v / 2] = pack2(p0, p1);
+          psum += p0 + p1;
+        }
       l_run += psum;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bf16x8 pb = as_bf16x8(make_uint4(pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]));
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int d0 = 0; d0 < NDO; d0 += VB) {
-          uint2 vlo[VB], vhi[VB];
-          if (u == 0 && d0 == 0) {
+        for (int u = 0; u < 2; ++u) {
+          const bf16x8 pb = as_bf16x8(make_uint4(pw[h][4 * u], pw[h][4 * u + 1], pw[h][4 * u + 2], pw[h][4 * u + 3]));
+#pragma unroll
+          for (int d0 = 0; d0 < NDO; d0 += VB) {
+            uint2 vlo[VB], vhi[VB];
+            if (h == 0 && u == 0 && d0 == 0) {
+#pragma unroll
+              for (int dt = 0; dt < VB; ++dt) {
+                vlo[dt] = vlo0[dt];
+                vhi[dt] = vhi0[dt];
+              }
+            } else {
+              read_v(h, u, d0, vlo, vhi);
+            }
 #pragma unroll
             for (int dt = 0; dt < VB; ++dt) {
-              vlo[dt] = vlo0[dt];
-              vhi[dt] = vhi0[dt];
+              const bf16x8 va = as_bf16x8(make_uint4(vlo[dt].x, vlo[dt].y, vhi[dt].x, vhi[dt].y));
+              if (FIRST && h == 0 && u == 0)
+                o[d0 + dt] = mfma32(va, pb, f32x16{});
+              else
+                o[d0 + dt] = mfma32(va, pb, o[d0 + dt]);
             }
-          } else {
-            read_v(u, d0, vlo, vhi);
           }
+        }
+    } else {
+      // ---- per half: online softmax in base 2, then O^T += V^T P^T (two
+      //      16-key steps; P^T slots e <-> S^T values 8 u + e).  The half's first
+      //      transposed V reads are issued ahead of its softmax.
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const uint8_t* vt0 = reinterpret_cast<const uint8_t*>(&sm.v[cur][0]) + vt_off0 + 32 * (NH == 2 ? h : kh_w) * HD * 2;
+        auto read_v = [&](int u, int d0, uint2 (&vlo)[VB], uint2 (&vhi)[VB]) {
+          const uint8_t* vt = vt0 + 16 * u * HD * 2;
 #pragma unroll
           for (int dt = 0; dt < VB; ++dt) {
-            const bf16x8 va = as_bf16x8(make_uint4(vlo[dt].x, vlo[dt].y, vhi[dt].x, vhi[dt].y));
-            if (FIRST && h == 0 && u == 0)
-              o[d0 + dt] = mfma32(va, pb, f32x16{});
-            else
-              o[d0 + dt] = mfma32(va, pb, o[d0 + dt]);
+            const unsigned dx = (64u * (dbase + d0 + dt)) ^ vx;
+            vlo[dt] = lds_tr16(reinterpret_cast<const bf16_t*>(vt + dx));
+            vhi[dt] = lds_tr16(reinterpret_cast<const bf16_t*>(vt + 8 * HD * 2 + dx));
+          }
+        };
+        uint2 vlo0[VB], vhi0[VB];
+        read_v(0, 0, vlo0, vhi0);
+        // the row max over this half's keys: raw scores (the scale is
+        // positive), then the row's other 16 keys in lane l ^ 32
+        float mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) mx = max3_f32(mx, sv[h][v], sv[h][v + 1]);
+        const float ms = mx * sc;
+        const auto mw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ms), __float_as_uint(ms), false, false);
+        const float mloc = fmaxf(__uint_as_float(mw[0]), __uint_as_float(mw[1]));
+        // Rescale only when some row's max grew past the reference by more than
+        // 2^8 (2^(s - reference) stays <= 256: exact enough in bf16 and far from
+        // fp32 overflow); otherwise keep it.  Rows whose reference is still
+        // -inf hold zero sums: nothing to rescale (a slice's first half-tile
+        // writes O with zero C operands and skips the pass entirely).
+        const bool grow = mloc > m_run + 8.f;
+        if (FIRST && h == 0) {
+          m_run = grow ? mloc : m_run;
+        } else if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          const float m_new = grow ? mloc : m_run;
+          if (__builtin_amdgcn_ballot_w64(grow && m_run != -INFINITY) != 0) {
+            const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+            for (int dt = 0; dt < NDO; ++dt) o[dt] = o[dt] * alpha;
+            l_run *= alpha;
+          }
+          m_run = m_new;
+        }
+        // a row that has seen no key yet (reference -inf, every score -inf)
+        // takes reference 0; its probabilities are exactly 0
+        const float nref = m_run == -INFINITY ? 0.f : -m_run;
+        // p = 2^(s scale - reference) (arguments <= 8 or -inf)
+        uint32_t pw[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[h][v], sc, nref));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[h][v + 1], sc, nref));
+          pw[v / 2] = pack2(p0, p1);
+          psum += p0 + p1;
+        }
+        l_run += psum;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const bf16x8 pb = as_bf16x8(make_uint4(pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]));
+#pragma unroll
+          for (int d0 = 0; d0 < NDO; d0 += VB) {
+            uint2 vlo[VB], vhi[VB];
+            if (u == 0 && d0 == 0) {
+#pragma unroll
+              for (int dt = 0; dt < VB; ++dt) {
+                vlo[dt] = vlo0[dt];
+                vhi[dt] = vhi0[dt];
+              }
+            } else {
+              read_v(u, d0, vlo, vhi);
+            }
+#pragma unroll
+            for (int dt = 0; dt < VB; ++dt) {
+              const bf16x8 va = as_bf16x8(make_uint4(vlo[dt].x, vlo[dt].y, vhi[dt].x, vhi[dt].y));
+              if (FIRST && h == 0 && u == 0)
+                o[d0 + dt] = mfma32(va, pb, f32x16{});
+              else
+                o[d0 + dt] = mfma32(va, pb, o[d0 + dt]);
+            }
           }
         }
       }
