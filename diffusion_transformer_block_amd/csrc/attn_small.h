@@ -321,7 +321,8 @@ __device__ bool attn_sm_task(const AttnSmArgs& a, int bh_in, int rb_in, int ks_i
     }
     // K fragment reads kept four ahead of their MFMAs: left to itself the
     // compiler reads each just before its MFMA and waits on it
-    if constexpr (NH == 2) attn_sched_reads_ahead<4>(std::make_integer_sequence<int, NH * NDS - 4>{});
+    constexpr int KRA = NH * NDS < 4 ? NH * NDS : 4;
+    attn_sched_reads_ahead<KRA>(std::make_integer_sequence<int, NH * NDS - KRA>{});
     f32x16 sv[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
