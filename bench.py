@@ -51,11 +51,11 @@ OP_KERNELS = {
 # the SHA-256 of the kernel sources when the counters were taken: a changed
 # kernel reports null until it is profiled again.
 TRAFFIC = {
-    "qkv_rope": {"fetch": 6554833, "write": 622592, "bytes": 7177425, "sources": "c73d352f374bfef6"},
-    "attention": {"fetch": 6105303, "write": 2924544, "bytes": 9029847, "sources": "c73d352f374bfef6"},
-    "o_proj": {"fetch": 7698487, "write": 2364416, "bytes": 10062903, "sources": "c73d352f374bfef6"},
-    "gate_up": {"fetch": 17928320, "write": 1048576, "bytes": 18976896, "sources": "c73d352f374bfef6"},
-    "down": {"fetch": 13874209, "write": 2364416, "bytes": 16238625, "sources": "c73d352f374bfef6"},
+    "qkv_rope": {"fetch": 6554892, "write": 622592, "bytes": 7177484, "sources": "ae32edf837ade30c"},
+    "attention": {"fetch": 6098272, "write": 2924544, "bytes": 9022816, "sources": "ae32edf837ade30c"},
+    "o_proj": {"fetch": 7698531, "write": 2364416, "bytes": 10062947, "sources": "ae32edf837ade30c"},
+    "gate_up": {"fetch": 17928358, "write": 1048576, "bytes": 18976934, "sources": "ae32edf837ade30c"},
+    "down": {"fetch": 13874179, "write": 2364416, "bytes": 16238595, "sources": "ae32edf837ade30c"},
 }
 TRAFFIC_FETCH_SCALE = 2.000   # FETCH_SIZE of a 256 MiB copy reads 128 MiB
 TRAFFIC_WRITE_SCALE = 1.000   # WRITE_SIZE of the same copy reads 256 MiB
