@@ -29,7 +29,9 @@
 //    registers (the QKV epilogue stores Q in exactly that operand order,
 //    qa_index), so a lane holds 16 keys of one query row;
 //  * online softmax per row in base 2 (scores pre-scaled by log2(e)/sqrt(d));
-//    the output is rescaled only when a row's max grows by more than 2^8;
+//    the output is rescaled only when a row's max grows by more than 2^8,
+//    checked once per 32-key half, or once per tile where a wave takes both
+//    halves;
 //  * O^T += V^T P^T: P^T is the B operand straight from the score registers
 //    (slot e of the u-th 16-key step is S^T value 8 u + e, keys
 //    16 u + 4 (l/32) + e or 16 u + 8 + 4 (l/32) + e - 4), V^T the A operand
