@@ -411,10 +411,25 @@ BigPlan big_plan(int M, int n_groups, int K) {
   // stream, whose small kernels then wait for free units (14.49 against
   // 14.36 ms for the prefix stage and a 16-step loop).
   if (2 * p.tiles <= cus) {
-    int best = 1;
-    for (int s = 2; s <= 8; s *= 2) {
-      if ((K / 64) % s != 0 || K / 32 / s < 8 || (long)p.tiles * s > cus) break;
-      best = s;
+    auto most_splits = [&](long t) {
+      int best = 1;
+      for (int s = 2; s <= 8; s *= 2) {
+        if ((K / 64) % s != 0 || K / 32 / s < 8 || t * s > cus) break;
+        best = s;
+      }
+      return best;
+    };
+    int best = most_splits(p.tiles);
+    // 128 x 128 tiles in more slices where one unit then moves fewer operand
+    // bytes ((rows + columns) x its K length): the 768-row O and down
+    // projections as 48 tiles in 4 slices (524 KiB per unit) instead of 96
+    // in 2 (768 KiB), 21.3 -> 19.6 us each, prefix stage 1.83 -> 1.80 ms;
+    // 8 slices, two units per compute unit, took 27.6 us
+    const long t2 = tiles(128, 128);
+    const int s2 = most_splits(t2);
+    if (t2 * s2 >= p.tiles * best && 256L * K / s2 < (long)(p.bm + p.bn) * K / best) {
+      p = BigPlan{128, 128, 1, (int)t2, (int)t2};
+      best = s2;
     }
     if (best > 1 && p.tiles <= kBigMaxSplitTiles) {
       p.splits = best;
