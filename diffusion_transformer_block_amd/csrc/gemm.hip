@@ -423,8 +423,8 @@ BigPlan big_plan(int M, int n_groups, int K) {
     // 128 x 128 tiles in more slices where one unit then moves fewer operand
     // bytes ((rows + columns) x its K length): the 768-row O and down
     // projections as 48 tiles in 4 slices (524 KiB per unit) instead of 96
-    // in 2 (768 KiB), 21.3 -> 19.6 us each, prefix stage 1.83 -> 1.80 ms;
-    // 8 slices, two units per compute unit, took 27.6 us
+    // in 2 (768 KiB): the 18-layer prefix stage 1,821 -> 1,795 us on one
+    // box; 8 slices, two units per compute unit, took 27.6 against 19.6 us
     const long t2 = tiles(128, 128);
     const int s2 = most_splits(t2);
     if (t2 * s2 >= p.tiles * best && 256L * K / s2 < (long)(p.bm + p.bn) * K / best) {
