@@ -213,6 +213,76 @@ def test_attention_dominates_output(shape):
     _attention_dominated(shape)
 
 
+def _keys_with_growing_max(shape, case, period=128):
+    """Scale each stream's cached keys by a step along the key axis: x0.25
+    on the first half of every `period` keys, x2 on the second (powers of
+    two: exact in bf16, so the oracle and the GPU read the same values).
+    Returns the scaled case."""
+    for st in case["streams"]:
+        P = st["k_prefix"].f32.shape[0]
+        a = np.where(np.arange(P) % period < period // 2, 0.25, 2.0).astype(np.float32)[:, None, None]
+        ks = st["k_prefix"].f32 * a
+        bits = synth.f32_to_bf16_bits(ks)
+        st["k_prefix"] = synth.Bf16(bits, synth.bf16_bits_to_f32(bits))
+    return case
+
+
+def _share_of_rescales(shape, case, w, period=128):
+    """Share of (query row, key period) pairs whose max score over the
+    period's second 64 keys exceeds the first 64's by more than 8 in base-2
+    units (the kernels' rescale threshold), from the oracle's own steps."""
+    st = f32_tree(case["streams"][0])
+    wf = f32_tree(w)
+    a = oracle.rms_norm(st["x"], wf["g_attn"], shape.rms_eps)
+    T, d, Hq, Hkv = shape.tokens, shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    P = st["k_prefix"].shape[0]
+    q = (a @ wf["w_q"]).reshape(T, Hq, d)
+    cos, sin = oracle.rope_tables(P + np.arange(T), d, shape.rope_base)
+    q = oracle.apply_rope(q, cos, sin)
+    hits = total = 0
+    for h in range(Hq):
+        s = q[:, h, :] @ st["k_prefix"][:, h * Hkv // Hq, :].T / np.sqrt(d) * np.log2(np.e)
+        for p0 in range(0, P - period + 1, period):
+            m1 = s[:, p0:p0 + period // 2].max(axis=1)
+            m2 = s[:, p0 + period // 2:p0 + period].max(axis=1)
+            hits += int(np.sum(m2 > m1 + 8))
+            total += T
+    return hits / max(total, 1)
+
+
+@pytest.mark.parametrize("shape", [
+    synth.small_shape("mqa_d256_1x64_longP", n_q_heads=2, n_kv_heads=1, head_dim=256, batch=1,
+                      tokens=64, prefix=3001, hidden=256, ffn=512),            # split output dims
+    LONG_SHAPES[0], LONG_SHAPES[1],                                             # 128-row blocks
+    synth.small_shape("mha_d128_3x65", n_q_heads=2, n_kv_heads=2, head_dim=128, batch=3,
+                      tokens=65, prefix=200, hidden=256, ffn=384),              # key halves
+], ids=lambda s: s.name)
+def test_attention_running_max_grows(shape):
+    """Cached keys scaled by a step (x0.25 on the first 64 of every 128 keys,
+    x2 on the next 64) on the attention-dominated block: in most key periods
+    a row's max jumps past the rescale threshold from one 64-key tile to the
+    next, so the rescale of the running output and sum runs in every
+    attention mode (its branch is taken when any row of a wave crosses).
+    The precondition is checked on the oracle's scores; the bound is the
+    attention-dominated one (2e-2 max|y|)."""
+    case = synth.block_case(shape, 0.1)
+    case = _keys_with_growing_max(shape, case)
+    w = dict(case["weights"])
+    w["w_down"] = synth.Bf16(np.zeros_like(w["w_down"].bits), np.zeros_like(w["w_down"].f32))
+    for st in case["streams"]:
+        xs = st["x"].f32 * np.float32(2.0 ** -6)
+        st["x"] = synth.Bf16(synth.f32_to_bf16_bits(xs), xs)
+    share = _share_of_rescales(shape, case, w)
+    say(f"{shape.name}: share of (row, period) pairs past the rescale threshold {share:.2f}")
+    assert share >= 0.25
+    y, _, _ = gpu_block(shape, case, w)
+    for b in range(shape.batch):
+        ry, _, _ = oracle_block(shape, case, b, weights=w)
+        e = max_err_ratio(y[b], ry)
+        say(f"  stream {b}: y {e:.2e}")
+        assert e <= 2e-2
+
+
 def test_ffn_branch_alone():
     shape = synth.AE_BLOCK
     case = synth.block_case(shape)
