@@ -185,8 +185,16 @@ LONG_SHAPES = [
 ]
 
 
+def _own_case(shape, qk_std=None):
+    """A block case whose stream entries may be replaced without touching
+    the cached one (synth.block_case is memoised)."""
+    case = dict(synth.block_case(shape, qk_std))
+    case["streams"] = [dict(st) for st in case["streams"]]
+    return case
+
+
 def _attention_dominated(shape, rows=None, streams=None):
-    case = synth.block_case(shape, 0.1)
+    case = _own_case(shape, 0.1)
     w = dict(case["weights"])
     w["w_down"] = synth.Bf16(np.zeros_like(w["w_down"].bits), np.zeros_like(w["w_down"].f32))
     for st in case["streams"]:
@@ -265,8 +273,7 @@ def test_attention_running_max_grows(shape):
     attention mode (its branch is taken when any row of a wave crosses).
     The precondition is checked on the oracle's scores; the bound is the
     attention-dominated one (2e-2 max|y|)."""
-    case = synth.block_case(shape, 0.1)
-    case = _keys_with_growing_max(shape, case)
+    case = _keys_with_growing_max(shape, _own_case(shape, 0.1))
     w = dict(case["weights"])
     w["w_down"] = synth.Bf16(np.zeros_like(w["w_down"].bits), np.zeros_like(w["w_down"].f32))
     for st in case["streams"]:
