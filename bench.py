@@ -51,11 +51,11 @@ OP_KERNELS = {
 # the SHA-256 of the kernel sources when the counters were taken: a changed
 # kernel reports null until it is profiled again.
 TRAFFIC = {
-    "qkv_rope": {"fetch": 6554892, "write": 622592, "bytes": 7177484, "sources": "ae32edf837ade30c"},
-    "attention": {"fetch": 6098272, "write": 2924544, "bytes": 9022816, "sources": "ae32edf837ade30c"},
-    "o_proj": {"fetch": 7698531, "write": 2364416, "bytes": 10062947, "sources": "ae32edf837ade30c"},
-    "gate_up": {"fetch": 17928358, "write": 1048576, "bytes": 18976934, "sources": "ae32edf837ade30c"},
-    "down": {"fetch": 13874179, "write": 2364416, "bytes": 16238595, "sources": "ae32edf837ade30c"},
+    "qkv_rope": {"fetch": 6569193, "write": 622592, "bytes": 7191785, "sources": "570addb6e6fbb8ce"},
+    "attention": {"fetch": 6098245, "write": 2924544, "bytes": 9022789, "sources": "570addb6e6fbb8ce"},
+    "o_proj": {"fetch": 6391381, "write": 2364416, "bytes": 8755797, "sources": "570addb6e6fbb8ce"},
+    "gate_up": {"fetch": 17930400, "write": 1048576, "bytes": 18978976, "sources": "570addb6e6fbb8ce"},
+    "down": {"fetch": 11118092, "write": 2364416, "bytes": 13482508, "sources": "570addb6e6fbb8ce"},
 }
 TRAFFIC_FETCH_SCALE = 2.000   # FETCH_SIZE of a 256 MiB copy reads 128 MiB
 TRAFFIC_WRITE_SCALE = 1.000   # WRITE_SIZE of the same copy reads 256 MiB
