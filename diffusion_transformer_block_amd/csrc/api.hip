@@ -488,7 +488,7 @@ bool small_plan_ok(const blk_config& c, int M, bool x_rowmajor) {
 // rows inside the denoise loop (x_frag / y_frag).
 void enqueue_block_small(const blk_config& c, const Layout& lay, const void* packed, int layer,
                          int B, int T, int P, const BlockIO& io, bool x_frag, bool y_frag, void* ws,
-                         const BlockWs& w, hipStream_t st) {
+                         const BlockWs& w, hipStream_t st, bool prefetch = false) {
   const int M = B * T, MT = mt_of(M);
   const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const uint8_t* lw = at<uint8_t>(packed, lay.layer0 + (size_t)layer * lay.layer_bytes);
@@ -542,7 +542,25 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     aa.part_o = at<bf16_t>(ws, w.sm_att_o);
     aa.part_ml = at<float>(ws, w.sm_att_ml);
-    launch_attn_sm(aa, d, st);
+    // (prefetch: the denoise loop, whose layers' weights stream from HBM)
+    // Workgroups beside the attention's tasks read the layer's O and gate/up
+    // weights, so those launches find them in the memory-side cache rather
+    // than in HBM: 128 of them took the 18 x 10 loop 7.33 -> 7.21 ms (96
+    // made the attention's tail wait for the prefetch, 176 crowded it;
+    // gate/up prefetched from the O launch slowed O by more than gate/up
+    // gained).  A single block call may find its weights resident, where the
+    // prefetch costs about 1 us (the 64-token stage 39.4 -> 40.45 us; four
+    // 16-token chunks replayed on one layer 48.6 -> 50.8 us), against 0.2 us
+    // saved when they are cold, so it is left to the loop; small ranges (the
+    // 16-token block's 1.2 MB: 17.20 -> 17.8 us) fit the cache anyway and
+    // are never fetched.
+    Prefetch pf;
+    if (prefetch && lay.wd - lay.wo >= ((size_t)8 << 20)) {
+      pf.p = lw + lay.wo;
+      pf.bytes = lay.wd - lay.wo;
+      pf.wgs = 128;
+    }
+    launch_attn_sm(aa, d, st, pf);
     op_done(BLK_OP_ATTENTION);
   }
   // 3. h = x + O W_o
@@ -825,7 +843,7 @@ void enqueue_flow(const blk_config& c, const Layout& lay, const void* packed, in
     for (int l = 0; l < n_layers; ++l) {
       BlockIO io{X[cur],  kp[l],  vp[l], 0, X[cur ^ 1], at<bf16_t>(ws, fw.kn),
                  at<bf16_t>(ws, fw.vn), 0};
-      enqueue_block_small(c, lay, packed, l, 1, T, P, io, true, true, ws, fw.blk, st);
+      enqueue_block_small(c, lay, packed, l, 1, T, P, io, true, true, ws, fw.blk, st, true);
       cur ^= 1;
     }
     FlowVelArgs va{X[cur],

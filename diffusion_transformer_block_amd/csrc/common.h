@@ -9,6 +9,14 @@
 
 namespace blk {
 
+// Bytes that later kernels read, fetched by `wgs` extra workgroups of a
+// launch while its tasks run.
+struct Prefetch {
+  const uint8_t* p = nullptr;
+  size_t bytes = 0;
+  int wgs = 0;
+};
+
 typedef uint16_t bf16_t;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -279,6 +287,27 @@ __host__ __device__ inline int col_of_group(const ColMapArgs& m, int g, int i) {
   }
   if (m.mode == kColGateUp) return i == 0 ? 16 * g : m.half_n + 16 * g;
   return 32 * g + 16 * i;
+}
+
+// An extra workgroup's share of the prefetch range: read (plain loads, so the
+// lines allocate in the memory-side cache) and dropped.
+__device__ inline void prefetch_range(const Prefetch& f, int i) {
+  const size_t n16 = f.bytes / 16;
+  const size_t per = (n16 + f.wgs - 1) / f.wgs;
+  const size_t b0 = (size_t)i * per, b1 = min(n16, b0 + per);
+  const uint4* p = reinterpret_cast<const uint4*>(f.p);
+  unsigned x = 0;
+  for (size_t j = b0 + threadIdx.x; j < b1; j += 256 * 8) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t k = j + 256 * u;
+      v[u] = k < b1 ? p[k] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x ^= v[u].x;
+  }
+  asm volatile("" ::"v"(x));
 }
 
 }  // namespace blk

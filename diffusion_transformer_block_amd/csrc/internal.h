@@ -199,7 +199,7 @@ void launch_sk_gateup(const SkArgs& ga, int gpw, const EpiGateUpS& e, hipStream_
 void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps, int* long_rows);
 size_t attn_sm_part_o_elems(int B, int T, int P, int Hq, int Hkv, int d);
 size_t attn_sm_part_ml_floats(int B, int T, int P, int Hq, int Hkv, int d);
-void launch_attn_sm(const AttnSmArgs& a, int head_dim, hipStream_t st);
+void launch_attn_sm(const AttnSmArgs& a, int head_dim, hipStream_t st, const Prefetch& pf = {});
 
 // ---------------------------------------------------------------- flow head
 struct FlowEmbedArgs {

@@ -263,13 +263,17 @@ void launch_sk_gateup(const SkArgs& ga, int gpw, const EpiGateUpS& e, hipStream_
 // ============================================================================ attention
 // (128-row mode: registers capped for two workgroups per compute unit)
 template <int HD, bool LONG, bool DSPLIT = false>
-__global__ __launch_bounds__(256, LONG ? 2 : 1) void attn_sm_kernel(AttnSmArgs a, int n_rb) {
+__global__ __launch_bounds__(256, LONG ? 2 : 1) void attn_sm_kernel(AttnSmArgs a, int n_rb, Prefetch pf) {
   extern __shared__ __attribute__((aligned(16))) char at_dsm[];
   // Tasks in the order (stream x kv head, key slice, row block), row block
   // fastest; the hardware deals workgroups round-robin over the 8 XCDs, so
   // hand each XCD a contiguous run of tasks: the row blocks that read the
-  // same K/V tiles then share one L2.
-  const int nwg = gridDim.x, id = blockIdx.x;
+  // same K/V tiles then share one L2.  Workgroups past the tasks prefetch.
+  const int nwg = (int)gridDim.x - pf.wgs, id = blockIdx.x;
+  if (id >= nwg) {
+    prefetch_range(pf, id - nwg);
+    return;
+  }
   const int xcd = id & 7, jx = id >> 3, qx = nwg >> 3, rx = nwg & 7;
   const int task = xcd * qx + min(xcd, rx) + jx;
   const int rb = task % n_rb, rest = task / n_rb;
@@ -285,7 +289,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnSmArgs a) {
 }
 
 template <int HD, bool LONG, bool DSPLIT = false>
-static void attn_sm_launch(const AttnSmArgs& a, hipStream_t st) {
+static void attn_sm_launch(const AttnSmArgs& a, Prefetch pf, hipStream_t st) {
   auto kern = attn_sm_kernel<HD, LONG, DSPLIT>;
   const size_t smem = sizeof(AttnSmSmem<HD>);
   static bool attr_set = false;
@@ -296,16 +300,19 @@ static void attn_sm_launch(const AttnSmArgs& a, hipStream_t st) {
   }
   const int G = a.Hq / a.Hkv;
   const int n_rb = (G * a.T + (LONG ? 127 : 63)) / (LONG ? 128 : 64);
-  hipLaunchKernelGGL(kern, dim3(a.splits * n_rb * a.B * a.Hkv), dim3(256), smem, st, a, n_rb);
+  const int n_task = a.splits * n_rb * a.B * a.Hkv;
+  // prefetch workgroups only on compute units the tasks leave free
+  pf.wgs = pf.p ? std::max(0, std::min(pf.wgs, device_cus() - n_task)) : 0;
+  hipLaunchKernelGGL(kern, dim3(n_task + pf.wgs), dim3(256), smem, st, a, n_rb, pf);
 }
 
 template <int HD>
-static void attn_sm_go(const AttnSmArgs& a, hipStream_t st) {
+static void attn_sm_go(const AttnSmArgs& a, const Prefetch& pf, hipStream_t st) {
   // (at HD 256 the 128-row variant spills; 64-row blocks over the one slice)
   bool launched = false;
   if constexpr (HD <= 128) {
     if (a.long_rows) {
-      attn_sm_launch<HD, true>(a, st);
+      attn_sm_launch<HD, true>(a, pf, st);
       launched = true;
     }
   }
@@ -315,9 +322,9 @@ static void attn_sm_go(const AttnSmArgs& a, hipStream_t st) {
   // than the merge saves (the 16-token block 17.25 -> 17.42 us)
   if (!launched) {
     if constexpr (HD == 256)
-      attn_sm_launch<HD, false, true>(a, st);
+      attn_sm_launch<HD, false, true>(a, pf, st);
     else
-      attn_sm_launch<HD, false>(a, st);
+      attn_sm_launch<HD, false>(a, pf, st);
   }
   if (a.splits > 1) {
     const int items = attn_combine_items(a.B, a.T, a.Hq, a.Hkv, HD);
@@ -325,11 +332,11 @@ static void attn_sm_go(const AttnSmArgs& a, hipStream_t st) {
   }
 }
 
-void launch_attn_sm(const AttnSmArgs& a, int head_dim, hipStream_t st) {
+void launch_attn_sm(const AttnSmArgs& a, int head_dim, hipStream_t st, const Prefetch& pf) {
   switch (head_dim) {
-    case 64: attn_sm_go<64>(a, st); break;
-    case 128: attn_sm_go<128>(a, st); break;
-    default: attn_sm_go<256>(a, st); break;
+    case 64: attn_sm_go<64>(a, pf, st); break;
+    case 128: attn_sm_go<128>(a, pf, st); break;
+    default: attn_sm_go<256>(a, pf, st); break;
   }
 }
 
