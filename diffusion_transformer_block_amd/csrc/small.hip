@@ -263,12 +263,25 @@ void launch_sk_gateup(const SkArgs& ga, int gpw, const EpiGateUpS& e, hipStream_
 // ============================================================================ attention
 // (128-row mode: registers capped for two workgroups per compute unit)
 template <int HD, bool LONG, bool DSPLIT = false>
-__global__ __launch_bounds__(256, LONG ? 2 : 1) void attn_sm_kernel(AttnSmArgs a, int n_rb, Prefetch pf) {
+__global__ __launch_bounds__(256, LONG ? 2 : 1) void attn_sm_kernel(AttnSmArgs a, int n_rb) {
   extern __shared__ __attribute__((aligned(16))) char at_dsm[];
   // Tasks in the order (stream x kv head, key slice, row block), row block
   // fastest; the hardware deals workgroups round-robin over the 8 XCDs, so
   // hand each XCD a contiguous run of tasks: the row blocks that read the
-  // same K/V tiles then share one L2.  Workgroups past the tasks prefetch.
+  // same K/V tiles then share one L2.
+  const int nwg = gridDim.x, id = blockIdx.x;
+  const int xcd = id & 7, jx = id >> 3, qx = nwg >> 3, rx = nwg & 7;
+  const int task = xcd * qx + min(xcd, rx) + jx;
+  const int rb = task % n_rb, rest = task / n_rb;
+  const int ks = rest % a.splits, bh = rest / a.splits;
+  attn_sm_task<HD, LONG, DSPLIT>(a, bh, rb, ks, *reinterpret_cast<AttnSmSmem<HD>*>(at_dsm), NoWait{});
+}
+
+// The same tasks plus pf.wgs workgroups past them that prefetch (a kernel of
+// its own: the extra argument and branch cost the plain launch 0.3 us).
+template <int HD, bool LONG, bool DSPLIT = false>
+__global__ __launch_bounds__(256, LONG ? 2 : 1) void attn_sm_pf_kernel(AttnSmArgs a, int n_rb, Prefetch pf) {
+  extern __shared__ __attribute__((aligned(16))) char at_dsm[];
   const int nwg = (int)gridDim.x - pf.wgs, id = blockIdx.x;
   if (id >= nwg) {
     prefetch_range(pf, id - nwg);
@@ -290,20 +303,31 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnSmArgs a) {
 
 template <int HD, bool LONG, bool DSPLIT = false>
 static void attn_sm_launch(const AttnSmArgs& a, Prefetch pf, hipStream_t st) {
-  auto kern = attn_sm_kernel<HD, LONG, DSPLIT>;
   const size_t smem = sizeof(AttnSmSmem<HD>);
+  const int G = a.Hq / a.Hkv;
+  const int n_rb = (G * a.T + (LONG ? 127 : 63)) / (LONG ? 128 : 64);
+  const int n_task = a.splits * n_rb * a.B * a.Hkv;
+  // prefetch workgroups only on compute units the tasks leave free
+  pf.wgs = pf.p ? std::max(0, std::min(pf.wgs, device_cus() - n_task)) : 0;
+  if (pf.wgs > 0) {
+    auto kern = attn_sm_pf_kernel<HD, LONG, DSPLIT>;
+    static bool attr_set = false;
+    if (!attr_set) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+      attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(n_task + pf.wgs), dim3(256), smem, st, a, n_rb, pf);
+    return;
+  }
+  auto kern = attn_sm_kernel<HD, LONG, DSPLIT>;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     attr_set = true;
   }
-  const int G = a.Hq / a.Hkv;
-  const int n_rb = (G * a.T + (LONG ? 127 : 63)) / (LONG ? 128 : 64);
-  const int n_task = a.splits * n_rb * a.B * a.Hkv;
-  // prefetch workgroups only on compute units the tasks leave free
-  pf.wgs = pf.p ? std::max(0, std::min(pf.wgs, device_cus() - n_task)) : 0;
-  hipLaunchKernelGGL(kern, dim3(n_task + pf.wgs), dim3(256), smem, st, a, n_rb, pf);
+  hipLaunchKernelGGL(kern, dim3(n_task), dim3(256), smem, st, a, n_rb);
 }
 
 template <int HD>
