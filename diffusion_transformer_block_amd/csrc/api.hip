@@ -542,7 +542,8 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     aa.part_o = at<bf16_t>(ws, w.sm_att_o);
     aa.part_ml = at<float>(ws, w.sm_att_ml);
-    // (prefetch: the denoise loop, whose layers' weights stream from HBM)
+    // (prefetch: chains of layers -- the denoise loop, the prefix stage --
+    // whose weights stream from HBM)
     // Workgroups beside the attention's tasks read the layer's O and gate/up
     // weights, so those launches find them in the memory-side cache rather
     // than in HBM: 128 of them took the 18 x 10 loop 7.33 -> 7.21 ms (96
@@ -551,7 +552,7 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     // gained).  A single block call may find its weights resident, where the
     // prefetch costs about 1 us (the 64-token stage 39.4 -> 40.45 us; four
     // 16-token chunks replayed on one layer 48.6 -> 50.8 us), against 0.2 us
-    // saved when they are cold, so it is left to the loop; small ranges (the
+    // saved when they are cold, so it is left to chains of layers; small ranges (the
     // 16-token block's 1.2 MB: 17.20 -> 17.8 us) fit the cache anyway and
     // are never fetched.
     Prefetch pf;
