@@ -51,11 +51,11 @@ OP_KERNELS = {
 # the SHA-256 of the kernel sources when the counters were taken: a changed
 # kernel reports null until it is profiled again.
 TRAFFIC = {
-    "qkv_rope": {"fetch": 6569236, "write": 622592, "bytes": 7191828, "sources": "6326a437073ad7ba"},
-    "attention": {"fetch": 6087904, "write": 2924544, "bytes": 9012448, "sources": "6326a437073ad7ba"},
-    "o_proj": {"fetch": 6391004, "write": 2364416, "bytes": 8755420, "sources": "6326a437073ad7ba"},
-    "gate_up": {"fetch": 17930462, "write": 1048576, "bytes": 18979038, "sources": "6326a437073ad7ba"},
-    "down": {"fetch": 11119021, "write": 2364416, "bytes": 13483437, "sources": "6326a437073ad7ba"},
+    "qkv_rope": {"fetch": 6569238, "write": 622592, "bytes": 7191830, "sources": "6326a437073ad7ba"},
+    "attention": {"fetch": 6087882, "write": 2924544, "bytes": 9012426, "sources": "6326a437073ad7ba"},
+    "o_proj": {"fetch": 6391377, "write": 2364416, "bytes": 8755793, "sources": "6326a437073ad7ba"},
+    "gate_up": {"fetch": 17930463, "write": 1048576, "bytes": 18979039, "sources": "6326a437073ad7ba"},
+    "down": {"fetch": 11118772, "write": 2364416, "bytes": 13483188, "sources": "6326a437073ad7ba"},
 }
 TRAFFIC_FETCH_SCALE = 2.000   # FETCH_SIZE of a 256 MiB copy reads 128 MiB
 TRAFFIC_WRITE_SCALE = 1.000   # WRITE_SIZE of the same copy reads 256 MiB
