@@ -717,8 +717,11 @@ def _gpu_prefill(shape, layers, x, max_pos):
 
 @pytest.mark.parametrize("shape,tokens", [
     (synth.AE_BLOCK, 768),                                                   # large-chunk path
+    # small path at the action-expert width: its attention launch also
+    # prefetches each layer's O and gate/up weights
+    (synth.AE_BLOCK, 48),
     (synth.small_shape("prefill_small", batch=1, n_kv_heads=1), 37),         # small path, ragged
-], ids=["ae_768", "small_37"])
+], ids=["ae_768", "ae_48", "small_37"])
 @pytest.mark.timeout(600)
 def test_prefix_prefill_caches(shape, tokens):
     """Three prefix layers: each layer's K (after RoPE) and V against the
