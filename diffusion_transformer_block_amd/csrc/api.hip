@@ -488,7 +488,8 @@ bool small_plan_ok(const blk_config& c, int M, bool x_rowmajor) {
 // rows inside the denoise loop (x_frag / y_frag).
 void enqueue_block_small(const blk_config& c, const Layout& lay, const void* packed, int layer,
                          int B, int T, int P, const BlockIO& io, bool x_frag, bool y_frag, void* ws,
-                         const BlockWs& w, hipStream_t st, bool prefetch = false) {
+                         const BlockWs& w, hipStream_t st, bool prefetch = false,
+                         const uint8_t* next_qkv = nullptr) {
   const int M = B * T, MT = mt_of(M);
   const int D = c.hidden, F = c.ffn, d = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const uint8_t* lw = at<uint8_t>(packed, lay.layer0 + (size_t)layer * lay.layer_bytes);
@@ -602,7 +603,15 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     ga.splits = p.splits;
     ga.counters = at<unsigned>(ws, w.ctr_d);
     EpiResidS e{h, 1, MT, nullptr, io.y, y_frag ? 1 : 0, MT, 0, D};
-    launch_sk_resid(ga, p.gpw, e, st);
+    // (next_qkv: the next layer's QKV weights, in the denoise loop) one
+    // prefetching workgroup per task reads them on the compute units the
+    // split GEMM leaves free: the loop 7.30 -> 7.16 ms (one box)
+    Prefetch pf;
+    if (prefetch && next_qkv && lay.wo - lay.wqkv >= ((size_t)4 << 20)) {
+      pf.p = next_qkv;
+      pf.bytes = lay.wo - lay.wqkv;
+    }
+    launch_sk_resid(ga, p.gpw, e, st, pf);
     op_done(BLK_OP_DOWN);
   }
 }
@@ -855,7 +864,10 @@ void enqueue_flow(const blk_config& c, const Layout& lay, const void* packed, in
     for (int l = 0; l < n_layers; ++l) {
       BlockIO io{X[cur],  kp[l],  vp[l], 0, X[cur ^ 1], at<bf16_t>(ws, fw.kn),
                  at<bf16_t>(ws, fw.vn), 0};
-      enqueue_block_small(c, lay, packed, l, 1, T, P, io, true, true, ws, fw.blk, st, true);
+      const uint8_t* next_qkv =
+          l + 1 < n_layers ? at<uint8_t>(packed, lay.layer0 + (size_t)(l + 1) * lay.layer_bytes + lay.wqkv)
+                           : nullptr;
+      enqueue_block_small(c, lay, packed, l, 1, T, P, io, true, true, ws, fw.blk, st, true, next_qkv);
       cur ^= 1;
     }
     FlowVelArgs va{X[cur],

@@ -193,7 +193,8 @@ SkPlan sk_plan(int M, int K, int n_groups, bool a_rowmajor);
 size_t sk_part_floats(int M, int K, int n_groups, bool a_rowmajor);
 int sk_nb(int KW, int gpw, int MT, int max_nb);
 void launch_sk_qkv(const SkArgs& ga, int gpw, bool a_rowmajor, const EpiQkvS& e, hipStream_t st);
-void launch_sk_resid(const SkArgs& ga, int gpw, const EpiResidS& e, hipStream_t st);
+void launch_sk_resid(const SkArgs& ga, int gpw, const EpiResidS& e, hipStream_t st,
+                     const Prefetch& pf = {});
 void launch_sk_gateup(const SkArgs& ga, int gpw, const EpiGateUpS& e, hipStream_t st);
 // long_rows: set to 1 for 128-row blocks over one key slice (NULL: 64-row blocks only)
 void attn_sm_plan(int B, int T, int P, int Hq, int Hkv, int* splits, int* kps, int* long_rows);

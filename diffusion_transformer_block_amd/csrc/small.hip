@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <cmath>
 
 #include "attn_small.h"
@@ -207,8 +208,30 @@ __global__ __launch_bounds__(256) void sk_kernel(SkArgs ga, Epi epi) {
                                   NoWait{});
 }
 
+// The same tasks plus a second grid layer of workgroups that prefetch (a
+// kernel of its own, so launches without a prefetch keep the plain one).
 template <int MT, int NB, int GPW, bool RMS, bool AROW, class Epi>
-static void sk_go(const SkArgs& ga, const Epi& e, hipStream_t st) {
+__global__ __launch_bounds__(256) void sk_pf_kernel(SkArgs ga, Epi epi, Prefetch pf) {
+  extern __shared__ __attribute__((aligned(16))) char sk_dsm[];
+  if (blockIdx.z != 0) {
+    prefetch_range(pf, (int)(blockIdx.x + blockIdx.y * gridDim.x));
+    return;
+  }
+  int gx = (int)blockIdx.x, split = (int)blockIdx.y;
+  if (gridDim.y > 1) {
+    const int nx = (int)gridDim.x, n = nx * (int)gridDim.y;
+    const int id = gx + split * nx;
+    const int xcd = id & 7, jx = id >> 3, qx = n >> 3, rx = n & 7;
+    const int task = xcd * qx + min(xcd, rx) + jx;
+    split = task / nx;
+    gx = task - split * nx;
+  }
+  sk_task<MT, NB, GPW, RMS, AROW>(ga, epi, gx, split, *reinterpret_cast<SkSmem<AROW, GPW>*>(sk_dsm),
+                                  NoWait{});
+}
+
+template <int MT, int NB, int GPW, bool RMS, bool AROW, class Epi>
+static void sk_go(const SkArgs& ga, const Epi& e, hipStream_t st, Prefetch pf) {
   auto kern = sk_kernel<MT, NB, GPW, RMS, AROW, Epi>;
   const size_t smem = sizeof(SkSmem<AROW, GPW>);
   static bool attr_set = false;
@@ -217,35 +240,51 @@ static void sk_go(const SkArgs& ga, const Epi& e, hipStream_t st) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3((ga.n_groups + GPW - 1) / GPW, ga.splits), dim3(256), smem, st, ga, e);
+  const int nx = (ga.n_groups + GPW - 1) / GPW;
+  // (only the residual launches prefetch: the denoise loop's down projections)
+  if constexpr (std::is_same_v<Epi, EpiResidS>) {
+    if (pf.p) {
+      auto kp = sk_pf_kernel<MT, NB, GPW, RMS, AROW, Epi>;
+      static bool pf_attr_set = false;
+      if (!pf_attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kp),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        pf_attr_set = true;
+      }
+      pf.wgs = nx * ga.splits;
+      hipLaunchKernelGGL(kp, dim3(nx, ga.splits, 2), dim3(256), smem, st, ga, e, pf);
+      return;
+    }
+  }
+  hipLaunchKernelGGL(kern, dim3(nx, ga.splits), dim3(256), smem, st, ga, e);
 }
 
 template <int MT, int GPW, bool RMS, bool AROW, class Epi>
-static void sk_go_nb(const SkArgs& ga, const Epi& e, hipStream_t st) {
+static void sk_go_nb(const SkArgs& ga, const Epi& e, hipStream_t st, const Prefetch& pf) {
   switch (sk_nb(ga.K / 32 / ga.splits / 4, GPW, MT, RMS ? 4 : 8)) {
-    case 8: sk_go<MT, 8, GPW, RMS, AROW>(ga, e, st); break;
-    case 4: sk_go<MT, 4, GPW, RMS, AROW>(ga, e, st); break;
-    case 2: sk_go<MT, 2, GPW, RMS, AROW>(ga, e, st); break;
-    default: sk_go<MT, 1, GPW, RMS, AROW>(ga, e, st); break;
+    case 8: sk_go<MT, 8, GPW, RMS, AROW>(ga, e, st, pf); break;
+    case 4: sk_go<MT, 4, GPW, RMS, AROW>(ga, e, st, pf); break;
+    case 2: sk_go<MT, 2, GPW, RMS, AROW>(ga, e, st, pf); break;
+    default: sk_go<MT, 1, GPW, RMS, AROW>(ga, e, st, pf); break;
   }
 }
 
 template <int MT, bool RMS, bool AROW, class Epi>
-static void sk_go_gpw(const SkArgs& ga, int gpw, const Epi& e, hipStream_t st) {
+static void sk_go_gpw(const SkArgs& ga, int gpw, const Epi& e, hipStream_t st, const Prefetch& pf) {
   if constexpr (kSkPlanMaxGpw >= 2) {
-    if (gpw == 2) return sk_go_nb<MT, 2, RMS, AROW>(ga, e, st);
+    if (gpw == 2) return sk_go_nb<MT, 2, RMS, AROW>(ga, e, st, pf);
   }
   (void)gpw;
-  sk_go_nb<MT, 1, RMS, AROW>(ga, e, st);
+  sk_go_nb<MT, 1, RMS, AROW>(ga, e, st, pf);
 }
 
 template <bool RMS, bool AROW, class Epi>
-static void sk_launch(const SkArgs& ga, int gpw, const Epi& e, hipStream_t st) {
+static void sk_launch(const SkArgs& ga, int gpw, const Epi& e, hipStream_t st, const Prefetch& pf = {}) {
   switch (mt_of(ga.M)) {
-    case 1: sk_go_gpw<1, RMS, AROW>(ga, gpw, e, st); break;
-    case 2: sk_go_gpw<2, RMS, AROW>(ga, gpw, e, st); break;
-    case 3: sk_go_gpw<3, RMS, AROW>(ga, gpw, e, st); break;
-    default: sk_go_gpw<4, RMS, AROW>(ga, gpw, e, st); break;
+    case 1: sk_go_gpw<1, RMS, AROW>(ga, gpw, e, st, pf); break;
+    case 2: sk_go_gpw<2, RMS, AROW>(ga, gpw, e, st, pf); break;
+    case 3: sk_go_gpw<3, RMS, AROW>(ga, gpw, e, st, pf); break;
+    default: sk_go_gpw<4, RMS, AROW>(ga, gpw, e, st, pf); break;
   }
 }
 
@@ -253,8 +292,8 @@ void launch_sk_qkv(const SkArgs& ga, int gpw, bool a_rowmajor, const EpiQkvS& e,
   if (a_rowmajor) sk_launch<true, true>(ga, gpw, e, st);
   else sk_launch<true, false>(ga, gpw, e, st);
 }
-void launch_sk_resid(const SkArgs& ga, int gpw, const EpiResidS& e, hipStream_t st) {
-  sk_launch<false, false>(ga, gpw, e, st);
+void launch_sk_resid(const SkArgs& ga, int gpw, const EpiResidS& e, hipStream_t st, const Prefetch& pf) {
+  sk_launch<false, false>(ga, gpw, e, st, pf);
 }
 void launch_sk_gateup(const SkArgs& ga, int gpw, const EpiGateUpS& e, hipStream_t st) {
   sk_launch<true, false>(ga, gpw, e, st);
