@@ -51,11 +51,11 @@ OP_KERNELS = {
 # the SHA-256 of the kernel sources when the counters were taken: a changed
 # kernel reports null until it is profiled again.
 TRAFFIC = {
-    "qkv_rope": {"fetch": 6569238, "write": 622592, "bytes": 7191830, "sources": "6326a437073ad7ba"},
-    "attention": {"fetch": 6087882, "write": 2924544, "bytes": 9012426, "sources": "6326a437073ad7ba"},
-    "o_proj": {"fetch": 6391377, "write": 2364416, "bytes": 8755793, "sources": "6326a437073ad7ba"},
-    "gate_up": {"fetch": 17930463, "write": 1048576, "bytes": 18979039, "sources": "6326a437073ad7ba"},
-    "down": {"fetch": 11118772, "write": 2364416, "bytes": 13483188, "sources": "6326a437073ad7ba"},
+    "qkv_rope": {"fetch": 6571292, "write": 622592, "bytes": 7193884, "sources": "047b3779ec37c6af"},
+    "attention": {"fetch": 6098413, "write": 2924544, "bytes": 9022957, "sources": "047b3779ec37c6af"},
+    "o_proj": {"fetch": 6389343, "write": 2364416, "bytes": 8753759, "sources": "047b3779ec37c6af"},
+    "gate_up": {"fetch": 17909966, "write": 1048576, "bytes": 18958542, "sources": "047b3779ec37c6af"},
+    "down": {"fetch": 11121739, "write": 2364416, "bytes": 13486155, "sources": "047b3779ec37c6af"},
 }
 TRAFFIC_FETCH_SCALE = 2.000   # FETCH_SIZE of a 256 MiB copy reads 128 MiB
 TRAFFIC_WRITE_SCALE = 1.000   # WRITE_SIZE of the same copy reads 256 MiB
