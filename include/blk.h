@@ -239,6 +239,9 @@ int blk_forward_noalloc(const blk_config* cfg, const void* packed, int layer, in
  * v_cache[l] (host arrays of n_layers device pointers, each bf16 [T][Hkv][d],
  * 16-byte aligned); the last layer computes only its keys and values.
  * ws: device workspace (query with ws == NULL), zero-filled before first use.
+ * Where a layer's attention leaves compute units free, its launch carries
+ * extra workgroups that read the layer's O and gate/up weights ahead of their
+ * GEMMs (the weights of a chain of layers stream from HBM).
  * Asynchronous on `stream`.  Errors: BLK_EINVAL, BLK_EUNSUPPORTED, BLK_ESIZE,
  * BLK_ESTATE, BLK_EHIP.
  */
@@ -259,7 +262,11 @@ int prefix_prefill(const blk_config* cfg, const void* packed, int n_layers, int 
  *   actions  device float32 [N][A]  a_{n_steps} (also the loop's running state)
  *   ws       device workspace (query with ws == NULL), zero-filled before first use
  * `packed` must hold a flow head prepared for exactly n_steps steps and at
- * least n_layers layers.  The whole loop is captured once into a hipGraph
+ * least n_layers layers.  Each layer's attention launch carries extra
+ * workgroups that read its O and gate/up weights, and its down projection
+ * workgroups that read the next layer's QKV weights, ahead of those launches
+ * (the weights of 18 layers stream from HBM every step).  The whole loop is
+ * captured once into a hipGraph
  * keyed on (packed, n_layers, n_steps, P, every pointer argument); later calls
  * with the same key replay it with one launch, a changed key captures anew
  * (capture synchronizes the device once).  The key's buffers must stay valid
