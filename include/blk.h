@@ -262,12 +262,12 @@ int prefix_prefill(const blk_config* cfg, const void* packed, int n_layers, int 
  *   actions  device float32 [N][A]  a_{n_steps} (also the loop's running state)
  *   ws       device workspace (query with ws == NULL), zero-filled before first use
  * `packed` must hold a flow head prepared for exactly n_steps steps and at
- * least n_layers layers.  Each layer's attention launch carries extra
- * workgroups that read its O and gate/up weights, and its down projection
- * workgroups that read the next layer's QKV weights, ahead of those launches
- * (the weights of 18 layers stream from HBM every step).  The whole loop is
- * captured once into a hipGraph
- * keyed on (packed, n_layers, n_steps, P, every pointer argument); later calls
+ * least n_layers layers.  For layers whose O + gate/up weights reach 8 MiB
+ * (and QKV weights 4 MiB), each attention launch carries extra workgroups that
+ * read the layer's O and gate/up weights, and each down projection workgroups
+ * that read the next layer's QKV weights, ahead of those launches (a stack of
+ * layers streams its weights from HBM every step).  The whole loop is
+ * captured once into a hipGraph keyed on (packed, n_layers, n_steps, P, every pointer argument); later calls
  * with the same key replay it with one launch, a changed key captures anew
  * (capture synchronizes the device once).  The key's buffers must stay valid
  * while the graph is cached (until blk_release or re-capture).
