@@ -239,9 +239,10 @@ int blk_forward_noalloc(const blk_config* cfg, const void* packed, int layer, in
  * v_cache[l] (host arrays of n_layers device pointers, each bf16 [T][Hkv][d],
  * 16-byte aligned); the last layer computes only its keys and values.
  * ws: device workspace (query with ws == NULL), zero-filled before first use.
- * Where a layer's attention leaves compute units free, its launch carries
- * extra workgroups that read the layer's O and gate/up weights ahead of their
- * GEMMs (the weights of a chain of layers stream from HBM).
+ * Where a layer's attention leaves compute units free and its O + gate/up
+ * weights reach 8 MiB, the attention launch carries extra workgroups that
+ * read those weights ahead of their GEMMs (the weights of a chain of layers
+ * stream from HBM).
  * Asynchronous on `stream`.  Errors: BLK_EINVAL, BLK_EUNSUPPORTED, BLK_ESIZE,
  * BLK_ESTATE, BLK_EHIP.
  */
