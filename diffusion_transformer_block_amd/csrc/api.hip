@@ -553,9 +553,9 @@ void enqueue_block_small(const blk_config& c, const Layout& lay, const void* pac
     // gained).  A single block call may find its weights resident, where the
     // prefetch costs about 1 us (the 64-token stage 39.4 -> 40.45 us; four
     // 16-token chunks replayed on one layer 48.6 -> 50.8 us), against 0.2 us
-    // saved when they are cold, so it is left to chains of layers; small ranges (the
-    // 16-token block's 1.2 MB: 17.20 -> 17.8 us) fit the cache anyway and
-    // are never fetched.
+    // saved when they are cold, so it is left to chains of layers.  Small
+    // ranges (the 16-token block's 1.2 MB: 17.20 -> 17.8 us) fit the cache
+    // anyway and are never fetched.
     Prefetch pf;
     if (prefetch && lay.wd - lay.wo >= ((size_t)8 << 20)) {
       pf.p = lw + lay.wo;
